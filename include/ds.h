@@ -1,0 +1,208 @@
+/*
+ * ds.h -- C ABI of the Double Sparsity decode-attention library (libds.so),
+ * HIP kernels for gfx950 (MI355X).
+ *
+ * Pages cited by title and section:
+ *   [DS]    "Double Sparsity" article, joto.ai blog archive 2025060420469:
+ *           "offline calibration" (heavy channels are fixed offline per
+ *           layer and head; their K values are copied into a contiguous label
+ *           cache at prefill and only the new token's values are added at each
+ *           decode step; labels may be kept in 4 bits) and "online forward
+ *           computation" (step 1 gathers the query at the heavy channels,
+ *           step 2 scores every cached token approximately from the labels,
+ *           step 3 picks the top-k tokens and runs exact attention on their
+ *           full K/V rows); "use in SGLang" (heavy-channel count, heavy-token
+ *           count, dense fallback below a threshold).
+ *   [LeanK] LeanK article, aitangshan.cn news 1293675, section 2.2 (a static,
+ *           hardware-aligned subset of K channels is kept per head) and
+ *           section 3.2 (attention over the pruned K).
+ *   [GQA]   grouped-query attention article, trdm.cn news 80600, section 4
+ *           (query heads form groups that share one K/V head).
+ *
+ * Conventions for every call:
+ *   - Pointers are device memory owned by the caller unless marked "host".
+ *     The library allocates nothing, keeps no state between calls and never
+ *     synchronises the stream.
+ *   - fp16 is IEEE binary16.  All arrays are row-major, last index fastest.
+ *   - Work is enqueued asynchronously on `stream`.  Arguments are validated on
+ *     the host before anything is enqueued; on any error the call returns a
+ *     negative ds_status and enqueues nothing.  A failed kernel launch returns
+ *     DS_ERR_HIP.  Values that live in device memory (index tables, sequence
+ *     lengths, positions) are not read by the host: out-of-range sequence
+ *     lengths are clamped on the device to [0, max_seq_len], out-of-range
+ *     positions are skipped; out-of-range channel or token indices in the
+ *     tables are undefined behaviour.
+ *   - Calls that share buffers must be ordered by the caller (same stream).
+ */
+#ifndef DS_H_
+#define DS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DS_ABI_VERSION 1
+
+typedef enum {
+  DS_OK = 0,
+  DS_ERR_ARG = -1,       /* missing pointer, bad enum value, bad range */
+  DS_ERR_SHAPE = -2,     /* inconsistent or unsupported dimensions */
+  DS_ERR_DTYPE = -3,     /* label dtype / channel count combination not supported */
+  DS_ERR_ALIGN = -4,     /* pointer or stride breaks the 16-byte alignment rule */
+  DS_ERR_WORKSPACE = -5, /* workspace missing or smaller than required */
+  DS_ERR_HIP = -6        /* the HIP runtime rejected a launch */
+} ds_status;
+
+/* Label cache element type ([DS] offline calibration: 4-bit labels). */
+typedef enum { DS_LABEL_F16 = 0, DS_LABEL_INT4 = 1 } ds_label_dtype;
+
+/* K/V cache description (host struct).
+ *   K: fp16 [batch][n_kv_heads][capacity][d_k], element strides k_stride =
+ *      {batch, kv head, token}; channel stride 1.
+ *   V: fp16 [batch][n_kv_heads][capacity][d_v], strides v_stride likewise.
+ * Query head h belongs to KV head h / G with G = n_q_heads / n_kv_heads
+ * ([GQA] section 4: consecutive query heads form a group).
+ * d_q is the query width (the model's head dim); d_k is the stored K width,
+ * equal to d_q unless K is LeanK-compacted to a kept subset of its columns.
+ * Limits: d_q <= 256; d_k and d_v multiples of 8 with d_k <= 128 and
+ * d_v == 128; G <= 8; capacity <= 2^24.
+ * Alignment: K, V 16-byte aligned; every stride a multiple of 8 elements. */
+typedef struct {
+  int32_t batch, n_q_heads, n_kv_heads;
+  int32_t d_q, d_k, d_v;
+  int32_t capacity;
+  int32_t reserved0; /* must be 0 */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+} ds_kv_desc;
+
+/* Label cache description (host struct) ([DS] offline calibration).
+ *   r      heavy channels per KV head, 1 <= r <= min(d_k, 128); even for INT4.
+ *   slots  token slots per (batch, KV head) row: slots >= capacity and
+ *          slots % 16 == 0 (keeps every row 16-byte aligned).
+ *   F16:   codes = fp16 [batch][n_kv_heads][slots][r]; scales = NULL.
+ *          Entry j of token t is K[b][g][t][chan[g][j]], bit for bit.
+ *   INT4:  codes = uint8 [batch][n_kv_heads][slots][r/2];
+ *          scales = fp16 [batch][n_kv_heads][slots].
+ *          Per token: amax = max_j |x_j| over its r heavy values (fp32),
+ *          scale = fp16_rn(amax / 7) (IEEE fp32 division), code_j =
+ *          clamp(round_half_even(x_j / scale), -7, 7) (IEEE fp32 division;
+ *          scale 0 gives code 0); byte i holds code 2i in its low nibble and
+ *          code 2i+1 in its high nibble, two's complement.
+ *   codes and scales are 16-byte aligned. */
+typedef struct {
+  int32_t r;
+  int32_t dtype; /* ds_label_dtype */
+  int32_t slots;
+  int32_t reserved0; /* must be 0 */
+  void* codes;
+  void* scales;
+} ds_label_desc;
+
+/* Label-cache build at prefill ([DS] offline calibration: every prefill
+ * token's heavy-channel values go from the K cache into the label cache).
+ * Writes label slots t in [t_begin, t_end) of every (batch, KV head) row.
+ *   K     fp16 K cache as described by kv (read only).
+ *   chan  int32 [n_kv_heads][r]: heavy channels, indices into the stored K
+ *         columns (0 <= chan < d_k); any order, duplicates allowed.
+ * Only batch, n_kv_heads, d_k, capacity and k_stride of kv are read.
+ * Errors: DS_ERR_ARG (null pointer, 0 <= t_begin <= t_end <= capacity
+ * violated), DS_ERR_SHAPE, DS_ERR_DTYPE, DS_ERR_ALIGN, DS_ERR_HIP. */
+ds_status ds_label_build(const ds_kv_desc* kv, const void* K, const int32_t* chan,
+                         const ds_label_desc* lab, int32_t t_begin, int32_t t_end,
+                         hipStream_t stream);
+
+/* Label-cache append at a decode step ([DS] offline calibration: only the new
+ * token's heavy-channel values are added).  For each batch row b, writes label
+ * slot pos[b] of every KV head from K[b][g][pos[b]].
+ *   pos   int32 [batch] device array: the slot whose K row was just written;
+ *         rows with pos[b] < 0 or pos[b] >= capacity are left untouched.
+ * The result is bit-identical to ds_label_build over the same slots.
+ * Errors: as ds_label_build. */
+ds_status ds_label_append(const ds_kv_desc* kv, const void* K, const int32_t* chan,
+                          const ds_label_desc* lab, const int32_t* pos, hipStream_t stream);
+
+/* Stages of ds_decode_attn, for optional timing events. */
+enum {
+  DS_STAGE_APPEND = 0,  /* label append of the current token (flag DS_DECODE_APPEND) */
+  DS_STAGE_SCORE = 1,   /* steps 1-2: query gather + approximate scores */
+  DS_STAGE_SELECT = 2,  /* step 3a: top-k select */
+  DS_STAGE_ATTN = 3,    /* step 3b: exact attention over the selected rows */
+  DS_STAGE_COMBINE = 4, /* merge of split partial results */
+  DS_STAGE_COUNT = 5
+};
+
+/* Flags for ds_decode_opts.flags. */
+#define DS_DECODE_APPEND 1u         /* first append label slot seq_lens[b]-1 (as ds_label_append) */
+#define DS_DECODE_VALIDATE_ONLY 2u  /* validate the arguments and return; enqueue nothing */
+#define DS_DECODE_UNFUSED 4u        /* force the separate score and select kernels */
+
+/* Optional decode settings (host struct; pass NULL for defaults). */
+typedef struct {
+  int32_t n_split;   /* 0: automatic; otherwise the number of partitions of each
+                        row's selected tokens in the attention pass (clamped to
+                        the range the workspace was sized for) */
+  uint32_t flags;    /* DS_DECODE_* */
+  hipEvent_t* stage_events; /* NULL, or DS_STAGE_COUNT + 1 events: event i is
+                               recorded on `stream` before stage i, the last one
+                               after the final stage (stages that launch nothing
+                               give empty intervals) */
+} ds_decode_opts;
+
+/* Workspace bytes that ds_decode_attn needs for these arguments (0 if they
+ * are invalid).  Depends only on the shapes, k and max_seq_len. */
+size_t ds_decode_attn_workspace_size(const ds_kv_desc* kv, const ds_label_desc* lab, int32_t k,
+                                     int32_t max_seq_len);
+
+/* One Double Sparsity decode step over all (batch, KV head) rows
+ * ([DS] online forward computation, steps 1-3):
+ *   1. qg[j] = sum over the group's query heads h of q[b][h][keep[g][chan[g][j]]]
+ *      (the group shares one token set, so its approximate score is read as
+ *      the sum of its heads' scores);
+ *   2. s[t] = sum_j qg[j] * label[b][g][t][j] (INT4: scale[t] * sum_j qg[j] *
+ *      code[t][j]) for t < S = seq_lens[b];
+ *   3. T = the min(k, S) tokens with the largest s, ties to the lower index;
+ *      each query head h of the group then gets exact softmax attention
+ *      o_h = sum_{t in T} softmax_t(sm_scale * q_h . K_t) V_t, with q_h read at
+ *      keep[g][c] for stored K column c ([LeanK] section 2.2).
+ * With k <= 0 every row attends all S tokens and no label is read (chan and
+ * lab may be NULL); with k >= S that row attends all its tokens (the dense
+ * fallback of [DS] "use in SGLang").  A row with S = 0 gets a zero output.
+ *   q           fp16 [batch][n_q_heads][d_q].
+ *   K, V        the caches (kv); the current token must already be written.
+ *   seq_lens    int32 [batch] device array: tokens per row, current included.
+ *   max_seq_len host upper bound of seq_lens (sizes the grid), <= capacity.
+ *   keep        int32 [n_kv_heads][d_k] device array: query channel of each
+ *               stored K column (LeanK); NULL means column c is channel c
+ *               (then d_k must equal d_q).
+ *   chan, lab   heavy channels and label cache as for ds_label_build.
+ *   sm_scale    softmax scale (e.g. 1/sqrt(head dim)).
+ *   out         fp16 [batch][n_q_heads][d_v]; fp32 accumulation.
+ *   topk_idx    NULL, or int32 [batch][n_kv_heads][k] receiving each row's
+ *               selected tokens in ascending order, padded with -1.
+ *   workspace   device scratch of at least ds_decode_attn_workspace_size()
+ *               bytes, 256-byte aligned; contents need no initialisation.
+ * Errors: DS_ERR_ARG, DS_ERR_SHAPE, DS_ERR_DTYPE, DS_ERR_ALIGN,
+ * DS_ERR_WORKSPACE, DS_ERR_HIP. */
+ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, const void* V,
+                         const int32_t* seq_lens, int32_t max_seq_len, const int32_t* keep,
+                         const int32_t* chan, const ds_label_desc* lab, int32_t k, float sm_scale,
+                         void* out, int32_t* topk_idx, void* workspace, size_t workspace_bytes,
+                         const ds_decode_opts* opts, hipStream_t stream);
+
+/* Static text for a status code (never NULL). */
+const char* ds_status_str(ds_status s);
+
+/* DS_ABI_VERSION of the loaded library. */
+int32_t ds_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DS_H_ */

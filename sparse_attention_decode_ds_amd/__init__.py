@@ -1,0 +1,231 @@
+"""Python binding of libds.so: Double Sparsity decode attention on MI355X.
+
+Argument marshalling only.  Every step of the path runs in the HIP kernels of
+``libds.so`` (see ``include/ds.h`` for the contract); PyTorch only provides
+device memory and the current stream.  If the library is missing, every call
+raises: there is no fallback path.
+
+Pages (cited by title and section): "Double Sparsity" article (joto.ai blog
+archive 2025060420469), sections "offline calibration" (label cache) and
+"online forward computation" (steps 1-3); LeanK article (aitangshan.cn news
+1293675) section 2.2 (the ``keep`` table); grouped-query attention article
+(trdm.cn news 80600) section 4.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libds.so")
+
+DS_OK = 0
+STATUS = {0: "DS_OK", -1: "DS_ERR_ARG", -2: "DS_ERR_SHAPE", -3: "DS_ERR_DTYPE",
+          -4: "DS_ERR_ALIGN", -5: "DS_ERR_WORKSPACE", -6: "DS_ERR_HIP"}
+LABEL_F16 = 0
+LABEL_INT4 = 1
+STAGE_COUNT = 5
+STAGES = ("append", "score", "select", "attn", "combine")
+DECODE_APPEND = 1
+DECODE_VALIDATE_ONLY = 2
+DECODE_UNFUSED = 4
+EXPORTS = ("ds_label_build", "ds_label_append", "ds_decode_attn_workspace_size",
+           "ds_decode_attn", "ds_status_str", "ds_abi_version")
+
+
+class DsError(RuntimeError):
+    def __init__(self, fn, code):
+        self.code = code
+        super().__init__("%s failed: %s (%d)" % (fn, STATUS.get(code, "?"), code))
+
+
+class KVDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("d_q", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("k_stride", ctypes.c_int64 * 3), ("v_stride", ctypes.c_int64 * 3)]
+
+
+class LabelDesc(ctypes.Structure):
+    _fields_ = [("r", ctypes.c_int32), ("dtype", ctypes.c_int32), ("slots", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p)]
+
+
+class DecodeOpts(ctypes.Structure):
+    _fields_ = [("n_split", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("stage_events", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libds.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libds.so is not built (run __graft_entry__.build()); "
+                              "there is no fallback path")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I32 = ctypes.c_void_p, ctypes.c_int32
+        lib.ds_label_build.argtypes = [P, P, P, P, I32, I32, P]
+        lib.ds_label_build.restype = ctypes.c_int
+        lib.ds_label_append.argtypes = [P, P, P, P, P, P]
+        lib.ds_label_append.restype = ctypes.c_int
+        lib.ds_decode_attn_workspace_size.argtypes = [P, P, I32, I32]
+        lib.ds_decode_attn_workspace_size.restype = ctypes.c_size_t
+        lib.ds_decode_attn.argtypes = [P, P, P, P, P, I32, P, P, P, I32, ctypes.c_float, P, P, P,
+                                       ctypes.c_size_t, P, P]
+        lib.ds_decode_attn.restype = ctypes.c_int
+        lib.ds_status_str.argtypes = [ctypes.c_int]
+        lib.ds_status_str.restype = ctypes.c_char_p
+        lib.ds_abi_version.argtypes = []
+        lib.ds_abi_version.restype = I32
+        _lib = lib
+    return _lib
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    if torch.cuda.is_available():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(0)
+
+
+def _check(fn, code):
+    if code != DS_OK:
+        raise DsError(fn, code)
+
+
+def kv_desc(K, V, n_q_heads: int, d_q: int | None = None) -> KVDesc:
+    """Describe K [B][H_kv][cap][d_k] and V [B][H_kv][cap][d_v] (fp16, unit channel stride)."""
+    B, Hkv, cap, d_k = K.shape
+    d = KVDesc()
+    d.batch, d.n_q_heads, d.n_kv_heads = B, n_q_heads, Hkv
+    d.d_q = d_k if d_q is None else d_q
+    d.d_k, d.d_v, d.capacity = d_k, V.shape[3], cap
+    for i in range(3):
+        d.k_stride[i] = K.stride(i)
+        d.v_stride[i] = V.stride(i)
+    return d
+
+
+@dataclass
+class LabelCache:
+    """Label-cache storage: fp16 [B][H_kv][slots][r], or int4 codes uint8
+    [B][H_kv][slots][r/2] + fp16 scales [B][H_kv][slots]."""
+    r: int
+    dtype: int
+    slots: int
+    codes: torch.Tensor
+    scales: torch.Tensor | None
+
+    @staticmethod
+    def allocate(B, Hkv, capacity, r, int4: bool, device="cuda"):
+        slots = (capacity + 63) // 64 * 64
+        if int4:
+            codes = torch.zeros((B, Hkv, slots, r // 2), dtype=torch.uint8, device=device)
+            scales = torch.zeros((B, Hkv, slots), dtype=torch.float16, device=device)
+            return LabelCache(r, LABEL_INT4, slots, codes, scales)
+        codes = torch.zeros((B, Hkv, slots, r), dtype=torch.float16, device=device)
+        return LabelCache(r, LABEL_F16, slots, codes, None)
+
+    def desc(self) -> LabelDesc:
+        d = LabelDesc()
+        d.r, d.dtype, d.slots, d.reserved0 = self.r, self.dtype, self.slots, 0
+        d.codes = self.codes.data_ptr()
+        d.scales = self.scales.data_ptr() if self.scales is not None else None
+        return d
+
+
+def label_build(K, chan, labels: LabelCache, t_begin: int, t_end: int, stream=None):
+    kv = kv_desc(K, K, 1)
+    lab = labels.desc()
+    _check("ds_label_build", load().ds_label_build(
+        ctypes.byref(kv), _p(K), _p(chan), ctypes.byref(lab), int(t_begin), int(t_end),
+        _stream(stream)))
+
+
+def label_append(K, chan, labels: LabelCache, pos, stream=None):
+    kv = kv_desc(K, K, 1)
+    lab = labels.desc()
+    _check("ds_label_append", load().ds_label_append(
+        ctypes.byref(kv), _p(K), _p(chan), ctypes.byref(lab), _p(pos), _stream(stream)))
+
+
+def workspace_size(K, V, n_q_heads, d_q, labels: LabelCache | None, k, max_seq_len) -> int:
+    kv = kv_desc(K, V, n_q_heads, d_q)
+    lab = labels.desc() if labels is not None else None
+    return int(load().ds_decode_attn_workspace_size(
+        ctypes.byref(kv), ctypes.byref(lab) if lab is not None else None, int(k), int(max_seq_len)))
+
+
+def decode_attn(q, K, V, seq_lens, max_seq_len: int, k: int, sm_scale: float,
+                chan=None, labels: LabelCache | None = None, keep=None, out=None,
+                topk_idx=None, workspace=None, n_split: int = 0, flags: int = 0,
+                stage_events=None, stream=None):
+    """One decode step (ds_decode_attn).  Returns ``out`` fp16 [B][H_q][d_v].
+    ``stage_events``: optional ctypes array of STAGE_COUNT + 1 hipEvent_t."""
+    B, Hq, d_q = q.shape
+    kv = kv_desc(K, V, Hq, d_q)
+    lab = labels.desc() if labels is not None else None
+    lib = load()
+    need = int(lib.ds_decode_attn_workspace_size(
+        ctypes.byref(kv), ctypes.byref(lab) if lab is not None else None, int(k),
+        int(max_seq_len)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, V.shape[3]), dtype=torch.float16, device=q.device)
+    opts = DecodeOpts()
+    opts.n_split, opts.flags = int(n_split), int(flags)
+    opts.stage_events = ctypes.cast(stage_events, ctypes.c_void_p) if stage_events is not None else None
+    _check("ds_decode_attn", lib.ds_decode_attn(
+        ctypes.byref(kv), _p(q), _p(K), _p(V), _p(seq_lens), int(max_seq_len), _p(keep), _p(chan),
+        ctypes.byref(lab) if lab is not None else None, int(k), float(sm_scale), _p(out),
+        _p(topk_idx), _p(workspace), workspace.numel() * workspace.element_size(),
+        ctypes.byref(opts), _stream(stream)))
+    return out
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (for the stage_events option and kernel timing)."""
+
+    def __init__(self, n: int):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                  ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.handles = (ctypes.c_void_p * n)()
+        for i in range(n):
+            rc = self._hip.hipEventCreate(ctypes.byref(self.handles, i * ctypes.sizeof(ctypes.c_void_p)))
+            if rc != 0:
+                raise RuntimeError("hipEventCreate failed: %d" % rc)
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = ctypes.c_float()
+        rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), self.handles[i], self.handles[j])
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return ms.value
+
+    def synchronize(self, i: int):
+        self._hip.hipEventSynchronize(self.handles[i])
+
+    def close(self):
+        for h in self.handles:
+            if h:
+                self._hip.hipEventDestroy(h)
+        self.handles = (ctypes.c_void_p * 0)()

@@ -1,0 +1,336 @@
+// api.hip -- the extern "C" entry points declared in ds.h: host-side
+// validation, workspace planning and kernel launches on the caller's stream.
+//
+// Pages cited by title and section:
+//   [DS]    "Double Sparsity" article, joto.ai blog archive 2025060420469,
+//           sections "offline calibration", "online forward computation"
+//           and "use in SGLang" (heavy-token count k; dense below threshold).
+//   [LeanK] LeanK article, aitangshan.cn news 1293675, section 2.2.
+//   [GQA]   grouped-query attention article, trdm.cn news 80600, section 4.
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "ds_internal.h"
+
+namespace ds {
+namespace {
+
+constexpr int64_t kMaxCapacity = int64_t(1) << 24;
+constexpr int kScoreChunk = 4096;      // tokens per chunked-score workgroup
+constexpr int kTargetAttnBlocks = 1024;
+constexpr int kMinTokensPerSplit = 64;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// K-side fields (all calls) and, for decode, the query and V fields.
+ds_status check_kv(const ds_kv_desc* kv, bool decode) {
+  if (!kv || kv->reserved0 != 0) return DS_ERR_ARG;
+  if (kv->batch < 1 || kv->n_kv_heads < 1) return DS_ERR_SHAPE;
+  if (kv->d_k < 8 || kv->d_k > 128 || kv->d_k % 8) return DS_ERR_SHAPE;
+  if (kv->capacity < 1 || kv->capacity > kMaxCapacity) return DS_ERR_SHAPE;
+  for (int i = 0; i < 3; ++i) {
+    if (kv->k_stride[i] < 0) return DS_ERR_SHAPE;
+    if (kv->k_stride[i] % 8) return DS_ERR_ALIGN;
+  }
+  if (!decode) return DS_OK;
+  if (kv->n_q_heads < 1 || kv->n_q_heads % kv->n_kv_heads) return DS_ERR_SHAPE;
+  if (kv->n_q_heads / kv->n_kv_heads > kMaxGroup) return DS_ERR_SHAPE;
+  if (kv->d_q < 1 || kv->d_q > 256) return DS_ERR_SHAPE;
+  if (kv->d_v != kDv) return DS_ERR_SHAPE;
+  for (int i = 0; i < 3; ++i) {
+    if (kv->v_stride[i] < 0) return DS_ERR_SHAPE;
+    if (kv->v_stride[i] % 8) return DS_ERR_ALIGN;
+  }
+  return DS_OK;
+}
+
+ds_status check_lab(const ds_kv_desc* kv, const ds_label_desc* lab) {
+  if (!lab || lab->reserved0 != 0) return DS_ERR_ARG;
+  if (lab->dtype != DS_LABEL_F16 && lab->dtype != DS_LABEL_INT4) return DS_ERR_DTYPE;
+  if (lab->r < 1 || lab->r > std::min(kv->d_k, 128)) return DS_ERR_SHAPE;
+  if (lab->dtype == DS_LABEL_INT4 && (lab->r & 1)) return DS_ERR_DTYPE;
+  if (lab->slots < kv->capacity || lab->slots % 16) return DS_ERR_SHAPE;
+  if (!lab->codes) return DS_ERR_ARG;
+  if (!aligned16(lab->codes)) return DS_ERR_ALIGN;
+  if (lab->dtype == DS_LABEL_INT4) {
+    if (!lab->scales) return DS_ERR_ARG;
+    if (!aligned16(lab->scales)) return DS_ERR_ALIGN;
+  }
+  return DS_OK;
+}
+
+LabelArgs label_args(const ds_kv_desc* kv, const void* K, const int32_t* chan,
+                     const ds_label_desc* lab) {
+  LabelArgs a;
+  memset(&a, 0, sizeof(a));
+  a.K = static_cast<const __half*>(K);
+  a.ks0 = kv->k_stride[0];
+  a.ks1 = kv->k_stride[1];
+  a.ks2 = kv->k_stride[2];
+  a.Hkv = kv->n_kv_heads;
+  a.d_k = kv->d_k;
+  a.cap = kv->capacity;
+  a.chan = chan;
+  a.r = lab->r;
+  a.is_int4 = lab->dtype == DS_LABEL_INT4;
+  a.slots = lab->slots;
+  if (a.is_int4) {
+    a.codes = static_cast<uint8_t*>(lab->codes);
+    a.scales = static_cast<__half*>(lab->scales);
+  } else {
+    a.lab16 = static_cast<__half*>(lab->codes);
+  }
+  return a;
+}
+
+// Everything ds_decode_attn derives from the shapes alone.
+struct Plan {
+  bool sparse;
+  int kk;           // tokens attended per row at most
+  int idx_cap;      // workspace index slots per row
+  int keys_stride;  // workspace key words per row
+  int n_chunks;
+  int split_cap;
+  size_t off_count, off_idx, off_keys, off_part, total;
+};
+
+Plan make_plan(const ds_kv_desc* kv, int k, int max_seq) {
+  Plan p;
+  memset(&p, 0, sizeof(p));
+  const int64_t rows = (int64_t)kv->batch * kv->n_kv_heads;
+  p.sparse = k > 0;
+  p.kk = p.sparse ? std::min(k, max_seq) : max_seq;
+  p.idx_cap = p.sparse ? std::max(p.kk, 1) : 0;
+  p.keys_stride = p.sparse ? (int)round_up(std::max(max_seq, 1), 64) : 0;
+  p.n_chunks = (int)std::max<int64_t>(1, ceil_div(max_seq, kScoreChunk));
+  p.split_cap = (int)std::min<int64_t>(kMaxSplit, std::max<int64_t>(1, ceil_div(p.kk, 16)));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (size_t)round_up((int64_t)bytes, 256);
+    return at;
+  };
+  p.off_count = take(rows * sizeof(int32_t));
+  p.off_idx = take(rows * (size_t)p.idx_cap * sizeof(int32_t));
+  p.off_keys = take(rows * (size_t)p.keys_stride * sizeof(uint32_t));
+  p.off_part = take((size_t)kv->batch * kv->n_q_heads * p.split_cap * kPartStride * sizeof(float));
+  p.total = off;
+  return p;
+}
+
+int auto_splits(const Plan& p, int64_t rows, int requested) {
+  int ns;
+  if (requested > 0) {
+    ns = requested;
+  } else {
+    ns = (int)ceil_div(kTargetAttnBlocks, std::max<int64_t>(rows, 1));
+    ns = (int)std::min<int64_t>(ns, std::max<int64_t>(1, ceil_div(p.kk, kMinTokensPerSplit)));
+  }
+  return std::max(1, std::min(ns, p.split_cap));
+}
+
+}  // namespace
+}  // namespace ds
+
+using namespace ds;
+
+extern "C" {
+
+const char* ds_status_str(ds_status s) {
+  switch (s) {
+    case DS_OK: return "ok";
+    case DS_ERR_ARG: return "invalid argument";
+    case DS_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case DS_ERR_DTYPE: return "unsupported label dtype";
+    case DS_ERR_ALIGN: return "misaligned pointer or stride";
+    case DS_ERR_WORKSPACE: return "workspace too small";
+    case DS_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t ds_abi_version(void) { return DS_ABI_VERSION; }
+
+ds_status ds_label_build(const ds_kv_desc* kv, const void* K, const int32_t* chan,
+                         const ds_label_desc* lab, int32_t t_begin, int32_t t_end,
+                         hipStream_t stream) {
+  ds_status st = check_kv(kv, false);
+  if (st) return st;
+  if ((st = check_lab(kv, lab))) return st;
+  if (!K || !chan) return DS_ERR_ARG;
+  if (!aligned16(K)) return DS_ERR_ALIGN;
+  if (t_begin < 0 || t_end < t_begin || t_end > kv->capacity) return DS_ERR_ARG;
+  if (t_end == t_begin) return DS_OK;
+  LabelArgs a = label_args(kv, K, chan, lab);
+  a.t_begin = t_begin;
+  a.t_end = t_end;
+  a.tiles_per_row = (int)ceil_div(t_end - t_begin, 64);
+  const int64_t blocks = (int64_t)kv->batch * kv->n_kv_heads * a.tiles_per_row;
+  if (blocks > INT32_MAX / 256) return DS_ERR_SHAPE;
+  return launch_label(a, (int)blocks, stream) == hipSuccess ? DS_OK : DS_ERR_HIP;
+}
+
+ds_status ds_label_append(const ds_kv_desc* kv, const void* K, const int32_t* chan,
+                          const ds_label_desc* lab, const int32_t* pos, hipStream_t stream) {
+  ds_status st = check_kv(kv, false);
+  if (st) return st;
+  if ((st = check_lab(kv, lab))) return st;
+  if (!K || !chan || !pos) return DS_ERR_ARG;
+  if (!aligned16(K)) return DS_ERR_ALIGN;
+  LabelArgs a = label_args(kv, K, chan, lab);
+  a.pos = pos;
+  a.n_items = kv->batch * kv->n_kv_heads;
+  return launch_label(a, (int)ceil_div(a.n_items, 64), stream) == hipSuccess ? DS_OK : DS_ERR_HIP;
+}
+
+size_t ds_decode_attn_workspace_size(const ds_kv_desc* kv, const ds_label_desc* lab, int32_t k,
+                                     int32_t max_seq_len) {
+  if (check_kv(kv, true)) return 0;
+  if (k > 0 && check_lab(kv, lab)) return 0;
+  if (max_seq_len < 0 || max_seq_len > kv->capacity) return 0;
+  return make_plan(kv, k, max_seq_len).total;
+}
+
+ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, const void* V,
+                         const int32_t* seq_lens, int32_t max_seq_len, const int32_t* keep,
+                         const int32_t* chan, const ds_label_desc* lab, int32_t k, float sm_scale,
+                         void* out, int32_t* topk_idx, void* workspace, size_t workspace_bytes,
+                         const ds_decode_opts* opts, hipStream_t stream) {
+  ds_status st = check_kv(kv, true);
+  if (st) return st;
+  const bool sparse = k > 0;
+  if (sparse) {
+    if ((st = check_lab(kv, lab))) return st;
+    if (!chan) return DS_ERR_ARG;
+  }
+  if (!q || !K || !V || !seq_lens || !out) return DS_ERR_ARG;
+  if (!aligned16(K) || !aligned16(V) || !aligned16(out)) return DS_ERR_ALIGN;
+  if (!keep && kv->d_k != kv->d_q) return DS_ERR_SHAPE;
+  if (max_seq_len < 0 || max_seq_len > kv->capacity) return DS_ERR_ARG;
+  const uint32_t flags = opts ? opts->flags : 0u;
+  if (flags & ~(DS_DECODE_APPEND | DS_DECODE_VALIDATE_ONLY | DS_DECODE_UNFUSED)) return DS_ERR_ARG;
+  if (opts && opts->n_split < 0) return DS_ERR_ARG;
+  if ((flags & DS_DECODE_APPEND) && !sparse) return DS_ERR_ARG;
+  if (!std::isfinite(sm_scale)) return DS_ERR_ARG;
+
+  const Plan p = make_plan(kv, k, max_seq_len);
+  if (workspace_bytes < p.total) return DS_ERR_WORKSPACE;
+  if (p.total > 0 && !workspace) return DS_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DS_ERR_ALIGN;
+  if (flags & DS_DECODE_VALIDATE_ONLY) return DS_OK;
+
+  const int B = kv->batch, Hkv = kv->n_kv_heads, G = kv->n_q_heads / kv->n_kv_heads;
+  const int64_t rows = (int64_t)B * Hkv;
+  char* ws = static_cast<char*>(workspace);
+  hipEvent_t* ev = opts ? opts->stage_events : nullptr;
+  auto mark = [&](int i) {
+    if (ev) (void)hipEventRecord(ev[i], stream);
+  };
+
+  mark(DS_STAGE_APPEND);
+  if (flags & DS_DECODE_APPEND) {
+    LabelArgs la = label_args(kv, K, chan, lab);
+    la.pos = seq_lens;
+    la.pos_minus_one = 1;
+    la.n_items = (int)rows;
+    if (launch_label(la, (int)ceil_div(rows, 64), stream) != hipSuccess) return DS_ERR_HIP;
+  }
+
+  const int32_t* idx = nullptr;
+  int idx_stride = 0;
+  int32_t* count = reinterpret_cast<int32_t*>(ws + p.off_count);
+  mark(DS_STAGE_SCORE);
+  if (sparse) {
+    ScoreArgs sa;
+    memset(&sa, 0, sizeof(sa));
+    sa.q = static_cast<const __half*>(q);
+    sa.Hq = kv->n_q_heads;
+    sa.d_q = kv->d_q;
+    sa.Hkv = Hkv;
+    sa.G = G;
+    sa.d_k = kv->d_k;
+    sa.keep = keep;
+    sa.chan = chan;
+    sa.r = lab->r;
+    sa.is_int4 = lab->dtype == DS_LABEL_INT4;
+    sa.slots = lab->slots;
+    if (sa.is_int4) {
+      sa.codes = static_cast<const uint8_t*>(lab->codes);
+      sa.scales = static_cast<const __half*>(lab->scales);
+    } else {
+      sa.lab16 = static_cast<const __half*>(lab->codes);
+    }
+    sa.seq_lens = seq_lens;
+    sa.max_seq = max_seq_len;
+    sa.k = k;
+    if (topk_idx) {
+      sa.idx = topk_idx;
+      sa.idx_stride = k;
+      sa.pad_idx = 1;
+    } else {
+      sa.idx = reinterpret_cast<int32_t*>(ws + p.off_idx);
+      sa.idx_stride = p.idx_cap;
+    }
+    sa.count = count;
+    sa.keys = reinterpret_cast<uint32_t*>(ws + p.off_keys);
+    sa.keys_stride = p.keys_stride;
+    sa.chunk = kScoreChunk;
+    sa.n_chunks = p.n_chunks;
+    idx = sa.idx;
+    idx_stride = sa.idx_stride;
+    const bool fused = max_seq_len <= kFuseMaxTokens && !(flags & DS_DECODE_UNFUSED);
+    if (fused) {
+      if (launch_score_select_fused(sa, (int)rows, stream) != hipSuccess) return DS_ERR_HIP;
+      mark(DS_STAGE_SELECT);
+    } else {
+      if (launch_score_chunks(sa, (int)rows, stream) != hipSuccess) return DS_ERR_HIP;
+      mark(DS_STAGE_SELECT);
+      if (launch_select_stream(sa, (int)rows, stream) != hipSuccess) return DS_ERR_HIP;
+    }
+  } else {
+    mark(DS_STAGE_SELECT);
+  }
+
+  AttnArgs aa;
+  memset(&aa, 0, sizeof(aa));
+  aa.q = static_cast<const __half*>(q);
+  aa.Hq = kv->n_q_heads;
+  aa.d_q = kv->d_q;
+  aa.K = static_cast<const __half*>(K);
+  aa.V = static_cast<const __half*>(V);
+  aa.ks0 = kv->k_stride[0];
+  aa.ks1 = kv->k_stride[1];
+  aa.ks2 = kv->k_stride[2];
+  aa.vs0 = kv->v_stride[0];
+  aa.vs1 = kv->v_stride[1];
+  aa.vs2 = kv->v_stride[2];
+  aa.Hkv = Hkv;
+  aa.d_k = kv->d_k;
+  aa.keep = keep;
+  aa.seq_lens = seq_lens;
+  aa.max_seq = max_seq_len;
+  aa.sparse = sparse;
+  aa.idx = idx;
+  aa.idx_stride = idx_stride;
+  aa.count = count;
+  aa.n_split = auto_splits(p, rows, opts ? opts->n_split : 0);
+  aa.tps = (int)std::max<int64_t>(1, round_up(ceil_div(std::max(p.kk, 1), aa.n_split), 16));
+  aa.n_split = (int)std::max<int64_t>(1, ceil_div(std::max(p.kk, 1), aa.tps));
+  aa.scale_log2 = sm_scale * 1.4426950408889634f;
+  aa.out = static_cast<__half*>(out);
+  aa.part = reinterpret_cast<float*>(ws + p.off_part);
+
+  mark(DS_STAGE_ATTN);
+  const bool final_out = aa.n_split == 1;
+  if (launch_attn(aa, (int)rows, G, final_out, stream) != hipSuccess) return DS_ERR_HIP;
+  mark(DS_STAGE_COMBINE);
+  if (!final_out && launch_combine(aa, B, stream) != hipSuccess) return DS_ERR_HIP;
+  mark(DS_STAGE_COUNT);
+  return DS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+// ds_internal.h -- shared declarations of the HIP implementation behind ds.h.
+//
+// Pages cited by title and section:
+//   [DS]    "Double Sparsity" article, joto.ai blog archive 2025060420469,
+//           sections "offline calibration" and "online forward computation".
+//   [LeanK] LeanK article, aitangshan.cn news 1293675, section 2.2.
+//   [GQA]   grouped-query attention article, trdm.cn news 80600, section 4.
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ds.h"
+
+namespace ds {
+
+// Rows whose scores fit this many fp32 keys in LDS take the fused
+// score+select kernel (one workgroup per (batch, KV head) row).
+constexpr int kFuseMaxTokens = 16384;
+// Attention splits per row are capped; partial results cost 528 B each.
+constexpr int kMaxSplit = 64;
+// Selected-token indices staged in LDS per attention workgroup.
+constexpr int kMaxTokensPerSplit = 2048;
+// Partial-result record: o[128] fp32, then m (log2 domain), l; padded to 16 B.
+constexpr int kDv = 128;
+constexpr int kPartStride = kDv + 4;
+// Query heads per KV head handled by the attention kernel.
+constexpr int kMaxGroup = 8;
+
+// ---------------------------------------------------------------------------
+// Launch arguments (plain structs passed by value to the kernels).
+// ---------------------------------------------------------------------------
+struct LabelArgs {
+  const __half* K;
+  int64_t ks0, ks1, ks2;
+  int32_t Hkv, d_k, cap;
+  const int32_t* chan;
+  int32_t r, is_int4, slots;
+  __half* lab16;
+  uint8_t* codes;
+  __half* scales;
+  // build: tile -> (row, 64 consecutive tokens of [t_begin, t_end))
+  int32_t t_begin, t_end, tiles_per_row;
+  // append (pos != nullptr): item -> (row, pos[b]); n_items = B * Hkv
+  const int32_t* pos;
+  int32_t n_items;
+  // append driven by seq_lens (pos = seq_lens, token = seq_lens[b] - 1)
+  int32_t pos_minus_one;
+};
+
+struct ScoreArgs {
+  const __half* q;
+  int32_t Hq, d_q, Hkv, G, d_k;
+  const int32_t* keep;  // [Hkv][d_k] or null
+  const int32_t* chan;  // [Hkv][r]
+  int32_t r, is_int4, slots;
+  const __half* lab16;
+  const uint8_t* codes;
+  const __half* scales;
+  const int32_t* seq_lens;
+  int32_t max_seq;
+  int32_t k;
+  // outputs
+  int32_t* idx;         // [rows][idx_stride]
+  int32_t idx_stride;
+  int32_t pad_idx;      // write -1 after the selection up to idx_stride
+  int32_t* count;       // [rows]
+  uint32_t* keys;       // [rows][keys_stride] (chunked path)
+  int32_t keys_stride;
+  int32_t chunk;        // tokens per score workgroup (chunked path)
+  int32_t n_chunks;
+};
+
+struct AttnArgs {
+  const __half* q;
+  int32_t Hq, d_q;
+  const __half* K;
+  const __half* V;
+  int64_t ks0, ks1, ks2, vs0, vs1, vs2;
+  int32_t Hkv, d_k;
+  const int32_t* keep;
+  const int32_t* seq_lens;
+  int32_t max_seq;
+  int32_t sparse;
+  const int32_t* idx;
+  int32_t idx_stride;
+  const int32_t* count;
+  int32_t n_split, tps;
+  float scale_log2;
+  __half* out;
+  float* part;
+};
+
+// Launchers (return the launch status of the last kernel they enqueue).
+hipError_t launch_label(const LabelArgs& a, int n_blocks, hipStream_t s);
+hipError_t launch_score_select_fused(const ScoreArgs& a, int rows, hipStream_t s);
+hipError_t launch_score_chunks(const ScoreArgs& a, int rows, hipStream_t s);
+hipError_t launch_select_stream(const ScoreArgs& a, int rows, hipStream_t s);
+hipError_t launch_attn(const AttnArgs& a, int rows, int G, bool final_out, hipStream_t s);
+hipError_t launch_combine(const AttnArgs& a, int B, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Device helpers.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float h2f(__half h) { return __half2float(h); }
+
+__device__ __forceinline__ void unpack8(const uint4 v, float* f) {
+  const __half2* h = reinterpret_cast<const __half2*>(&v);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float2 x = __half22float2(h[i]);
+    f[2 * i] = x.x;
+    f[2 * i + 1] = x.y;
+  }
+}
+
+// Order-preserving map from fp32 to uint32 (larger value -> larger key);
+// -0 is folded onto +0 first.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive prefix sum of one uint32 per thread over a workgroup of NT
+// threads; `tmp` holds NT/64 words of LDS.  Contains two barriers.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[w] = x;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    uint32_t t = tmp[i];
+    before += (i < w) ? t : 0u;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + x - v;
+}
+
+// Sum over the 16 lanes of a row (lanes 16i .. 16i+15) with DPP moves:
+// swap neighbours, swap pairs, mirror within 8, mirror within 16.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));
+  return x;
+}
+
+}  // namespace ds

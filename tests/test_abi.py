@@ -1,0 +1,160 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/ds.h declares, and its host-side validation returns the documented
+status codes before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ds = pytest.importorskip("sparse_attention_decode_ds_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ds.LIB_PATH):
+        pytest.skip("libds.so not built")
+    return ds.load()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "ds.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ds_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(ds.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ds_abi_version() == 1
+    for code in range(0, -7, -1):
+        s = lib.ds_status_str(code).decode()
+        assert s and s != "unknown status"
+    assert lib.ds_status_str(-99).decode() == "unknown status"
+
+
+FAKE = 0x100000  # an aligned address; never dereferenced on these paths
+
+
+def _kv(**over):
+    d = ds.KVDesc()
+    vals = dict(batch=2, n_q_heads=28, n_kv_heads=4, d_q=128, d_k=128, d_v=128, capacity=1000)
+    vals.update({k: v for k, v in over.items() if not k.endswith("stride")})
+    for k, v in vals.items():
+        setattr(d, k, v)
+    ks = over.get("k_stride", (4 * 1000 * 128, 1000 * 128, 128))
+    vs = over.get("v_stride", (4 * 1000 * 128, 1000 * 128, 128))
+    for i in range(3):
+        d.k_stride[i] = ks[i]
+        d.v_stride[i] = vs[i]
+    return d
+
+
+def _lab(**over):
+    d = ds.LabelDesc()
+    vals = dict(r=16, dtype=ds.LABEL_F16, slots=1024, reserved0=0, codes=FAKE, scales=None)
+    vals.update(over)
+    for k, v in vals.items():
+        setattr(d, k, v)
+    return d
+
+
+def _decode(lib, kv=None, lab=None, k=64, max_seq=900, ws_bytes=1 << 30, flags=ds.DECODE_VALIDATE_ONLY,
+            q=FAKE, K=FAKE, V=FAKE, seq=FAKE, out=FAKE, chan=FAKE, keep=None, ws=FAKE,
+            n_split=0, scale=0.088):
+    kv = kv or _kv()
+    lab = lab if lab is not None else _lab()
+    opts = ds.DecodeOpts()
+    opts.n_split, opts.flags = n_split, flags
+    P = ctypes.c_void_p
+    return lib.ds_decode_attn(ctypes.byref(kv), P(q), P(K), P(V), P(seq), max_seq, P(keep),
+                              P(chan), ctypes.byref(lab) if lab is not False else None, k, scale,
+                              P(out), None, P(ws), ws_bytes, ctypes.byref(opts), None)
+
+
+def test_validate_only_accepts_good_arguments(lib):
+    assert _decode(lib) == 0
+    assert _decode(lib, k=0, lab=False, chan=None) == 0                    # dense, no labels
+    assert _decode(lib, lab=_lab(dtype=ds.LABEL_INT4, r=8, scales=FAKE)) == 0
+    kv = _kv(d_k=32, k_stride=(4 * 1000 * 32, 1000 * 32, 32))
+    assert _decode(lib, kv=kv, keep=FAKE, lab=_lab(r=8)) == 0                # LeanK
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(kv=_kv(n_q_heads=30)), -2),                 # heads not divisible
+    (dict(kv=_kv(n_q_heads=40, n_kv_heads=4)), -2),   # group of 10 > 8
+    (dict(kv=_kv(d_v=64)), -2),
+    (dict(kv=_kv(d_k=36)), -2),
+    (dict(kv=_kv(capacity=0)), -2),
+    (dict(kv=_kv(reserved0=1)), -1),
+    (dict(kv=_kv(k_stride=(4 * 1000 * 128, 1000 * 128, 132))), -4),
+    (dict(lab=_lab(r=0)), -2),
+    (dict(lab=_lab(r=129)), -2),
+    (dict(lab=_lab(dtype=ds.LABEL_INT4, r=7, scales=FAKE)), -3),
+    (dict(lab=_lab(dtype=5)), -3),
+    (dict(lab=_lab(slots=999)), -2),
+    (dict(lab=_lab(slots=1000 + 4)), -2),
+    (dict(lab=_lab(codes=None)), -1),
+    (dict(lab=_lab(codes=FAKE + 8)), -4),
+    (dict(lab=_lab(dtype=ds.LABEL_INT4, r=8, scales=None)), -1),
+    (dict(chan=None), -1),
+    (dict(q=None), -1),
+    (dict(out=FAKE + 2), -4),
+    (dict(K=FAKE + 4), -4),
+    (dict(max_seq=1001), -1),
+    (dict(max_seq=-1), -1),
+    (dict(ws_bytes=16), -5),
+    (dict(ws=None), -5),
+    (dict(ws=FAKE + 64), -4),
+    (dict(flags=ds.DECODE_VALIDATE_ONLY | 64), -1),
+    (dict(n_split=-2), -1),
+    (dict(k=0, lab=False, chan=None, flags=ds.DECODE_VALIDATE_ONLY | ds.DECODE_APPEND), -1),
+    (dict(kv=_kv(d_k=32, k_stride=(4 * 1000 * 32, 1000 * 32, 32)), lab=_lab(r=8)), -2),  # no keep
+    (dict(scale=float("nan")), -1),
+])
+def test_validation_errors(lib, case, code):
+    assert _decode(lib, **case) == code
+
+
+def test_workspace_size(lib):
+    kv = _kv()
+    lab = _lab()
+    n = lib.ds_decode_attn_workspace_size(ctypes.byref(kv), ctypes.byref(lab), 64, 900)
+    assert n > 0 and n % 256 == 0
+    assert _decode(lib, ws_bytes=n) == 0
+    assert _decode(lib, ws_bytes=n - 1) == -5
+    assert lib.ds_decode_attn_workspace_size(ctypes.byref(kv), ctypes.byref(lab), 64, 5000) == 0
+    assert lib.ds_decode_attn_workspace_size(ctypes.byref(_kv(d_v=7)), ctypes.byref(lab), 64, 9) == 0
+    assert lib.ds_decode_attn_workspace_size(ctypes.byref(kv), None, 0, 900) > 0
+
+
+def test_label_calls_validate_before_launch(lib):
+    kv = _kv()
+    P = ctypes.c_void_p
+    lab = _lab()
+    assert lib.ds_label_build(ctypes.byref(kv), P(FAKE), P(FAKE), ctypes.byref(lab), 5, 3, None) == -1
+    assert lib.ds_label_build(ctypes.byref(kv), P(FAKE), P(FAKE), ctypes.byref(lab), 0, 1001, None) == -1
+    assert lib.ds_label_build(ctypes.byref(kv), None, P(FAKE), ctypes.byref(lab), 0, 10, None) == -1
+    assert lib.ds_label_build(ctypes.byref(kv), P(FAKE + 2), P(FAKE), ctypes.byref(lab), 0, 10, None) == -4
+    assert lib.ds_label_build(ctypes.byref(kv), P(FAKE), P(FAKE), ctypes.byref(lab), 7, 7, None) == 0
+    # label calls read only the K-side fields of the descriptor
+    kq = _kv(n_q_heads=1, d_v=32, d_q=7)
+    assert lib.ds_label_build(ctypes.byref(kq), P(FAKE), P(FAKE), ctypes.byref(lab), 7, 7, None) == 0
+    bad = _lab(dtype=ds.LABEL_INT4, r=3, scales=FAKE)
+    assert lib.ds_label_append(ctypes.byref(kv), P(FAKE), P(FAKE), ctypes.byref(bad), P(FAKE), None) == -3
+    assert lib.ds_label_append(ctypes.byref(kv), P(FAKE), P(FAKE), ctypes.byref(lab), None, None) == -1
+
+
+def test_product_has_no_fallback():
+    """The binding refuses to run without the HIP library (no CPU path)."""
+    import importlib
+    mod = importlib.import_module("sparse_attention_decode_ds_amd")
+    src = open(mod.__file__).read()
+    assert "oracle" not in src.replace("there is no fallback", "")
+    assert "import oracle" not in src and "numpy" not in src

@@ -1,0 +1,288 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Needs an MI355X and the built libds.so."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import ds_check
+
+pytestmark = pytest.mark.gpu
+
+ds = pytest.importorskip("sparse_attention_decode_ds_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ds.load()
+    yield
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _note(msg):
+    print(msg, flush=True)
+
+
+def prefill(cfg, inp, upto):
+    labels = ds.LabelCache.allocate(cfg.B, cfg.Hkv, cfg.cap, cfg.r, cfg.int4)
+    ds.label_build(inp.K, inp.chan, labels, 0, upto)
+    return labels
+
+
+def run(cfg, inp, labels, seq_lens, max_seq, k=None, **kw):
+    k = cfg.k if k is None else k
+    topk = None
+    if k > 0:
+        topk = torch.full((cfg.B, cfg.Hkv, k), -7, dtype=torch.int32, device="cuda")
+    out = ds.decode_attn(inp.q, inp.K, inp.V, seq_lens, max_seq, k, cfg.sm_scale, chan=inp.chan,
+                         labels=labels if k > 0 else None, keep=inp.keep, topk_idx=topk, **kw)
+    torch.cuda.synchronize()
+    return out, topk
+
+
+# ---------------------------------------------------------------------------
+# label cache
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("r,int4", [(8, True), (16, True), (6, True), (16, False), (8, False),
+                                    (5, False)])
+def test_label_build_and_append_bitexact(r, int4):
+    cfg = synth.small("lab", B=3, Hq=4, Hkv=4, S0=197, steps=5, r=r, int4=int4, seed=31)
+    _note("label r=%d int4=%d" % (r, int4))
+    # strided K: the cache lives inside a larger buffer (token stride 136 elements)
+    big = synth.normal_tensor((cfg.B, cfg.Hkv, cfg.cap, 136), 5, 2, "cuda")
+    K = big[..., :128]
+    chan = torch.tensor([sorted(np.random.default_rng(g).choice(128, r, replace=False))
+                         for g in range(cfg.Hkv)], dtype=torch.int32, device="cuda")
+    labels = ds.LabelCache.allocate(cfg.B, cfg.Hkv, cfg.cap, r, int4)
+    ds.label_build(K, chan, labels, 0, 61)
+    ds.label_build(K, chan, labels, 61, cfg.S0)
+    for t in range(cfg.S0, cfg.cap):
+        pos = torch.tensor([t, t if t % 2 else -1, cfg.cap + 3], dtype=torch.int32, device="cuda")
+        ds.label_append(K, chan, labels, pos)
+    torch.cuda.synchronize()
+    Kh = K.cpu().numpy()
+    ref = oracle.Labels.empty(cfg.B, cfg.Hkv, labels.slots, r, int4)
+    oracle.label_build(Kh, chan.cpu().numpy(), ref, 0, cfg.S0)
+    for t in range(cfg.S0, cfg.cap):
+        oracle.label_append(Kh, chan.cpu().numpy(), ref,
+                            np.array([t, t if t % 2 else -1, cfg.cap + 3], np.int32))
+    if int4:
+        assert np.array_equal(labels.codes.cpu().numpy(), ref.codes)
+        assert np.array_equal(labels.scales.cpu().numpy().view(np.uint16), ref.scales)
+    else:
+        assert np.array_equal(labels.codes.cpu().numpy().view(np.uint16), ref.f16)
+
+
+def test_label_int4_golden_rows():
+    """The hand-worked int4 rows through the HIP label kernel."""
+    import json
+    import os
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                        "int4_label_cases.json")))["cases"]
+    cases = [c for c in cases if "x" in c]
+    K = torch.zeros((1, 1, len(cases), 128), dtype=torch.float16)
+    for i, c in enumerate(cases):
+        K[0, 0, i, :8] = torch.tensor(c["x"], dtype=torch.float16)
+    K = K.cuda()
+    chan = torch.arange(8, dtype=torch.int32, device="cuda")[None]
+    labels = ds.LabelCache.allocate(1, 1, len(cases), 8, True)
+    ds.label_build(K, chan, labels, 0, len(cases))
+    torch.cuda.synchronize()
+    for i, c in enumerate(cases):
+        assert labels.codes[0, 0, i].cpu().tolist() == c["bytes"], c["id"]
+        assert int(labels.scales[0, 0, i].cpu().view(torch.int16).item()) & 0xFFFF == c["scale_bits"]
+
+
+# ---------------------------------------------------------------------------
+# decode step, small shapes (several tiles and ragged tails)
+# ---------------------------------------------------------------------------
+
+SMALL = {
+    "mha_f16_r16": dict(B=2, Hq=4, Hkv=4, S0=700, r=16, k=48, int4=False),
+    "mha_int4_r8": dict(B=3, Hq=4, Hkv=4, S0=1300, r=8, k=100, int4=True),
+    "gqa7_f16_r16": dict(B=2, Hq=28, Hkv=4, S0=900, r=16, k=64, int4=False),
+    "gqa4_int4_r8": dict(B=2, Hq=16, Hkv=4, S0=513, r=8, k=33, int4=True),
+    "gqa2_int4_r16": dict(B=2, Hq=4, Hkv=2, S0=450, r=16, k=40, int4=True),
+    "generic_f16_r12": dict(B=2, Hq=6, Hkv=3, S0=333, r=12, k=20, int4=False),
+    "generic_int4_r6": dict(B=2, Hq=3, Hkv=3, S0=270, r=6, k=25, int4=True),
+    "leank_dense": dict(B=2, Hq=28, Hkv=4, S0=650, r=0, k=0, int4=False, d_k=32),
+    "leank_ds": dict(B=2, Hq=28, Hkv=4, S0=650, r=8, k=70, int4=False, d_k=32),
+    "leank48_ds": dict(B=2, Hq=8, Hkv=2, S0=400, r=8, k=50, int4=True, d_k=48),
+    "g8_dense": dict(B=1, Hq=16, Hkv=2, S0=300, r=0, k=0, int4=False),
+}
+
+
+def _small_inputs(name, **over):
+    kw = dict(SMALL[name])
+    kw.update(over)
+    cfg = synth.small(name, steps=3, seed=100 + len(name), **kw)
+    inp = synth.make_inputs(cfg, "cuda")
+    return cfg, inp
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+@pytest.mark.parametrize("mode", ["default", "unfused", "split3", "append_flag"])
+def test_decode_small(name, mode):
+    cfg, inp = _small_inputs(name)
+    _note("decode %s %s" % (name, mode))
+    S = cfg.S0 + 1
+    labels = None
+    kw = {}
+    if cfg.k > 0:
+        labels = prefill(cfg, inp, cfg.S0 if mode == "append_flag" else S)
+        if mode == "append_flag":
+            kw["flags"] = ds.DECODE_APPEND
+    elif mode == "append_flag":
+        pytest.skip("dense: no labels")
+    if mode == "unfused":
+        kw["flags"] = ds.DECODE_UNFUSED
+    if mode == "split3":
+        kw["n_split"] = 3
+    seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
+    out, topk = run(cfg, inp, labels, seq, S, **kw)
+    rows = ds_check.sample_rows(cfg, 64)
+    ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k, out,
+                        topk, rows)
+
+
+@pytest.mark.parametrize("unfused", [False, True])
+def test_ragged_lengths_and_degenerate_rows(unfused):
+    """Per-row lengths: empty, one token, below/at/just above k, full."""
+    cfg, inp = _small_inputs("mha_int4_r8", B=7)
+    k = cfg.k
+    lens = [0, 1, k - 1, k, k + 1, cfg.S0 // 2 + 3, cfg.S0 + 1]
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    labels = prefill(cfg, inp, cfg.S0 + 1)
+    out, topk = run(cfg, inp, labels, seq, cfg.S0 + 1,
+                    flags=ds.DECODE_UNFUSED if unfused else 0)
+    assert not out[0].any()
+    rows = ds_check.sample_rows(cfg, 1000)
+    ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, k, out, topk,
+                        rows, label_upto=cfg.S0 + 1)
+
+
+def test_k_at_least_seq_and_dense_equal():
+    """k >= S attends every token: same output as the dense path (k <= 0)."""
+    cfg, inp = _small_inputs("gqa4_int4_r8")
+    S = cfg.S0 + 1
+    seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
+    labels = prefill(cfg, inp, S)
+    a, ta = run(cfg, inp, labels, seq, S, k=S + 10)
+    b, _ = run(cfg, inp, None, seq, S, k=0)
+    assert torch.equal(ta[..., :S].cpu(), torch.arange(S, dtype=torch.int32).expand(cfg.B, cfg.Hkv, S))
+    assert (ta[..., S:] == -1).all()
+    err = ds_check.rel_err_rows(a.float().cpu().numpy(), b.float().cpu().numpy()).max()
+    assert err <= 1e-3
+
+
+def test_all_equal_scores_pick_lowest_indices():
+    """Heavy channels all zero: every approximate score is 0 and the tie rule
+    keeps tokens 0 .. k-1 exactly."""
+    cfg, inp = _small_inputs("mha_f16_r16")
+    for g in range(cfg.Hkv):
+        inp.K[:, g][..., inp.chan[g].long()] = 0
+    S = cfg.S0 + 1
+    seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
+    for unfused in (False, True):
+        labels = prefill(cfg, inp, S)
+        out, topk = run(cfg, inp, labels, seq, S, flags=ds.DECODE_UNFUSED if unfused else 0)
+        assert torch.equal(topk.cpu(), torch.arange(cfg.k, dtype=torch.int32).expand_as(topk.cpu()))
+        ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k, out,
+                            topk, ds_check.sample_rows(cfg, 100), strict_sets=True)
+
+
+def test_integer_ties_exact():
+    """Integer-valued labels give exact fp32 ties; sets must match the oracle
+    exactly (same scores on both sides, ties to the lower index)."""
+    cfg, inp = _small_inputs("mha_f16_r16")
+    gen = torch.Generator().manual_seed(3)
+    for g in range(cfg.Hkv):
+        ints = torch.randint(-2, 3, (cfg.B, cfg.cap, cfg.r), generator=gen).to(torch.float16)
+        inp.K[:, g][..., inp.chan[g].long()] = ints.cuda()
+    inp.q.copy_(torch.randint(-2, 3, inp.q.shape, generator=gen).to(torch.float16).cuda())
+    S = cfg.S0 + 1
+    seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
+    labels = prefill(cfg, inp, S)
+    for unfused in (False, True):
+        out, topk = run(cfg, inp, labels, seq, S, flags=ds.DECODE_UNFUSED if unfused else 0)
+        ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k, out,
+                            topk, ds_check.sample_rows(cfg, 100), strict_sets=True)
+
+
+def test_split_count_invariance_and_determinism():
+    cfg, inp = _small_inputs("mha_int4_r8")
+    S = cfg.S0 + 1
+    seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
+    labels = prefill(cfg, inp, S)
+    base, t0 = run(cfg, inp, labels, seq, S, n_split=1)
+    again, t1 = run(cfg, inp, labels, seq, S, n_split=1)
+    assert torch.equal(base, again) and torch.equal(t0, t1)       # bitwise repeatable
+    for ns in (2, 3, 7):
+        o, t = run(cfg, inp, labels, seq, S, n_split=ns)
+        assert torch.equal(t, t0)
+        err = ds_check.rel_err_rows(o.float().cpu().numpy(), base.float().cpu().numpy()).max()
+        assert err <= 1e-3, (ns, err)
+
+
+def test_workspace_is_not_read_uninitialised():
+    """Garbage in the workspace must not change the result."""
+    cfg, inp = _small_inputs("gqa7_f16_r16")
+    S = cfg.S0 + 1
+    seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
+    labels = prefill(cfg, inp, S)
+    need = ds.workspace_size(inp.K, inp.V, cfg.Hq, cfg.D, labels, cfg.k, S)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+    a, ta = run(cfg, inp, labels, seq, S, workspace=ws)
+    ws.fill_(0x7F)
+    b, tb = run(cfg, inp, labels, seq, S, workspace=ws)
+    assert torch.equal(a, b) and torch.equal(ta, tb)
+
+
+def test_decode_steps_with_appends():
+    """Several decode steps: append the current token, then decode."""
+    cfg, inp = _small_inputs("gqa2_int4_r16")
+    labels = prefill(cfg, inp, cfg.S0)
+    for step in range(cfg.steps):
+        S = cfg.S0 + step + 1
+        seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
+        ds.label_append(inp.K, inp.chan, labels, seq - 1)
+        q = synth.make_q(cfg, "cuda", step)
+        inp.q.copy_(q)
+        out, topk = run(cfg, inp, labels, seq, cfg.cap)
+        ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k, out,
+                            topk, ds_check.sample_rows(cfg, 100))
+
+
+# ---------------------------------------------------------------------------
+# the workloads at full size (sampled rows)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,n_rows", [("tiny", 32), ("llama2_7b_4k", 12),
+                                         ("qwen25_7b_gqa_8k", 8), ("long_128k", 6),
+                                         ("leank_dense", 6), ("leank_ds", 8)])
+def test_workload_full_size(name, n_rows):
+    cfg = synth.CONFIGS[name]
+    _note("workload %s" % name)
+    inp = synth.make_inputs(cfg, "cuda")
+    labels = prefill(cfg, inp, cfg.S0) if cfg.k > 0 else None
+    last = 2 if cfg.steps >= 2 else 0
+    for step in range(last + 1):       # decode a few steps, check the last one
+        S = cfg.S0 + step + 1
+        seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
+        inp.q.copy_(synth.make_q(cfg, "cuda", step))
+        out, topk = run(cfg, inp, labels, seq, cfg.cap,
+                        flags=ds.DECODE_APPEND if cfg.k > 0 else 0)
+    rows = ds_check.sample_rows(cfg, n_rows, seed=5)
+    res = ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k,
+                              out, topk, rows)
+    _note("workload %s: %s" % (name, res))
+    del inp, labels, out, topk
+    gc.collect()
+    torch.cuda.empty_cache()
