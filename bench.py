@@ -97,6 +97,9 @@ def main():
     ap.add_argument("--unfused", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage-events", choices=["all", "attn", "none"], default="all",
+                    help="HIP events per timed step: every stage boundary, only around the "
+                         "attention kernel, or none")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -160,7 +163,14 @@ def main():
         flags |= ds.DECODE_UNFUSED
     total = args.warmup + args.steps
     n_ev = ds.STAGE_COUNT + 1
-    events = ds.HipEvents(args.steps * n_ev)
+    if args.stage_events == "all":
+        skip = ()
+    elif args.stage_events == "attn":
+        skip = [i for i in range(args.steps * n_ev)
+                if i % n_ev not in (ds.STAGES.index("attn"), ds.STAGES.index("attn") + 1)]
+    else:
+        skip = range(args.steps * n_ev)
+    events = ds.HipEvents(args.steps * n_ev, skip=skip)
     calls = []
     keep = []  # keeps ctypes objects alive
     for i in range(total):
@@ -171,8 +181,8 @@ def main():
         opts = ds.DecodeOpts()
         opts.n_split, opts.flags = args.n_split, flags
         ti = i - args.warmup
-        if ti >= 0:
-            opts.stage_events = ctypes.addressof(events.handles) + ti * n_ev * ctypes.sizeof(ctypes.c_void_p)
+        if ti >= 0 and args.stage_events != "none":
+            opts.stage_events = events.slot_address(ti * n_ev)
         keep.append((kv, lab, opts))
         P = ctypes.c_void_p
         calls.append((ctypes.byref(kv), P(qs[i % n_q].data_ptr()), P(Ks[l].data_ptr()),
@@ -203,16 +213,21 @@ def main():
     for i in range(K_steps):
         b = i * n_ev
         for s, name in enumerate(ds.STAGES):
-            stage_ms[name].append(events.elapsed_ms(b + s, b + s + 1))
-        step_ms.append(events.elapsed_ms(b, b + ds.STAGE_COUNT))
-    mean = {k: sum(v) / len(v) for k, v in stage_ms.items()}
+            if events.handles[b + s] and events.handles[b + s + 1]:
+                stage_ms[name].append(events.elapsed_ms(b + s, b + s + 1))
+        if events.handles[b] and events.handles[b + ds.STAGE_COUNT]:
+            step_ms.append(events.elapsed_ms(b, b + ds.STAGE_COUNT))
+    mean = {k: (sum(v) / len(v) if v else None) for k, v in stage_ms.items()}
+    if not step_ms:
+        step_ms = [wall / K_steps * 1e3]
     step_ms_sorted = sorted(step_ms)
     med_step = step_ms_sorted[len(step_ms) // 2]
     S_mid = cfg.S0 + 1 + (K_steps // L) // 2
     ab = algorithmic_bytes(cfg, S_mid)
     attn_bytes = ab["rows"] + ab["q_out"]
     dom = "attn"
-    achieved = attn_bytes / (mean["attn"] * 1e-3) / 1e9
+    attn_ms = mean["attn"] if mean["attn"] else float("nan")
+    achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
     step_bytes = ab["labels"] + ab["rows"] + ab["q_out"]
     result = {
         "metric": METRIC,
@@ -235,10 +250,11 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None,
                      "algorithmic_bytes_per_launch": attn_bytes,
-                     "avg_launch_us": round(mean["attn"] * 1e3, 3)},
+                     "avg_launch_us": round(attn_ms * 1e3, 3), "events": args.stage_events},
         "step": {"median_us": round(med_step * 1e3, 3),
                  "p90_us": round(step_ms_sorted[int(0.9 * (len(step_ms) - 1))] * 1e3, 3),
-                 "stage_mean_us": {k: round(v * 1e3, 3) for k, v in mean.items()},
+                 "stage_mean_us": {k: (round(v * 1e3, 3) if v is not None else None)
+                                   for k, v in mean.items()},
                  "algorithmic_bytes": step_bytes,
                  "hbm_gbs_at_median": round(step_bytes / (med_step * 1e-3) / 1e9, 1),
                  "hbm_frac_at_median": round(step_bytes / (med_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

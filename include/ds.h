@@ -148,10 +148,11 @@ typedef struct {
                         row's selected tokens in the attention pass (clamped to
                         the range the workspace was sized for) */
   uint32_t flags;    /* DS_DECODE_* */
-  hipEvent_t* stage_events; /* NULL, or DS_STAGE_COUNT + 1 events: event i is
-                               recorded on `stream` before stage i, the last one
-                               after the final stage (stages that launch nothing
-                               give empty intervals) */
+  hipEvent_t* stage_events; /* NULL, or DS_STAGE_COUNT + 1 event slots: event i
+                               is recorded on `stream` before stage i, the last
+                               one after the final stage (stages that launch
+                               nothing give empty intervals); NULL slots are
+                               skipped */
 } ds_decode_opts;
 
 /* Workspace bytes that ds_decode_attn needs for these arguments (0 if they

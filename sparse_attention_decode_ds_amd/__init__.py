@@ -199,9 +199,10 @@ def decode_attn(q, K, V, seq_lens, max_seq_len: int, k: int, sm_scale: float,
 
 
 class HipEvents:
-    """Raw hipEvent_t handles (for the stage_events option and kernel timing)."""
+    """Raw hipEvent_t handles (for the stage_events option and kernel timing).
+    ``handles`` is a ctypes array of n slots; slots listed in ``skip`` stay NULL."""
 
-    def __init__(self, n: int):
+    def __init__(self, n: int, skip=()):
         self._hip = ctypes.CDLL("libamdhip64.so")
         self._hip.hipEventCreate.argtypes = [ctypes.c_void_p]
         self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
@@ -209,10 +210,16 @@ class HipEvents:
         self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.handles = (ctypes.c_void_p * n)()
+        skip = set(skip)
         for i in range(n):
+            if i in skip:
+                continue
             rc = self._hip.hipEventCreate(ctypes.byref(self.handles, i * ctypes.sizeof(ctypes.c_void_p)))
             if rc != 0:
                 raise RuntimeError("hipEventCreate failed: %d" % rc)
+
+    def slot_address(self, i: int) -> int:
+        return ctypes.addressof(self.handles) + i * ctypes.sizeof(ctypes.c_void_p)
 
     def elapsed_ms(self, i: int, j: int) -> float:
         ms = ctypes.c_float()

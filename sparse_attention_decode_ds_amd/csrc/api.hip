@@ -122,6 +122,33 @@ Plan make_plan(const ds_kv_desc* kv, int k, int max_seq) {
   return p;
 }
 
+AttnArgs attn_args(const ds_kv_desc* kv, const void* q, const void* K, const void* V,
+                   const int32_t* seq_lens, int max_seq_len, const int32_t* keep, float sm_scale,
+                   void* out, char* ws, const Plan& p) {
+  AttnArgs aa;
+  memset(&aa, 0, sizeof(aa));
+  aa.q = static_cast<const __half*>(q);
+  aa.Hq = kv->n_q_heads;
+  aa.d_q = kv->d_q;
+  aa.K = static_cast<const __half*>(K);
+  aa.V = static_cast<const __half*>(V);
+  aa.ks0 = kv->k_stride[0];
+  aa.ks1 = kv->k_stride[1];
+  aa.ks2 = kv->k_stride[2];
+  aa.vs0 = kv->v_stride[0];
+  aa.vs1 = kv->v_stride[1];
+  aa.vs2 = kv->v_stride[2];
+  aa.Hkv = kv->n_kv_heads;
+  aa.d_k = kv->d_k;
+  aa.keep = keep;
+  aa.seq_lens = seq_lens;
+  aa.max_seq = max_seq_len;
+  aa.scale_log2 = sm_scale * 1.4426950408889634f;
+  aa.out = static_cast<__half*>(out);
+  aa.part = reinterpret_cast<float*>(ws + p.off_part);
+  return aa;
+}
+
 int auto_splits(const Plan& p, int64_t rows, int requested) {
   int ns;
   if (requested > 0) {
@@ -228,11 +255,13 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
   char* ws = static_cast<char*>(workspace);
   hipEvent_t* ev = opts ? opts->stage_events : nullptr;
   auto mark = [&](int i) {
-    if (ev) (void)hipEventRecord(ev[i], stream);
+    if (ev && ev[i]) (void)hipEventRecord(ev[i], stream);
   };
 
   mark(DS_STAGE_APPEND);
-  if (flags & DS_DECODE_APPEND) {
+  const bool fused_step = sparse && G == 1 && !(flags & DS_DECODE_UNFUSED) &&
+                          decode_fused_fits(max_seq_len, k, lab->r, lab->dtype == DS_LABEL_INT4);
+  if ((flags & DS_DECODE_APPEND) && !fused_step) {
     LabelArgs la = label_args(kv, K, chan, lab);
     la.pos = seq_lens;
     la.pos_minus_one = 1;
@@ -282,6 +311,21 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
     sa.n_chunks = p.n_chunks;
     idx = sa.idx;
     idx_stride = sa.idx_stride;
+    // One kernel for the whole step when the row's keys and token list fit
+    // in LDS and the group is one query head.
+    if (fused_step) {
+      LabelArgs la = label_args(kv, K, chan, lab);
+      AttnArgs aa = attn_args(kv, q, K, V, seq_lens, max_seq_len, keep, sm_scale, out, ws, p);
+      aa.n_split = 1;
+      mark(DS_STAGE_SELECT);
+      mark(DS_STAGE_ATTN);
+      if (launch_decode_fused(sa, aa, la, (flags & DS_DECODE_APPEND) ? 1 : 0, (int)rows, stream) !=
+          hipSuccess)
+        return DS_ERR_HIP;
+      mark(DS_STAGE_COMBINE);
+      mark(DS_STAGE_COUNT);
+      return DS_OK;
+    }
     const bool fused = max_seq_len <= kFuseMaxTokens && !(flags & DS_DECODE_UNFUSED);
     if (fused) {
       if (launch_score_select_fused(sa, (int)rows, stream) != hipSuccess) return DS_ERR_HIP;
@@ -295,24 +339,7 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
     mark(DS_STAGE_SELECT);
   }
 
-  AttnArgs aa;
-  memset(&aa, 0, sizeof(aa));
-  aa.q = static_cast<const __half*>(q);
-  aa.Hq = kv->n_q_heads;
-  aa.d_q = kv->d_q;
-  aa.K = static_cast<const __half*>(K);
-  aa.V = static_cast<const __half*>(V);
-  aa.ks0 = kv->k_stride[0];
-  aa.ks1 = kv->k_stride[1];
-  aa.ks2 = kv->k_stride[2];
-  aa.vs0 = kv->v_stride[0];
-  aa.vs1 = kv->v_stride[1];
-  aa.vs2 = kv->v_stride[2];
-  aa.Hkv = Hkv;
-  aa.d_k = kv->d_k;
-  aa.keep = keep;
-  aa.seq_lens = seq_lens;
-  aa.max_seq = max_seq_len;
+  AttnArgs aa = attn_args(kv, q, K, V, seq_lens, max_seq_len, keep, sm_scale, out, ws, p);
   aa.sparse = sparse;
   aa.idx = idx;
   aa.idx_stride = idx_stride;
@@ -320,9 +347,6 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
   aa.n_split = auto_splits(p, rows, opts ? opts->n_split : 0);
   aa.tps = (int)std::max<int64_t>(1, round_up(ceil_div(std::max(p.kk, 1), aa.n_split), 16));
   aa.n_split = (int)std::max<int64_t>(1, ceil_div(std::max(p.kk, 1), aa.tps));
-  aa.scale_log2 = sm_scale * 1.4426950408889634f;
-  aa.out = static_cast<__half*>(out);
-  aa.part = reinterpret_cast<float*>(ws + p.off_part);
 
   mark(DS_STAGE_ATTN);
   const bool final_out = aa.n_split == 1;

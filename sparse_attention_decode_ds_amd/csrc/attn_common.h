@@ -1,0 +1,230 @@
+// attn_common.h -- device code for step 3b of a Double Sparsity decode step:
+// exact softmax attention over a set of tokens' full K/V rows.
+//
+// [DS] "online forward computation", step 3: attention over the top-k tokens
+// uses the full query, K and V (not the channel-sparse ones).  [GQA] section
+// 4: the G query heads of a group read the same K/V rows, so each selected row
+// is loaded once and applied to all G heads.  [LeanK] section 2.2: K may be
+// stored compacted to d_k kept columns; the query is read at those channels.
+//
+// Layout: a workgroup of 4 waves = 16 rows of 16 lanes ("slots").  Each slot
+// walks its own tokens; lane c holds K and V channels [8c, 8c+8) as one
+// 16-byte load each and keeps an online-softmax state per head (running max m
+// in the log2 domain, sum l, unnormalised output o).  Loads of the next group
+// of tokens are in flight while the current group is consumed (two register
+// buffers in ping-pong).  The 16 states are merged with shuffles and LDS.
+#pragma once
+
+#include "ds_internal.h"
+
+namespace ds {
+
+constexpr int kAttnThreads = 256;
+constexpr int kSlots = 16;
+#ifndef DS_ATTN_UNROLL
+#define DS_ATTN_UNROLL 4
+#endif
+constexpr int kUnroll = DS_ATTN_UNROLL;  // tokens per slot and group
+constexpr float kNegInf = -__builtin_huge_valf();
+
+template <int G>
+struct AttnAcc {
+  float o[G][8];
+  float m[G];
+  float l[G];
+};
+
+template <int G>
+struct AttnRed {
+  float v[4][G][kDv + 2];
+};
+
+// Merge weights of two online-softmax states; either may be empty (m = -inf).
+__device__ __forceinline__ void merge_weights(float m, float m2, float& w1, float& w2, float& mx) {
+  mx = fmaxf(m, m2);
+  w1 = (m == kNegInf) ? 0.0f : exp2f(m - mx);
+  w2 = (m2 == kNegInf) ? 0.0f : exp2f(m2 - mx);
+}
+
+// Query of each head at stored-K channels [8c, 8c+8), scaled so that exp2 of
+// the dot product is exp of the logit; zero for lanes past d_k.
+template <int G>
+__device__ __forceinline__ void load_query(const AttnArgs& a, int b, int g, int c, bool kl,
+                                           float (&qf)[G][8]) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const __half* qh = a.q + ((int64_t)b * a.Hq + (int64_t)g * G + h) * a.d_q;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float v = 0.0f;
+      if (kl) {
+        const int ch = c * 8 + i;
+        const int qc = a.keep ? a.keep[(int64_t)g * a.d_k + ch] : ch;
+        v = h2f(qh[qc]) * a.scale_log2;
+      }
+      qf[h][i] = v;
+    }
+  }
+}
+
+template <int G>
+__device__ __forceinline__ void acc_init(AttnAcc<G>& acc) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    acc.m[h] = kNegInf;
+    acc.l[h] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc.o[h][i] = 0.0f;
+  }
+}
+
+// Accumulate tokens tok(i), i in [0, n), slot `slot` taking i = slot, slot+16, ...
+// Kr, Vr point at channel 8c of the row's token 0.
+template <int G, typename TokFn>
+__device__ __forceinline__ void attend(const AttnArgs& a, const __half* Kr, const __half* Vr,
+                                       bool kl, int slot, int n, TokFn tok,
+                                       const float (&qf)[G][8], AttnAcc<G>& acc) {
+  constexpr int kStep = kSlots * kUnroll;
+  auto issue = [&](int base, uint4* kk, uint4* vv) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      kk[u] = make_uint4(0, 0, 0, 0);
+      vv[u] = make_uint4(0, 0, 0, 0);
+      const int i = base + u * kSlots;
+      if (i < n) {
+        const int64_t t = tok(i);
+        if (kl) kk[u] = ld_stream(Kr + t * a.ks2);
+        vv[u] = ld_stream(Vr + t * a.vs2);
+      }
+    }
+  };
+  auto consume = [&](int base, const uint4* kk, const uint4* vv) {
+    float s[kUnroll][G];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float kf[8];
+      unpack8(kk[u], kf);
+      const bool valid = base + u * kSlots < n;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float d = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d += qf[h][i] * kf[i];
+        d = row16_sum(d);
+        s[u][h] = valid ? d : kNegInf;
+      }
+    }
+    float vf[kUnroll][8];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) unpack8(vv[u], vf[u]);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mx = acc.m[h];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) mx = fmaxf(mx, s[u][h]);
+      if (mx == kNegInf) continue;
+      const float alpha = exp2f(acc.m[h] - mx);
+      float p[kUnroll];
+      float ps = 0.0f;
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        p[u] = exp2f(s[u][h] - mx);
+        ps += p[u];
+      }
+      acc.l[h] = acc.l[h] * alpha + ps;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float o = acc.o[h][i] * alpha;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) o += p[u] * vf[u][i];
+        acc.o[h][i] = o;
+      }
+      acc.m[h] = mx;
+    }
+  };
+  uint4 ka[kUnroll], va[kUnroll], kb[kUnroll], vb[kUnroll];
+  issue(slot, ka, va);
+  for (int base = slot; base < n; base += 2 * kStep) {
+    issue(base + kStep, kb, vb);
+    consume(base, ka, va);
+    if (base + kStep >= n) break;
+    issue(base + 2 * kStep, ka, va);
+    consume(base + kStep, kb, vb);
+  }
+}
+
+// Merge the 16 slot states and write either the fp16 output (FINAL) or the
+// (o, m, l) partial of split `split`.  Every thread of the workgroup calls it.
+template <int G, bool FINAL>
+__device__ __forceinline__ void attn_finish(const AttnArgs& a, AttnAcc<G>& acc, AttnRed<G>& red,
+                                            int b, int g, int split) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int c = lane & 15;
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float m2 = __shfl_xor(acc.m[h], off, 64);
+      const float l2 = __shfl_xor(acc.l[h], off, 64);
+      float w1, w2, mx;
+      merge_weights(acc.m[h], m2, w1, w2, mx);
+      acc.l[h] = acc.l[h] * w1 + l2 * w2;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        acc.o[h][i] = acc.o[h][i] * w1 + __shfl_xor(acc.o[h][i], off, 64) * w2;
+      acc.m[h] = mx;
+    }
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) red.v[w][h][c * 8 + i] = acc.o[h][i];
+      if (c == 0) {
+        red.v[w][h][kDv] = acc.m[h];
+        red.v[w][h][kDv + 1] = acc.l[h];
+      }
+    }
+  }
+  __syncthreads();
+  if (tid >= G * 16) return;
+  const int h = tid >> 4;
+  const int cc = tid & 15;
+  float M = kNegInf;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, red.v[ww][h][kDv]);
+  float L = 0.0f, O[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) O[i] = 0.0f;
+  if (M != kNegInf) {
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float mw = red.v[ww][h][kDv];
+      if (mw == kNegInf) continue;
+      const float sc = exp2f(mw - M);
+      L += sc * red.v[ww][h][kDv + 1];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) O[i] += sc * red.v[ww][h][cc * 8 + i];
+    }
+  }
+  const int64_t bh = (int64_t)b * a.Hq + (int64_t)g * G + h;
+  if (FINAL) {
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    __half2 r2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r2[i] = __floats2half2_rn(O[2 * i] * inv, O[2 * i + 1] * inv);
+    *reinterpret_cast<uint4*>(a.out + bh * kDv + cc * 8) = *reinterpret_cast<const uint4*>(r2);
+  } else {
+    float* dst = a.part + (bh * a.n_split + split) * kPartStride;
+    *reinterpret_cast<float4*>(dst + cc * 8) = make_float4(O[0], O[1], O[2], O[3]);
+    *reinterpret_cast<float4*>(dst + cc * 8 + 4) = make_float4(O[4], O[5], O[6], O[7]);
+    if (cc == 0) {
+      dst[kDv] = M;
+      dst[kDv + 1] = L;
+    }
+  }
+}
+
+}  // namespace ds

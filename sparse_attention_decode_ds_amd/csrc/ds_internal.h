@@ -17,7 +17,12 @@ namespace ds {
 
 // Rows whose scores fit this many fp32 keys in LDS take the fused
 // score+select kernel (one workgroup per (batch, KV head) row).
-constexpr int kFuseMaxTokens = 16384;
+constexpr int kFuseMaxTokens = 12288;
+// The fully fused decode kernel (append + score + select + attention in one
+// 256-thread workgroup per row) keeps up to TPT scores per thread in
+// registers and the selected token list in LDS.
+constexpr int kDecodeFusedTPT = 24;  // rows up to 6144 tokens
+constexpr int kDecodeFusedMaxK = 2048;
 // Attention splits per row are capped; partial results cost 528 B each.
 constexpr int kMaxSplit = 64;
 // Selected-token indices staged in LDS per attention workgroup.
@@ -99,11 +104,26 @@ hipError_t launch_score_chunks(const ScoreArgs& a, int rows, hipStream_t s);
 hipError_t launch_select_stream(const ScoreArgs& a, int rows, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int rows, int G, bool final_out, hipStream_t s);
 hipError_t launch_combine(const AttnArgs& a, int B, hipStream_t s);
+hipError_t launch_decode_fused(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la,
+                               int append, int rows, hipStream_t s);
+bool decode_fused_fits(int max_seq, int k, int r, int is_int4);
 
 // ---------------------------------------------------------------------------
 // Device helpers.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float h2f(__half h) { return __half2float(h); }
+
+// 16-byte load with the nontemporal hint: data read once per step (K/V rows,
+// labels) streams through the caches instead of displacing reused lines.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+#ifdef DS_NO_NT_LOADS
+  return *reinterpret_cast<const uint4*>(p);
+#else
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#endif
+}
 
 __device__ __forceinline__ void unpack8(const uint4 v, float* f) {
   const __half2* h = reinterpret_cast<const __half2*>(&v);
