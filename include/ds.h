@@ -140,7 +140,9 @@ enum {
 /* Flags for ds_decode_opts.flags. */
 #define DS_DECODE_APPEND 1u         /* first append label slot seq_lens[b]-1 (as ds_label_append) */
 #define DS_DECODE_VALIDATE_ONLY 2u  /* validate the arguments and return; enqueue nothing */
-#define DS_DECODE_UNFUSED 4u        /* force the separate score and select kernels */
+#define DS_DECODE_UNFUSED 4u        /* do not run the step as a single kernel */
+#define DS_DECODE_STREAM 8u         /* select over every score streamed from memory (no
+                                       local top-M pre-selection) */
 
 /* Optional decode settings (host struct; pass NULL for defaults). */
 typedef struct {

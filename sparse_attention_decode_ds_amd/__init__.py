@@ -32,6 +32,7 @@ STAGES = ("append", "score", "select", "attn", "combine")
 DECODE_APPEND = 1
 DECODE_VALIDATE_ONLY = 2
 DECODE_UNFUSED = 4
+DECODE_STREAM = 8
 EXPORTS = ("ds_label_build", "ds_label_append", "ds_decode_attn_workspace_size",
            "ds_decode_attn", "ds_status_str", "ds_abi_version")
 

@@ -93,9 +93,13 @@ struct Plan {
   int kk;           // tokens attended per row at most
   int idx_cap;      // workspace index slots per row
   int keys_stride;  // workspace key words per row
-  int n_chunks;
+  int n_chunks;     // streaming select: score chunks per row
+  int local_chunk;  // local top-M select: tokens per chunk workgroup
+  int local_nch;    // and chunks per row
+  int cand_stride;  // candidate slots per row
   int split_cap;
-  size_t off_count, off_idx, off_keys, off_part, total;
+  size_t off_count, off_idx, off_keys, off_cand_key, off_cand_idx, off_cand_cnt, off_cand_theta;
+  size_t off_part, total;
 };
 
 Plan make_plan(const ds_kv_desc* kv, int k, int max_seq) {
@@ -107,6 +111,12 @@ Plan make_plan(const ds_kv_desc* kv, int k, int max_seq) {
   p.idx_cap = p.sparse ? std::max(p.kk, 1) : 0;
   p.keys_stride = p.sparse ? (int)round_up(std::max(max_seq, 1), 64) : 0;
   p.n_chunks = (int)std::max<int64_t>(1, ceil_div(max_seq, kScoreChunk));
+  // Local top-M chunks: 4096 tokens, halved while the grid would have fewer
+  // than ~4 workgroups per compute unit.
+  p.local_chunk = 4096;
+  while (p.local_chunk > 512 && rows * ceil_div(max_seq, p.local_chunk) < 1024) p.local_chunk /= 2;
+  p.local_nch = (int)std::max<int64_t>(1, ceil_div(max_seq, p.local_chunk));
+  p.cand_stride = p.sparse ? (int)std::min<int64_t>(kMergeCap, round_up(std::max(max_seq, 1), 64)) : 0;
   p.split_cap = (int)std::min<int64_t>(kMaxSplit, std::max<int64_t>(1, ceil_div(p.kk, 16)));
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -117,6 +127,11 @@ Plan make_plan(const ds_kv_desc* kv, int k, int max_seq) {
   p.off_count = take(rows * sizeof(int32_t));
   p.off_idx = take(rows * (size_t)p.idx_cap * sizeof(int32_t));
   p.off_keys = take(rows * (size_t)p.keys_stride * sizeof(uint32_t));
+  const size_t nch = p.sparse ? (size_t)p.local_nch : 0;
+  p.off_cand_key = take(rows * (size_t)p.cand_stride * sizeof(uint32_t));
+  p.off_cand_idx = take(rows * (size_t)p.cand_stride * sizeof(int32_t));
+  p.off_cand_cnt = take(rows * nch * sizeof(int32_t));
+  p.off_cand_theta = take(rows * nch * sizeof(uint32_t));
   p.off_part = take((size_t)kv->batch * kv->n_q_heads * p.split_cap * kPartStride * sizeof(float));
   p.total = off;
   return p;
@@ -239,7 +254,8 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
   if (!keep && kv->d_k != kv->d_q) return DS_ERR_SHAPE;
   if (max_seq_len < 0 || max_seq_len > kv->capacity) return DS_ERR_ARG;
   const uint32_t flags = opts ? opts->flags : 0u;
-  if (flags & ~(DS_DECODE_APPEND | DS_DECODE_VALIDATE_ONLY | DS_DECODE_UNFUSED)) return DS_ERR_ARG;
+  if (flags & ~(DS_DECODE_APPEND | DS_DECODE_VALIDATE_ONLY | DS_DECODE_UNFUSED | DS_DECODE_STREAM))
+    return DS_ERR_ARG;
   if (opts && opts->n_split < 0) return DS_ERR_ARG;
   if ((flags & DS_DECODE_APPEND) && !sparse) return DS_ERR_ARG;
   if (!std::isfinite(sm_scale)) return DS_ERR_ARG;
@@ -259,9 +275,14 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
   };
 
   mark(DS_STAGE_APPEND);
-  const bool fused_step = sparse && G == 1 && !(flags & DS_DECODE_UNFUSED) &&
+  // Paths for the score and select: one kernel for the whole step (single
+  // query head, short rows), local top-M + exact merge, or a full streaming
+  // select over every score.
+  const bool fused_step = sparse && G == 1 && !(flags & (DS_DECODE_UNFUSED | DS_DECODE_STREAM)) &&
                           decode_fused_fits(max_seq_len, k, lab->r, lab->dtype == DS_LABEL_INT4);
-  if ((flags & DS_DECODE_APPEND) && !fused_step) {
+  const bool local_path = sparse && !fused_step && !(flags & DS_DECODE_STREAM) &&
+                          p.local_nch <= kMaxLocalChunks;
+  if ((flags & DS_DECODE_APPEND) && !fused_step && !local_path) {
     LabelArgs la = label_args(kv, K, chan, lab);
     la.pos = seq_lens;
     la.pos_minus_one = 1;
@@ -309,6 +330,11 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
     sa.keys_stride = p.keys_stride;
     sa.chunk = kScoreChunk;
     sa.n_chunks = p.n_chunks;
+    sa.cand_key = reinterpret_cast<uint32_t*>(ws + p.off_cand_key);
+    sa.cand_idx = reinterpret_cast<int32_t*>(ws + p.off_cand_idx);
+    sa.cand_cnt = reinterpret_cast<int32_t*>(ws + p.off_cand_cnt);
+    sa.cand_theta = reinterpret_cast<uint32_t*>(ws + p.off_cand_theta);
+    sa.cand_stride = p.cand_stride;
     idx = sa.idx;
     idx_stride = sa.idx_stride;
     // One kernel for the whole step when the row's keys and token list fit
@@ -326,10 +352,15 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
       mark(DS_STAGE_COUNT);
       return DS_OK;
     }
-    const bool fused = max_seq_len <= kFuseMaxTokens && !(flags & DS_DECODE_UNFUSED);
-    if (fused) {
-      if (launch_score_select_fused(sa, (int)rows, stream) != hipSuccess) return DS_ERR_HIP;
+    if (local_path) {
+      LabelArgs la = label_args(kv, K, chan, lab);
+      sa.chunk = p.local_chunk;
+      sa.n_chunks = p.local_nch;
+      if (launch_score_local(sa, la, (flags & DS_DECODE_APPEND) ? 1 : 0, (int)rows, stream) !=
+          hipSuccess)
+        return DS_ERR_HIP;
       mark(DS_STAGE_SELECT);
+      if (launch_select_merge(sa, (int)rows, stream) != hipSuccess) return DS_ERR_HIP;
     } else {
       if (launch_score_chunks(sa, (int)rows, stream) != hipSuccess) return DS_ERR_HIP;
       mark(DS_STAGE_SELECT);

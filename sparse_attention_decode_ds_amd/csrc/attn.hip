@@ -52,38 +52,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
 // Log-sum-exp merge of the split partials: 16 lanes per (batch, query head).
 __global__ __launch_bounds__(kAttnThreads) void k_combine(AttnArgs a, int n_rows) {
   const int rq = blockIdx.x * (kAttnThreads / 16) + (threadIdx.x >> 4);
-  const int c = threadIdx.x & 15;
   if (rq >= n_rows) return;
-  const float* p = a.part + (int64_t)rq * a.n_split * kPartStride;
-  float M = kNegInf;
-  for (int sp = 0; sp < a.n_split; ++sp) M = fmaxf(M, p[sp * kPartStride + kDv]);
-  float L = 0.0f, O[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) O[i] = 0.0f;
-  if (M != kNegInf) {
-    for (int sp = 0; sp < a.n_split; ++sp) {
-      const float* q = p + sp * kPartStride;
-      const float ms = q[kDv];
-      if (ms == kNegInf) continue;
-      const float sc = exp2f(ms - M);
-      L += sc * q[kDv + 1];
-      const float4 x0 = *reinterpret_cast<const float4*>(q + c * 8);
-      const float4 x1 = *reinterpret_cast<const float4*>(q + c * 8 + 4);
-      O[0] += sc * x0.x;
-      O[1] += sc * x0.y;
-      O[2] += sc * x0.z;
-      O[3] += sc * x0.w;
-      O[4] += sc * x1.x;
-      O[5] += sc * x1.y;
-      O[6] += sc * x1.z;
-      O[7] += sc * x1.w;
-    }
-  }
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  __half2 r2[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r2[i] = __floats2half2_rn(O[2 * i] * inv, O[2 * i + 1] * inv);
-  *reinterpret_cast<uint4*>(a.out + (int64_t)rq * kDv + c * 8) = *reinterpret_cast<const uint4*>(r2);
+  merge_partials(a, rq, threadIdx.x & 15);
 }
 
 template <int G>

@@ -153,6 +153,10 @@ __device__ __forceinline__ void attend(const AttnArgs& a, const __half* Kr, cons
   }
 }
 
+template <int G, bool FINAL>
+__device__ __forceinline__ void attn_store(const AttnArgs& a, AttnRed<G>& red, int b, int g,
+                                           int split);
+
 // Merge the 16 slot states and write either the fp16 output (FINAL) or the
 // (o, m, l) partial of split `split`.  Every thread of the workgroup calls it.
 template <int G, bool FINAL>
@@ -190,6 +194,16 @@ __device__ __forceinline__ void attn_finish(const AttnArgs& a, AttnAcc<G>& acc, 
   }
   __syncthreads();
   if (tid >= G * 16) return;
+  attn_store<G, FINAL>(a, red, b, g, split);
+}
+
+// Workgroup merge of the four wave states in `red` and the store, by threads
+// (h, c) with h < G (the others do nothing).
+template <int G, bool FINAL>
+__device__ __forceinline__ void attn_store(const AttnArgs& a, AttnRed<G>& red, int b, int g,
+                                           int split) {
+  const int tid = threadIdx.x;
+  if (tid >= G * 16) return;
   const int h = tid >> 4;
   const int cc = tid & 15;
   float M = kNegInf;
@@ -225,6 +239,41 @@ __device__ __forceinline__ void attn_finish(const AttnArgs& a, AttnAcc<G>& acc, 
       dst[kDv + 1] = L;
     }
   }
+}
+
+// Log-sum-exp merge of the n_split partials of query head row `rq`
+// (16 lanes, lane c covers channels [8c, 8c+8)); fp16 output.
+__device__ __forceinline__ void merge_partials(const AttnArgs& a, int64_t rq, int c) {
+  const float* p = a.part + rq * a.n_split * kPartStride;
+  float M = kNegInf;
+  for (int sp = 0; sp < a.n_split; ++sp) M = fmaxf(M, p[sp * kPartStride + kDv]);
+  float L = 0.0f, O[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) O[i] = 0.0f;
+  if (M != kNegInf) {
+    for (int sp = 0; sp < a.n_split; ++sp) {
+      const float* q = p + sp * kPartStride;
+      const float ms = q[kDv];
+      if (ms == kNegInf) continue;
+      const float sc = exp2f(ms - M);
+      L += sc * q[kDv + 1];
+      const float4 x0 = *reinterpret_cast<const float4*>(q + c * 8);
+      const float4 x1 = *reinterpret_cast<const float4*>(q + c * 8 + 4);
+      O[0] += sc * x0.x;
+      O[1] += sc * x0.y;
+      O[2] += sc * x0.z;
+      O[3] += sc * x0.w;
+      O[4] += sc * x1.x;
+      O[5] += sc * x1.y;
+      O[6] += sc * x1.z;
+      O[7] += sc * x1.w;
+    }
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  __half2 r2[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r2[i] = __floats2half2_rn(O[2 * i] * inv, O[2 * i + 1] * inv);
+  *reinterpret_cast<uint4*>(a.out + rq * kDv + c * 8) = *reinterpret_cast<const uint4*>(r2);
 }
 
 }  // namespace ds

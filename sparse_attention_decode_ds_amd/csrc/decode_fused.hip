@@ -47,66 +47,6 @@ struct FusedScratch {
   AttnRed<1> red;
 };
 
-// Inclusive prefix sum over the 64 lanes of a wave (DPP: shifts within rows
-// of 16, then row broadcasts).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);  // row_shr:1
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);  // row_shr:2
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);  // row_shr:4
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);  // row_shr:8
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false); // row_bcast:15
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false); // row_bcast:31
-  return x;
-}
-
-__device__ __forceinline__ uint32_t bin_of(float s, float mn, float scale) {
-  float x = (s - mn) * scale;
-  x = fminf(fmaxf(x, 0.0f), 2047.0f);  // NaN (0 * inf) maps to 0
-  return (uint32_t)x;
-}
-
-// Label of token t from the K row staged in LDS (wave 0), written to the
-// label cache exactly as the label kernel writes it; its score (same
-// operation order as the label-vector scores) goes to f.snew.
-template <bool INT4, typename F>
-__device__ __forceinline__ void append_label(const LabelArgs& la, int row, int t, F& f, int r,
-                                             bool with_score) {
-  const int lane = threadIdx.x;  // wave 0 only
-  const int64_t slot = (int64_t)row * la.slots + t;
-  float sf = 1.0f;
-  if (!INT4) {
-    for (int j = lane; j < r; j += 64) {
-      const __half v = f.knew[f.chan[j]];
-      la.lab16[slot * r + j] = v;
-      f.lnew[j] = h2f(v);
-    }
-  } else {
-    float amax = 0.0f;
-    for (int j = lane; j < r; j += 64) amax = fmaxf(amax, fabsf(h2f(f.knew[f.chan[j]])));
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-    const __half s16 = __float2half_rn(amax / 7.0f);  // IEEE division, round to nearest even
-    sf = h2f(s16);
-    for (int j = lane; j < r; j += 64) {
-      float v = 0.0f;
-      if (sf != 0.0f) v = fminf(fmaxf(rintf(h2f(f.knew[f.chan[j]]) / sf), -7.0f), 7.0f);
-      f.lnew[j] = v;
-    }
-    __builtin_amdgcn_wave_barrier();
-    for (int p = lane; p < (r >> 1); p += 64) {
-      const int c0 = (int)f.lnew[2 * p], c1 = (int)f.lnew[2 * p + 1];
-      la.codes[slot * (r >> 1) + p] = (uint8_t)((c0 & 0xF) | ((c1 & 0xF) << 4));
-    }
-    if (lane == 0) la.scales[slot] = s16;
-  }
-  __builtin_amdgcn_wave_barrier();
-  if (with_score && lane == 0) {
-    float acc = 0.0f;
-    for (int j = 0; j < r; ++j) acc = fmaf(f.qg[j], f.lnew[j], acc);
-    f.snew = INT4 ? sf * acc : acc;
-  }
-}
-
 template <int R, bool INT4, int TPT>
 __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs aa, LabelArgs la,
                                                       int append) {

@@ -15,14 +15,17 @@
 
 namespace ds {
 
-// Rows whose scores fit this many fp32 keys in LDS take the fused
-// score+select kernel (one workgroup per (batch, KV head) row).
-constexpr int kFuseMaxTokens = 12288;
 // The fully fused decode kernel (append + score + select + attention in one
 // 256-thread workgroup per row) keeps up to TPT scores per thread in
 // registers and the selected token list in LDS.
 constexpr int kDecodeFusedTPT = 24;  // rows up to 6144 tokens
 constexpr int kDecodeFusedMaxK = 2048;
+// Local top-M select: chunk workgroups keep a superset of their share of the
+// top k (at most kMergeCap candidates per row in all), then one workgroup per
+// row selects exactly among the candidates.
+constexpr int kMergeCap = 16384;
+constexpr int kMaxLocalChunks = 256;
+constexpr int kLocalTPT = 16;  // chunk tokens per thread (chunks up to 4096 tokens)
 // Attention splits per row are capped; partial results cost 528 B each.
 constexpr int kMaxSplit = 64;
 // Selected-token indices staged in LDS per attention workgroup.
@@ -75,6 +78,13 @@ struct ScoreArgs {
   int32_t keys_stride;
   int32_t chunk;        // tokens per score workgroup (chunked path)
   int32_t n_chunks;
+  // local top-M path: per row kMergeCap candidate slots, chunk c owns
+  // [c * cap_row, (c + 1) * cap_row) with cap_row = kMergeCap / chunks_of_row
+  uint32_t* cand_key;   // [rows][kMergeCap]
+  int32_t* cand_idx;    // [rows][kMergeCap]
+  int32_t* cand_cnt;    // [rows][n_chunks], -1: overflow
+  uint32_t* cand_theta; // [rows][n_chunks], smallest kept key (0: chunk kept whole)
+  int32_t cand_stride;  // candidate slots per row (<= kMergeCap)
 };
 
 struct AttnArgs {
@@ -99,7 +109,6 @@ struct AttnArgs {
 
 // Launchers (return the launch status of the last kernel they enqueue).
 hipError_t launch_label(const LabelArgs& a, int n_blocks, hipStream_t s);
-hipError_t launch_score_select_fused(const ScoreArgs& a, int rows, hipStream_t s);
 hipError_t launch_score_chunks(const ScoreArgs& a, int rows, hipStream_t s);
 hipError_t launch_select_stream(const ScoreArgs& a, int rows, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int rows, int G, bool final_out, hipStream_t s);
@@ -107,6 +116,9 @@ hipError_t launch_combine(const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_decode_fused(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la,
                                int append, int rows, hipStream_t s);
 bool decode_fused_fits(int max_seq, int k, int r, int is_int4);
+hipError_t launch_score_local(const ScoreArgs& sa, const LabelArgs& la, int append, int rows,
+                              hipStream_t s);
+hipError_t launch_select_merge(const ScoreArgs& sa, int rows, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Device helpers.

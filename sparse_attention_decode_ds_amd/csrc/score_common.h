@@ -516,6 +516,226 @@ __device__ void emit_global(const uint32_t* keys, int n, Threshold th, int32_t* 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Helpers for register-resident scores (one score per slot, tokens ordered
+// round-major across the workgroup).
+// ---------------------------------------------------------------------------
+// Inclusive prefix sum over the 64 lanes of a wave (DPP: shifts within rows
+// of 16, then row broadcasts).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false); // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false); // row_bcast:31
+  return x;
+}
+
+__device__ __forceinline__ uint32_t bin_of(float s, float mn, float scale) {
+  float x = (s - mn) * scale;
+  x = fminf(fmaxf(x, 0.0f), 2047.0f);  // NaN (0 * inf) maps to 0
+  return (uint32_t)x;
+}
+
+// Label of token t from the K row staged in LDS (wave 0), written to the
+// label cache exactly as the label kernel writes it; its score (same
+// operation order as the label-vector scores) goes to f.snew.
+template <bool INT4, typename F>
+__device__ __forceinline__ void append_label(const LabelArgs& la, int row, int t, F& f, int r,
+                                             bool with_score) {
+  const int lane = threadIdx.x & 63;  // one wave
+  const int64_t slot = (int64_t)row * la.slots + t;
+  float sf = 1.0f;
+  if (!INT4) {
+    for (int j = lane; j < r; j += 64) {
+      const __half v = f.knew[f.chan[j]];
+      la.lab16[slot * r + j] = v;
+      f.lnew[j] = h2f(v);
+    }
+  } else {
+    float amax = 0.0f;
+    for (int j = lane; j < r; j += 64) amax = fmaxf(amax, fabsf(h2f(f.knew[f.chan[j]])));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    const __half s16 = __float2half_rn(amax / 7.0f);  // IEEE division, round to nearest even
+    sf = h2f(s16);
+    for (int j = lane; j < r; j += 64) {
+      float v = 0.0f;
+      if (sf != 0.0f) v = fminf(fmaxf(rintf(h2f(f.knew[f.chan[j]]) / sf), -7.0f), 7.0f);
+      f.lnew[j] = v;
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int p = lane; p < (r >> 1); p += 64) {
+      const int c0 = (int)f.lnew[2 * p], c1 = (int)f.lnew[2 * p + 1];
+      la.codes[slot * (r >> 1) + p] = (uint8_t)((c0 & 0xF) | ((c1 & 0xF) << 4));
+    }
+    if (lane == 0) la.scales[slot] = s16;
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (with_score && lane == 0) {
+    float acc = 0.0f;
+    for (int j = 0; j < r; ++j) acc = fmaf(f.qg[j], f.lnew[j], acc);
+    f.snew = INT4 ? sf * acc : acc;
+  }
+}
+
+// Register-resident selection.  Thread tid holds items (j * NT + tid) * VT + e
+// for rounds j < JMAX and elements e < VT in sc[j * VT + e]; valid(j, e) says
+// whether that slot holds an item, order(j, e) gives its position in the row
+// (ties go to the lower position).  The k largest are characterised by two
+// keys e_lo <= e_hi and a quota: items with key > e_hi are taken, items with
+// key in [e_lo, e_hi] are taken lowest position first, `need` of them.  Items
+// of the boundary linear bin span [kmin, kmax] and bins are monotone, so a key
+// inside that span lies in the boundary bin.
+struct RegSel {
+  uint32_t e_lo, e_hi, need;
+};
+
+template <int NT, int VT, int JMAX, typename Valid, typename Order>
+__device__ RegSel reg_select(const float* sc, Valid valid, Order order, uint32_t k, float mn,
+                             float mx, SelScratch& ss, uint32_t* scan_tmp) {
+  const int tid = threadIdx.x;
+  const float bscale = 2048.0f / (mx - mn);  // +inf when all scores are equal: every key in bin 0
+  for (int i = tid; i < kHistBins; i += NT) ss.hist[i] = 0u;
+  if (tid < 8) ss.misc[tid] = tid == 3 ? 0xFFFFFFFFu : 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < JMAX; ++j)
+#pragma unroll
+    for (int e = 0; e < VT; ++e)
+      if (valid(j, e)) atomicAdd(&ss.hist[bin_of(sc[j * VT + e], mn, bscale)], 1u);
+  __syncthreads();
+  find_digit<NT>(ss.hist, k, ss.misc + 4, scan_tmp);
+  const uint32_t bstar = ss.misc[4];
+  const uint32_t cnt = ss.misc[6];
+  RegSel r;
+  r.need = k - ss.misc[5];
+  const bool few = cnt <= (uint32_t)kRankMax;
+#pragma unroll
+  for (int j = 0; j < JMAX; ++j)
+#pragma unroll
+    for (int e = 0; e < VT; ++e)
+      if (valid(j, e) && bin_of(sc[j * VT + e], mn, bscale) == bstar) {
+        const uint32_t key = score_key(sc[j * VT + e]);
+        atomicMin(&ss.misc[3], key);
+        atomicMax(&ss.misc[7], key);
+        if (few) {
+          const uint32_t pos = atomicAdd(&ss.misc[0], 1u);
+          ss.cand_key[pos] = key;
+          ss.cand_idx[pos] = order(j, e);
+        }
+      }
+  __syncthreads();
+  r.e_lo = ss.misc[3];
+  r.e_hi = ss.misc[7];
+  if (cnt == r.need) return r;  // the whole boundary bin is taken
+  if (few) {
+    for (int i = tid; i < (int)cnt; i += NT) {
+      const uint32_t ki = ss.cand_key[i];
+      const int ti = ss.cand_idx[i];
+      uint32_t rank = 0;
+      for (int m = 0; m < (int)cnt; ++m) {
+        const uint32_t km = ss.cand_key[m];
+        rank += (km > ki) || (km == ki && ss.cand_idx[m] < ti);
+      }
+      if (rank == r.need - 1) ss.misc[1] = ki;  // the last key taken
+    }
+    __syncthreads();
+    const uint32_t T = ss.misc[1];
+    for (int i = tid; i < (int)cnt; i += NT)
+      if (ss.cand_key[i] > T) atomicAdd(&ss.misc[2], 1u);
+    __syncthreads();
+    r.e_lo = r.e_hi = T;
+    r.need -= ss.misc[2];
+    return r;
+  }
+  // Many keys in the boundary bin (clustered or equal scores): radix passes
+  // over the key bits inside it.
+  uint32_t prefix = 0u, pmask = 0u;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
+    __syncthreads();
+    for (int i = tid; i < kHistBins; i += NT) ss.hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < JMAX; ++j)
+#pragma unroll
+      for (int e = 0; e < VT; ++e) {
+        if (!valid(j, e)) continue;
+        const float sv = sc[j * VT + e];
+        const uint32_t key = score_key(sv);
+        if ((key & pmask) == prefix && bin_of(sv, mn, bscale) == bstar)
+          atomicAdd(&ss.hist[(key >> shift) & dmask], 1u);
+      }
+    __syncthreads();
+    find_digit<NT>(ss.hist, r.need, ss.misc + 4, scan_tmp);
+    const uint32_t d = ss.misc[4], ab = ss.misc[5], c2 = ss.misc[6];
+    prefix |= d << shift;
+    pmask |= dmask << shift;
+    r.need -= ab;
+    if (c2 == r.need) break;
+  }
+  __syncthreads();
+  r.e_lo = max(r.e_lo, prefix);
+  r.e_hi = min(r.e_hi, prefix | ~pmask);
+  return r;
+}
+
+// Ordered emission of the items taken by `r`: put(pos, j, e) with pos the
+// item's rank among the taken items in position order.  tot holds
+// JMAX * (NT / 64) words of LDS.  One barrier.
+template <int NT, int VT, int JMAX, typename Valid, typename Put>
+__device__ __forceinline__ void reg_emit(const float* sc, Valid valid, const RegSel& r,
+                                         uint32_t* tot, Put put) {
+  constexpr int W = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  auto cls = [&](float sv) {
+    const uint32_t key = score_key(sv);
+    return key > r.e_hi ? 2 : (key >= r.e_lo ? 1 : 0);
+  };
+  uint32_t ex[JMAX];
+#pragma unroll
+  for (int j = 0; j < JMAX; ++j) {
+    uint32_t packed = 0u;
+#pragma unroll
+    for (int e = 0; e < VT; ++e) {
+      if (!valid(j, e)) continue;
+      const int cl = cls(sc[j * VT + e]);
+      packed += cl == 2 ? 1u : (cl == 1 ? 0x10000u : 0u);
+    }
+    const uint32_t incl = wave_incl_scan(packed);
+    ex[j] = incl - packed;
+    if (lane == 63) tot[j * W + w] = incl;
+  }
+  __syncthreads();
+  uint32_t run = 0u;
+#pragma unroll
+  for (int j = 0; j < JMAX; ++j) {
+    uint32_t pre = 0u, rowt = 0u;
+#pragma unroll
+    for (int ww = 0; ww < W; ++ww) {
+      const uint32_t t = tot[j * W + ww];
+      pre += ww < w ? t : 0u;
+      rowt += t;
+    }
+    const uint32_t base = run + pre + ex[j];
+    uint32_t ab = base & 0xFFFFu, eb = base >> 16;
+#pragma unroll
+    for (int e = 0; e < VT; ++e) {
+      if (!valid(j, e)) continue;
+      const int cl = cls(sc[j * VT + e]);
+      if (cl == 2 || (cl == 1 && eb < r.need)) put(ab + min(eb, r.need), j, e);
+      ab += cl == 2;
+      eb += cl == 1;
+    }
+    run += rowt;
+  }
+}
+
 __device__ __forceinline__ int row_len(const ScoreArgs& a, int b) {
   return min(max(a.seq_lens[b], 0), a.max_seq);
 }

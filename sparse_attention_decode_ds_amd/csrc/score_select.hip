@@ -1,13 +1,8 @@
-// score_select.hip -- standalone score and select kernels (steps 1-2 and 3a
-// of a Double Sparsity decode step, [DS] "online forward computation"), used
-// when the attention runs as a separate pass.
-//
-//  * k_score_select: one workgroup per (batch, KV head) row for rows that fit
-//    in LDS; scores become keys in LDS and the linear-bin select of
-//    score_common.h picks the top k.
-//  * k_score_chunk + k_select_stream: rows too long for LDS; many workgroups
-//    per row write keys to the workspace, then one workgroup per row runs a
-//    radix select over them (they are still cache resident).
+// score_select.hip -- streaming score and select kernels (steps 1-2 and 3a
+// of a Double Sparsity decode step, [DS] "online forward computation") for
+// rows outside the other paths' limits: many workgroups per row write every
+// score as a key to the workspace, then one workgroup per row runs a radix
+// select over them (they are still cache resident).
 #include "score_common.h"
 
 namespace ds {
@@ -31,40 +26,6 @@ __device__ __forceinline__ void finish_row(const ScoreArgs& a, int row) {
   if (a.pad_idx)
     for (int t = a.k + threadIdx.x; t < a.idx_stride; t += NT) out[t] = -1;
   if (threadIdx.x == 0) a.count[row] = a.k;
-}
-
-template <int NT, int R, bool INT4>
-__global__ __launch_bounds__(NT) void k_score_select(ScoreArgs a) {
-  extern __shared__ uint32_t keys[];
-  __shared__ float qg[128];
-  __shared__ SelScratch sc;
-  __shared__ uint32_t scan_tmp[NT / 64];
-  __shared__ float mm_tmp[2 * NT / 64];
-
-  const int row = blockIdx.x;
-  const int b = row / a.Hkv;
-  const int g = row - b * a.Hkv;
-  const int S = row_len(a, b);
-  if (emit_all_if_short<NT>(a, row, S)) return;
-
-  const RowPtrs p = row_ptrs(a, row);
-  float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
-  score_range<NT, R, INT4>(
-      a, p, qg, 0, S,
-      [&](int t, float s, uint32_t key) {
-        keys[t] = key;
-        mn = fminf(mn, s);
-        mx = fmaxf(mx, s);
-      },
-      [&]() {
-        gather_query(a, b, g, qg);
-        __syncthreads();
-      });
-  block_minmax<NT>(mn, mx, mm_tmp);  // its barriers also publish keys[]
-  const Sel s = select_lds<NT>(keys, S, (uint32_t)a.k, mn, mx, sc, scan_tmp);
-  int32_t* out = a.idx + (int64_t)row * a.idx_stride;
-  emit_sel_lds<NT>(keys, S, s, [&](int pos, int t) { out[pos] = t; }, scan_tmp);
-  finish_row<NT>(a, row);
 }
 
 template <int NT, int R, bool INT4>
@@ -104,7 +65,6 @@ __global__ __launch_bounds__(NT) void k_select_stream(ScoreArgs a) {
   finish_row<NT>(a, row);
 }
 
-constexpr int kFusedThreads = 256;
 constexpr int kChunkThreads = 256;
 constexpr int kSelectThreads = 1024;
 
@@ -123,23 +83,11 @@ struct Pick {
 };
 
 template <int NT, int R, bool INT4>
-struct FusedK {
-  static constexpr auto fn = k_score_select<NT, R, INT4>;
-};
-template <int NT, int R, bool INT4>
 struct ChunkK {
   static constexpr auto fn = k_score_chunk<NT, R, INT4>;
 };
 
 }  // namespace
-
-hipError_t launch_score_select_fused(const ScoreArgs& a, int rows, hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  void* fn = Pick<FusedK, kFusedThreads>::get(a.r, a.is_int4 != 0);
-  const size_t lds = (size_t)max(a.max_seq, 1) * sizeof(uint32_t);
-  void* args[] = {const_cast<ScoreArgs*>(&a)};
-  return hipLaunchKernel(fn, dim3(rows), dim3(kFusedThreads), args, lds, s);
-}
 
 hipError_t launch_score_chunks(const ScoreArgs& a, int rows, hipStream_t s) {
   if (rows <= 0 || a.n_chunks <= 0) return hipSuccess;

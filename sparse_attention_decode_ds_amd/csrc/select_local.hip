@@ -1,0 +1,439 @@
+// select_local.hip -- exact top-k for long rows in two kernels ([DS] "online
+// forward computation", steps 1-3a), without writing every score to memory.
+//
+// k_score_local: one workgroup per (row, chunk of CH tokens).  It appends the
+//   current token's label when the chunk holds it ([DS] "offline
+//   calibration"), scores the chunk into registers and keeps a superset of
+//   the chunk's share of the row's top k: with quota M, every token whose
+//   linear bin (between the chunk's min and max score) is at or above the bin
+//   of the chunk's M-th largest score.  Kept tokens (key, index) go to the
+//   row's candidate area in ascending index order, together with the
+//   smallest kept key theta (0 when the chunk is kept whole).
+//
+// k_select_merge: one workgroup per row gathers the candidates (chunk order,
+//   so ascending token order), selects the k largest exactly (linear bins +
+//   exact boundary resolution, score_common.h) and emits them in order.  The
+//   result is exact when every chunk that dropped tokens has theta <= the
+//   smallest selected key (every dropped key is then strictly smaller).  If a
+//   chunk overflowed its slots or that check fails, the workgroup re-scores
+//   the whole row into the workspace and runs a plain radix select over it.
+#include "score_common.h"
+
+namespace ds {
+namespace {
+
+constexpr int kNTL = 256;
+constexpr int kWavesL = kNTL / 64;
+constexpr int kNTM = 1024;
+
+__device__ __forceinline__ int chunks_of(int S, int CH) { return (S + CH - 1) / CH; }
+__device__ __forceinline__ int cap_of(int stride, int n_ch) { return stride / max(n_ch, 1); }
+// Quota per chunk: twice the expected share of the top k (at least 64),
+// bounded by the chunk size and by 7/8 of the chunk's candidate slots.
+__device__ __forceinline__ int quota_of(int S, int k, int CH, int cap) {
+  const float expected = (float)k * (float)CH / (float)S;
+  int m = max(64, (int)(2.0f * expected) + 1);
+  m = min(m, CH);
+  m = min(m, cap - cap / 8);
+  return m;
+}
+
+struct LocalScratch {
+  __half qrows[kMaxGroup][256];
+  int32_t chan[128];
+  int32_t keep[128];
+  __half knew[128];
+  float lnew[128];
+  float qg[128];
+  float snew;
+  float mm_tmp[2 * kWavesL];
+  uint32_t scan_tmp[kWavesL];
+  SelScratch sel;
+  uint32_t tot[kLocalTPT][kWavesL];
+  uint32_t theta;
+};
+
+template <int R, bool INT4>
+__global__ __launch_bounds__(kNTL, 4) void k_score_local(ScoreArgs sa, LabelArgs la, int append) {
+  using Vec = typename VecSel<R, INT4>::type;
+  constexpr int VT = Vec::VT;
+  constexpr int JMAX = kLocalTPT / VT;
+  constexpr int UNR = 4;
+  constexpr int QR = R > 0 ? R : 1;
+  __shared__ LocalScratch f;
+
+  const int row = blockIdx.x / sa.n_chunks;
+  const int c = blockIdx.x - row * sa.n_chunks;
+  const int b = row / sa.Hkv;
+  const int g = row - b * sa.Hkv;
+  const int S = row_len(sa, b);
+  const int CH = sa.chunk;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int r = sa.r;
+  const int t_beg = c * CH;
+  const int t_end = min(S, t_beg + CH);
+  if (t_beg >= t_end) return;
+  const int t_new = S - 1;
+  const bool has_new = append && t_new >= t_beg && t_new < t_end;
+  const bool sparse = S > sa.k;
+
+  // --- setup: small loads first --------------------------------------------
+  if (sparse) {
+    const __half* qh = sa.q + ((int64_t)b * sa.Hq + (int64_t)g * sa.G) * sa.d_q;
+    for (int i = tid; i < sa.G * sa.d_q; i += kNTL) f.qrows[i / sa.d_q][i % sa.d_q] = qh[i];
+    if (sa.keep)
+      for (int i = tid; i < sa.d_k; i += kNTL) f.keep[i] = sa.keep[(int64_t)g * sa.d_k + i];
+  }
+  for (int j = tid; j < r; j += kNTL) f.chan[j] = sa.chan[(int64_t)g * r + j];
+  if (has_new && tid < (la.d_k >> 3)) {
+    const __half* kr = la.K + (int64_t)b * la.ks0 + (int64_t)g * la.ks1 + (int64_t)t_new * la.ks2;
+    *reinterpret_cast<uint4*>(&f.knew[tid * 8]) = *reinterpret_cast<const uint4*>(kr + tid * 8);
+  }
+  if (!sparse) {  // the row attends every token; only the label append is due
+    __syncthreads();
+    if (has_new && tid < 64) append_label<INT4>(la, row, t_new, f, r, false);
+    return;
+  }
+
+  const RowPtrs p = row_ptrs(sa, row);
+  const int n_vec = (t_end - t_beg + VT - 1) / VT;
+  const int v0 = t_beg / VT;
+  const int J = (n_vec + kNTL - 1) / kNTL;
+  Vec vec[UNR];
+#pragma unroll
+  for (int u = 0; u < UNR; ++u) {
+    const int v = u * kNTL + tid;
+    if (v < n_vec) vec[u].load(p, v0 + v);
+  }
+  __syncthreads();
+  if (tid < r) {
+    const int col = f.chan[tid];
+    const int qc = sa.keep ? f.keep[col] : col;
+    float acc = 0.0f;
+    for (int h = 0; h < sa.G; ++h) acc += h2f(f.qrows[h][qc]);
+    f.qg[tid] = acc;
+  }
+  __syncthreads();
+  if (has_new && tid < 64) append_label<INT4>(la, row, t_new, f, r, true);
+  float qreg[QR];
+  const float* qg = f.qg;
+  if (R > 0) {
+#pragma unroll
+    for (int j = 0; j < QR; ++j) qreg[j] = f.qg[j];
+    qg = qreg;
+  }
+
+  // --- score into registers --------------------------------------------------
+  auto token = [&](int j, int e) { return t_beg + (j * kNTL + tid) * VT + e; };
+  auto valid = [&](int j, int e) { return token(j, e) < t_end; };
+  float sc[kLocalTPT];
+  float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
+#pragma unroll
+  for (int j0 = 0; j0 < JMAX; j0 += UNR) {
+    if (j0 > 0) {
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int v = (j0 + u) * kNTL + tid;
+        if (j0 + u < JMAX && v < n_vec) vec[u].load(p, v0 + v);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int j = j0 + u;
+      if (j >= JMAX) continue;
+      const int v = j * kNTL + tid;
+      float s[VT];
+#pragma unroll
+      for (int e = 0; e < VT; ++e) s[e] = 0.0f;
+      if (v < n_vec) vec[u].score(qg, r, s);
+#pragma unroll
+      for (int e = 0; e < VT; ++e) {
+        sc[j * VT + e] = s[e];
+        if (v < n_vec && valid(j, e) && !(has_new && token(j, e) == t_new)) {
+          mn = fminf(mn, s[e]);
+          mx = fmaxf(mx, s[e]);
+        }
+      }
+    }
+  }
+  if (has_new) {
+    __syncthreads();
+    const float sn = f.snew;
+#pragma unroll
+    for (int j = 0; j < JMAX; ++j)
+#pragma unroll
+      for (int e = 0; e < VT; ++e)
+        if (token(j, e) == t_new) sc[j * VT + e] = sn;
+    mn = fminf(mn, sn);
+    mx = fmaxf(mx, sn);
+  }
+
+  // --- local threshold ---------------------------------------------------------
+  const int n_ch = chunks_of(S, CH);
+  const int cap = cap_of(sa.cand_stride, n_ch);
+  const int M = quota_of(S, sa.k, CH, cap);
+  const int n_c = t_end - t_beg;
+  const bool keep_all = n_c <= M;
+  int kept = n_c;
+  // bit (j * VT + e) of keptm: slot kept (valid and at or above the quota bin)
+  uint32_t keptm = 0u;
+  uint32_t tmin = 0xFFFFFFFFu;
+  if (!keep_all) {
+    block_minmax<kNTL>(mn, mx, f.mm_tmp);
+    const float bmn = mn;
+    const float bscale = 2048.0f / (mx - mn);  // +inf if all equal: every key in bin 0
+    SelScratch& ss = f.sel;
+    for (int i = tid; i < kHistBins; i += kNTL) ss.hist[i] = 0u;
+    if (tid == 0) f.theta = 0xFFFFFFFFu;
+    __syncthreads();
+    uint32_t bins[kLocalTPT];
+#pragma unroll
+    for (int j = 0; j < JMAX; ++j)
+#pragma unroll
+      for (int e = 0; e < VT; ++e) {
+        bins[j * VT + e] = bin_of(sc[j * VT + e], bmn, bscale);
+        if (j < J && valid(j, e)) atomicAdd(&ss.hist[bins[j * VT + e]], 1u);
+      }
+    __syncthreads();
+    find_digit<kNTL>(ss.hist, (uint32_t)M, ss.misc + 4, f.scan_tmp);
+    const uint32_t bM = ss.misc[4];
+    kept = (int)(ss.misc[5] + ss.misc[6]);
+    if (kept > cap) {  // the boundary bin is too full for this chunk's slots
+      if (tid == 0) sa.cand_cnt[(int64_t)row * sa.n_chunks + c] = -1;
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < JMAX; ++j)
+#pragma unroll
+      for (int e = 0; e < VT; ++e)
+        if (j < J && valid(j, e) && bins[j * VT + e] >= bM) {
+          keptm |= 1u << (j * VT + e);
+          if (bins[j * VT + e] == bM) tmin = min(tmin, score_key(sc[j * VT + e]));
+        }
+  } else {
+#pragma unroll
+    for (int j = 0; j < JMAX; ++j)
+#pragma unroll
+      for (int e = 0; e < VT; ++e)
+        if (j < J && valid(j, e)) keptm |= 1u << (j * VT + e);
+  }
+
+  // --- ordered emission of the kept tokens ---------------------------------------
+  uint32_t* ck = sa.cand_key + (int64_t)row * sa.cand_stride + (int64_t)c * cap;
+  int32_t* ci = sa.cand_idx + (int64_t)row * sa.cand_stride + (int64_t)c * cap;
+  uint32_t ex[JMAX];
+#pragma unroll
+  for (int j = 0; j < JMAX; ++j) {
+    ex[j] = 0u;
+    if (j >= J) continue;
+    const uint32_t cnt = __builtin_popcount((keptm >> (j * VT)) & ((1u << VT) - 1u));
+    const uint32_t incl = wave_incl_scan(cnt);
+    ex[j] = incl - cnt;
+    if (lane == 63) f.tot[j][w] = incl;
+  }
+  if (!keep_all) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) tmin = min(tmin, (uint32_t)__shfl_xor((int)tmin, o, 64));
+    if (lane == 0) atomicMin(&f.theta, tmin);
+  }
+  __syncthreads();
+  uint32_t run = 0u;
+#pragma unroll
+  for (int j = 0; j < JMAX; ++j) {
+    if (j >= J) continue;
+    uint32_t pre = 0u, rowt = 0u;
+#pragma unroll
+    for (int ww = 0; ww < kWavesL; ++ww) {
+      const uint32_t t = f.tot[j][ww];
+      pre += ww < w ? t : 0u;
+      rowt += t;
+    }
+    uint32_t pos = run + pre + ex[j];
+#pragma unroll
+    for (int e = 0; e < VT; ++e) {
+      if (keptm & (1u << (j * VT + e))) {
+        ck[pos] = score_key(sc[j * VT + e]);
+        ci[pos] = token(j, e);
+        ++pos;
+      }
+    }
+    run += rowt;
+  }
+  if (tid == 0) {
+    sa.cand_cnt[(int64_t)row * sa.n_chunks + c] = kept;
+    sa.cand_theta[(int64_t)row * sa.n_chunks + c] = keep_all ? 0u : f.theta;
+  }
+}
+
+struct MergeScratch {
+  uint32_t keys[kMergeCap];
+  int32_t idx[kMergeCap];
+  SelScratch sel;
+  int32_t ch_off[kMaxLocalChunks + 1];
+  uint32_t ch_theta[kMaxLocalChunks];
+  uint32_t scan_tmp[kNTM / 64];
+  float mm_tmp[2 * kNTM / 64];
+  uint32_t flag;  // 1: fall back to the full select
+  uint32_t tmin;  // smallest selected key
+};
+
+template <int R, bool INT4>
+__global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
+  __shared__ MergeScratch f;
+  const int row = blockIdx.x;
+  const int b = row / sa.Hkv;
+  const int g = row - b * sa.Hkv;
+  const int S = row_len(sa, b);
+  const int tid = threadIdx.x;
+  int32_t* out = sa.idx + (int64_t)row * sa.idx_stride;
+
+  if (S <= sa.k) {  // every token
+    for (int t = tid; t < S; t += kNTM) out[t] = t;
+    if (sa.pad_idx)
+      for (int t = S + tid; t < sa.idx_stride; t += kNTM) out[t] = -1;
+    if (tid == 0) sa.count[row] = S;
+    return;
+  }
+  const int n_ch = chunks_of(S, sa.chunk);
+  const int cap = cap_of(sa.cand_stride, n_ch);
+  if (tid == 0) {
+    uint32_t bad = n_ch > kMaxLocalChunks ? 1u : 0u;
+    int off = 0;
+    for (int c = 0; c < n_ch && !bad; ++c) {
+      const int cnt = sa.cand_cnt[(int64_t)row * sa.n_chunks + c];
+      if (cnt < 0 || cnt > cap) bad = 1u;
+      f.ch_off[c] = off;
+      f.ch_theta[c] = sa.cand_theta[(int64_t)row * sa.n_chunks + c];
+      off += max(cnt, 0);
+    }
+    f.ch_off[min(n_ch, kMaxLocalChunks)] = off;
+    if (off < sa.k) bad = 1u;
+    f.flag = bad;
+    f.tmin = 0xFFFFFFFFu;
+  }
+  __syncthreads();
+  bool full = f.flag != 0u;
+
+  if (!full) {
+    const int n = f.ch_off[n_ch];
+    float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
+    // Gather the chunk segments into one ordered array: every slot of the
+    // candidate area is visited once, all loads independent.
+    const uint32_t* ck = sa.cand_key + (int64_t)row * sa.cand_stride;
+    const int32_t* ci = sa.cand_idx + (int64_t)row * sa.cand_stride;
+    const int slots = n_ch * cap;
+    constexpr int U = 4;
+    for (int i0 = tid; i0 < slots; i0 += kNTM * U) {
+      uint32_t kk[U];
+      int32_t ii[U];
+      int dst[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * kNTM;
+        dst[u] = -1;
+        if (i < slots) {
+          const int c = i / cap;
+          const int j = i - c * cap;
+          if (j < f.ch_off[c + 1] - f.ch_off[c]) {
+            dst[u] = f.ch_off[c] + j;
+            kk[u] = ck[i];
+            ii[u] = ci[i];
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (dst[u] >= 0) {
+          f.keys[dst[u]] = kk[u];
+          f.idx[dst[u]] = ii[u];
+          const float sv = key_float(kk[u]);
+          mn = fminf(mn, sv);
+          mx = fmaxf(mx, sv);
+        }
+      }
+    }
+    block_minmax<kNTM>(mn, mx, f.mm_tmp);  // its barriers also publish keys[] and idx[]
+    const Sel s = select_lds<kNTM>(f.keys, n, (uint32_t)sa.k, mn, mx, f.sel, f.scan_tmp);
+    uint32_t tmin = 0xFFFFFFFFu;
+    emit_sel_lds<kNTM>(
+        f.keys, n, s,
+        [&](int pos, int t) {
+          out[pos] = f.idx[t];
+          tmin = min(tmin, f.keys[t]);
+        },
+        f.scan_tmp);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) tmin = min(tmin, (uint32_t)__shfl_xor((int)tmin, o, 64));
+    if ((tid & 63) == 0) atomicMin(&f.tmin, tmin);
+    __syncthreads();
+    if (tid < n_ch && f.ch_theta[tid] > f.tmin) atomicOr(&f.flag, 1u);
+    __syncthreads();
+    full = f.flag != 0u;
+  }
+
+  if (full) {
+    // Re-score the whole row into the workspace, then a radix select over it.
+    __shared__ float qg[128];
+    const RowPtrs p = row_ptrs(sa, row);
+    uint32_t* kr = sa.keys + (int64_t)row * sa.keys_stride;
+    score_range<kNTM, R, INT4>(
+        sa, p, qg, 0, S, [&](int t, float, uint32_t key) { kr[t] = key; },
+        [&]() {
+          gather_query(sa, b, g, qg);
+          __syncthreads();
+        });
+    __threadfence_block();
+    __syncthreads();
+    const Threshold th =
+        radix_select_global<kNTM>(kr, S, (uint32_t)sa.k, f.sel.hist, f.scan_tmp, f.sel.misc);
+    emit_global<kNTM>(kr, S, th, out, f.scan_tmp);
+  }
+  if (sa.pad_idx)
+    for (int t = sa.k + tid; t < sa.idx_stride; t += kNTM) out[t] = -1;
+  if (tid == 0) sa.count[row] = sa.k;
+}
+
+template <int R, bool INT4>
+hipError_t launch_local_rt(const ScoreArgs& sa, const LabelArgs& la, int append, int rows,
+                           hipStream_t s) {
+  hipLaunchKernelGGL((k_score_local<R, INT4>), dim3(rows * sa.n_chunks), dim3(kNTL), 0, s, sa, la,
+                     append);
+  return hipGetLastError();
+}
+
+template <int R, bool INT4>
+hipError_t launch_merge_rt(const ScoreArgs& sa, int rows, hipStream_t s) {
+  hipLaunchKernelGGL((k_select_merge<R, INT4>), dim3(rows), dim3(kNTM), 0, s, sa);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_score_local(const ScoreArgs& sa, const LabelArgs& la, int append, int rows,
+                              hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (sa.is_int4) {
+    if (sa.r == 8) return launch_local_rt<8, true>(sa, la, append, rows, s);
+    if (sa.r == 16) return launch_local_rt<16, true>(sa, la, append, rows, s);
+    return launch_local_rt<0, true>(sa, la, append, rows, s);
+  }
+  if (sa.r == 8) return launch_local_rt<8, false>(sa, la, append, rows, s);
+  if (sa.r == 16) return launch_local_rt<16, false>(sa, la, append, rows, s);
+  return launch_local_rt<0, false>(sa, la, append, rows, s);
+}
+
+hipError_t launch_select_merge(const ScoreArgs& sa, int rows, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (sa.is_int4) {
+    if (sa.r == 8) return launch_merge_rt<8, true>(sa, rows, s);
+    if (sa.r == 16) return launch_merge_rt<16, true>(sa, rows, s);
+    return launch_merge_rt<0, true>(sa, rows, s);
+  }
+  if (sa.r == 8) return launch_merge_rt<8, false>(sa, rows, s);
+  if (sa.r == 16) return launch_merge_rt<16, false>(sa, rows, s);
+  return launch_merge_rt<0, false>(sa, rows, s);
+}
+
+}  // namespace ds

@@ -128,7 +128,7 @@ def _small_inputs(name, **over):
 
 
 @pytest.mark.parametrize("name", sorted(SMALL))
-@pytest.mark.parametrize("mode", ["default", "unfused", "split3", "append_flag"])
+@pytest.mark.parametrize("mode", ["default", "unfused", "stream", "split3", "append_flag"])
 def test_decode_small(name, mode):
     cfg, inp = _small_inputs(name)
     _note("decode %s %s" % (name, mode))
@@ -143,6 +143,8 @@ def test_decode_small(name, mode):
         pytest.skip("dense: no labels")
     if mode == "unfused":
         kw["flags"] = ds.DECODE_UNFUSED
+    if mode == "stream":
+        kw["flags"] = ds.DECODE_STREAM
     if mode == "split3":
         kw["n_split"] = 3
     seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
@@ -214,6 +216,33 @@ def test_integer_ties_exact():
         out, topk = run(cfg, inp, labels, seq, S, flags=ds.DECODE_UNFUSED if unfused else 0)
         ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k, out,
                             topk, ds_check.sample_rows(cfg, 100), strict_sets=True)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_local_select_fallbacks(mode):
+    """Long rows are pre-selected per chunk, then merged.  mode 0: the whole
+    top k sits in the first chunk (more than its quota), so the merge's
+    completeness check fails; mode 1: a chunk of equal scores overflows its
+    candidate slots.  Both must fall back to the full select and stay exact."""
+    cfg, inp = _small_inputs("mha_int4_r8", B=2, S0=1800, k=100)
+    q = inp.q.float()
+    for b in range(cfg.B):
+        for g in range(cfg.Hkv):
+            ch = inp.chan[g].long()
+            if mode == 0:
+                sgn = torch.sign(q[b, g, ch]).to(torch.float16)
+                sgn[sgn == 0] = 1
+                inp.K[b, g, :150][:, ch] = 60 * sgn
+            else:
+                inp.K[b, g, 512:1024][:, ch] = 0
+    S = cfg.S0 + 1
+    seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
+    labels = prefill(cfg, inp, S)
+    out, topk = run(cfg, inp, labels, seq, S, flags=ds.DECODE_UNFUSED)
+    ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k, out,
+                        topk, ds_check.sample_rows(cfg, 100))
+    if mode == 0:
+        assert (topk < 150).all()
 
 
 def test_split_count_invariance_and_determinism():
