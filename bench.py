@@ -35,16 +35,111 @@ HBM_PEAK_GBS = 8000.0
 
 
 def algorithmic_bytes(cfg, S):
-    """Bytes the step must move for one layer at length S (all rows):
-    labels S*lambda per (b, g), lambda = 2r (fp16) or r/2 + 2 (int4 + fp16
-    scale); min(k, S) K/V rows of (d_k + d_v) * 2 bytes per (b, g); q and out."""
+    """Bytes one step must move for one layer at length S (all rows): the
+    label stream (S * lam per (b, g) row, lam = 2r for fp16 labels, r/2 + 2 for
+    int4 codes + fp16 scale), the min(k, S) selected K/V rows of
+    (d_k + d_v) * 2 bytes per row, the label append (r K values read, lam
+    bytes written per row), the query read and the output written."""
     rows = cfg.B * cfg.Hkv
     lam = 0
     if cfg.k > 0:
         lam = cfg.r // 2 + 2 if cfg.int4 else 2 * cfg.r
     kk = min(cfg.k, S) if cfg.k > 0 else S
-    q_out = cfg.B * cfg.Hq * (cfg.D + cfg.d_v) * 2
-    return {"labels": rows * S * lam, "rows": rows * kk * (cfg.d_k + cfg.d_v) * 2, "q_out": q_out}
+    return {"labels": rows * S * lam,
+            "append": rows * (2 * cfg.r + lam) if cfg.k > 0 else 0,
+            "rows": rows * kk * (cfg.d_k + cfg.d_v) * 2,
+            "q": cfg.B * cfg.Hq * cfg.D * 2,
+            "out": cfg.B * cfg.Hq * cfg.d_v * 2}
+
+
+def dominant_kernel(plan, ab):
+    """The kernel that takes most of a step on this path, its name prefix in
+    profiles, and its algorithmic bytes per launch."""
+    if plan["path"] == "fused":
+        return "k_decode_fused", sum(ab.values())
+    final = plan["n_split"] == 1
+    return "k_attn", ab["rows"] + ab["q"] + (ab["out"] if final else 0)
+
+
+def source_hash():
+    """Hash of the kernel sources: a stored counter record is only used while
+    the kernels it was taken on are unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "sparse_attention_decode_ds_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+
+
+def stored_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the stored counter record, or None
+    if there is none or the kernel sources changed since it was taken."""
+    try:
+        rec = json.load(open(traffic_path(workload)))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash() or rec.get("kernel") != kernel:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def _pmc_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            yield r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"]), r.get("Dispatch_Id")
+
+
+def _pmc_mean(path, counter, match):
+    """Mean over dispatches whose kernel name contains `match` of the counter
+    (values of one dispatch summed, e.g. over XCDs)."""
+    per = {}
+    for name, cn, v, did in _pmc_rows(path):
+        if cn == counter and match in name:
+            per[did] = per.get(did, 0.0) + v
+    return (sum(per.values()) / len(per), len(per)) if per else (None, 0)
+
+
+def write_traffic(args):
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+    WRITE_SIZE, each with --calib-copy-mb) into the stored counter record."""
+    import sparse_attention_decode_ds_amd as ds
+    import synth
+    fetch_csv, write_csv = args.traffic_from
+    cfg = synth.CONFIGS[args.workload]
+    kern = args.traffic_kernel
+    calib_kib = args.calib_copy_mb * 1024.0
+    cf, ncf = _pmc_mean(fetch_csv, "FETCH_SIZE", "neg_kernel")
+    cw, ncw = _pmc_mean(write_csv, "WRITE_SIZE", "neg_kernel")
+    kf, nkf = _pmc_mean(fetch_csv, "FETCH_SIZE", kern)
+    kw, nkw = _pmc_mean(write_csv, "WRITE_SIZE", kern)
+    if None in (cf, cw, kf, kw):
+        print("bench.py: counters missing (calibration %s/%s, kernel %s/%s)" % (cf, cw, kf, kw),
+              file=sys.stderr)
+        return 1
+    f_fetch, f_write = calib_kib / cf, calib_kib / cw
+    rec = {"workload": cfg.name, "kernel": kern, "source_hash": source_hash(),
+           "fetch_kib_per_launch": round(kf, 1), "write_kib_per_launch": round(kw, 1),
+           "dispatches": [nkf, nkw],
+           "calibration": {"copy_mib": args.calib_copy_mb, "fetch_kib": round(cf, 1),
+                           "write_kib": round(cw, 1), "dispatches": [ncf, ncw],
+                           "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4)},
+           "bytes_per_launch": int(round((kf * f_fetch + kw * f_write) * 1024.0)),
+           "commands": args.traffic_cmd or []}
+    dst = args.traffic_out or traffic_path(cfg.name)
+    os.makedirs(os.path.dirname(os.path.abspath(dst)), exist_ok=True)
+    with open(dst, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+    return 0
 
 
 def cpu_baseline(cfg, inp, seconds):
@@ -92,16 +187,24 @@ def main():
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="llama2_7b_4k")
-    ap.add_argument("--layers", type=int, default=8, help="independent layer caches rotated per step")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="independent layer caches rotated per step (0: enough that one "
+                         "rotation is far larger than the Infinity Cache, 2 to 8)")
     ap.add_argument("--n-split", type=int, default=0)
     ap.add_argument("--unfused", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--stage-events", choices=["all", "attn", "none"], default="all",
-                    help="HIP events per timed step: every stage boundary, only around the "
-                         "attention kernel, or none")
+    ap.add_argument("--stage-events", choices=["kernel", "all", "none"], default="kernel",
+                    help="second pass of --steps steps with HIP events around the dominant "
+                         "kernel only, around every stage, or no second pass")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the stored counter record from two rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, WRITE_SIZE counter_collection.csv) and exit")
+    ap.add_argument("--traffic-kernel", default="k_decode_fused")
+    ap.add_argument("--traffic-cmd", action="append", help="command recorded with the counters")
+    ap.add_argument("--traffic-out", default=None, help="record path (default: under profiles/)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -109,6 +212,8 @@ def main():
         print("bench.py: this build runs the decode path on one GPU only; "
               "--gpus %d (WORLD_SIZE %d) is not supported" % (args.gpus, world), file=sys.stderr)
         return 2
+    if args.traffic_from:
+        return write_traffic(args)
 
     import torch
 
@@ -119,15 +224,20 @@ def main():
     torch.cuda.set_device(0)
     lib = ds.load()
     cfg = synth.CONFIGS[args.workload]
-    L = max(1, args.layers)
     dev = "cuda"
+    # Enough layer copies that one rotation moves well over the 256 MB
+    # Infinity Cache (about 1.5 GB of step bytes), 2 to 8 copies.
+    step0 = sum(algorithmic_bytes(cfg, cfg.S0 + 1).values())
+    L = args.layers if args.layers > 0 else max(2, min(8, int(math.ceil(1.5e9 / step0))))
 
     if args.calib_copy_mb > 0:
-        n = args.calib_copy_mb * (1 << 20)
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        # A plain streaming kernel of known size (reads and writes n bytes),
+        # the reference for the HBM byte counters.
+        n = args.calib_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(5):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
@@ -155,88 +265,94 @@ def main():
     print("bench: inputs ready (%.1f GB of K/V)" % (
         L * (inp.K.numel() + inp.V.numel()) * 2 / 1e9), flush=True)
 
-    # Pre-marshalled ctypes arguments per (layer, step): the timed loop only
-    # calls into the library.
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     flags = ds.DECODE_APPEND if cfg.k > 0 else 0
     if args.unfused:
         flags |= ds.DECODE_UNFUSED
-    total = args.warmup + args.steps
+    S_mid = cfg.S0 + 1 + min(cfg.steps - 1, (args.steps // L) // 2)
+    plan = ds.decode_plan(inp.K, inp.V, cfg.Hq, cfg.D, labs[0], cfg.k, S_mid, args.n_split, flags)
+    ab = algorithmic_bytes(cfg, S_mid)
+    dom, dom_bytes = dominant_kernel(plan, ab)
+    dom_stage = ds.STAGES.index("attn")  # both dominant kernels run in the attention stage
+
+    # Pre-marshalled ctypes arguments per (layer, step): the timed loops only
+    # call into the library.
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     n_ev = ds.STAGE_COUNT + 1
+    total = args.warmup + 2 * args.steps
     if args.stage_events == "all":
         skip = ()
-    elif args.stage_events == "attn":
-        skip = [i for i in range(args.steps * n_ev)
-                if i % n_ev not in (ds.STAGES.index("attn"), ds.STAGES.index("attn") + 1)]
     else:
-        skip = range(args.steps * n_ev)
+        skip = [i for i in range(args.steps * n_ev) if i % n_ev not in (dom_stage, dom_stage + 1)]
     events = ds.HipEvents(args.steps * n_ev, skip=skip)
-    calls = []
+    P = ctypes.c_void_p
     keep = []  # keeps ctypes objects alive
-    for i in range(total):
+
+    def make_call(i, ev_base):
         l = i % L
         j = (i // L) % cfg.steps
         kv = ds.kv_desc(Ks[l], Vs[l], cfg.Hq, cfg.D)
         lab = labs[l].desc() if labs[l] is not None else None
         opts = ds.DecodeOpts()
         opts.n_split, opts.flags = args.n_split, flags
-        ti = i - args.warmup
-        if ti >= 0 and args.stage_events != "none":
-            opts.stage_events = events.slot_address(ti * n_ev)
+        if ev_base is not None:
+            opts.stage_events = events.slot_address(ev_base)
         keep.append((kv, lab, opts))
-        P = ctypes.c_void_p
-        calls.append((ctypes.byref(kv), P(qs[i % n_q].data_ptr()), P(Ks[l].data_ptr()),
-                      P(Vs[l].data_ptr()), P(seqs[j].data_ptr()), cfg.S0 + j + 1, P(
-                          inp.keep.data_ptr()) if inp.keep is not None else None,
-                      P(inp.chan.data_ptr()) if inp.chan is not None else None,
-                      ctypes.byref(lab) if lab is not None else None, cfg.k, cfg.sm_scale,
-                      P(out.data_ptr()), None, P(ws.data_ptr()), ws.numel(), ctypes.byref(opts),
-                      stream))
+        return (ctypes.byref(kv), P(qs[i % n_q].data_ptr()), P(Ks[l].data_ptr()),
+                P(Vs[l].data_ptr()), P(seqs[j].data_ptr()), cfg.S0 + j + 1,
+                P(inp.keep.data_ptr()) if inp.keep is not None else None,
+                P(inp.chan.data_ptr()) if inp.chan is not None else None,
+                ctypes.byref(lab) if lab is not None else None, cfg.k, cfg.sm_scale,
+                P(out.data_ptr()), None, P(ws.data_ptr()), ws.numel(), ctypes.byref(opts),
+                stream)
+
+    warm = [make_call(i, None) for i in range(args.warmup)]
+    timed = [make_call(args.warmup + i, None) for i in range(args.steps)]
+    kpass = [make_call(args.warmup + i, i * n_ev) for i in range(args.steps)]
     fn = lib.ds_decode_attn
 
-    for i in range(args.warmup):
-        rc = fn(*calls[i])
+    for c in warm:
+        rc = fn(*c)
         assert rc == 0, ds.STATUS.get(rc, rc)
     torch.cuda.synchronize()
 
+    # Timed region: K steps, nothing but the library calls.
     t0 = time.perf_counter()
-    for i in range(args.warmup, total):
-        fn(*calls[i])
+    for c in timed:
+        fn(*c)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    K_steps = args.steps
-    value = cfg.B * K_steps / wall
-    # per-stage durations from the HIP events recorded inside the timed region
+    # Kernel-timing pass: the same K steps again, HIP events recorded on the
+    # library's stream around the dominant kernel (or every stage).
     stage_ms = {name: [] for name in ds.STAGES}
     step_ms = []
-    for i in range(K_steps):
-        b = i * n_ev
-        for s, name in enumerate(ds.STAGES):
-            if events.handles[b + s] and events.handles[b + s + 1]:
-                stage_ms[name].append(events.elapsed_ms(b + s, b + s + 1))
-        if events.handles[b] and events.handles[b + ds.STAGE_COUNT]:
-            step_ms.append(events.elapsed_ms(b, b + ds.STAGE_COUNT))
+    if args.stage_events != "none":
+        for c in kpass:
+            fn(*c)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            b = i * n_ev
+            for si, name in enumerate(ds.STAGES):
+                if events.handles[b + si] and events.handles[b + si + 1]:
+                    stage_ms[name].append(events.elapsed_ms(b + si, b + si + 1))
+            if events.handles[b] and events.handles[b + ds.STAGE_COUNT]:
+                step_ms.append(events.elapsed_ms(b, b + ds.STAGE_COUNT))
     mean = {k: (sum(v) / len(v) if v else None) for k, v in stage_ms.items()}
-    if not step_ms:
-        step_ms = [wall / K_steps * 1e3]
-    step_ms_sorted = sorted(step_ms)
-    med_step = step_ms_sorted[len(step_ms) // 2]
-    S_mid = cfg.S0 + 1 + (K_steps // L) // 2
-    ab = algorithmic_bytes(cfg, S_mid)
-    attn_bytes = ab["rows"] + ab["q_out"]
-    dom = "attn"
-    attn_ms = mean["attn"] if mean["attn"] else float("nan")
-    achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
-    step_bytes = ab["labels"] + ab["rows"] + ab["q_out"]
+
+    value = cfg.B * args.steps / wall
+    ms_step = wall / args.steps * 1e3
+    dom_ms = mean["attn"]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9 if dom_ms else None
+    traffic = stored_traffic(cfg.name, dom)
+    step_bytes = sum(ab.values())
     result = {
         "metric": METRIC,
         "value": round(value, 1),
         "unit": "queries/s",
         "n_gpus": 1,
-        "steps": K_steps,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / K_steps * 1e3, 5),
+        "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -245,21 +361,27 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.B, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv,
                    "head_dim": cfg.D, "k_cols": cfg.d_k, "prefill": cfg.S0, "r": cfg.r,
                    "k": cfg.k, "labels": ("int4" if cfg.int4 else "fp16") if cfg.k > 0 else None,
-                   "storage": "fp16 q/K/V", "layer_caches": L, "note": cfg.note},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
-                     "algorithmic_bytes_per_launch": attn_bytes,
-                     "avg_launch_us": round(attn_ms * 1e3, 3), "events": args.stage_events},
-        "step": {"median_us": round(med_step * 1e3, 3),
-                 "p90_us": round(step_ms_sorted[int(0.9 * (len(step_ms) - 1))] * 1e3, 3),
+                   "storage": "fp16 q/K/V", "layer_caches": L, "path": plan["path"],
+                   "n_split": plan["n_split"], "note": cfg.note},
+        "roofline": {"bound": "hbm", "kernel": dom,
+                     "achieved": round(achieved, 1) if achieved else None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": dom_bytes,
+                     "avg_launch_us": round(dom_ms * 1e3, 3) if dom_ms else None,
+                     "timing": "HIP events around the kernel on its stream, a second pass "
+                               "of the same %d steps" % args.steps},
+        "step": {"algorithmic_bytes": step_bytes,
+                 "hbm_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+                 "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "bytes": ab,
                  "stage_mean_us": {k: (round(v * 1e3, 3) if v is not None else None)
-                                   for k, v in mean.items()},
-                 "algorithmic_bytes": step_bytes,
-                 "hbm_gbs_at_median": round(step_bytes / (med_step * 1e-3) / 1e9, 1),
-                 "hbm_frac_at_median": round(step_bytes / (med_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                 "hbm_gbs_wall": round(step_bytes * K_steps / wall / 1e9, 1)},
+                                   for k, v in mean.items()}},
     }
+    if step_ms:
+        st = sorted(step_ms)
+        result["step"]["median_us_events"] = round(st[len(st) // 2] * 1e3, 3)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     events.close()

@@ -157,6 +157,28 @@ typedef struct {
                                skipped */
 } ds_decode_opts;
 
+/* Kernel paths of ds_decode_attn. */
+enum {
+  DS_PATH_DENSE = 0,  /* k <= 0: attention over every token, no label read */
+  DS_PATH_FUSED = 1,  /* one kernel per step: one workgroup per (batch, KV head)
+                         row appends, scores, selects and attends (single
+                         query head per group, rows short enough for LDS) */
+  DS_PATH_LOCAL = 2,  /* chunked scores with a local top-M per chunk, an exact
+                         merge per row, split attention, merge of splits */
+  DS_PATH_STREAM = 3  /* every score streamed to the workspace, a radix select
+                         per row, split attention, merge of splits */
+};
+
+/* What a ds_decode_attn call with these arguments runs (host struct, filled
+ * by ds_decode_attn_plan). */
+typedef struct {
+  int32_t path;             /* DS_PATH_* */
+  int32_t n_split;          /* partitions of each row's tokens in the attention pass */
+  int32_t tokens_per_split; /* at most this many tokens per partition */
+  int32_t kernels;          /* kernel launches per call */
+  size_t workspace_bytes;   /* as ds_decode_attn_workspace_size */
+} ds_decode_plan;
+
 /* Workspace bytes that ds_decode_attn needs for these arguments (0 if they
  * are invalid).  Depends only on the shapes, k and max_seq_len. */
 size_t ds_decode_attn_workspace_size(const ds_kv_desc* kv, const ds_label_desc* lab, int32_t k,
@@ -197,6 +219,14 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
                          const int32_t* chan, const ds_label_desc* lab, int32_t k, float sm_scale,
                          void* out, int32_t* topk_idx, void* workspace, size_t workspace_bytes,
                          const ds_decode_opts* opts, hipStream_t stream);
+
+/* Host-only query: fills *plan for a ds_decode_attn call with these shapes,
+ * k, max_seq_len and options (no device pointer is read and nothing is
+ * enqueued).  Errors: DS_ERR_ARG (plan NULL, max_seq_len or n_split out of
+ * range) and the shape and dtype errors of ds_decode_attn. */
+ds_status ds_decode_attn_plan(const ds_kv_desc* kv, const ds_label_desc* lab, int32_t k,
+                              int32_t max_seq_len, const ds_decode_opts* opts,
+                              ds_decode_plan* plan);
 
 /* Static text for a status code (never NULL). */
 const char* ds_status_str(ds_status s);

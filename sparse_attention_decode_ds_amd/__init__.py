@@ -33,8 +33,9 @@ DECODE_APPEND = 1
 DECODE_VALIDATE_ONLY = 2
 DECODE_UNFUSED = 4
 DECODE_STREAM = 8
+PATHS = ("dense", "fused", "local", "stream")
 EXPORTS = ("ds_label_build", "ds_label_append", "ds_decode_attn_workspace_size",
-           "ds_decode_attn", "ds_status_str", "ds_abi_version")
+           "ds_decode_attn_plan", "ds_decode_attn", "ds_status_str", "ds_abi_version")
 
 
 class DsError(RuntimeError):
@@ -62,6 +63,12 @@ class DecodeOpts(ctypes.Structure):
                 ("stage_events", ctypes.c_void_p)]
 
 
+class DecodePlan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("n_split", ctypes.c_int32),
+                ("tokens_per_split", ctypes.c_int32), ("kernels", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
 _lib = None
 
 
@@ -80,6 +87,8 @@ def load() -> ctypes.CDLL:
         lib.ds_label_append.restype = ctypes.c_int
         lib.ds_decode_attn_workspace_size.argtypes = [P, P, I32, I32]
         lib.ds_decode_attn_workspace_size.restype = ctypes.c_size_t
+        lib.ds_decode_attn_plan.argtypes = [P, P, I32, I32, P, P]
+        lib.ds_decode_attn_plan.restype = ctypes.c_int
         lib.ds_decode_attn.argtypes = [P, P, P, P, P, I32, P, P, P, I32, ctypes.c_float, P, P, P,
                                        ctypes.c_size_t, P, P]
         lib.ds_decode_attn.restype = ctypes.c_int
@@ -169,6 +178,23 @@ def workspace_size(K, V, n_q_heads, d_q, labels: LabelCache | None, k, max_seq_l
     lab = labels.desc() if labels is not None else None
     return int(load().ds_decode_attn_workspace_size(
         ctypes.byref(kv), ctypes.byref(lab) if lab is not None else None, int(k), int(max_seq_len)))
+
+
+def decode_plan(K, V, n_q_heads, d_q, labels: LabelCache | None, k, max_seq_len,
+                n_split: int = 0, flags: int = 0) -> dict:
+    """What ds_decode_attn runs for these shapes (ds_decode_attn_plan): the
+    path name, attention splits, tokens per split, kernel launches, workspace."""
+    kv = kv_desc(K, V, n_q_heads, d_q)
+    lab = labels.desc() if labels is not None else None
+    opts = DecodeOpts()
+    opts.n_split, opts.flags = int(n_split), int(flags)
+    pl = DecodePlan()
+    _check("ds_decode_attn_plan", load().ds_decode_attn_plan(
+        ctypes.byref(kv), ctypes.byref(lab) if lab is not None else None, int(k),
+        int(max_seq_len), ctypes.byref(opts), ctypes.byref(pl)))
+    return {"path": PATHS[pl.path], "n_split": pl.n_split,
+            "tokens_per_split": pl.tokens_per_split, "kernels": pl.kernels,
+            "workspace_bytes": int(pl.workspace_bytes)}
 
 
 def decode_attn(q, K, V, seq_lens, max_seq_len: int, k: int, sm_scale: float,

@@ -175,6 +175,37 @@ int auto_splits(const Plan& p, int64_t rows, int requested) {
   return std::max(1, std::min(ns, p.split_cap));
 }
 
+// Which kernels a call runs, and the attention split.
+struct Route {
+  int path;  // DS_PATH_*
+  int n_split, tps;
+};
+
+Route route(const ds_kv_desc* kv, const ds_label_desc* lab, int k, int max_seq, uint32_t flags,
+            int n_split_req, const Plan& p) {
+  Route r;
+  const int G = kv->n_q_heads / kv->n_kv_heads;
+  const int64_t rows = (int64_t)kv->batch * kv->n_kv_heads;
+  if (!p.sparse)
+    r.path = DS_PATH_DENSE;
+  else if (G == 1 && !(flags & (DS_DECODE_UNFUSED | DS_DECODE_STREAM)) &&
+           decode_fused_fits(max_seq, k, lab->r, lab->dtype == DS_LABEL_INT4))
+    r.path = DS_PATH_FUSED;
+  else if (!(flags & DS_DECODE_STREAM) && p.local_nch <= kMaxLocalChunks)
+    r.path = DS_PATH_LOCAL;
+  else
+    r.path = DS_PATH_STREAM;
+  if (r.path == DS_PATH_FUSED) {
+    r.n_split = 1;
+    r.tps = std::max(p.kk, 1);
+    return r;
+  }
+  r.n_split = auto_splits(p, rows, n_split_req);
+  r.tps = (int)std::max<int64_t>(1, round_up(ceil_div(std::max(p.kk, 1), r.n_split), 16));
+  r.n_split = (int)std::max<int64_t>(1, ceil_div(std::max(p.kk, 1), r.tps));
+  return r;
+}
+
 }  // namespace
 }  // namespace ds
 
@@ -237,6 +268,30 @@ size_t ds_decode_attn_workspace_size(const ds_kv_desc* kv, const ds_label_desc* 
   return make_plan(kv, k, max_seq_len).total;
 }
 
+ds_status ds_decode_attn_plan(const ds_kv_desc* kv, const ds_label_desc* lab, int32_t k,
+                              int32_t max_seq_len, const ds_decode_opts* opts,
+                              ds_decode_plan* plan) {
+  if (!plan) return DS_ERR_ARG;
+  ds_status st = check_kv(kv, true);
+  if (st) return st;
+  if (k > 0 && (st = check_lab(kv, lab))) return st;
+  if (max_seq_len < 0 || max_seq_len > kv->capacity) return DS_ERR_ARG;
+  if (opts && opts->n_split < 0) return DS_ERR_ARG;
+  const uint32_t flags = opts ? opts->flags : 0u;
+  const Plan p = make_plan(kv, k, max_seq_len);
+  const Route r = route(kv, lab, k, max_seq_len, flags, opts ? opts->n_split : 0, p);
+  plan->path = r.path;
+  plan->n_split = r.n_split;
+  plan->tokens_per_split = r.tps;
+  int n = 1;  // the attention pass, or the fused kernel
+  if (r.path == DS_PATH_LOCAL) n += 2;
+  if (r.path == DS_PATH_STREAM) n += 2 + ((flags & DS_DECODE_APPEND) ? 1 : 0);
+  if (r.path != DS_PATH_FUSED && r.n_split > 1) ++n;
+  plan->kernels = n;
+  plan->workspace_bytes = p.total;
+  return DS_OK;
+}
+
 ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, const void* V,
                          const int32_t* seq_lens, int32_t max_seq_len, const int32_t* keep,
                          const int32_t* chan, const ds_label_desc* lab, int32_t k, float sm_scale,
@@ -278,10 +333,9 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
   // Paths for the score and select: one kernel for the whole step (single
   // query head, short rows), local top-M + exact merge, or a full streaming
   // select over every score.
-  const bool fused_step = sparse && G == 1 && !(flags & (DS_DECODE_UNFUSED | DS_DECODE_STREAM)) &&
-                          decode_fused_fits(max_seq_len, k, lab->r, lab->dtype == DS_LABEL_INT4);
-  const bool local_path = sparse && !fused_step && !(flags & DS_DECODE_STREAM) &&
-                          p.local_nch <= kMaxLocalChunks;
+  const Route rt = route(kv, lab, k, max_seq_len, flags, opts ? opts->n_split : 0, p);
+  const bool fused_step = rt.path == DS_PATH_FUSED;
+  const bool local_path = rt.path == DS_PATH_LOCAL;
   if ((flags & DS_DECODE_APPEND) && !fused_step && !local_path) {
     LabelArgs la = label_args(kv, K, chan, lab);
     la.pos = seq_lens;
@@ -375,9 +429,8 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
   aa.idx = idx;
   aa.idx_stride = idx_stride;
   aa.count = count;
-  aa.n_split = auto_splits(p, rows, opts ? opts->n_split : 0);
-  aa.tps = (int)std::max<int64_t>(1, round_up(ceil_div(std::max(p.kk, 1), aa.n_split), 16));
-  aa.n_split = (int)std::max<int64_t>(1, ceil_div(std::max(p.kk, 1), aa.tps));
+  aa.n_split = rt.n_split;
+  aa.tps = rt.tps;
 
   mark(DS_STAGE_ATTN);
   const bool final_out = aa.n_split == 1;

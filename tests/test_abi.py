@@ -134,6 +134,51 @@ def test_workspace_size(lib):
     assert lib.ds_decode_attn_workspace_size(ctypes.byref(kv), None, 0, 900) > 0
 
 
+def _plan(lib, kv, lab, k, max_seq, flags=0, n_split=0):
+    opts = ds.DecodeOpts()
+    opts.n_split, opts.flags = n_split, flags
+    pl = ds.DecodePlan()
+    rc = lib.ds_decode_attn_plan(ctypes.byref(kv), ctypes.byref(lab) if lab is not None else None,
+                                 k, max_seq, ctypes.byref(opts), ctypes.byref(pl))
+    return rc, pl
+
+
+def _mha(B, H, cap):
+    return _kv(batch=B, n_q_heads=H, n_kv_heads=H, capacity=cap,
+               k_stride=(H * cap * 128, cap * 128, 128), v_stride=(H * cap * 128, cap * 128, 128))
+
+
+def test_decode_plan_paths(lib):
+    """The plan query names the path each workload shape takes."""
+    int4 = dict(dtype=ds.LABEL_INT4, r=8, scales=FAKE)
+    # Llama-2-7B-shaped 4K rows, k = 256, single query head per group: one kernel.
+    rc, pl = _plan(lib, _mha(32, 32, 4160), _lab(slots=4160, **int4), 256, 4097)
+    assert rc == 0 and ds.PATHS[pl.path] == "fused" and pl.kernels == 1 and pl.n_split == 1
+    # 128K rows, k = 8192: local top-M + merge, split attention + combine.
+    rc, pl = _plan(lib, _mha(4, 32, 131088), _lab(slots=131088, **int4), 8192, 131073)
+    assert rc == 0 and ds.PATHS[pl.path] == "local" and pl.n_split > 1 and pl.kernels == 4
+    assert pl.n_split * pl.tokens_per_split >= 8192
+    # GQA groups (7 query heads per KV head) never take the one-kernel path.
+    rc, pl = _plan(lib, _kv(batch=64, capacity=8224, k_stride=(4 * 8224 * 128, 8224 * 128, 128),
+                            v_stride=(4 * 8224 * 128, 8224 * 128, 128)), _lab(slots=8224), 256, 8193)
+    assert rc == 0 and ds.PATHS[pl.path] == "local"
+    # Flags force the other paths; k <= 0 is dense.
+    kv, lab = _mha(32, 32, 4160), _lab(slots=4160, **int4)
+    rc, pl = _plan(lib, kv, lab, 256, 4097, flags=ds.DECODE_UNFUSED)
+    assert rc == 0 and ds.PATHS[pl.path] == "local"
+    rc, pl = _plan(lib, kv, lab, 256, 4097, flags=ds.DECODE_STREAM | ds.DECODE_APPEND)
+    assert rc == 0 and ds.PATHS[pl.path] == "stream" and pl.kernels >= 4
+    rc, pl = _plan(lib, kv, None, 0, 4097)
+    assert rc == 0 and ds.PATHS[pl.path] == "dense" and pl.n_split >= 1
+    assert pl.workspace_bytes == lib.ds_decode_attn_workspace_size(ctypes.byref(kv), None, 0, 4097)
+    rc, pl = _plan(lib, kv, lab, 256, 4097, n_split=4, flags=ds.DECODE_UNFUSED)
+    assert rc == 0 and pl.n_split == 4 and pl.tokens_per_split == 64
+    # errors
+    assert _plan(lib, kv, lab, 256, 5000)[0] == -1
+    assert _plan(lib, _kv(d_v=64), lab, 256, 100)[0] == -2
+    assert lib.ds_decode_attn_plan(ctypes.byref(kv), ctypes.byref(lab), 256, 4097, None, None) == -1
+
+
 def test_label_calls_validate_before_launch(lib):
     kv = _kv()
     P = ctypes.c_void_p
