@@ -176,6 +176,9 @@ typedef struct {
   int32_t n_split;          /* partitions of each row's tokens in the attention pass */
   int32_t tokens_per_split; /* at most this many tokens per partition */
   int32_t kernels;          /* kernel launches per call */
+  int32_t chunk;            /* tokens per scoring workgroup (local and stream
+                               paths; 0 otherwise) */
+  int32_t reserved0;
   size_t workspace_bytes;   /* as ds_decode_attn_workspace_size */
 } ds_decode_plan;
 

@@ -66,6 +66,7 @@ class DecodeOpts(ctypes.Structure):
 class DecodePlan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("n_split", ctypes.c_int32),
                 ("tokens_per_split", ctypes.c_int32), ("kernels", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("reserved0", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -193,7 +194,7 @@ def decode_plan(K, V, n_q_heads, d_q, labels: LabelCache | None, k, max_seq_len,
         ctypes.byref(kv), ctypes.byref(lab) if lab is not None else None, int(k),
         int(max_seq_len), ctypes.byref(opts), ctypes.byref(pl)))
     return {"path": PATHS[pl.path], "n_split": pl.n_split,
-            "tokens_per_split": pl.tokens_per_split, "kernels": pl.kernels,
+            "tokens_per_split": pl.tokens_per_split, "kernels": pl.kernels, "chunk": pl.chunk,
             "workspace_bytes": int(pl.workspace_bytes)}
 
 

@@ -111,9 +111,9 @@ Plan make_plan(const ds_kv_desc* kv, int k, int max_seq) {
   p.idx_cap = p.sparse ? std::max(p.kk, 1) : 0;
   p.keys_stride = p.sparse ? (int)round_up(std::max(max_seq, 1), 64) : 0;
   p.n_chunks = (int)std::max<int64_t>(1, ceil_div(max_seq, kScoreChunk));
-  // Local top-M chunks: 4096 tokens, halved while the grid would have fewer
-  // than ~4 workgroups per compute unit.
-  p.local_chunk = 4096;
+  // Local top-M chunks: 8192 tokens (512-thread workgroups), halved while the
+  // grid would have fewer than ~4 workgroups per compute unit.
+  p.local_chunk = kMaxLocalChunk;
   while (p.local_chunk > 512 && rows * ceil_div(max_seq, p.local_chunk) < 1024) p.local_chunk /= 2;
   p.local_nch = (int)std::max<int64_t>(1, ceil_div(max_seq, p.local_chunk));
   p.cand_stride = p.sparse ? (int)std::min<int64_t>(kMergeCap, round_up(std::max(max_seq, 1), 64)) : 0;
@@ -288,6 +288,8 @@ ds_status ds_decode_attn_plan(const ds_kv_desc* kv, const ds_label_desc* lab, in
   if (r.path == DS_PATH_STREAM) n += 2 + ((flags & DS_DECODE_APPEND) ? 1 : 0);
   if (r.path != DS_PATH_FUSED && r.n_split > 1) ++n;
   plan->kernels = n;
+  plan->chunk = r.path == DS_PATH_LOCAL ? p.local_chunk : (r.path == DS_PATH_STREAM ? kScoreChunk : 0);
+  plan->reserved0 = 0;
   plan->workspace_bytes = p.total;
   return DS_OK;
 }

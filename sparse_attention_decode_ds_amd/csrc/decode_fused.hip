@@ -11,11 +11,12 @@
 //   score    the label stream is scored into registers: thread tid holds the
 //            vectors v = j * 256 + tid, so token order is (round j, wave,
 //            lane, element);
-//   select   exact top-k on the register-resident scores: linear-bin
-//            histogram, then exact resolution of the boundary bin (rank count
-//            or radix passes), see score_common.h;
-//   emit     ordered compaction into an ascending token list in LDS (wave
-//            scans per round plus one exchange of wave totals);
+//   select   exact top-k on the register-resident scores (reg_select:
+//            linear-bin histogram, then exact resolution of the boundary bin
+//            by rank count or radix passes);
+//   emit     ordered compaction into an ascending token list in LDS
+//            (reg_emit: wave scans per round plus one exchange of wave
+//            totals);
 //   attend   exact attention over the list (attn_common.h), fp16 output.
 //
 // Used when the row fits the register budget (S <= 256 * TPT tokens, TPT
@@ -23,6 +24,10 @@
 // is a single head.
 #include "attn_common.h"
 #include "score_common.h"
+
+#ifndef DS_FUSED_ALL_LOADS
+#define DS_FUSED_ALL_LOADS 1
+#endif
 
 namespace ds {
 namespace {
@@ -37,15 +42,17 @@ struct FusedScratch {
   int32_t keep[128];
   __half knew[128];  // K row of the appended token
   float lnew[128];   // its label values (int4: codes)
-  float qg[128];
+  QueryLds q;        // the gathered query
   float snew;        // its score
   float mm_tmp[2 * kWaves];
   uint32_t scan_tmp[kWaves];
   SelScratch sel;
-  uint32_t tot[TPT][kWaves];  // per round and wave: taken | equal << 16
+  uint32_t tot[TPT * kWaves];  // per round and wave: taken | equal << 16
   int32_t lidx[kDecodeFusedMaxK];
   AttnRed<1> red;
 };
+
+
 
 template <int R, bool INT4, int TPT>
 __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs aa, LabelArgs la,
@@ -53,8 +60,9 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
   using Vec = typename VecSel<R, INT4>::type;
   constexpr int VT = Vec::VT;
   constexpr int JMAX = TPT / VT;  // rounds of vectors per thread
-  constexpr int UNR = 4;
-  constexpr int QR = R > 0 ? R : 1;
+  // label vectors in flight per thread: all of them when they fit in about
+  // 40 registers, else 4 at a time
+  constexpr int UNR = DS_FUSED_ALL_LOADS && JMAX * (int)sizeof(Vec) <= 160 ? JMAX : 4;
   __shared__ FusedScratch<TPT> f;
 
   const int row = blockIdx.x;
@@ -87,7 +95,8 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
 
   const RowPtrs p = row_ptrs(sa, row);
   const int n_vec = sparse ? (S + VT - 1) / VT : 0;
-  const int J = (n_vec + kNT - 1) / kNT;
+  const int v_last = n_vec - 1;  // the only vector that may be partial; it holds t_new
+  const int jn = (n_vec + kNT - 1) / kNT;  // rounds holding any vector (uniform)
   Vec vec[UNR];
 #pragma unroll
   for (int u = 0; u < UNR; ++u) {
@@ -95,26 +104,28 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
     if (v < n_vec) vec[u].load(p, v);
   }
   __syncthreads();
-  if (tid < r) {
-    const int col = f.chan[tid];
-    f.qg[tid] = h2f(f.qrow[sa.keep ? f.keep[col] : col]);
+  {
+    float qgv = 0.0f;
+    if (tid < r) {
+      const int col = f.chan[tid];
+      qgv = h2f(f.qrow[sa.keep ? f.keep[col] : col]);
+    }
+    store_query(INT4, r, qgv, f.q);
   }
   __syncthreads();
 
   if (!sparse) {
-    if (do_append && tid < 64) append_label<INT4>(la, row, t_new, f, r, false);
+    if (do_append && tid < 64) append_label<R, INT4>(la, row, t_new, f, r, false);
   } else {
-    if (do_append && tid < 64) append_label<INT4>(la, row, t_new, f, r, true);
-    float qreg[QR];
-    const float* qg = f.qg;
-    if (R > 0) {
-#pragma unroll
-      for (int j = 0; j < QR; ++j) qreg[j] = f.qg[j];
-      qg = qreg;
-    }
+    if (do_append && tid < 64) append_label<R, INT4>(la, row, t_new, f, r, true);
+    typename Vec::Q q;
+    q.load(f.q);
     // --- score into registers ----------------------------------------------
+    // Slots without a token (and the appended token until its score is
+    // known) hold -inf, which the select treats as empty.
+    constexpr float kEmpty = -__builtin_huge_valf();
     float sc[TPT];
-    float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
+    float mn = __builtin_huge_valf(), mx = kEmpty;
 #pragma unroll
     for (int j0 = 0; j0 < JMAX; j0 += UNR) {
       if (j0 > 0) {
@@ -131,176 +142,54 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
         const int v = j * kNT + tid;
         float s[VT];
 #pragma unroll
-        for (int e = 0; e < VT; ++e) s[e] = 0.0f;
-        if (v < n_vec) vec[u].score(qg, r, s);
+        for (int e = 0; e < VT; ++e) s[e] = kEmpty;
+        if (v < v_last) {  // a full vector of real tokens
+          vec[u].score(q, r, s);
 #pragma unroll
-        for (int e = 0; e < VT; ++e) {
-          const int t = v * VT + e;
-          sc[j * VT + e] = s[e];
-          if (v < n_vec && t < S && t != (do_append ? t_new : -1)) {
+          for (int e = 0; e < VT; ++e) {
             mn = fminf(mn, s[e]);
             mx = fmaxf(mx, s[e]);
           }
+        } else if (v == v_last) {
+          vec[u].score(q, r, s);
+#pragma unroll
+          for (int e = 0; e < VT; ++e) {
+            const int t = v * VT + e;
+            if (t >= S || (do_append && t == t_new)) {
+              s[e] = kEmpty;
+            } else {
+              mn = fminf(mn, s[e]);
+              mx = fmaxf(mx, s[e]);
+            }
+          }
         }
+#pragma unroll
+        for (int e = 0; e < VT; ++e) sc[j * VT + e] = s[e];
       }
     }
     if (do_append) {
       __syncthreads();
       const float sn = f.snew;
-      const int vn = t_new / VT;
-      if ((vn & (kNT - 1)) == tid) {
-        const int jn = vn / kNT;
+      if ((v_last & (kNT - 1)) == tid) {
+        const int jl = v_last / kNT;
 #pragma unroll
         for (int j = 0; j < JMAX; ++j)
 #pragma unroll
           for (int e = 0; e < VT; ++e)
-            if (j == jn && e == t_new - vn * VT) sc[j * VT + e] = sn;
+            if (j == jl && e == t_new - v_last * VT) sc[j * VT + e] = sn;
       }
       mn = fminf(mn, sn);
       mx = fmaxf(mx, sn);
     }
     block_minmax<kNT>(mn, mx, f.mm_tmp);
 
-    auto valid = [&](int j, int e) { return (j * kNT + tid) * VT + e < S; };
+    // --- exact select and ordered emission into the LDS token list ---------
     auto token = [&](int j, int e) { return (j * kNT + tid) * VT + e; };
-
-    // --- select ------------------------------------------------------------
-    // Histogram of linear bins, then the boundary bin b* (holding the k-th
-    // largest score) is resolved exactly.  The outcome is two keys E_lo <=
-    // E_hi and a quota: keys above E_hi are taken, keys in [E_lo, E_hi] are
-    // taken lowest index first up to the quota.  Keys in b* span [kmin, kmax]
-    // and bins are monotone, so a key inside that span lies in b*.
-    SelScratch& ss = f.sel;
-    const float bmn = mn;
-    const float bscale = 2048.0f / (mx - mn);  // +inf when all scores are equal: every key in bin 0
-    for (int i = tid; i < kHistBins; i += kNT) ss.hist[i] = 0u;
-    if (tid < 8) ss.misc[tid] = tid == 3 ? 0xFFFFFFFFu : 0u;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < JMAX; ++j)
-#pragma unroll
-      for (int e = 0; e < VT; ++e)
-        if (j < J && valid(j, e)) atomicAdd(&ss.hist[bin_of(sc[j * VT + e], bmn, bscale)], 1u);
-    __syncthreads();
-    find_digit<kNT>(ss.hist, (uint32_t)sa.k, ss.misc + 4, f.scan_tmp);
-    const uint32_t bstar = ss.misc[4];
-    const uint32_t cnt = ss.misc[6];
-    uint32_t need = (uint32_t)sa.k - ss.misc[5];
-    const bool few = cnt <= (uint32_t)kRankMax;
-#pragma unroll
-    for (int j = 0; j < JMAX; ++j)
-#pragma unroll
-      for (int e = 0; e < VT; ++e)
-        if (j < J && valid(j, e) && bin_of(sc[j * VT + e], bmn, bscale) == bstar) {
-          const uint32_t key = score_key(sc[j * VT + e]);
-          atomicMin(&ss.misc[3], key);
-          atomicMax(&ss.misc[7], key);
-          if (few) {
-            const uint32_t pos = atomicAdd(&ss.misc[0], 1u);
-            ss.cand_key[pos] = key;
-            ss.cand_idx[pos] = token(j, e);
-          }
-        }
-    __syncthreads();
-    uint32_t e_lo = ss.misc[3], e_hi = ss.misc[7];
-    if (cnt != need) {
-      if (few) {
-        for (int i = tid; i < (int)cnt; i += kNT) {
-          const uint32_t ki = ss.cand_key[i];
-          const int ti = ss.cand_idx[i];
-          uint32_t rank = 0;
-          for (int m = 0; m < (int)cnt; ++m) {
-            const uint32_t km = ss.cand_key[m];
-            rank += (km > ki) || (km == ki && ss.cand_idx[m] < ti);
-          }
-          if (rank == need - 1) ss.misc[1] = ki;  // the last key taken
-        }
-        __syncthreads();
-        const uint32_t T = ss.misc[1];
-        for (int i = tid; i < (int)cnt; i += kNT)
-          if (ss.cand_key[i] > T) atomicAdd(&ss.misc[2], 1u);
-        __syncthreads();
-        e_lo = e_hi = T;
-        need -= ss.misc[2];
-      } else {
-        // many keys in b* (clustered or equal scores): radix passes over the
-        // key bits inside b*
-        uint32_t prefix = 0u, pmask = 0u;
-#pragma unroll 1
-        for (int pass = 0; pass < 3; ++pass) {
-          const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-          const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
-          __syncthreads();
-          for (int i = tid; i < kHistBins; i += kNT) ss.hist[i] = 0u;
-          __syncthreads();
-#pragma unroll
-          for (int j = 0; j < JMAX; ++j)
-#pragma unroll
-            for (int e = 0; e < VT; ++e) {
-              if (j >= J || !valid(j, e)) continue;
-              const float sv = sc[j * VT + e];
-              const uint32_t key = score_key(sv);
-              if ((key & pmask) == prefix && bin_of(sv, bmn, bscale) == bstar)
-                atomicAdd(&ss.hist[(key >> shift) & dmask], 1u);
-            }
-          __syncthreads();
-          find_digit<kNT>(ss.hist, need, ss.misc + 4, f.scan_tmp);
-          const uint32_t d = ss.misc[4], ab = ss.misc[5], c2 = ss.misc[6];
-          prefix |= d << shift;
-          pmask |= dmask << shift;
-          need -= ab;
-          if (c2 == need) break;
-        }
-        e_lo = max(e_lo, prefix);
-        e_hi = min(e_hi, prefix | ~pmask);
-      }
-    }
-
-    // --- ordered emission ----------------------------------------------------
-    auto cls = [&](float sv) {
-      const uint32_t key = score_key(sv);
-      return key > e_hi ? 2 : (key >= e_lo ? 1 : 0);
-    };
-    uint32_t ex[JMAX];
-#pragma unroll
-    for (int j = 0; j < JMAX; ++j) {
-      ex[j] = 0u;
-      if (j >= J) continue;
-      uint32_t packed = 0u;
-#pragma unroll
-      for (int e = 0; e < VT; ++e) {
-        if (!valid(j, e)) continue;
-        const int cl = cls(sc[j * VT + e]);
-        packed += cl == 2 ? 1u : (cl == 1 ? 0x10000u : 0u);
-      }
-      const uint32_t incl = wave_incl_scan(packed);
-      ex[j] = incl - packed;
-      if (lane == 63) f.tot[j][w] = incl;
-    }
-    __syncthreads();
-    uint32_t run = 0u;
-#pragma unroll
-    for (int j = 0; j < JMAX; ++j) {
-      if (j >= J) continue;
-      uint32_t pre = 0u, rowt = 0u;
-#pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
-        const uint32_t t = f.tot[j][ww];
-        pre += ww < w ? t : 0u;
-        rowt += t;
-      }
-      const uint32_t base = run + pre + ex[j];
-      uint32_t ab = base & 0xFFFFu, eb = base >> 16;
-#pragma unroll
-      for (int e = 0; e < VT; ++e) {
-        if (!valid(j, e)) continue;
-        const int cl = cls(sc[j * VT + e]);
-        if (cl == 2 || (cl == 1 && eb < need)) f.lidx[ab + min(eb, need)] = token(j, e);
-        ab += cl == 2;
-        eb += cl == 1;
-      }
-      run += rowt;
-    }
+    auto valid = [&](int j, int) { return j < jn; };  // empty slots hold -inf
+    const RegSel rs =
+        reg_select<kNT, VT, JMAX>(sc, valid, token, (uint32_t)sa.k, mn, mx, f.sel, f.scan_tmp);
+    reg_emit<kNT, VT, JMAX>(sc, valid, rs, f.tot,
+                            [&](uint32_t pos, int j, int e) { f.lidx[pos] = token(j, e); });
     __syncthreads();
   }
   const int n_sel = sparse ? sa.k : S;
@@ -358,9 +247,14 @@ bool decode_fused_fits(int max_seq, int k, int r, int is_int4) {
   return max_seq <= kNT * kDecodeFusedTPT && (k >= max_seq || k <= kDecodeFusedMaxK);
 }
 
+// Scores per thread: the smallest of 8, 20 and 24 that holds the longest row,
+// so that no round of register slots is entirely empty for long rows of the
+// common lengths.
 hipError_t launch_decode_fused(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la,
                                int append, int rows, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  if (sa.max_seq <= kNT * 8) return launch_tpt<8>(sa, aa, la, append, rows, s);
+  if (sa.max_seq <= kNT * 20) return launch_tpt<20>(sa, aa, la, append, rows, s);
   return launch_tpt<kDecodeFusedTPT>(sa, aa, la, append, rows, s);
 }
 

@@ -25,7 +25,8 @@ constexpr int kDecodeFusedMaxK = 2048;
 // row selects exactly among the candidates.
 constexpr int kMergeCap = 16384;
 constexpr int kMaxLocalChunks = 256;
-constexpr int kLocalTPT = 16;  // chunk tokens per thread (chunks up to 4096 tokens)
+constexpr int kMaxLocalChunk = 8192;  // tokens per local-select chunk at most (512 * kLocalTPT)
+constexpr int kLocalTPT = 16;  // chunk tokens per thread of the local-select score kernel
 // Attention splits per row are capped; partial results cost 528 B each.
 constexpr int kMaxSplit = 64;
 // Selected-token indices staged in LDS per attention workgroup.
@@ -155,18 +156,25 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (DPP: shifts within rows
+// of 16, then row broadcasts).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false); // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false); // row_bcast:31
+  return x;
+}
+
 // Exclusive prefix sum of one uint32 per thread over a workgroup of NT
 // threads; `tmp` holds NT/64 words of LDS.  Contains two barriers.
 template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == 63) tmp[w] = x;
   __syncthreads();
   uint32_t before = 0, tot = 0;

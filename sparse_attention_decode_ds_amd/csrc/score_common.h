@@ -43,16 +43,120 @@ __device__ __forceinline__ RowPtrs row_ptrs(const ScoreArgs& a, int row) {
   return p;
 }
 
-// Step 1: qg[j] = sum over the group's query heads of q[h][keep[chan[j]]].
-__device__ __forceinline__ void gather_query(const ScoreArgs& a, int b, int g, float* qg) {
-  for (int j = threadIdx.x; j < a.r; j += blockDim.x) {
+// ---------------------------------------------------------------------------
+// Step 1: the gathered query, kept in LDS in two forms.
+// ---------------------------------------------------------------------------
+// qg[j] (fp32) for every label dtype.  For int4 labels with r <= 16 also a
+// fixed-point copy: with e the exponent such that max_j |qg[j]| < 2^e,
+// qi[j] = rint(qg[j] * 2^(24 - e)) is split into seven balanced base-16
+// digits in [-8, 7]; dig[w][d] packs digit d of channels 8w .. 8w + 7 (nibble
+// i = channel 8w + i, the order of the int4 codes).  Then
+// sum_j qi[j] * c[j] = sum_d 16^d * (4-bit dot products of dig[.][d] with the
+// code words), exactly in int32 (|qi| <= 2^24, |c| <= 7, r <= 16), and the
+// score is that integer times 2^(e - 24) times the token's scale.
+struct QueryLds {
+  float qg[128];
+  uint32_t dig[2][7];
+  float inv;  // 2^(e - 24)
+};
+
+// Reductions over lanes 0 .. 15 of a wave with DPP row shifts (lanes with no
+// source read 0, so the inputs must be >= 0 for the max): after the call
+// lane 15 holds the result over lanes 0 .. 15, and for the OR lane 7 holds
+// the OR over lanes 0 .. 7.
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, true)));
+  return x;
+}
+__device__ __forceinline__ uint32_t row_or8(uint32_t x) {
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  return x;
+}
+
+// Fixed-point digits of the query (one whole wave; lane j < r <= 16 holds
+// qg[j]).
+__device__ __forceinline__ void make_qdig(float qgv, int r, QueryLds& q) {
+  const int lane = threadIdx.x & 63;
+  const bool on = lane < r;
+  const float amax =
+      __int_as_float(__builtin_amdgcn_readlane(__float_as_int(row_max16(on ? fabsf(qgv) : 0.0f)), 15));
+  const int e = amax > 0.0f ? ilogbf(amax) + 1 : 0;
+  int x = on ? (int)rintf(ldexpf(qgv, 24 - e)) : 0;
+#pragma unroll
+  for (int d = 0; d < 7; ++d) {
+    const int dg = ((x + 8) & 15) - 8;
+    x = (x - dg) / 16;  // exact: x - dg is a multiple of 16
+    const uint32_t wd = row_or8(on ? (uint32_t)(dg & 15) << (4 * (lane & 7)) : 0u);
+    if (lane == 7) q.dig[0][d] = wd;
+    if (lane == 15) q.dig[1][d] = wd;
+  }
+  if (lane == 0) q.inv = ldexpf(1.0f, e - 24);
+}
+
+// Thread tid < r holds qg[tid] in qgv: store it, and for int4 labels with
+// r <= 16 let wave 0 derive the digits.  The caller synchronises afterwards.
+__device__ __forceinline__ void store_query(bool int4, int r, float qgv, QueryLds& q) {
+  const int tid = threadIdx.x;
+  if (tid < r) q.qg[tid] = qgv;
+  if (int4 && r <= 16 && tid < 64) make_qdig(tid < r ? qgv : 0.0f, r, q);
+}
+
+// qg[j] = sum over the group's query heads of q[h][keep[chan[j]]], read from
+// global memory (blockDim.x >= r).
+__device__ __forceinline__ void gather_query(const ScoreArgs& a, int b, int g, QueryLds& q) {
+  const int j = threadIdx.x;
+  float acc = 0.0f;
+  if (j < a.r) {
     const int col = a.chan[(int64_t)g * a.r + j];
     const int qc = a.keep ? a.keep[(int64_t)g * a.d_k + col] : col;
     const __half* qh = a.q + ((int64_t)b * a.Hq + (int64_t)g * a.G) * a.d_q + qc;
-    float acc = 0.0f;
     for (int h = 0; h < a.G; ++h) acc += h2f(qh[(int64_t)h * a.d_q]);
-    qg[j] = acc;
   }
+  store_query(a.is_int4 != 0, a.r, acc, q);
+}
+
+// Query operands in registers, one type per label vector.
+template <int R>
+struct QFloat {
+  float v[R];
+  __device__ __forceinline__ void load(const QueryLds& l) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) v[j] = l.qg[j];
+  }
+};
+template <int W>
+struct QDig {
+  uint32_t d[W][7];
+  float inv;
+  __device__ __forceinline__ void load(const QueryLds& l) {
+#pragma unroll
+    for (int w = 0; w < W; ++w)
+#pragma unroll
+      for (int i = 0; i < 7; ++i) d[w][i] = l.dig[w][i];
+    inv = l.inv;
+  }
+};
+struct QPtr {
+  const float* qg;
+  __device__ __forceinline__ void load(const QueryLds& l) { qg = l.qg; }
+};
+
+// sum_j qi[j] * c[j] for the code words w[0 .. W-1] (8 channels each).
+template <int W>
+__device__ __forceinline__ int dot_dig(const QDig<W>& q, const uint32_t* w) {
+  int acc = 0;
+#pragma unroll
+  for (int d = 6; d >= 0; --d) {
+    acc *= 16;
+#pragma unroll
+    for (int i = 0; i < W; ++i) acc = __builtin_amdgcn_sdot8((int)q.d[i][d], (int)w[i], acc, false);
+  }
+  return acc;
 }
 
 __device__ __forceinline__ int nib(uint32_t w, int j) {
@@ -60,72 +164,67 @@ __device__ __forceinline__ int nib(uint32_t w, int j) {
 }
 
 // Step 2 for one vector of VT consecutive tokens.  R = 0 is the generic
-// path (any r, scalar loads); the others use 16-byte label loads.  Every
-// variant accumulates fmaf(qg[j], label[j], acc) over j in order (then
-// times the int4 scale), so a token's score does not depend on the path.
+// path (any r, scalar loads, fmaf over j in order).  int4 labels with r = 8
+// or 16 use the exact integer dot products of the fixed-point query; fp16
+// labels accumulate fmaf(qg[j], label[j], acc) over j in order.  The label
+// append computes the new token's score the same way, so a token's score
+// does not depend on which kernel computes it.
 template <int R, bool INT4>
 struct LabelVec;
 
 template <>
 struct LabelVec<8, true> {  // 4 tokens: 16 B of codes + 8 B of scales
   static constexpr int VT = 4;
+  using Q = QDig<1>;
   uint4 c;
   uint2 s;
   __device__ __forceinline__ void load(const RowPtrs& p, int v) {
     c = ld_stream(reinterpret_cast<const uint4*>(p.codes) + v);
     s = reinterpret_cast<const uint2*>(p.scales)[v];
   }
-  __device__ __forceinline__ void score(const float* qg, int, float* out) const {
+  __device__ __forceinline__ void score(const Q& q, int, float* out) const {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
     const __half2 s01 = *reinterpret_cast<const __half2*>(&s.x);
     const __half2 s23 = *reinterpret_cast<const __half2*>(&s.y);
     const float sc[4] = {__low2float(s01), __high2float(s01), __low2float(s23), __high2float(s23)};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc = fmaf(qg[j], (float)nib(w[u], j), acc);
-      out[u] = sc[u] * acc;
-    }
+    for (int u = 0; u < 4; ++u) out[u] = (float)dot_dig<1>(q, &w[u]) * (sc[u] * q.inv);
   }
 };
 
 template <>
 struct LabelVec<16, true> {  // 2 tokens: 16 B of codes + 4 B of scales
   static constexpr int VT = 2;
+  using Q = QDig<2>;
   uint4 c;
   uint32_t s;
   __device__ __forceinline__ void load(const RowPtrs& p, int v) {
     c = ld_stream(reinterpret_cast<const uint4*>(p.codes) + v);
     s = reinterpret_cast<const uint32_t*>(p.scales)[v];
   }
-  __device__ __forceinline__ void score(const float* qg, int, float* out) const {
+  __device__ __forceinline__ void score(const Q& q, int, float* out) const {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
     const __half2 s01 = *reinterpret_cast<const __half2*>(&s);
     const float sc[2] = {__low2float(s01), __high2float(s01)};
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc = fmaf(qg[j], (float)nib(w[2 * u + (j >> 3)], j & 7), acc);
-      out[u] = sc[u] * acc;
-    }
+    for (int u = 0; u < 2; ++u) out[u] = (float)dot_dig<2>(q, &w[2 * u]) * (sc[u] * q.inv);
   }
 };
 
 template <>
 struct LabelVec<8, false> {  // 1 token: 8 fp16 labels
   static constexpr int VT = 1;
+  using Q = QFloat<8>;
   uint4 c;
   __device__ __forceinline__ void load(const RowPtrs& p, int v) {
     c = ld_stream(reinterpret_cast<const uint4*>(p.lab16) + v);
   }
-  __device__ __forceinline__ void score(const float* qg, int, float* out) const {
+  __device__ __forceinline__ void score(const Q& q, int, float* out) const {
     float f[8];
     unpack8(c, f);
     float acc = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc = fmaf(qg[j], f[j], acc);
+    for (int j = 0; j < 8; ++j) acc = fmaf(q.v[j], f[j], acc);
     out[0] = acc;
   }
 };
@@ -133,18 +232,19 @@ struct LabelVec<8, false> {  // 1 token: 8 fp16 labels
 template <>
 struct LabelVec<16, false> {  // 1 token: 16 fp16 labels
   static constexpr int VT = 1;
+  using Q = QFloat<16>;
   uint4 c0, c1;
   __device__ __forceinline__ void load(const RowPtrs& p, int v) {
     c0 = ld_stream(reinterpret_cast<const uint4*>(p.lab16) + 2 * v);
     c1 = ld_stream(reinterpret_cast<const uint4*>(p.lab16) + 2 * v + 1);
   }
-  __device__ __forceinline__ void score(const float* qg, int, float* out) const {
+  __device__ __forceinline__ void score(const Q& q, int, float* out) const {
     float f[16];
     unpack8(c0, f);
     unpack8(c1, f + 8);
     float acc = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc = fmaf(qg[j], f[j], acc);
+    for (int j = 0; j < 16; ++j) acc = fmaf(q.v[j], f[j], acc);
     out[0] = acc;
   }
 };
@@ -152,25 +252,26 @@ struct LabelVec<16, false> {  // 1 token: 16 fp16 labels
 template <bool INT4>
 struct LabelVec0 {  // generic r: 1 token, scalar loads, qg read from LDS
   static constexpr int VT = 1;
+  using Q = QPtr;
   const RowPtrs* p;
   int t;
   __device__ __forceinline__ void load(const RowPtrs& pp, int v) {
     p = &pp;
     t = v;
   }
-  __device__ __forceinline__ void score(const float* qg, int r, float* out) const {
+  __device__ __forceinline__ void score(const Q& q, int r, float* out) const {
     float acc = 0.0f;
     if (INT4) {
       const uint8_t* c = p->codes + (int64_t)t * (r >> 1);
       for (int j = 0; j < r; ++j) {
         const int byte = c[j >> 1];
         const int v = (j & 1) ? (byte >> 4) : (byte & 0xF);
-        acc = fmaf(qg[j], (float)(v >= 8 ? v - 16 : v), acc);
+        acc = fmaf(q.qg[j], (float)(v >= 8 ? v - 16 : v), acc);
       }
       out[0] = h2f(p->scales[t]) * acc;
     } else {
       const __half* c = p->lab16 + (int64_t)t * r;
-      for (int j = 0; j < r; ++j) acc = fmaf(qg[j], h2f(c[j]), acc);
+      for (int j = 0; j < r; ++j) acc = fmaf(q.qg[j], h2f(c[j]), acc);
       out[0] = acc;
     }
   }
@@ -191,17 +292,16 @@ struct NoHook {
 
 // Scores of tokens [t_beg, t_end) (t_beg a multiple of the vector width) as
 // keys: store(t, score, key).  The first batch of label loads is issued
-// before `hook` runs (every thread calls it exactly once; it fills qg_lds and
-// may synchronise the workgroup), so the label latency overlaps the query
+// before `hook` runs (every thread calls it exactly once; it fills ql and
+// synchronises the workgroup), so the label latency overlaps the query
 // gather.
 template <int NT, int R, bool INT4, typename Store, typename Hook>
 __device__ __forceinline__ void score_range(const ScoreArgs& a, const RowPtrs& p,
-                                            const float* qg_lds, int t_beg, int t_end,
+                                            const QueryLds& ql, int t_beg, int t_end,
                                             Store store, Hook hook) {
   using Vec = typename VecSel<R, INT4>::type;
   constexpr int VT = Vec::VT;
   constexpr int UNR = 4;
-  constexpr int QR = R > 0 ? R : 1;
   const int v_beg = t_beg / VT;
   const int v_end = (t_end + VT - 1) / VT;
   Vec vec[UNR];
@@ -212,20 +312,15 @@ __device__ __forceinline__ void score_range(const ScoreArgs& a, const RowPtrs& p
     if (v < v_end) vec[u].load(p, v);
   }
   hook();
-  float qreg[QR];
-  const float* qg = qg_lds;
-  if (R > 0) {
-#pragma unroll
-    for (int j = 0; j < QR; ++j) qreg[j] = qg_lds[j];
-    qg = qreg;
-  }
+  typename Vec::Q q;
+  q.load(ql);
   for (;;) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int v = v0 + u * NT;
       if (v < v_end) {
         float s[VT];
-        vec[u].score(qg, a.r, s);
+        vec[u].score(q, a.r, s);
 #pragma unroll
         for (int e = 0; e < VT; ++e) {
           const int t = v * VT + e;
@@ -295,33 +390,29 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t need, 
 }
 
 // ---------------------------------------------------------------------------
-// Linear-bin select over keys held in LDS.
+// Exact selection.
 // ---------------------------------------------------------------------------
-struct Sel {
-  float mn, scale;         // bin = clamp((score - mn) * scale, 0, 2047)
-  uint32_t bstar;          // bin of the k-th largest key
-  uint32_t prefix, pmask;  // refinement inside that bin
-  uint32_t need;           // keys of the "equal" class to take, lowest index first
-};
-
 __device__ __forceinline__ float key_float(uint32_t key) {
   const uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
   return __uint_as_float(u);
 }
 
-__device__ __forceinline__ uint32_t lin_bin(uint32_t key, float mn, float scale) {
-  float x = (key_float(key) - mn) * scale;
-  x = fminf(fmaxf(x, 0.0f), 2047.0f);  // NaN (0 * inf) maps to 0
-  return (uint32_t)x;
-}
-
-// 2: taken, 1: equal class, 0: not taken.
-__device__ __forceinline__ int sel_class(uint32_t key, const Sel& s) {
-  const uint32_t bin = lin_bin(key, s.mn, s.scale);
-  if (bin != s.bstar) return bin > s.bstar ? 2 : 0;
-  const uint32_t km = key & s.pmask;
-  return km > s.prefix ? 2 : (km == s.prefix ? 1 : 0);
-}
+// Linear bins between the smallest and largest valid score mn <= mx:
+// bin(s) = trunc(clamp((s - mn) * scale + 1.5, 0, 2047.5)), a monotone
+// function of s that puts every valid score in bins 1 .. 2047 and -inf (the
+// marker of an empty slot) in bin 0; all valid scores share bin 1 when
+// mn == mx.  Since k never exceeds the number of valid items, the k-th
+// largest never lies in bin 0.
+struct LinBins {
+  float mn, scale;
+  __device__ __forceinline__ LinBins(float lo, float hi) : mn(lo), scale(1.0f) {
+    const float span = hi - lo;
+    if (span > 0.0f && span <= 3.402823466e38f) scale = fminf(2046.0f / span, 3.402823466e38f);
+  }
+  __device__ __forceinline__ uint32_t operator()(float s) const {
+    return (uint32_t)__builtin_amdgcn_fmed3f(fmaf(s - mn, scale, 1.5f), 0.0f, 2047.5f);
+  }
+};
 
 struct SelScratch {
   uint32_t hist[kHistBins];
@@ -332,109 +423,6 @@ struct SelScratch {
 
 // Exact selection of the k largest of n keys (k < n) in LDS, ties to the
 // lower index.  mn, mx: smallest and largest score of the row.
-template <int NT>
-__device__ Sel select_lds(const uint32_t* keys, int n, uint32_t k, float mn, float mx,
-                          SelScratch& sc, uint32_t* scan_tmp) {
-  Sel s;
-  s.mn = mn;
-  s.scale = 2048.0f / (mx - mn);  // +inf when all scores are equal: every key in bin 0
-  for (int i = threadIdx.x; i < kHistBins; i += NT) sc.hist[i] = 0u;
-  if (threadIdx.x < 8) sc.misc[threadIdx.x] = 0u;
-  __syncthreads();
-  for (int t = threadIdx.x; t < n; t += NT) atomicAdd(&sc.hist[lin_bin(keys[t], s.mn, s.scale)], 1u);
-  __syncthreads();
-  find_digit<NT>(sc.hist, k, sc.misc + 4, scan_tmp);
-  s.bstar = sc.misc[4];
-  const uint32_t above = sc.misc[5], cnt = sc.misc[6];
-  s.prefix = 0u;
-  s.pmask = 0u;
-  s.need = k - above;
-  if (cnt == s.need) return s;  // the whole bin is taken
-
-  if (cnt <= (uint32_t)kRankMax) {
-    // gather the bin's keys, rank them exactly
-    for (int t = threadIdx.x; t < n; t += NT) {
-      const uint32_t key = keys[t];
-      if (lin_bin(key, s.mn, s.scale) == s.bstar) {
-        const uint32_t p = atomicAdd(&sc.misc[0], 1u);
-        sc.cand_key[p] = key;
-        sc.cand_idx[p] = t;
-      }
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < (int)cnt; i += NT) {
-      const uint32_t ki = sc.cand_key[i];
-      const int ti = sc.cand_idx[i];
-      uint32_t rank = 0;
-      for (int j = 0; j < (int)cnt; ++j) {
-        const uint32_t kj = sc.cand_key[j];
-        rank += (kj > ki) || (kj == ki && sc.cand_idx[j] < ti);
-      }
-      if (rank == s.need - 1) sc.misc[1] = ki;  // the last key taken
-    }
-    __syncthreads();
-    const uint32_t T = sc.misc[1];
-    for (int i = threadIdx.x; i < (int)cnt; i += NT)
-      if (sc.cand_key[i] > T) atomicAdd(&sc.misc[2], 1u);
-    __syncthreads();
-    s.prefix = T;
-    s.pmask = 0xFFFFFFFFu;
-    s.need -= sc.misc[2];
-    __syncthreads();
-    return s;
-  }
-
-  // Many keys in one bin (clustered or equal scores): radix passes over the
-  // key bits of that bin.
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
-    for (int i = threadIdx.x; i < kHistBins; i += NT) sc.hist[i] = 0u;
-    __syncthreads();
-    for (int t = threadIdx.x; t < n; t += NT) {
-      const uint32_t key = keys[t];
-      if ((key & s.pmask) == s.prefix && lin_bin(key, s.mn, s.scale) == s.bstar)
-        atomicAdd(&sc.hist[(key >> shift) & dmask], 1u);
-    }
-    __syncthreads();
-    find_digit<NT>(sc.hist, s.need, sc.misc + 4, scan_tmp);
-    const uint32_t d = sc.misc[4], ab = sc.misc[5], c2 = sc.misc[6];
-    s.prefix |= d << shift;
-    s.pmask |= dmask << shift;
-    s.need -= ab;
-    if (c2 == s.need) break;
-  }
-  __syncthreads();
-  return s;
-}
-
-// Ordered output over LDS keys: each thread owns a contiguous segment (odd
-// length, so the strided LDS reads spread over the banks).  n < 65536.
-template <int NT, typename Out>
-__device__ void emit_sel_lds(const uint32_t* keys, int n, const Sel& s, Out out,
-                             uint32_t* scan_tmp) {
-  int seg = (n + NT - 1) / NT;
-  seg |= 1;
-  const int beg = (int)threadIdx.x * seg;
-  const int end = min(n, beg + seg);
-  uint32_t na = 0, ne = 0;
-  for (int t = beg; t < end; ++t) {
-    const int c = sel_class(keys[t], s);
-    na += c == 2;
-    ne += c == 1;
-  }
-  uint32_t total;
-  const uint32_t ex = block_excl_scan<NT>(na | (ne << 16), scan_tmp, &total);
-  uint32_t ab = ex & 0xFFFFu, eb = ex >> 16;
-  for (int t = beg; t < end; ++t) {
-    const int c = sel_class(keys[t], s);
-    if (c == 2 || (c == 1 && eb < s.need)) out(ab + min(eb, s.need), t);
-    ab += c == 2;
-    eb += c == 1;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Plain radix select over keys in memory (rows too long for LDS).
 // ---------------------------------------------------------------------------
@@ -517,34 +505,17 @@ __device__ void emit_global(const uint32_t* keys, int n, Threshold th, int32_t* 
 }
 
 // ---------------------------------------------------------------------------
-// Helpers for register-resident scores (one score per slot, tokens ordered
-// round-major across the workgroup).
+// Register-resident scores: the label append and the selection.
 // ---------------------------------------------------------------------------
-// Inclusive prefix sum over the 64 lanes of a wave (DPP: shifts within rows
-// of 16, then row broadcasts).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);  // row_shr:1
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);  // row_shr:2
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);  // row_shr:4
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);  // row_shr:8
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false); // row_bcast:15
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false); // row_bcast:31
-  return x;
-}
-
-__device__ __forceinline__ uint32_t bin_of(float s, float mn, float scale) {
-  float x = (s - mn) * scale;
-  x = fminf(fmaxf(x, 0.0f), 2047.0f);  // NaN (0 * inf) maps to 0
-  return (uint32_t)x;
-}
-
-// Label of token t from the K row staged in LDS (wave 0), written to the
-// label cache exactly as the label kernel writes it; its score (same
-// operation order as the label-vector scores) goes to f.snew.
-template <bool INT4, typename F>
+// Label of token t from the K row staged in LDS (one whole wave), written to
+// the label cache exactly as the label kernel writes it.  With with_score its
+// score goes to f.snew, computed as the label vector of type
+// VecSel<R, INT4> scores a stored label (int4 r = 8 or 16: the fixed-point
+// query in f.q; otherwise fmaf over j in order, then the int4 scale).
+template <int R, bool INT4, typename F>
 __device__ __forceinline__ void append_label(const LabelArgs& la, int row, int t, F& f, int r,
                                              bool with_score) {
-  const int lane = threadIdx.x & 63;  // one wave
+  const int lane = threadIdx.x & 63;
   const int64_t slot = (int64_t)row * la.slots + t;
   float sf = 1.0f;
   if (!INT4) {
@@ -556,8 +527,12 @@ __device__ __forceinline__ void append_label(const LabelArgs& la, int row, int t
   } else {
     float amax = 0.0f;
     for (int j = lane; j < r; j += 64) amax = fmaxf(amax, fabsf(h2f(f.knew[f.chan[j]])));
+    if (R == 8 || R == 16) {
+      amax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(row_max16(amax)), 15));
+    } else {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+      for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    }
     const __half s16 = __float2half_rn(amax / 7.0f);  // IEEE division, round to nearest even
     sf = h2f(s16);
     for (int j = lane; j < r; j += 64) {
@@ -573,30 +548,51 @@ __device__ __forceinline__ void append_label(const LabelArgs& la, int row, int t
     if (lane == 0) la.scales[slot] = s16;
   }
   __builtin_amdgcn_wave_barrier();
-  if (with_score && lane == 0) {
+  if (INT4 && (R == 8 || R == 16)) {
+    // the code words of the new token (nibble i of word w = channel 8w + i)
+    const int c = lane < r ? (int)f.lnew[lane] : 0;
+    const uint32_t wd = row_or8(lane < r ? (uint32_t)(c & 15) << (4 * (lane & 7)) : 0u);
+    const uint32_t w[2] = {(uint32_t)__builtin_amdgcn_readlane((int)wd, 7),
+                           (uint32_t)__builtin_amdgcn_readlane((int)wd, 15)};
+    if (with_score && lane == 0) {
+      QDig<(R == 16 ? 2 : 1)> qd;
+      qd.load(f.q);
+      f.snew = (float)dot_dig(qd, w) * (sf * qd.inv);
+    }
+  } else if (with_score && lane == 0) {
     float acc = 0.0f;
-    for (int j = 0; j < r; ++j) acc = fmaf(f.qg[j], f.lnew[j], acc);
+    for (int j = 0; j < r; ++j) acc = fmaf(f.q.qg[j], f.lnew[j], acc);
     f.snew = INT4 ? sf * acc : acc;
   }
 }
 
 // Register-resident selection.  Thread tid holds items (j * NT + tid) * VT + e
-// for rounds j < JMAX and elements e < VT in sc[j * VT + e]; valid(j, e) says
-// whether that slot holds an item, order(j, e) gives its position in the row
-// (ties go to the lower position).  The k largest are characterised by two
+// for rounds j < JMAX and elements e < VT in sc[j * VT + e]; a slot counts if
+// valid(j, e) and its score is not -inf (the empty marker: such slots fall in
+// bin 0, below every item, and never match a class), order(j, e) gives its
+// position in the row (ties go to the lower position).  The k largest are characterised by two
 // keys e_lo <= e_hi and a quota: items with key > e_hi are taken, items with
 // key in [e_lo, e_hi] are taken lowest position first, `need` of them.  Items
 // of the boundary linear bin span [kmin, kmax] and bins are monotone, so a key
-// inside that span lies in the boundary bin.
+// inside that span lies in the boundary bin.  mn, mx: smallest and largest
+// valid score.
 struct RegSel {
   uint32_t e_lo, e_hi, need;
 };
 
-template <int NT, int VT, int JMAX, typename Valid, typename Order>
+struct NoBstarHook {
+  __device__ __forceinline__ void operator()(uint32_t, const LinBins&) const {}
+};
+
+// on_bstar(bstar, bin) runs on every thread once the boundary bin is known:
+// every valid item with bin(score) > bstar is among the k largest.
+template <int NT, int VT, int JMAX, typename Valid, typename Order,
+          typename OnBstar = NoBstarHook>
 __device__ RegSel reg_select(const float* sc, Valid valid, Order order, uint32_t k, float mn,
-                             float mx, SelScratch& ss, uint32_t* scan_tmp) {
+                             float mx, SelScratch& ss, uint32_t* scan_tmp,
+                             OnBstar on_bstar = OnBstar()) {
   const int tid = threadIdx.x;
-  const float bscale = 2048.0f / (mx - mn);  // +inf when all scores are equal: every key in bin 0
+  const LinBins bin(mn, mx);
   for (int i = tid; i < kHistBins; i += NT) ss.hist[i] = 0u;
   if (tid < 8) ss.misc[tid] = tid == 3 ? 0xFFFFFFFFu : 0u;
   __syncthreads();
@@ -604,11 +600,12 @@ __device__ RegSel reg_select(const float* sc, Valid valid, Order order, uint32_t
   for (int j = 0; j < JMAX; ++j)
 #pragma unroll
     for (int e = 0; e < VT; ++e)
-      if (valid(j, e)) atomicAdd(&ss.hist[bin_of(sc[j * VT + e], mn, bscale)], 1u);
+      if (valid(j, e)) atomicAdd(&ss.hist[bin(sc[j * VT + e])], 1u);
   __syncthreads();
   find_digit<NT>(ss.hist, k, ss.misc + 4, scan_tmp);
   const uint32_t bstar = ss.misc[4];
   const uint32_t cnt = ss.misc[6];
+  on_bstar(bstar, bin);
   RegSel r;
   r.need = k - ss.misc[5];
   const bool few = cnt <= (uint32_t)kRankMax;
@@ -616,7 +613,7 @@ __device__ RegSel reg_select(const float* sc, Valid valid, Order order, uint32_t
   for (int j = 0; j < JMAX; ++j)
 #pragma unroll
     for (int e = 0; e < VT; ++e)
-      if (valid(j, e) && bin_of(sc[j * VT + e], mn, bscale) == bstar) {
+      if (valid(j, e) && bin(sc[j * VT + e]) == bstar) {
         const uint32_t key = score_key(sc[j * VT + e]);
         atomicMin(&ss.misc[3], key);
         atomicMax(&ss.misc[7], key);
@@ -667,7 +664,7 @@ __device__ RegSel reg_select(const float* sc, Valid valid, Order order, uint32_t
         if (!valid(j, e)) continue;
         const float sv = sc[j * VT + e];
         const uint32_t key = score_key(sv);
-        if ((key & pmask) == prefix && bin_of(sv, mn, bscale) == bstar)
+        if ((key & pmask) == prefix && bin(sv) == bstar)
           atomicAdd(&ss.hist[(key >> shift) & dmask], 1u);
       }
     __syncthreads();
@@ -687,16 +684,20 @@ __device__ RegSel reg_select(const float* sc, Valid valid, Order order, uint32_t
 // Ordered emission of the items taken by `r`: put(pos, j, e) with pos the
 // item's rank among the taken items in position order.  tot holds
 // JMAX * (NT / 64) words of LDS.  One barrier.
+// The classes are decided on the scores: key(s) > e_hi iff s > f_hi and
+// key(s) >= e_lo iff s >= f_lo, with f_hi the largest float whose key is at
+// most e_hi and f_lo the smallest float whose key is at least e_lo.  Both
+// keys lie between the smallest and largest key of the row, so the floats are
+// finite; every such key is a float's key except 0x7FFFFFFF, which lies
+// between the keys of -denorm_min and of +-0.
 template <int NT, int VT, int JMAX, typename Valid, typename Put>
 __device__ __forceinline__ void reg_emit(const float* sc, Valid valid, const RegSel& r,
                                          uint32_t* tot, Put put) {
   constexpr int W = NT / 64;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  auto cls = [&](float sv) {
-    const uint32_t key = score_key(sv);
-    return key > r.e_hi ? 2 : (key >= r.e_lo ? 1 : 0);
-  };
+  const float f_lo = key_float(r.e_lo == 0x7FFFFFFFu ? 0x80000000u : r.e_lo);
+  const float f_hi = key_float(r.e_hi == 0x7FFFFFFFu ? 0x7FFFFFFEu : r.e_hi);
   uint32_t ex[JMAX];
 #pragma unroll
   for (int j = 0; j < JMAX; ++j) {
@@ -704,8 +705,8 @@ __device__ __forceinline__ void reg_emit(const float* sc, Valid valid, const Reg
 #pragma unroll
     for (int e = 0; e < VT; ++e) {
       if (!valid(j, e)) continue;
-      const int cl = cls(sc[j * VT + e]);
-      packed += cl == 2 ? 1u : (cl == 1 ? 0x10000u : 0u);
+      const float sv = sc[j * VT + e];
+      packed += sv > f_hi ? 1u : (sv >= f_lo ? 0x10000u : 0u);
     }
     const uint32_t incl = wave_incl_scan(packed);
     ex[j] = incl - packed;
@@ -727,10 +728,11 @@ __device__ __forceinline__ void reg_emit(const float* sc, Valid valid, const Reg
 #pragma unroll
     for (int e = 0; e < VT; ++e) {
       if (!valid(j, e)) continue;
-      const int cl = cls(sc[j * VT + e]);
-      if (cl == 2 || (cl == 1 && eb < r.need)) put(ab + min(eb, r.need), j, e);
-      ab += cl == 2;
-      eb += cl == 1;
+      const float sv = sc[j * VT + e];
+      const bool A = sv > f_hi, E = !A && sv >= f_lo;
+      if (A || (E && eb < r.need)) put(ab + min(eb, r.need), j, e);
+      ab += A;
+      eb += E;
     }
     run += rowt;
   }

@@ -30,7 +30,7 @@ __device__ __forceinline__ void finish_row(const ScoreArgs& a, int row) {
 
 template <int NT, int R, bool INT4>
 __global__ __launch_bounds__(NT) void k_score_chunk(ScoreArgs a) {
-  __shared__ float qg[128];
+  __shared__ QueryLds qg;
   const int row = blockIdx.x / a.n_chunks;
   const int c = blockIdx.x - row * a.n_chunks;
   const int b = row / a.Hkv;

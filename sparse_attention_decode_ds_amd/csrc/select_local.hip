@@ -22,8 +22,6 @@
 namespace ds {
 namespace {
 
-constexpr int kNTL = 256;
-constexpr int kWavesL = kNTL / 64;
 constexpr int kNTM = 1024;
 
 __device__ __forceinline__ int chunks_of(int S, int CH) { return (S + CH - 1) / CH; }
@@ -38,29 +36,32 @@ __device__ __forceinline__ int quota_of(int S, int k, int CH, int cap) {
   return m;
 }
 
+template <int NT>
 struct LocalScratch {
   __half qrows[kMaxGroup][256];
   int32_t chan[128];
   int32_t keep[128];
   __half knew[128];
   float lnew[128];
-  float qg[128];
+  QueryLds q;
   float snew;
-  float mm_tmp[2 * kWavesL];
-  uint32_t scan_tmp[kWavesL];
+  float mm_tmp[2 * (NT / 64)];
+  uint32_t scan_tmp[NT / 64];
   SelScratch sel;
-  uint32_t tot[kLocalTPT][kWavesL];
+  uint32_t tot[kLocalTPT][NT / 64];
   uint32_t theta;
 };
 
-template <int R, bool INT4>
-__global__ __launch_bounds__(kNTL, 4) void k_score_local(ScoreArgs sa, LabelArgs la, int append) {
+// NT threads score a chunk of at most NT * kLocalTPT tokens.
+template <int NT, int R, bool INT4>
+__global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la, int append) {
+  constexpr int kNTL = NT;
+  constexpr int kWavesL = NT / 64;
   using Vec = typename VecSel<R, INT4>::type;
   constexpr int VT = Vec::VT;
   constexpr int JMAX = kLocalTPT / VT;
   constexpr int UNR = 4;
-  constexpr int QR = R > 0 ? R : 1;
-  __shared__ LocalScratch f;
+  __shared__ LocalScratch<NT> f;
 
   const int row = blockIdx.x / sa.n_chunks;
   const int c = blockIdx.x - row * sa.n_chunks;
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(kNTL, 4) void k_score_local(ScoreArgs sa, LabelArgs
   }
   if (!sparse) {  // the row attends every token; only the label append is due
     __syncthreads();
-    if (has_new && tid < 64) append_label<INT4>(la, row, t_new, f, r, false);
+    if (has_new && tid < 64) append_label<R, INT4>(la, row, t_new, f, r, false);
     return;
   }
 
@@ -108,22 +109,19 @@ __global__ __launch_bounds__(kNTL, 4) void k_score_local(ScoreArgs sa, LabelArgs
     if (v < n_vec) vec[u].load(p, v0 + v);
   }
   __syncthreads();
-  if (tid < r) {
-    const int col = f.chan[tid];
-    const int qc = sa.keep ? f.keep[col] : col;
+  {
     float acc = 0.0f;
-    for (int h = 0; h < sa.G; ++h) acc += h2f(f.qrows[h][qc]);
-    f.qg[tid] = acc;
+    if (tid < r) {
+      const int col = f.chan[tid];
+      const int qc = sa.keep ? f.keep[col] : col;
+      for (int h = 0; h < sa.G; ++h) acc += h2f(f.qrows[h][qc]);
+    }
+    store_query(INT4, r, acc, f.q);
   }
   __syncthreads();
-  if (has_new && tid < 64) append_label<INT4>(la, row, t_new, f, r, true);
-  float qreg[QR];
-  const float* qg = f.qg;
-  if (R > 0) {
-#pragma unroll
-    for (int j = 0; j < QR; ++j) qreg[j] = f.qg[j];
-    qg = qreg;
-  }
+  if (has_new && tid < 64) append_label<R, INT4>(la, row, t_new, f, r, true);
+  typename Vec::Q q;
+  q.load(f.q);
 
   // --- score into registers --------------------------------------------------
   auto token = [&](int j, int e) { return t_beg + (j * kNTL + tid) * VT + e; };
@@ -147,7 +145,7 @@ __global__ __launch_bounds__(kNTL, 4) void k_score_local(ScoreArgs sa, LabelArgs
       float s[VT];
 #pragma unroll
       for (int e = 0; e < VT; ++e) s[e] = 0.0f;
-      if (v < n_vec) vec[u].score(qg, r, s);
+      if (v < n_vec) vec[u].score(q, r, s);
 #pragma unroll
       for (int e = 0; e < VT; ++e) {
         sc[j * VT + e] = s[e];
@@ -182,8 +180,7 @@ __global__ __launch_bounds__(kNTL, 4) void k_score_local(ScoreArgs sa, LabelArgs
   uint32_t tmin = 0xFFFFFFFFu;
   if (!keep_all) {
     block_minmax<kNTL>(mn, mx, f.mm_tmp);
-    const float bmn = mn;
-    const float bscale = 2048.0f / (mx - mn);  // +inf if all equal: every key in bin 0
+    const LinBins bin(mn, mx);
     SelScratch& ss = f.sel;
     for (int i = tid; i < kHistBins; i += kNTL) ss.hist[i] = 0u;
     if (tid == 0) f.theta = 0xFFFFFFFFu;
@@ -193,7 +190,7 @@ __global__ __launch_bounds__(kNTL, 4) void k_score_local(ScoreArgs sa, LabelArgs
     for (int j = 0; j < JMAX; ++j)
 #pragma unroll
       for (int e = 0; e < VT; ++e) {
-        bins[j * VT + e] = bin_of(sc[j * VT + e], bmn, bscale);
+        bins[j * VT + e] = bin(sc[j * VT + e]);
         if (j < J && valid(j, e)) atomicAdd(&ss.hist[bins[j * VT + e]], 1u);
       }
     __syncthreads();
@@ -267,16 +264,17 @@ __global__ __launch_bounds__(kNTL, 4) void k_score_local(ScoreArgs sa, LabelArgs
   }
 }
 
+constexpr int kMergeJ = kMergeCap / kNTM;  // candidate slots per thread
+
 struct MergeScratch {
-  uint32_t keys[kMergeCap];
-  int32_t idx[kMergeCap];
   SelScratch sel;
-  int32_t ch_off[kMaxLocalChunks + 1];
+  int32_t ch_cnt[kMaxLocalChunks];
   uint32_t ch_theta[kMaxLocalChunks];
   uint32_t scan_tmp[kNTM / 64];
   float mm_tmp[2 * kNTM / 64];
+  uint32_t tot[kMergeJ * (kNTM / 64)];
   uint32_t flag;  // 1: fall back to the full select
-  uint32_t tmin;  // smallest selected key
+  uint32_t total; // candidates of the row
 };
 
 template <int R, bool INT4>
@@ -298,84 +296,77 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
   }
   const int n_ch = chunks_of(S, sa.chunk);
   const int cap = cap_of(sa.cand_stride, n_ch);
-  if (tid == 0) {
-    uint32_t bad = n_ch > kMaxLocalChunks ? 1u : 0u;
-    int off = 0;
-    for (int c = 0; c < n_ch && !bad; ++c) {
-      const int cnt = sa.cand_cnt[(int64_t)row * sa.n_chunks + c];
-      if (cnt < 0 || cnt > cap) bad = 1u;
-      f.ch_off[c] = off;
-      f.ch_theta[c] = sa.cand_theta[(int64_t)row * sa.n_chunks + c];
-      off += max(cnt, 0);
+  const int slots = n_ch * cap;  // <= cand_stride <= kMergeCap
+
+  // Candidate slot i = j * kNTM + tid of this thread; chunk c owns slots
+  // [c * cap, c * cap + cnt_c), in ascending token order, so slot order is
+  // token order.  Every load is issued before the counts are known.
+  const uint32_t* ck = sa.cand_key + (int64_t)row * sa.cand_stride;
+  const int32_t* ci = sa.cand_idx + (int64_t)row * sa.cand_stride;
+  float sc[kMergeJ];
+  int32_t tok[kMergeJ];
+#pragma unroll
+  for (int j = 0; j < kMergeJ; ++j) {
+    const int i = j * kNTM + tid;
+    uint32_t key = 0u;
+    tok[j] = 0;
+    if (i < slots) {
+      key = ck[i];
+      tok[j] = ci[i];
     }
-    f.ch_off[min(n_ch, kMaxLocalChunks)] = off;
-    if (off < sa.k) bad = 1u;
-    f.flag = bad;
-    f.tmin = 0xFFFFFFFFu;
+    sc[j] = key_float(key);
+  }
+  if (tid == 0) {
+    f.flag = n_ch > kMaxLocalChunks ? 1u : 0u;
+    f.total = 0u;
   }
   __syncthreads();
-  bool full = f.flag != 0u;
+  if (tid < min(n_ch, kMaxLocalChunks)) {
+    const int cnt = sa.cand_cnt[(int64_t)row * sa.n_chunks + tid];
+    f.ch_cnt[tid] = cnt;
+    f.ch_theta[tid] = sa.cand_theta[(int64_t)row * sa.n_chunks + tid];
+    if (cnt < 0 || cnt > cap) atomicOr(&f.flag, 1u);
+    atomicAdd(&f.total, (uint32_t)max(cnt, 0));
+  }
+  __syncthreads();
+  bool full = f.flag != 0u || f.total < (uint32_t)sa.k;
 
   if (!full) {
-    const int n = f.ch_off[n_ch];
+    // valid slots as a bit mask: chunk of slot i is floor(i / cap)
+    uint32_t vmask = 0u;
     float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
-    // Gather the chunk segments into one ordered array: every slot of the
-    // candidate area is visited once, all loads independent.
-    const uint32_t* ck = sa.cand_key + (int64_t)row * sa.cand_stride;
-    const int32_t* ci = sa.cand_idx + (int64_t)row * sa.cand_stride;
-    const int slots = n_ch * cap;
-    constexpr int U = 4;
-    for (int i0 = tid; i0 < slots; i0 += kNTM * U) {
-      uint32_t kk[U];
-      int32_t ii[U];
-      int dst[U];
+    const float inv_cap = 1.0f / (float)cap;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * kNTM;
-        dst[u] = -1;
-        if (i < slots) {
-          const int c = i / cap;
-          const int j = i - c * cap;
-          if (j < f.ch_off[c + 1] - f.ch_off[c]) {
-            dst[u] = f.ch_off[c] + j;
-            kk[u] = ck[i];
-            ii[u] = ci[i];
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (dst[u] >= 0) {
-          f.keys[dst[u]] = kk[u];
-          f.idx[dst[u]] = ii[u];
-          const float sv = key_float(kk[u]);
-          mn = fminf(mn, sv);
-          mx = fmaxf(mx, sv);
-        }
+    for (int j = 0; j < kMergeJ; ++j) {
+      const int i = j * kNTM + tid;
+      if (i >= slots) continue;
+      int c = (int)((float)i * inv_cap);
+      c += (i >= (c + 1) * cap) ? 1 : 0;
+      c -= (i < c * cap) ? 1 : 0;
+      if (i - c * cap < f.ch_cnt[c]) {
+        vmask |= 1u << j;
+        mn = fminf(mn, sc[j]);
+        mx = fmaxf(mx, sc[j]);
       }
     }
-    block_minmax<kNTM>(mn, mx, f.mm_tmp);  // its barriers also publish keys[] and idx[]
-    const Sel s = select_lds<kNTM>(f.keys, n, (uint32_t)sa.k, mn, mx, f.sel, f.scan_tmp);
-    uint32_t tmin = 0xFFFFFFFFu;
-    emit_sel_lds<kNTM>(
-        f.keys, n, s,
-        [&](int pos, int t) {
-          out[pos] = f.idx[t];
-          tmin = min(tmin, f.keys[t]);
-        },
-        f.scan_tmp);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) tmin = min(tmin, (uint32_t)__shfl_xor((int)tmin, o, 64));
-    if ((tid & 63) == 0) atomicMin(&f.tmin, tmin);
-    __syncthreads();
-    if (tid < n_ch && f.ch_theta[tid] > f.tmin) atomicOr(&f.flag, 1u);
+    block_minmax<kNTM>(mn, mx, f.mm_tmp);
+    auto valid = [&](int j, int) { return ((vmask >> j) & 1u) != 0u; };
+    auto order = [&](int j, int) { return j * kNTM + tid; };
+    const RegSel rs = reg_select<kNTM, 1, kMergeJ>(sc, valid, order, (uint32_t)sa.k, mn, mx, f.sel,
+                                                  f.scan_tmp);
+    // Complete iff every chunk that dropped tokens (theta != 0) has theta at
+    // or below the smallest selected key; e_lo is at or below that key.
+    if (tid < min(n_ch, kMaxLocalChunks) && f.ch_theta[tid] > rs.e_lo) atomicOr(&f.flag, 1u);
     __syncthreads();
     full = f.flag != 0u;
+    if (!full)
+      reg_emit<kNTM, 1, kMergeJ>(sc, valid, rs, f.tot,
+                                 [&](uint32_t pos, int j, int) { out[pos] = tok[j]; });
   }
 
   if (full) {
     // Re-score the whole row into the workspace, then a radix select over it.
-    __shared__ float qg[128];
+    __shared__ QueryLds qg;
     const RowPtrs p = row_ptrs(sa, row);
     uint32_t* kr = sa.keys + (int64_t)row * sa.keys_stride;
     score_range<kNTM, R, INT4>(
@@ -398,8 +389,11 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
 template <int R, bool INT4>
 hipError_t launch_local_rt(const ScoreArgs& sa, const LabelArgs& la, int append, int rows,
                            hipStream_t s) {
-  hipLaunchKernelGGL((k_score_local<R, INT4>), dim3(rows * sa.n_chunks), dim3(kNTL), 0, s, sa, la,
-                     append);
+  const dim3 grid(rows * sa.n_chunks);
+  if (sa.chunk > 256 * kLocalTPT)
+    hipLaunchKernelGGL((k_score_local<512, R, INT4>), grid, dim3(512), 0, s, sa, la, append);
+  else
+    hipLaunchKernelGGL((k_score_local<256, R, INT4>), grid, dim3(256), 0, s, sa, la, append);
   return hipGetLastError();
 }
 

@@ -218,6 +218,23 @@ def test_integer_ties_exact():
                             topk, ds_check.sample_rows(cfg, 100), strict_sets=True)
 
 
+@pytest.mark.parametrize("S0,r,int4,k", [(2100, 8, True, 200), (4200, 16, False, 1500),
+                                         (5500, 8, True, 700), (6140, 16, True, 2048)])
+def test_fused_row_lengths(S0, r, int4, k):
+    """The one-kernel path at the row lengths of each register budget (8, 20
+    and 24 scores per thread), with the label append of the current token."""
+    cfg, inp = _small_inputs("mha_int4_r8", B=2, S0=S0, r=r, int4=int4, k=k)
+    _note("fused S0=%d r=%d int4=%s k=%d" % (S0, r, int4, k))
+    S = cfg.S0 + 1
+    seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
+    labels = prefill(cfg, inp, cfg.S0)
+    plan = ds.decode_plan(inp.K, inp.V, cfg.Hq, cfg.D, labels, k, S)
+    assert plan["path"] == "fused"
+    out, topk = run(cfg, inp, labels, seq, S, flags=ds.DECODE_APPEND)
+    ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k, out,
+                        topk, ds_check.sample_rows(cfg, 100), label_upto=S)
+
+
 @pytest.mark.parametrize("mode", [0, 1])
 def test_local_select_fallbacks(mode):
     """Long rows are pre-selected per chunk, then merged.  mode 0: the whole
@@ -243,6 +260,39 @@ def test_local_select_fallbacks(mode):
                         topk, ds_check.sample_rows(cfg, 100))
     if mode == 0:
         assert (topk < 150).all()
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_local_select_fallbacks_wide_chunks(mode):
+    """The same two fallbacks with 8192-token chunks (512-thread score
+    workgroups): 256 rows of 32769 tokens, k = 400, a quota of 201 per chunk.
+    mode 0: the top 450 tokens all sit in chunk 0; mode 1: chunk 1 holds
+    8192 equal scores, more than its candidate slots."""
+    cfg, inp = _small_inputs("mha_int4_r8", B=2, Hq=128, Hkv=128, S0=32768, k=400)
+    _note("local fallbacks, 8192-token chunks, mode %d" % mode)
+    S = cfg.S0 + 1
+    q = inp.q.float()
+    for b in range(cfg.B):
+        for g in range(cfg.Hkv):
+            ch = inp.chan[g].long()
+            if mode == 0:
+                sgn = torch.sign(q[b, g, ch]).to(torch.float16)
+                sgn[sgn == 0] = 1
+                inp.K[b, g, :450][:, ch] = 60 * sgn
+            else:
+                inp.K[b, g, 8192:16384][:, ch] = 0
+    seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
+    labels = prefill(cfg, inp, S)
+    plan = ds.decode_plan(inp.K, inp.V, cfg.Hq, cfg.D, labels, cfg.k, S, flags=ds.DECODE_UNFUSED)
+    assert plan["path"] == "local" and plan["chunk"] == 8192
+    out, topk = run(cfg, inp, labels, seq, S, flags=ds.DECODE_UNFUSED)
+    ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k, out,
+                        topk, ds_check.sample_rows(cfg, 24, seed=3))
+    if mode == 0:
+        assert (topk < 450).all()
+    del inp, labels, out, topk
+    gc.collect()
+    torch.cuda.empty_cache()
 
 
 def test_split_count_invariance_and_determinism():
