@@ -19,6 +19,7 @@ namespace {
 
 constexpr int64_t kMaxCapacity = int64_t(1) << 24;
 constexpr int kScoreChunk = 4096;      // tokens per chunked-score workgroup
+constexpr int64_t kLocalSlotsPerCu = 256;  // compute units: chunk workgroups of 2048 threads per CU
 constexpr int kTargetAttnBlocks = 1024;
 constexpr int kMinTokensPerSplit = 64;
 
@@ -111,10 +112,33 @@ Plan make_plan(const ds_kv_desc* kv, int k, int max_seq) {
   p.idx_cap = p.sparse ? std::max(p.kk, 1) : 0;
   p.keys_stride = p.sparse ? (int)round_up(std::max(max_seq, 1), 64) : 0;
   p.n_chunks = (int)std::max<int64_t>(1, ceil_div(max_seq, kScoreChunk));
-  // Local top-M chunks: 8192 tokens (512-thread workgroups), halved while the
-  // grid would have fewer than ~4 workgroups per compute unit.
-  p.local_chunk = kMaxLocalChunk;
-  while (p.local_chunk > 512 && rows * ceil_div(max_seq, p.local_chunk) < 1024) p.local_chunk /= 2;
+  // Local top-M chunks (at least 1024 tokens unless the row is shorter).  A
+  // chunk workgroup costs a fixed latency plus its tokens per thread, and the
+  // chunks run in rounds of as many workgroups as the chip holds at once
+  // (1024 of 512 threads, 2048 of 256): a last round with a few workgroups
+  // costs as much as a full one.  The merge then costs about its candidates
+  // (quota per chunk, twice the expected share of k) per merge thread.  Pick
+  // the chunk count with the lowest total.
+  {
+    const int64_t S = std::max(max_seq, 1);
+    double best = 1e300;
+    p.local_chunk = kMaxLocalChunk;
+    const int64_t n_hi = std::min<int64_t>(kMaxLocalChunks, std::max<int64_t>(1, ceil_div(S, 1024)));
+    for (int64_t n = ceil_div(S, kMaxLocalChunk); n <= n_hi; ++n) {
+      const int64_t chunk = round_up(ceil_div(S, n), 64);
+      const int64_t nch = ceil_div(S, chunk);
+      const int threads = chunk > 4096 ? 512 : 256;
+      const int64_t slots = kLocalSlotsPerCu * (2048 / threads);
+      const double rounds = (double)ceil_div(rows * nch, slots);
+      const double quota = std::min<double>((double)chunk,
+                                            std::max(64.0, 2.0 * std::max(k, 0) * chunk / S + 1));
+      const double cost = rounds * (16.0 + (double)ceil_div(chunk, threads)) + nch * quota / 1024.0;
+      if (cost < best - 1e-9) {
+        best = cost;
+        p.local_chunk = (int)chunk;
+      }
+    }
+  }
   p.local_nch = (int)std::max<int64_t>(1, ceil_div(max_seq, p.local_chunk));
   p.cand_stride = p.sparse ? (int)std::min<int64_t>(kMergeCap, round_up(std::max(max_seq, 1), 64)) : 0;
   p.split_cap = (int)std::min<int64_t>(kMaxSplit, std::max<int64_t>(1, ceil_div(p.kk, 16)));

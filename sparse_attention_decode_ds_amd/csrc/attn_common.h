@@ -242,32 +242,54 @@ __device__ __forceinline__ void attn_store(const AttnArgs& a, AttnRed<G>& red, i
 }
 
 // Log-sum-exp merge of the n_split partials of query head row `rq`
-// (16 lanes, lane c covers channels [8c, 8c+8)); fp16 output.
+// (16 lanes, lane c covers channels [8c, 8c+8)); fp16 output.  The partials
+// are read in groups of 8 whose loads are all in flight together, and
+// merged into a running (max, sum, output) state.
 __device__ __forceinline__ void merge_partials(const AttnArgs& a, int64_t rq, int c) {
+  constexpr int kB = 8;
   const float* p = a.part + rq * a.n_split * kPartStride;
-  float M = kNegInf;
-  for (int sp = 0; sp < a.n_split; ++sp) M = fmaxf(M, p[sp * kPartStride + kDv]);
-  float L = 0.0f, O[8];
+  float M = kNegInf, L = 0.0f, O[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) O[i] = 0.0f;
-  if (M != kNegInf) {
-    for (int sp = 0; sp < a.n_split; ++sp) {
-      const float* q = p + sp * kPartStride;
-      const float ms = q[kDv];
-      if (ms == kNegInf) continue;
-      const float sc = exp2f(ms - M);
-      L += sc * q[kDv + 1];
-      const float4 x0 = *reinterpret_cast<const float4*>(q + c * 8);
-      const float4 x1 = *reinterpret_cast<const float4*>(q + c * 8 + 4);
-      O[0] += sc * x0.x;
-      O[1] += sc * x0.y;
-      O[2] += sc * x0.z;
-      O[3] += sc * x0.w;
-      O[4] += sc * x1.x;
-      O[5] += sc * x1.y;
-      O[6] += sc * x1.z;
-      O[7] += sc * x1.w;
+  for (int s0 = 0; s0 < a.n_split; s0 += kB) {
+    float4 x0[kB], x1[kB];
+    float m[kB], l[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      m[u] = kNegInf;
+      l[u] = 0.0f;
+      x0[u] = x1[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (s0 + u < a.n_split) {
+        const float* q = p + (int64_t)(s0 + u) * kPartStride;
+        x0[u] = *reinterpret_cast<const float4*>(q + c * 8);
+        x1[u] = *reinterpret_cast<const float4*>(q + c * 8 + 4);
+        const float2 ml = *reinterpret_cast<const float2*>(q + kDv);
+        m[u] = ml.x;
+        l[u] = ml.y;
+      }
     }
+    float Mn = M;
+#pragma unroll
+    for (int u = 0; u < kB; ++u) Mn = fmaxf(Mn, m[u]);
+    if (Mn == kNegInf) continue;  // every partial so far is empty
+    const float al = M == kNegInf ? 0.0f : exp2f(M - Mn);
+    L *= al;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) O[i] *= al;
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const float w = m[u] == kNegInf ? 0.0f : exp2f(m[u] - Mn);
+      L += w * l[u];
+      O[0] += w * x0[u].x;
+      O[1] += w * x0[u].y;
+      O[2] += w * x0[u].z;
+      O[3] += w * x0[u].w;
+      O[4] += w * x1[u].x;
+      O[5] += w * x1[u].y;
+      O[6] += w * x1[u].z;
+      O[7] += w * x1[u].w;
+    }
+    M = Mn;
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   __half2 r2[4];

@@ -25,8 +25,7 @@ constexpr int kDecodeFusedMaxK = 2048;
 // row selects exactly among the candidates.
 constexpr int kMergeCap = 16384;
 constexpr int kMaxLocalChunks = 256;
-constexpr int kMaxLocalChunk = 8192;  // tokens per local-select chunk at most (512 * kLocalTPT)
-constexpr int kLocalTPT = 16;  // chunk tokens per thread of the local-select score kernel
+constexpr int kMaxLocalChunk = 10240;  // tokens per local-select chunk at most (512 threads x 20)
 // Attention splits per row are capped; partial results cost 528 B each.
 constexpr int kMaxSplit = 64;
 // Selected-token indices staged in LDS per attention workgroup.

@@ -575,7 +575,7 @@ __device__ __forceinline__ void append_label(const LabelArgs& la, int row, int t
 // key in [e_lo, e_hi] are taken lowest position first, `need` of them.  Items
 // of the boundary linear bin span [kmin, kmax] and bins are monotone, so a key
 // inside that span lies in the boundary bin.  mn, mx: smallest and largest
-// valid score.
+// valid score.  Bin 0 (empty slots) stays out of the histogram.
 struct RegSel {
   uint32_t e_lo, e_hi, need;
 };
@@ -596,11 +596,14 @@ __device__ RegSel reg_select(const float* sc, Valid valid, Order order, uint32_t
   for (int i = tid; i < kHistBins; i += NT) ss.hist[i] = 0u;
   if (tid < 8) ss.misc[tid] = tid == 3 ? 0xFFFFFFFFu : 0u;
   __syncthreads();
+  // (empty slots are left out of the histogram: they would all hit bin 0)
 #pragma unroll
   for (int j = 0; j < JMAX; ++j)
 #pragma unroll
-    for (int e = 0; e < VT; ++e)
-      if (valid(j, e)) atomicAdd(&ss.hist[bin(sc[j * VT + e])], 1u);
+    for (int e = 0; e < VT; ++e) {
+      const uint32_t bi = bin(sc[j * VT + e]);
+      if (valid(j, e) && bi != 0u) atomicAdd(&ss.hist[bi], 1u);
+    }
   __syncthreads();
   find_digit<NT>(ss.hist, k, ss.misc + 4, scan_tmp);
   const uint32_t bstar = ss.misc[4];

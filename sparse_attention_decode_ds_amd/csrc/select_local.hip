@@ -25,18 +25,22 @@ namespace {
 constexpr int kNTM = 1024;
 
 __device__ __forceinline__ int chunks_of(int S, int CH) { return (S + CH - 1) / CH; }
-__device__ __forceinline__ int cap_of(int stride, int n_ch) { return stride / max(n_ch, 1); }
-// Quota per chunk: twice the expected share of the top k (at least 64),
-// bounded by the chunk size and by 7/8 of the chunk's candidate slots.
-__device__ __forceinline__ int quota_of(int S, int k, int CH, int cap) {
-  const float expected = (float)k * (float)CH / (float)S;
-  int m = max(64, (int)(2.0f * expected) + 1);
-  m = min(m, CH);
-  m = min(m, cap - cap / 8);
-  return m;
-}
+// Quota and candidate slots per chunk.  The quota M is twice the chunk's
+// expected share of the top k (at least 64, at most the chunk); a chunk owns
+// `cap` slots: M with an eighth and 64 to spare for the boundary bin, within
+// the row's slots.  Writer and reader compute the same numbers.
+struct Quota {
+  int M, cap;
+  __device__ __forceinline__ Quota(int S, int k, int CH, int stride, int n_ch) {
+    const float expected = (float)k * (float)CH / (float)max(S, 1);
+    int m0 = max(64, (int)(2.0f * expected) + 1);
+    m0 = min(m0, CH);
+    cap = min(stride / max(n_ch, 1), m0 + m0 / 8 + 64);
+    M = min(m0, cap - cap / 8);
+  }
+};
 
-template <int NT>
+template <int NT, int TPT>
 struct LocalScratch {
   __half qrows[kMaxGroup][256];
   int32_t chan[128];
@@ -48,20 +52,21 @@ struct LocalScratch {
   float mm_tmp[2 * (NT / 64)];
   uint32_t scan_tmp[NT / 64];
   SelScratch sel;
-  uint32_t tot[kLocalTPT][NT / 64];
+  uint32_t tot[TPT][NT / 64];
   uint32_t theta;
 };
 
-// NT threads score a chunk of at most NT * kLocalTPT tokens.
-template <int NT, int R, bool INT4>
+// NT threads score a chunk of at most NT * TPT tokens.  Empty slots (past
+// the chunk, and the appended token until its score is known) hold -inf.
+template <int NT, int TPT, int R, bool INT4>
 __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la, int append) {
-  constexpr int kNTL = NT;
   constexpr int kWavesL = NT / 64;
   using Vec = typename VecSel<R, INT4>::type;
   constexpr int VT = Vec::VT;
-  constexpr int JMAX = kLocalTPT / VT;
+  constexpr int JMAX = TPT / VT;
   constexpr int UNR = 4;
-  __shared__ LocalScratch<NT> f;
+  constexpr float kEmpty = -__builtin_huge_valf();
+  __shared__ LocalScratch<NT, TPT> f;
 
   const int row = blockIdx.x / sa.n_chunks;
   const int c = blockIdx.x - row * sa.n_chunks;
@@ -83,11 +88,11 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la, 
   // --- setup: small loads first --------------------------------------------
   if (sparse) {
     const __half* qh = sa.q + ((int64_t)b * sa.Hq + (int64_t)g * sa.G) * sa.d_q;
-    for (int i = tid; i < sa.G * sa.d_q; i += kNTL) f.qrows[i / sa.d_q][i % sa.d_q] = qh[i];
+    for (int i = tid; i < sa.G * sa.d_q; i += NT) f.qrows[i / sa.d_q][i % sa.d_q] = qh[i];
     if (sa.keep)
-      for (int i = tid; i < sa.d_k; i += kNTL) f.keep[i] = sa.keep[(int64_t)g * sa.d_k + i];
+      for (int i = tid; i < sa.d_k; i += NT) f.keep[i] = sa.keep[(int64_t)g * sa.d_k + i];
   }
-  for (int j = tid; j < r; j += kNTL) f.chan[j] = sa.chan[(int64_t)g * r + j];
+  for (int j = tid; j < r; j += NT) f.chan[j] = sa.chan[(int64_t)g * r + j];
   if (has_new && tid < (la.d_k >> 3)) {
     const __half* kr = la.K + (int64_t)b * la.ks0 + (int64_t)g * la.ks1 + (int64_t)t_new * la.ks2;
     *reinterpret_cast<uint4*>(&f.knew[tid * 8]) = *reinterpret_cast<const uint4*>(kr + tid * 8);
@@ -100,12 +105,13 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la, 
 
   const RowPtrs p = row_ptrs(sa, row);
   const int n_vec = (t_end - t_beg + VT - 1) / VT;
+  const int v_last = n_vec - 1;  // the only vector that may be partial or hold t_new
   const int v0 = t_beg / VT;
-  const int J = (n_vec + kNTL - 1) / kNTL;
+  const int jn = (n_vec + NT - 1) / NT;  // rounds holding any vector (uniform)
   Vec vec[UNR];
 #pragma unroll
   for (int u = 0; u < UNR; ++u) {
-    const int v = u * kNTL + tid;
+    const int v = u * NT + tid;
     if (v < n_vec) vec[u].load(p, v0 + v);
   }
   __syncthreads();
@@ -124,16 +130,15 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la, 
   q.load(f.q);
 
   // --- score into registers --------------------------------------------------
-  auto token = [&](int j, int e) { return t_beg + (j * kNTL + tid) * VT + e; };
-  auto valid = [&](int j, int e) { return token(j, e) < t_end; };
-  float sc[kLocalTPT];
-  float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
+  auto token = [&](int j, int e) { return t_beg + (j * NT + tid) * VT + e; };
+  float sc[TPT];
+  float mn = __builtin_huge_valf(), mx = kEmpty;
 #pragma unroll
   for (int j0 = 0; j0 < JMAX; j0 += UNR) {
     if (j0 > 0) {
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
-        const int v = (j0 + u) * kNTL + tid;
+        const int v = (j0 + u) * NT + tid;
         if (j0 + u < JMAX && v < n_vec) vec[u].load(p, v0 + v);
       }
     }
@@ -141,60 +146,79 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la, 
     for (int u = 0; u < UNR; ++u) {
       const int j = j0 + u;
       if (j >= JMAX) continue;
-      const int v = j * kNTL + tid;
+      const int v = j * NT + tid;
       float s[VT];
 #pragma unroll
-      for (int e = 0; e < VT; ++e) s[e] = 0.0f;
-      if (v < n_vec) vec[u].score(q, r, s);
+      for (int e = 0; e < VT; ++e) s[e] = kEmpty;
+      if (v < v_last) {
+        vec[u].score(q, r, s);
 #pragma unroll
-      for (int e = 0; e < VT; ++e) {
-        sc[j * VT + e] = s[e];
-        if (v < n_vec && valid(j, e) && !(has_new && token(j, e) == t_new)) {
+        for (int e = 0; e < VT; ++e) {
           mn = fminf(mn, s[e]);
           mx = fmaxf(mx, s[e]);
         }
+      } else if (v == v_last) {
+        vec[u].score(q, r, s);
+#pragma unroll
+        for (int e = 0; e < VT; ++e) {
+          const int t = token(j, e);
+          if (t >= t_end || (has_new && t == t_new)) {
+            s[e] = kEmpty;
+          } else {
+            mn = fminf(mn, s[e]);
+            mx = fmaxf(mx, s[e]);
+          }
+        }
       }
+#pragma unroll
+      for (int e = 0; e < VT; ++e) sc[j * VT + e] = s[e];
     }
   }
   if (has_new) {
     __syncthreads();
     const float sn = f.snew;
+    if ((v_last & (NT - 1)) == tid) {
+      const int jl = v_last / NT;
 #pragma unroll
-    for (int j = 0; j < JMAX; ++j)
+      for (int j = 0; j < JMAX; ++j)
 #pragma unroll
-      for (int e = 0; e < VT; ++e)
-        if (token(j, e) == t_new) sc[j * VT + e] = sn;
+        for (int e = 0; e < VT; ++e)
+          if (j == jl && token(j, e) == t_new) sc[j * VT + e] = sn;
+    }
     mn = fminf(mn, sn);
     mx = fmaxf(mx, sn);
   }
 
   // --- local threshold ---------------------------------------------------------
   const int n_ch = chunks_of(S, CH);
-  const int cap = cap_of(sa.cand_stride, n_ch);
-  const int M = quota_of(S, sa.k, CH, cap);
+  const Quota qu(S, sa.k, CH, sa.cand_stride, n_ch);
+  const int cap = qu.cap;
+  const int M = qu.M;
   const int n_c = t_end - t_beg;
   const bool keep_all = n_c <= M;
   int kept = n_c;
-  // bit (j * VT + e) of keptm: slot kept (valid and at or above the quota bin)
+  // bit (j * VT + e) of keptm: slot kept
   uint32_t keptm = 0u;
   uint32_t tmin = 0xFFFFFFFFu;
   if (!keep_all) {
-    block_minmax<kNTL>(mn, mx, f.mm_tmp);
+    block_minmax<NT>(mn, mx, f.mm_tmp);
     const LinBins bin(mn, mx);
     SelScratch& ss = f.sel;
-    for (int i = tid; i < kHistBins; i += kNTL) ss.hist[i] = 0u;
+    for (int i = tid; i < kHistBins; i += NT) ss.hist[i] = 0u;
     if (tid == 0) f.theta = 0xFFFFFFFFu;
     __syncthreads();
-    uint32_t bins[kLocalTPT];
 #pragma unroll
     for (int j = 0; j < JMAX; ++j)
+      if (j < jn) {
 #pragma unroll
-      for (int e = 0; e < VT; ++e) {
-        bins[j * VT + e] = bin(sc[j * VT + e]);
-        if (j < J && valid(j, e)) atomicAdd(&ss.hist[bins[j * VT + e]], 1u);
+        for (int e = 0; e < VT; ++e) {
+          const uint32_t bi = bin(sc[j * VT + e]);
+          if (bi != 0u) atomicAdd(&ss.hist[bi], 1u);  // bin 0: empty slots
+        }
       }
     __syncthreads();
-    find_digit<kNTL>(ss.hist, (uint32_t)M, ss.misc + 4, f.scan_tmp);
+    // the bin of the M-th largest: every valid key lies in bins 1 .. 2047
+    find_digit<NT>(ss.hist, (uint32_t)M, ss.misc + 4, f.scan_tmp);
     const uint32_t bM = ss.misc[4];
     kept = (int)(ss.misc[5] + ss.misc[6]);
     if (kept > cap) {  // the boundary bin is too full for this chunk's slots
@@ -203,18 +227,22 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la, 
     }
 #pragma unroll
     for (int j = 0; j < JMAX; ++j)
+      if (j < jn) {
 #pragma unroll
-      for (int e = 0; e < VT; ++e)
-        if (j < J && valid(j, e) && bins[j * VT + e] >= bM) {
-          keptm |= 1u << (j * VT + e);
-          if (bins[j * VT + e] == bM) tmin = min(tmin, score_key(sc[j * VT + e]));
+        for (int e = 0; e < VT; ++e) {
+          const uint32_t bj = bin(sc[j * VT + e]);
+          if (bj >= bM) {
+            keptm |= 1u << (j * VT + e);
+            if (bj == bM) tmin = min(tmin, score_key(sc[j * VT + e]));
+          }
         }
+      }
   } else {
 #pragma unroll
     for (int j = 0; j < JMAX; ++j)
 #pragma unroll
       for (int e = 0; e < VT; ++e)
-        if (j < J && valid(j, e)) keptm |= 1u << (j * VT + e);
+        if (j < jn && sc[j * VT + e] != kEmpty) keptm |= 1u << (j * VT + e);
   }
 
   // --- ordered emission of the kept tokens ---------------------------------------
@@ -224,7 +252,7 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la, 
 #pragma unroll
   for (int j = 0; j < JMAX; ++j) {
     ex[j] = 0u;
-    if (j >= J) continue;
+    if (j >= jn) continue;
     const uint32_t cnt = __builtin_popcount((keptm >> (j * VT)) & ((1u << VT) - 1u));
     const uint32_t incl = wave_incl_scan(cnt);
     ex[j] = incl - cnt;
@@ -239,7 +267,7 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la, 
   uint32_t run = 0u;
 #pragma unroll
   for (int j = 0; j < JMAX; ++j) {
-    if (j >= J) continue;
+    if (j >= jn) continue;
     uint32_t pre = 0u, rowt = 0u;
 #pragma unroll
     for (int ww = 0; ww < kWavesL; ++ww) {
@@ -295,7 +323,7 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
     return;
   }
   const int n_ch = chunks_of(S, sa.chunk);
-  const int cap = cap_of(sa.cand_stride, n_ch);
+  const int cap = Quota(S, sa.k, sa.chunk, sa.cand_stride, n_ch).cap;
   const int slots = n_ch * cap;  // <= cand_stride <= kMergeCap
 
   // Candidate slot i = j * kNTM + tid of this thread; chunk c owns slots
@@ -332,25 +360,29 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
   bool full = f.flag != 0u || f.total < (uint32_t)sa.k;
 
   if (!full) {
-    // valid slots as a bit mask: chunk of slot i is floor(i / cap)
-    uint32_t vmask = 0u;
+    // Slots past their chunk's count become empty (-inf); the chunk of slot
+    // i is floor(i / cap).
     float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
     const float inv_cap = 1.0f / (float)cap;
 #pragma unroll
     for (int j = 0; j < kMergeJ; ++j) {
       const int i = j * kNTM + tid;
-      if (i >= slots) continue;
-      int c = (int)((float)i * inv_cap);
-      c += (i >= (c + 1) * cap) ? 1 : 0;
-      c -= (i < c * cap) ? 1 : 0;
-      if (i - c * cap < f.ch_cnt[c]) {
-        vmask |= 1u << j;
+      bool ok = false;
+      if (i < slots) {
+        int c = (int)((float)i * inv_cap);
+        c += (i >= (c + 1) * cap) ? 1 : 0;
+        c -= (i < c * cap) ? 1 : 0;
+        ok = i - c * cap < f.ch_cnt[c];
+      }
+      if (ok) {
         mn = fminf(mn, sc[j]);
         mx = fmaxf(mx, sc[j]);
+      } else {
+        sc[j] = -__builtin_huge_valf();
       }
     }
     block_minmax<kNTM>(mn, mx, f.mm_tmp);
-    auto valid = [&](int j, int) { return ((vmask >> j) & 1u) != 0u; };
+    auto valid = [&](int j, int) { return j * kNTM < slots; };  // empty slots hold -inf
     auto order = [&](int j, int) { return j * kNTM + tid; };
     const RegSel rs = reg_select<kNTM, 1, kMergeJ>(sc, valid, order, (uint32_t)sa.k, mn, mx, f.sel,
                                                   f.scan_tmp);
@@ -390,10 +422,12 @@ template <int R, bool INT4>
 hipError_t launch_local_rt(const ScoreArgs& sa, const LabelArgs& la, int append, int rows,
                            hipStream_t s) {
   const dim3 grid(rows * sa.n_chunks);
-  if (sa.chunk > 256 * kLocalTPT)
-    hipLaunchKernelGGL((k_score_local<512, R, INT4>), grid, dim3(512), 0, s, sa, la, append);
+  if (sa.chunk > 512 * 16)
+    hipLaunchKernelGGL((k_score_local<512, 20, R, INT4>), grid, dim3(512), 0, s, sa, la, append);
+  else if (sa.chunk > 256 * 16)
+    hipLaunchKernelGGL((k_score_local<512, 16, R, INT4>), grid, dim3(512), 0, s, sa, la, append);
   else
-    hipLaunchKernelGGL((k_score_local<256, R, INT4>), grid, dim3(256), 0, s, sa, la, append);
+    hipLaunchKernelGGL((k_score_local<256, 16, R, INT4>), grid, dim3(256), 0, s, sa, la, append);
   return hipGetLastError();
 }
 

@@ -239,9 +239,10 @@ def test_fused_row_lengths(S0, r, int4, k):
 def test_local_select_fallbacks(mode):
     """Long rows are pre-selected per chunk, then merged.  mode 0: the whole
     top k sits in the first chunk (more than its quota), so the merge's
-    completeness check fails; mode 1: a chunk of equal scores overflows its
-    candidate slots.  Both must fall back to the full select and stay exact."""
-    cfg, inp = _small_inputs("mha_int4_r8", B=2, S0=1800, k=100)
+    completeness check fails; mode 1: a whole chunk of equal scores overflows
+    its candidate slots.  Both must fall back to the full select and stay
+    exact."""
+    cfg, inp = _small_inputs("mha_int4_r8", B=2, S0=6000, k=100)
     q = inp.q.float()
     for b in range(cfg.B):
         for g in range(cfg.Hkv):
@@ -251,10 +252,12 @@ def test_local_select_fallbacks(mode):
                 sgn[sgn == 0] = 1
                 inp.K[b, g, :150][:, ch] = 60 * sgn
             else:
-                inp.K[b, g, 512:1024][:, ch] = 0
+                inp.K[b, g, 1024:3072][:, ch] = 0
     S = cfg.S0 + 1
     seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
     labels = prefill(cfg, inp, S)
+    plan = ds.decode_plan(inp.K, inp.V, cfg.Hq, cfg.D, labels, cfg.k, S, flags=ds.DECODE_UNFUSED)
+    assert plan["path"] == "local" and plan["chunk"] <= 2048   # several chunks, quota 64 < k
     out, topk = run(cfg, inp, labels, seq, S, flags=ds.DECODE_UNFUSED)
     ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k, out,
                         topk, ds_check.sample_rows(cfg, 100))
@@ -264,12 +267,13 @@ def test_local_select_fallbacks(mode):
 
 @pytest.mark.parametrize("mode", [0, 1])
 def test_local_select_fallbacks_wide_chunks(mode):
-    """The same two fallbacks with 8192-token chunks (512-thread score
-    workgroups): 256 rows of 32769 tokens, k = 400, a quota of 201 per chunk.
-    mode 0: the top 450 tokens all sit in chunk 0; mode 1: chunk 1 holds
-    8192 equal scores, more than its candidate slots."""
+    """The same two fallbacks with chunks of over 8192 tokens (512-thread
+    score workgroups, 20 scores per thread): 256 rows of 32769 tokens in four
+    chunks, k = 400, a quota of about 200 per chunk.  mode 0: the top 450
+    tokens all sit in chunk 0; mode 1: chunk 1 holds over 8000 equal scores,
+    more than its candidate slots."""
     cfg, inp = _small_inputs("mha_int4_r8", B=2, Hq=128, Hkv=128, S0=32768, k=400)
-    _note("local fallbacks, 8192-token chunks, mode %d" % mode)
+    _note("local fallbacks, wide chunks, mode %d" % mode)
     S = cfg.S0 + 1
     q = inp.q.float()
     for b in range(cfg.B):
@@ -284,7 +288,7 @@ def test_local_select_fallbacks_wide_chunks(mode):
     seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
     labels = prefill(cfg, inp, S)
     plan = ds.decode_plan(inp.K, inp.V, cfg.Hq, cfg.D, labels, cfg.k, S, flags=ds.DECODE_UNFUSED)
-    assert plan["path"] == "local" and plan["chunk"] == 8192
+    assert plan["path"] == "local" and plan["chunk"] > 8192
     out, topk = run(cfg, inp, labels, seq, S, flags=ds.DECODE_UNFUSED)
     ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k, out,
                         topk, ds_check.sample_rows(cfg, 24, seed=3))
