@@ -188,13 +188,17 @@ AttnArgs attn_args(const ds_kv_desc* kv, const void* q, const void* K, const voi
   return aa;
 }
 
-int auto_splits(const Plan& p, int64_t rows, int requested) {
+// Attention partitions per row: about kTargetAttnBlocks workgroups in all,
+// each with at least 64 tokens (128 for query groups, whose workgroups take
+// 16-token tiles per wave).
+int auto_splits(const Plan& p, int64_t rows, int G, int requested) {
   int ns;
   if (requested > 0) {
     ns = requested;
   } else {
+    const int min_tok = G > 1 ? 2 * kMinTokensPerSplit : kMinTokensPerSplit;
     ns = (int)ceil_div(kTargetAttnBlocks, std::max<int64_t>(rows, 1));
-    ns = (int)std::min<int64_t>(ns, std::max<int64_t>(1, ceil_div(p.kk, kMinTokensPerSplit)));
+    ns = (int)std::min<int64_t>(ns, std::max<int64_t>(1, ceil_div(p.kk, min_tok)));
   }
   return std::max(1, std::min(ns, p.split_cap));
 }
@@ -224,7 +228,7 @@ Route route(const ds_kv_desc* kv, const ds_label_desc* lab, int k, int max_seq, 
     r.tps = std::max(p.kk, 1);
     return r;
   }
-  r.n_split = auto_splits(p, rows, n_split_req);
+  r.n_split = auto_splits(p, rows, G, n_split_req);
   r.tps = (int)std::max<int64_t>(1, round_up(ceil_div(std::max(p.kk, 1), r.n_split), 16));
   r.n_split = (int)std::max<int64_t>(1, ceil_div(std::max(p.kk, 1), r.tps));
   return r;

@@ -68,19 +68,12 @@ hipError_t launch_g(const AttnArgs& a, int rows, bool final_out, hipStream_t s) 
 
 }  // namespace
 
+// Single-head groups stream rows through the vector units; groups of 2 to 8
+// query heads take the matrix-core kernel (attn_gqa.hip).
 hipError_t launch_attn(const AttnArgs& a, int rows, int G, bool final_out, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  switch (G) {
-    case 1: return launch_g<1>(a, rows, final_out, s);
-    case 2: return launch_g<2>(a, rows, final_out, s);
-    case 3: return launch_g<3>(a, rows, final_out, s);
-    case 4: return launch_g<4>(a, rows, final_out, s);
-    case 5: return launch_g<5>(a, rows, final_out, s);
-    case 6: return launch_g<6>(a, rows, final_out, s);
-    case 7: return launch_g<7>(a, rows, final_out, s);
-    case 8: return launch_g<8>(a, rows, final_out, s);
-    default: return hipErrorInvalidValue;
-  }
+  if (G == 1) return launch_g<1>(a, rows, final_out, s);
+  return launch_attn_gqa(a, rows, G, final_out, s);
 }
 
 hipError_t launch_combine(const AttnArgs& a, int B, hipStream_t s) {

@@ -112,6 +112,7 @@ hipError_t launch_label(const LabelArgs& a, int n_blocks, hipStream_t s);
 hipError_t launch_score_chunks(const ScoreArgs& a, int rows, hipStream_t s);
 hipError_t launch_select_stream(const ScoreArgs& a, int rows, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int rows, int G, bool final_out, hipStream_t s);
+hipError_t launch_attn_gqa(const AttnArgs& a, int rows, int G, bool final_out, hipStream_t s);
 hipError_t launch_combine(const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_decode_fused(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la,
                                int append, int rows, hipStream_t s);
