@@ -686,7 +686,7 @@ __device__ RegSel reg_select(const float* sc, Valid valid, Order order, uint32_t
 
 // Ordered emission of the items taken by `r`: put(pos, j, e) with pos the
 // item's rank among the taken items in position order.  tot holds
-// JMAX * (NT / 64) words of LDS.  One barrier.
+// JMAX * (NT / 64) words of LDS.  One barrier (two for more than 64 words).
 // The classes are decided on the scores: key(s) > e_hi iff s > f_hi and
 // key(s) >= e_lo iff s >= f_lo, with f_hi the largest float whose key is at
 // most e_hi and f_lo the smallest float whose key is at least e_lo.  Both
@@ -716,17 +716,49 @@ __device__ __forceinline__ void reg_emit(const float* sc, Valid valid, const Reg
     if (lane == 63) tot[j * W + w] = incl;
   }
   __syncthreads();
+  // Position of each (round, wave) group among all groups in item order:
+  // small tables are summed by every thread; large ones are turned into
+  // exclusive prefixes in place by wave 0 first (one more barrier).
+  constexpr int N = JMAX * W;
+  constexpr bool kScan = N > 64;
+  if (kScan) {
+    constexpr int E = (N + 63) / 64;
+    if (w == 0) {
+      uint32_t v[E];
+      uint32_t sum = 0u;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const int at = lane * E + i;
+        v[i] = at < N ? tot[at] : 0u;
+        sum += v[i];
+      }
+      uint32_t run0 = wave_incl_scan(sum) - sum;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const int at = lane * E + i;
+        if (at < N) tot[at] = run0;
+        run0 += v[i];
+      }
+    }
+    __syncthreads();
+  }
   uint32_t run = 0u;
 #pragma unroll
   for (int j = 0; j < JMAX; ++j) {
-    uint32_t pre = 0u, rowt = 0u;
+    uint32_t base;
+    if (kScan) {
+      base = tot[j * W + w] + ex[j];
+    } else {
+      uint32_t pre = 0u, rowt = 0u;
 #pragma unroll
-    for (int ww = 0; ww < W; ++ww) {
-      const uint32_t t = tot[j * W + ww];
-      pre += ww < w ? t : 0u;
-      rowt += t;
+      for (int ww = 0; ww < W; ++ww) {
+        const uint32_t t = tot[j * W + ww];
+        pre += ww < w ? t : 0u;
+        rowt += t;
+      }
+      base = run + pre + ex[j];
+      run += rowt;
     }
-    const uint32_t base = run + pre + ex[j];
     uint32_t ab = base & 0xFFFFu, eb = base >> 16;
 #pragma unroll
     for (int e = 0; e < VT; ++e) {
@@ -737,7 +769,6 @@ __device__ __forceinline__ void reg_emit(const float* sc, Valid valid, const Reg
       ab += A;
       eb += E;
     }
-    run += rowt;
   }
 }
 
