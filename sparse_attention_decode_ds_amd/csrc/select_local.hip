@@ -292,7 +292,8 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la, 
   }
 }
 
-constexpr int kMergeJ = kMergeCap / kNTM;  // candidate slots per thread
+constexpr int kMergeVT = 4;                             // consecutive slots per thread and round
+constexpr int kMergeJ = kMergeCap / (kNTM * kMergeVT);  // rounds
 
 struct MergeScratch {
   SelScratch sel;
@@ -326,23 +327,30 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
   const int cap = Quota(S, sa.k, sa.chunk, sa.cand_stride, n_ch).cap;
   const int slots = n_ch * cap;  // <= cand_stride <= kMergeCap
 
-  // Candidate slot i = j * kNTM + tid of this thread; chunk c owns slots
-  // [c * cap, c * cap + cnt_c), in ascending token order, so slot order is
-  // token order.  Every load is issued before the counts are known.
+  // Candidate slots (j * kNTM + tid) * 4 + e of this thread; chunk c owns
+  // slots [c * cap, c * cap + cnt_c), in ascending token order, so slot order
+  // is token order.  Every load is issued before the counts are known (a
+  // group of four that starts below `slots` lies inside the row's area).
+  constexpr int VTM = kMergeVT;
   const uint32_t* ck = sa.cand_key + (int64_t)row * sa.cand_stride;
   const int32_t* ci = sa.cand_idx + (int64_t)row * sa.cand_stride;
-  float sc[kMergeJ];
-  int32_t tok[kMergeJ];
+  float sc[kMergeJ * VTM];
+  int32_t tok[kMergeJ * VTM];
 #pragma unroll
   for (int j = 0; j < kMergeJ; ++j) {
-    const int i = j * kNTM + tid;
-    uint32_t key = 0u;
-    tok[j] = 0;
+    const int i = (j * kNTM + tid) * VTM;
+    uint4 kk = make_uint4(0u, 0u, 0u, 0u), tt = make_uint4(0u, 0u, 0u, 0u);
     if (i < slots) {
-      key = ck[i];
-      tok[j] = ci[i];
+      kk = *reinterpret_cast<const uint4*>(ck + i);
+      tt = *reinterpret_cast<const uint4*>(ci + i);
     }
-    sc[j] = key_float(key);
+    const uint32_t kv[4] = {kk.x, kk.y, kk.z, kk.w};
+    const uint32_t tv[4] = {tt.x, tt.y, tt.z, tt.w};
+#pragma unroll
+    for (int e = 0; e < VTM; ++e) {
+      sc[j * VTM + e] = key_float(kv[e]);
+      tok[j * VTM + e] = (int32_t)tv[e];
+    }
   }
   if (tid == 0) {
     f.flag = n_ch > kMaxLocalChunks ? 1u : 0u;
@@ -365,35 +373,38 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
     float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
     const float inv_cap = 1.0f / (float)cap;
 #pragma unroll
-    for (int j = 0; j < kMergeJ; ++j) {
-      const int i = j * kNTM + tid;
-      bool ok = false;
-      if (i < slots) {
-        int c = (int)((float)i * inv_cap);
-        c += (i >= (c + 1) * cap) ? 1 : 0;
-        c -= (i < c * cap) ? 1 : 0;
-        ok = i - c * cap < f.ch_cnt[c];
+    for (int j = 0; j < kMergeJ; ++j)
+#pragma unroll
+      for (int e = 0; e < VTM; ++e) {
+        const int i = (j * kNTM + tid) * VTM + e;
+        bool ok = false;
+        if (i < slots) {
+          int c = (int)((float)i * inv_cap);
+          c += (i >= (c + 1) * cap) ? 1 : 0;
+          c -= (i < c * cap) ? 1 : 0;
+          ok = i - c * cap < f.ch_cnt[c];
+        }
+        if (ok) {
+          mn = fminf(mn, sc[j * VTM + e]);
+          mx = fmaxf(mx, sc[j * VTM + e]);
+        } else {
+          sc[j * VTM + e] = -__builtin_huge_valf();
+        }
       }
-      if (ok) {
-        mn = fminf(mn, sc[j]);
-        mx = fmaxf(mx, sc[j]);
-      } else {
-        sc[j] = -__builtin_huge_valf();
-      }
-    }
     block_minmax<kNTM>(mn, mx, f.mm_tmp);
-    auto valid = [&](int j, int) { return j * kNTM < slots; };  // empty slots hold -inf
-    auto order = [&](int j, int) { return j * kNTM + tid; };
-    const RegSel rs = reg_select<kNTM, 1, kMergeJ>(sc, valid, order, (uint32_t)sa.k, mn, mx, f.sel,
-                                                  f.scan_tmp);
+    auto valid = [&](int j, int) { return j * kNTM * VTM < slots; };  // empty slots hold -inf
+    auto order = [&](int j, int e) { return (j * kNTM + tid) * VTM + e; };
+    const RegSel rs = reg_select<kNTM, VTM, kMergeJ>(sc, valid, order, (uint32_t)sa.k, mn, mx,
+                                                    f.sel, f.scan_tmp);
     // Complete iff every chunk that dropped tokens (theta != 0) has theta at
     // or below the smallest selected key; e_lo is at or below that key.
     if (tid < min(n_ch, kMaxLocalChunks) && f.ch_theta[tid] > rs.e_lo) atomicOr(&f.flag, 1u);
     __syncthreads();
     full = f.flag != 0u;
     if (!full)
-      reg_emit<kNTM, 1, kMergeJ>(sc, valid, rs, f.tot,
-                                 [&](uint32_t pos, int j, int) { out[pos] = tok[j]; });
+      reg_emit<kNTM, VTM, kMergeJ>(sc, valid, rs, f.tot, [&](uint32_t pos, int j, int e) {
+        out[pos] = tok[j * VTM + e];
+      });
   }
 
   if (full) {
