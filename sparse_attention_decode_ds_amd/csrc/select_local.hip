@@ -108,13 +108,15 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la, 
   const int v_last = n_vec - 1;  // the only vector that may be partial or hold t_new
   const int v0 = t_beg / VT;
   const int jn = (n_vec + NT - 1) / NT;  // rounds holding any vector (uniform)
+  // The label loads go out after the small setup loads have landed: issued
+  // together, the setup loads wait behind every workgroup's label stream.
   Vec vec[UNR];
+  __syncthreads();
 #pragma unroll
   for (int u = 0; u < UNR; ++u) {
     const int v = u * NT + tid;
     if (v < n_vec) vec[u].load(p, v0 + v);
   }
-  __syncthreads();
   {
     float acc = 0.0f;
     if (tid < r) {
