@@ -370,8 +370,8 @@ def main():
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": dom_bytes,
                      "avg_launch_us": round(dom_ms * 1e3, 3) if dom_ms else None,
-                     "timing": "HIP events around the kernel on its stream, a second pass "
-                               "of the same %d steps" % args.steps},
+                     "timing": "HIP events recorded by the kernel's own launch at its start "
+                               "and end, in a second pass of the same %d steps" % args.steps},
         "step": {"algorithmic_bytes": step_bytes,
                  "hbm_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
                  "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

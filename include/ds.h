@@ -154,7 +154,10 @@ typedef struct {
                                is recorded on `stream` before stage i, the last
                                one after the final stage (stages that launch
                                nothing give empty intervals); NULL slots are
-                               skipped */
+                               skipped.  The attention stage is one kernel:
+                               when slots DS_STAGE_ATTN and DS_STAGE_COMBINE
+                               are both given, that launch records them at the
+                               kernel's own start and end */
 } ds_decode_opts;
 
 /* Kernel paths of ds_decode_attn. */

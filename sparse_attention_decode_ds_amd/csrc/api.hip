@@ -358,6 +358,16 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
   auto mark = [&](int i) {
     if (ev && ev[i]) (void)hipEventRecord(ev[i], stream);
   };
+  // The attention stage is one kernel: when both of its events are given,
+  // the launch records them at the kernel's own start and end.
+  KEvents attn_ev;
+  if (ev && ev[DS_STAGE_ATTN] && ev[DS_STAGE_COMBINE]) {
+    attn_ev.start = ev[DS_STAGE_ATTN];
+    attn_ev.stop = ev[DS_STAGE_COMBINE];
+  }
+  auto mark_attn = [&](int i) {
+    if (!attn_ev.start) mark(i);
+  };
 
   mark(DS_STAGE_APPEND);
   // Paths for the score and select: one kernel for the whole step (single
@@ -428,11 +438,11 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
       AttnArgs aa = attn_args(kv, q, K, V, seq_lens, max_seq_len, keep, sm_scale, out, ws, p);
       aa.n_split = 1;
       mark(DS_STAGE_SELECT);
-      mark(DS_STAGE_ATTN);
-      if (launch_decode_fused(sa, aa, la, (flags & DS_DECODE_APPEND) ? 1 : 0, (int)rows, stream) !=
-          hipSuccess)
+      mark_attn(DS_STAGE_ATTN);
+      if (launch_decode_fused(sa, aa, la, (flags & DS_DECODE_APPEND) ? 1 : 0, (int)rows, stream,
+                              attn_ev) != hipSuccess)
         return DS_ERR_HIP;
-      mark(DS_STAGE_COMBINE);
+      mark_attn(DS_STAGE_COMBINE);
       mark(DS_STAGE_COUNT);
       return DS_OK;
     }
@@ -462,10 +472,10 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
   aa.n_split = rt.n_split;
   aa.tps = rt.tps;
 
-  mark(DS_STAGE_ATTN);
+  mark_attn(DS_STAGE_ATTN);
   const bool final_out = aa.n_split == 1;
-  if (launch_attn(aa, (int)rows, G, final_out, stream) != hipSuccess) return DS_ERR_HIP;
-  mark(DS_STAGE_COMBINE);
+  if (launch_attn(aa, (int)rows, G, final_out, stream, attn_ev) != hipSuccess) return DS_ERR_HIP;
+  mark_attn(DS_STAGE_COMBINE);
   if (!final_out && launch_combine(aa, B, stream) != hipSuccess) return DS_ERR_HIP;
   mark(DS_STAGE_COUNT);
   return DS_OK;

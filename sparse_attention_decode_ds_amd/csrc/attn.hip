@@ -57,23 +57,21 @@ __global__ __launch_bounds__(kAttnThreads) void k_combine(AttnArgs a, int n_rows
 }
 
 template <int G>
-hipError_t launch_g(const AttnArgs& a, int rows, bool final_out, hipStream_t s) {
+hipError_t launch_g(const AttnArgs& a, int rows, bool final_out, hipStream_t s, const KEvents& ev) {
   const dim3 grid(rows * a.n_split);
-  if (final_out)
-    hipLaunchKernelGGL((k_attn<G, true>), grid, dim3(kAttnThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_attn<G, false>), grid, dim3(kAttnThreads), 0, s, a);
-  return hipGetLastError();
+  if (final_out) return launch_k(k_attn<G, true>, grid, dim3(kAttnThreads), s, ev, a);
+  return launch_k(k_attn<G, false>, grid, dim3(kAttnThreads), s, ev, a);
 }
 
 }  // namespace
 
 // Single-head groups stream rows through the vector units; groups of 2 to 8
 // query heads take the matrix-core kernel (attn_gqa.hip).
-hipError_t launch_attn(const AttnArgs& a, int rows, int G, bool final_out, hipStream_t s) {
+hipError_t launch_attn(const AttnArgs& a, int rows, int G, bool final_out, hipStream_t s,
+                       const KEvents& ev) {
   if (rows <= 0) return hipSuccess;
-  if (G == 1) return launch_g<1>(a, rows, final_out, s);
-  return launch_attn_gqa(a, rows, G, final_out, s);
+  if (G == 1) return launch_g<1>(a, rows, final_out, s, ev);
+  return launch_attn_gqa(a, rows, G, final_out, s, ev);
 }
 
 hipError_t launch_combine(const AttnArgs& a, int B, hipStream_t s) {

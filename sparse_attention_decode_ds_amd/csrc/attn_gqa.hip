@@ -191,27 +191,25 @@ __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a) {
 }
 
 template <int G>
-hipError_t launch_g(const AttnArgs& a, int rows, bool final_out, hipStream_t s) {
+hipError_t launch_g(const AttnArgs& a, int rows, bool final_out, hipStream_t s, const KEvents& ev) {
   const dim3 grid(rows * a.n_split);
-  if (final_out)
-    hipLaunchKernelGGL((k_attn_gqa<G, true>), grid, dim3(kGT), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_attn_gqa<G, false>), grid, dim3(kGT), 0, s, a);
-  return hipGetLastError();
+  if (final_out) return launch_k(k_attn_gqa<G, true>, grid, dim3(kGT), s, ev, a);
+  return launch_k(k_attn_gqa<G, false>, grid, dim3(kGT), s, ev, a);
 }
 
 }  // namespace
 
-hipError_t launch_attn_gqa(const AttnArgs& a, int rows, int G, bool final_out, hipStream_t s) {
+hipError_t launch_attn_gqa(const AttnArgs& a, int rows, int G, bool final_out, hipStream_t s,
+                           const KEvents& ev) {
   if (rows <= 0) return hipSuccess;
   switch (G) {
-    case 2: return launch_g<2>(a, rows, final_out, s);
-    case 3: return launch_g<3>(a, rows, final_out, s);
-    case 4: return launch_g<4>(a, rows, final_out, s);
-    case 5: return launch_g<5>(a, rows, final_out, s);
-    case 6: return launch_g<6>(a, rows, final_out, s);
-    case 7: return launch_g<7>(a, rows, final_out, s);
-    case 8: return launch_g<8>(a, rows, final_out, s);
+    case 2: return launch_g<2>(a, rows, final_out, s, ev);
+    case 3: return launch_g<3>(a, rows, final_out, s, ev);
+    case 4: return launch_g<4>(a, rows, final_out, s, ev);
+    case 5: return launch_g<5>(a, rows, final_out, s, ev);
+    case 6: return launch_g<6>(a, rows, final_out, s, ev);
+    case 7: return launch_g<7>(a, rows, final_out, s, ev);
+    case 8: return launch_g<8>(a, rows, final_out, s, ev);
     default: return hipErrorInvalidValue;
   }
 }

@@ -220,23 +220,21 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
 
 template <int R, bool INT4, int TPT>
 hipError_t launch_rt(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la, int append,
-                     int rows, hipStream_t s) {
-  hipLaunchKernelGGL((k_decode_fused<R, INT4, TPT>), dim3(rows), dim3(kNT), 0, s, sa, aa, la,
-                     append);
-  return hipGetLastError();
+                     int rows, hipStream_t s, const KEvents& ev) {
+  return launch_k(k_decode_fused<R, INT4, TPT>, dim3(rows), dim3(kNT), s, ev, sa, aa, la, append);
 }
 
 template <int TPT>
 hipError_t launch_tpt(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la, int append,
-                      int rows, hipStream_t s) {
+                      int rows, hipStream_t s, const KEvents& ev) {
   if (sa.is_int4) {
-    if (sa.r == 8) return launch_rt<8, true, TPT>(sa, aa, la, append, rows, s);
-    if (sa.r == 16) return launch_rt<16, true, TPT>(sa, aa, la, append, rows, s);
-    return launch_rt<0, true, TPT>(sa, aa, la, append, rows, s);
+    if (sa.r == 8) return launch_rt<8, true, TPT>(sa, aa, la, append, rows, s, ev);
+    if (sa.r == 16) return launch_rt<16, true, TPT>(sa, aa, la, append, rows, s, ev);
+    return launch_rt<0, true, TPT>(sa, aa, la, append, rows, s, ev);
   }
-  if (sa.r == 8) return launch_rt<8, false, TPT>(sa, aa, la, append, rows, s);
-  if (sa.r == 16) return launch_rt<16, false, TPT>(sa, aa, la, append, rows, s);
-  return launch_rt<0, false, TPT>(sa, aa, la, append, rows, s);
+  if (sa.r == 8) return launch_rt<8, false, TPT>(sa, aa, la, append, rows, s, ev);
+  if (sa.r == 16) return launch_rt<16, false, TPT>(sa, aa, la, append, rows, s, ev);
+  return launch_rt<0, false, TPT>(sa, aa, la, append, rows, s, ev);
 }
 
 }  // namespace
@@ -251,11 +249,11 @@ bool decode_fused_fits(int max_seq, int k, int r, int is_int4) {
 // so that no round of register slots is entirely empty for long rows of the
 // common lengths.
 hipError_t launch_decode_fused(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la,
-                               int append, int rows, hipStream_t s) {
+                               int append, int rows, hipStream_t s, const KEvents& ev) {
   if (rows <= 0) return hipSuccess;
-  if (sa.max_seq <= kNT * 8) return launch_tpt<8>(sa, aa, la, append, rows, s);
-  if (sa.max_seq <= kNT * 20) return launch_tpt<20>(sa, aa, la, append, rows, s);
-  return launch_tpt<kDecodeFusedTPT>(sa, aa, la, append, rows, s);
+  if (sa.max_seq <= kNT * 8) return launch_tpt<8>(sa, aa, la, append, rows, s, ev);
+  if (sa.max_seq <= kNT * 20) return launch_tpt<20>(sa, aa, la, append, rows, s, ev);
+  return launch_tpt<kDecodeFusedTPT>(sa, aa, la, append, rows, s, ev);
 }
 
 }  // namespace ds

@@ -7,6 +7,7 @@
 //   [GQA]   grouped-query attention article, trdm.cn news 80600, section 4.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -107,15 +108,33 @@ struct AttnArgs {
   float* part;
 };
 
+// Optional timing events recorded by a launch itself, at the kernel's start
+// and end (both or neither).
+struct KEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <typename F, typename... Args>
+inline hipError_t launch_k(F kernel, dim3 grid, dim3 block, hipStream_t s, const KEvents& ev,
+                           Args... args) {
+  if (ev.start && ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  return hipGetLastError();
+}
+
 // Launchers (return the launch status of the last kernel they enqueue).
 hipError_t launch_label(const LabelArgs& a, int n_blocks, hipStream_t s);
 hipError_t launch_score_chunks(const ScoreArgs& a, int rows, hipStream_t s);
 hipError_t launch_select_stream(const ScoreArgs& a, int rows, hipStream_t s);
-hipError_t launch_attn(const AttnArgs& a, int rows, int G, bool final_out, hipStream_t s);
-hipError_t launch_attn_gqa(const AttnArgs& a, int rows, int G, bool final_out, hipStream_t s);
+hipError_t launch_attn(const AttnArgs& a, int rows, int G, bool final_out, hipStream_t s,
+                       const KEvents& ev = KEvents());
+hipError_t launch_attn_gqa(const AttnArgs& a, int rows, int G, bool final_out, hipStream_t s,
+                           const KEvents& ev = KEvents());
 hipError_t launch_combine(const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_decode_fused(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la,
-                               int append, int rows, hipStream_t s);
+                               int append, int rows, hipStream_t s, const KEvents& ev = KEvents());
 bool decode_fused_fits(int max_seq, int k, int r, int is_int4);
 hipError_t launch_score_local(const ScoreArgs& sa, const LabelArgs& la, int append, int rows,
                               hipStream_t s);
