@@ -117,6 +117,7 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
   if (!sparse) {
     if (do_append && tid < 64) append_label<R, INT4>(la, row, t_new, f, r, false);
   } else {
+    sel_clear<kNT>(f.sel);  // published by the barrier after the scores
     if (do_append && tid < 64) append_label<R, INT4>(la, row, t_new, f, r, true);
     typename Vec::Q q;
     q.load(f.q);
@@ -167,8 +168,24 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
         for (int e = 0; e < VT; ++e) sc[j * VT + e] = s[e];
       }
     }
+    // Row min and max: wave partials, one barrier (which also publishes the
+    // appended token's score and the cleared select scratch).
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      mn = fminf(mn, __shfl_xor(mn, o, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    }
+    if (lane == 0) {
+      f.mm_tmp[w] = mn;
+      f.mm_tmp[kWaves + w] = mx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      mn = fminf(mn, f.mm_tmp[i]);
+      mx = fmaxf(mx, f.mm_tmp[kWaves + i]);
+    }
     if (do_append) {
-      __syncthreads();
       const float sn = f.snew;
       if ((v_last & (kNT - 1)) == tid) {
         const int jl = v_last / kNT;
@@ -181,13 +198,12 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
       mn = fminf(mn, sn);
       mx = fmaxf(mx, sn);
     }
-    block_minmax<kNT>(mn, mx, f.mm_tmp);
 
     // --- exact select and ordered emission into the LDS token list ---------
     auto token = [&](int j, int e) { return (j * kNT + tid) * VT + e; };
     auto valid = [&](int j, int) { return j < jn; };  // empty slots hold -inf
-    const RegSel rs =
-        reg_select<kNT, VT, JMAX>(sc, valid, token, (uint32_t)sa.k, mn, mx, f.sel, f.scan_tmp);
+    const RegSel rs = reg_select<kNT, VT, JMAX, true>(sc, valid, token, (uint32_t)sa.k, mn, mx,
+                                                      f.sel, f.scan_tmp);
     reg_emit<kNT, VT, JMAX>(sc, valid, rs, f.tot,
                             [&](uint32_t pos, int j, int e) { f.lidx[pos] = token(j, e); });
     __syncthreads();

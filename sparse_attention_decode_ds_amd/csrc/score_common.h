@@ -362,16 +362,22 @@ __device__ __forceinline__ void block_minmax(float& mn, float& mx, float* tmp) {
 
 // Bin (of 2048, descending order) holding the need-th largest key: writes
 // sel[0] = bin, sel[1] = keys in higher bins, sel[2] = keys in that bin.
+// Two barriers: wave totals of the per-thread bin sums, then the result.
 template <int NT>
 __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t need, uint32_t* sel,
                                            uint32_t* scan_tmp) {
   constexpr int BPT = kHistBins / NT;
   const int hi = kHistBins - 1 - (int)threadIdx.x * BPT;
+  const int w = threadIdx.x >> 6;
   uint32_t local = 0;
 #pragma unroll
   for (int i = 0; i < BPT; ++i) local += hist[hi - i];
-  uint32_t total;
-  const uint32_t excl = block_excl_scan<NT>(local, scan_tmp, &total);
+  const uint32_t incl = wave_incl_scan(local);
+  if ((threadIdx.x & 63) == 63) scan_tmp[w] = incl;
+  __syncthreads();
+  uint32_t excl = incl - local;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) excl += i < w ? scan_tmp[i] : 0u;
   if (excl < need && need <= excl + local) {
     uint32_t acc = excl;
 #pragma unroll
@@ -586,16 +592,25 @@ struct NoBstarHook {
 
 // on_bstar(bstar, bin) runs on every thread once the boundary bin is known:
 // every valid item with bin(score) > bstar is among the k largest.
-template <int NT, int VT, int JMAX, typename Valid, typename Order,
+// Clears the histogram and the scalars of reg_select; a caller that runs
+// it before one of its own barriers passes CLEARED = true to reg_select.
+template <int NT>
+__device__ __forceinline__ void sel_clear(SelScratch& ss) {
+  for (int i = threadIdx.x; i < kHistBins; i += NT) ss.hist[i] = 0u;
+  if (threadIdx.x < 8) ss.misc[threadIdx.x] = threadIdx.x == 3 ? 0xFFFFFFFFu : 0u;
+}
+
+template <int NT, int VT, int JMAX, bool CLEARED = false, typename Valid, typename Order,
           typename OnBstar = NoBstarHook>
 __device__ RegSel reg_select(const float* sc, Valid valid, Order order, uint32_t k, float mn,
                              float mx, SelScratch& ss, uint32_t* scan_tmp,
                              OnBstar on_bstar = OnBstar()) {
   const int tid = threadIdx.x;
   const LinBins bin(mn, mx);
-  for (int i = tid; i < kHistBins; i += NT) ss.hist[i] = 0u;
-  if (tid < 8) ss.misc[tid] = tid == 3 ? 0xFFFFFFFFu : 0u;
-  __syncthreads();
+  if (!CLEARED) {
+    sel_clear<NT>(ss);
+    __syncthreads();
+  }
   // (empty slots are left out of the histogram: they would all hit bin 0)
 #pragma unroll
   for (int j = 0; j < JMAX; ++j)
