@@ -78,26 +78,55 @@ __device__ __forceinline__ void acc_init(AttnAcc<G>& acc) {
   }
 }
 
-// Accumulate tokens tok(i), i in [0, n), slot `slot` taking i = slot, slot+16, ...
+// Token loads of one slot in flight: two groups of kUnroll tokens (list
+// positions base + 16 u), consumed alternately.
+struct AttnLoads {
+  uint4 ka[kUnroll], va[kUnroll], kb[kUnroll], vb[kUnroll];
+};
+
+// Loads of the tokens tok(i), i = base + 16 u in [lo, hi), into kk/vv; with
+// `fill` the other entries are left as they are, else they are zeroed.
 // Kr, Vr point at channel 8c of the row's token 0.
-template <int G, typename TokFn>
-__device__ __forceinline__ void attend(const AttnArgs& a, const __half* Kr, const __half* Vr,
-                                       bool kl, int slot, int n, TokFn tok,
-                                       const float (&qf)[G][8], AttnAcc<G>& acc) {
-  constexpr int kStep = kSlots * kUnroll;
-  auto issue = [&](int base, uint4* kk, uint4* vv) {
+template <typename TokFn>
+__device__ __forceinline__ void attn_issue(const AttnArgs& a, const __half* Kr, const __half* Vr,
+                                           bool kl, int base, int lo, int hi, TokFn tok, uint4* kk,
+                                           uint4* vv, bool fill) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+  for (int u = 0; u < kUnroll; ++u) {
+    const int i = base + u * kSlots;
+    if (!fill) {
       kk[u] = make_uint4(0, 0, 0, 0);
       vv[u] = make_uint4(0, 0, 0, 0);
-      const int i = base + u * kSlots;
-      if (i < n) {
-        const int64_t t = tok(i);
-        if (kl) kk[u] = ld_stream(Kr + t * a.ks2);
-        vv[u] = ld_stream(Vr + t * a.vs2);
-      }
     }
-  };
+    if (i >= lo && i < hi) {
+      const int64_t t = tok(i);
+      if (kl) kk[u] = ld_stream(Kr + t * a.ks2);
+      vv[u] = ld_stream(Vr + t * a.vs2);
+    }
+  }
+}
+
+// The first two groups of slot `slot` restricted to list positions [lo, hi):
+// prime (fill = false) zeroes what it does not load; a later call with
+// fill = true loads the positions that were not ready yet.
+template <typename TokFn>
+__device__ __forceinline__ void attend_prime(const AttnArgs& a, const __half* Kr, const __half* Vr,
+                                             bool kl, int slot, int lo, int hi, TokFn tok,
+                                             AttnLoads& L, bool fill) {
+  constexpr int kStep = kSlots * kUnroll;
+  attn_issue(a, Kr, Vr, kl, slot, lo, hi, tok, L.ka, L.va, fill);
+  attn_issue(a, Kr, Vr, kl, slot + kStep, lo, hi, tok, L.kb, L.vb, fill);
+}
+
+// Accumulate tokens tok(i), i in [0, n), slot `slot` taking i = slot, slot+16, ...,
+// with the first two groups already in L (attend_prime); each group is
+// reloaded with the group after next as soon as it is consumed.
+template <int G, typename TokFn>
+__device__ __forceinline__ void attend_run(const AttnArgs& a, const __half* Kr, const __half* Vr,
+                                           bool kl, int slot, int n, TokFn tok,
+                                           const float (&qf)[G][8], AttnAcc<G>& acc,
+                                           AttnLoads& L) {
+  constexpr int kStep = kSlots * kUnroll;
   auto consume = [&](int base, const uint4* kk, const uint4* vv) {
     float s[kUnroll][G];
 #pragma unroll
@@ -142,15 +171,22 @@ __device__ __forceinline__ void attend(const AttnArgs& a, const __half* Kr, cons
       acc.m[h] = mx;
     }
   };
-  uint4 ka[kUnroll], va[kUnroll], kb[kUnroll], vb[kUnroll];
-  issue(slot, ka, va);
   for (int base = slot; base < n; base += 2 * kStep) {
-    issue(base + kStep, kb, vb);
-    consume(base, ka, va);
+    consume(base, L.ka, L.va);
+    if (base + 2 * kStep < n) attn_issue(a, Kr, Vr, kl, base + 2 * kStep, 0, n, tok, L.ka, L.va, false);
     if (base + kStep >= n) break;
-    issue(base + 2 * kStep, ka, va);
-    consume(base + kStep, kb, vb);
+    consume(base + kStep, L.kb, L.vb);
+    if (base + 3 * kStep < n) attn_issue(a, Kr, Vr, kl, base + 3 * kStep, 0, n, tok, L.kb, L.vb, false);
   }
+}
+
+template <int G, typename TokFn>
+__device__ __forceinline__ void attend(const AttnArgs& a, const __half* Kr, const __half* Vr,
+                                       bool kl, int slot, int n, TokFn tok,
+                                       const float (&qf)[G][8], AttnAcc<G>& acc) {
+  AttnLoads L;
+  attend_prime(a, Kr, Vr, kl, slot, 0, n, tok, L, false);
+  attend_run<G>(a, Kr, Vr, kl, slot, n, tok, qf, acc, L);
 }
 
 template <int G, bool FINAL>
@@ -164,7 +200,7 @@ __device__ __forceinline__ void attn_finish(const AttnArgs& a, AttnAcc<G>& acc, 
                                             int b, int g, int split) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = wave_id();
   const int c = lane & 15;
 #pragma unroll
   for (int off = 16; off <= 32; off <<= 1) {

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a) {
   const int n_here = max(0, min(n_tok - t0, a.tps));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = wave_id();
   const int m16 = lane & 15;  // token of the K operand; head of the query operand and scores
   const int kg = lane >> 4;   // channel group [32 kg, 32 kg + 32)
 

@@ -11,13 +11,15 @@
 //   score    the label stream is scored into registers: thread tid holds the
 //            vectors v = j * 256 + tid, so token order is (round j, wave,
 //            lane, element);
-//   select   exact top-k on the register-resident scores (reg_select:
-//            linear-bin histogram, then exact resolution of the boundary bin
-//            by rank count or radix passes);
-//   emit     ordered compaction into an ascending token list in LDS
-//            (reg_emit: wave scans per round plus one exchange of wave
-//            totals);
+//   select   exact top-k on the register-resident scores into an LDS token
+//            list (list_select_a/b: linear-bin histogram, the tokens of the
+//            bins above the boundary bin listed first, then the boundary bin
+//            resolved by rank count or radix passes);
 //   attend   exact attention over the list (attn_common.h), fp16 output.
+//            The first K/V loads of every slot go out as soon as the first
+//            part of the list is written, while the boundary is resolved.
+//            When the caller asks for the selected set, it is written in
+//            ascending order by an ordered compaction (reg_emit).
 //
 // Used when the row fits the register budget (S <= 256 * TPT tokens, TPT
 // scores per thread), k is small enough for the LDS list and the query group
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
   const int S = row_len(sa, b);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = wave_id();
   const int c = lane & 15;
   const int slot = w * 4 + (lane >> 4);
   const bool kl = c < (aa.d_k >> 3);
@@ -97,11 +99,16 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
   const int n_vec = sparse ? (S + VT - 1) / VT : 0;
   const int v_last = n_vec - 1;  // the only vector that may be partial; it holds t_new
   const int jn = (n_vec + kNT - 1) / kNT;  // rounds holding any vector (uniform)
+  // The first label loads go out before the row's length arrives (one
+  // dependent load less ahead of the label stream): every slot below the
+  // batch bound max_seq (<= slots, a multiple of 16) is fetched.
+  const int n_vec_ld =
+      sa.k > 0 && sa.max_seq > sa.k ? (min(sa.max_seq, sa.slots) + VT - 1) / VT : 0;
   Vec vec[UNR];
 #pragma unroll
   for (int u = 0; u < UNR; ++u) {
     const int v = u * kNT + tid;
-    if (v < n_vec) vec[u].load(p, v);
+    if (v < n_vec_ld) vec[u].load(p, v);
   }
   __syncthreads();
   {
@@ -114,11 +121,25 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
   }
   __syncthreads();
 
+  // The append runs on the last wave: the first one holds the row's tail
+  // vectors (round JMAX - 1 when S is just above a multiple of 256 VT).
+  constexpr int kAppendWave = kWaves - 1;
+  // Attention: lane c of slot `slot` holds K/V channels [8c, 8c + 8); the
+  // query row at the stored K columns' channels, scaled for exp2.
+  const __half* Kr = aa.K + (int64_t)b * aa.ks0 + (int64_t)g * aa.ks1 + c * 8;
+  const __half* Vr = aa.V + (int64_t)b * aa.vs0 + (int64_t)g * aa.vs1 + c * 8;
+  auto tok = [&](int i) { return sparse ? (int64_t)f.lidx[i] : (int64_t)i; };
+  AttnLoads L;
   if (!sparse) {
-    if (do_append && tid < 64) append_label<R, INT4>(la, row, t_new, f, r, false);
+    if (do_append && w == kAppendWave) append_label<R, INT4>(la, row, t_new, f, r, false);
+    if (sa.pad_idx) {
+      int32_t* out = sa.idx + (int64_t)row * sa.idx_stride;
+      for (int i = tid; i < sa.idx_stride; i += kNT) out[i] = i < S ? i : -1;
+    }
+    attend_prime(aa, Kr, Vr, kl, slot, 0, S, tok, L, false);
   } else {
     sel_clear<kNT>(f.sel);  // published by the barrier after the scores
-    if (do_append && tid < 64) append_label<R, INT4>(la, row, t_new, f, r, true);
+    if (do_append && w == kAppendWave) append_label<R, INT4>(la, row, t_new, f, r, true);
     typename Vec::Q q;
     q.load(f.q);
     // --- score into registers ----------------------------------------------
@@ -199,22 +220,30 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
       mx = fmaxf(mx, sn);
     }
 
-    // --- exact select and ordered emission into the LDS token list ---------
+    // --- exact select into the LDS token list --------------------------------
+    // Tokens of the bins above the boundary bin are listed first; their K/V
+    // loads go out while the boundary bin is resolved.
     auto token = [&](int j, int e) { return (j * kNT + tid) * VT + e; };
     auto valid = [&](int j, int) { return j < jn; };  // empty slots hold -inf
-    const RegSel rs = reg_select<kNT, VT, JMAX, true>(sc, valid, token, (uint32_t)sa.k, mn, mx,
-                                                      f.sel, f.scan_tmp);
-    reg_emit<kNT, VT, JMAX>(sc, valid, rs, f.tot,
-                            [&](uint32_t pos, int j, int e) { f.lidx[pos] = token(j, e); });
-    __syncthreads();
+    const LinBins bin(mn, mx);
+    const ListSel ls = list_select_a<kNT, VT, JMAX>(sc, valid, token, (uint32_t)sa.k, bin, f.sel,
+                                                    f.scan_tmp, f.lidx);
+    // first group of every slot, as far as the list is known (unless the
+    // boundary bin needs radix passes, which want the registers)
+    const bool early = ls.cnt <= (uint32_t)kRankMax;
+    if (early) attn_issue(aa, Kr, Vr, kl, slot, 0, (int)ls.n_a, tok, L.ka, L.va, false);
+    const RegSel rs = list_select_b<kNT, VT, JMAX>(sc, valid, token, bin, ls, f.sel, f.scan_tmp,
+                                                   f.tot, f.lidx);
+    attn_issue(aa, Kr, Vr, kl, slot, early ? (int)ls.n_a : 0, sa.k, tok, L.ka, L.va, early);
+    if (sa.pad_idx) {  // caller asked for the selected set, ascending
+      int32_t* out = sa.idx + (int64_t)row * sa.idx_stride;
+      reg_emit<kNT, VT, JMAX>(sc, valid, rs, f.tot,
+                              [&](uint32_t pos, int j, int e) { out[pos] = token(j, e); });
+      for (int i = sa.k + tid; i < sa.idx_stride; i += kNT) out[i] = -1;
+    }
+    attn_issue(aa, Kr, Vr, kl, slot + kSlots * kUnroll, 0, sa.k, tok, L.kb, L.vb, false);
   }
   const int n_sel = sparse ? sa.k : S;
-
-  if (sa.pad_idx) {  // caller asked for the selected set
-    int32_t* out = sa.idx + (int64_t)row * sa.idx_stride;
-    for (int i = tid; i < sa.idx_stride; i += kNT)
-      out[i] = i < n_sel ? (sparse ? f.lidx[i] : i) : -1;
-  }
 
   // --- attention ---------------------------------------------------------------
   float qf[1][8];
@@ -225,12 +254,7 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
   }
   AttnAcc<1> acc;
   acc_init<1>(acc);
-  const __half* Kr = aa.K + (int64_t)b * aa.ks0 + (int64_t)g * aa.ks1 + c * 8;
-  const __half* Vr = aa.V + (int64_t)b * aa.vs0 + (int64_t)g * aa.vs1 + c * 8;
-  if (sparse)
-    attend<1>(aa, Kr, Vr, kl, slot, n_sel, [&](int i) { return (int64_t)f.lidx[i]; }, qf, acc);
-  else
-    attend<1>(aa, Kr, Vr, kl, slot, n_sel, [&](int i) { return (int64_t)i; }, qf, acc);
+  attend_run<1>(aa, Kr, Vr, kl, slot, n_sel, tok, qf, acc, L);
   attn_finish<1, true>(aa, acc, f.red, b, g, 0);
 }
 

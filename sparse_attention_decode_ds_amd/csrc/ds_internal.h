@@ -175,6 +175,11 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave (DPP: shifts within rows
 // of 16, then row broadcasts).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
@@ -192,7 +197,7 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
 template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = wave_id();
   const uint32_t x = wave_incl_scan(v);
   if (lane == 63) tmp[w] = x;
   __syncthreads();

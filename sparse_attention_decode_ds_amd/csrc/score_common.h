@@ -346,7 +346,7 @@ __device__ __forceinline__ void block_minmax(float& mn, float& mx, float* tmp) {
     mn = fminf(mn, __shfl_xor(mn, o, 64));
     mx = fmaxf(mx, __shfl_xor(mx, o, 64));
   }
-  const int w = threadIdx.x >> 6;
+  const int w = wave_id();
   if ((threadIdx.x & 63) == 0) {
     tmp[w] = mn;
     tmp[NT / 64 + w] = mx;
@@ -368,7 +368,7 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t need, 
                                            uint32_t* scan_tmp) {
   constexpr int BPT = kHistBins / NT;
   const int hi = kHistBins - 1 - (int)threadIdx.x * BPT;
-  const int w = threadIdx.x >> 6;
+  const int w = wave_id();
   uint32_t local = 0;
 #pragma unroll
   for (int i = 0; i < BPT; ++i) local += hist[hi - i];
@@ -424,7 +424,7 @@ struct SelScratch {
   uint32_t hist[kHistBins];
   uint32_t cand_key[kRankMax];
   int32_t cand_idx[kRankMax];
-  uint32_t misc[8];
+  uint32_t misc[12];
 };
 
 // Exact selection of the k largest of n keys (k < n) in LDS, ties to the
@@ -597,7 +597,47 @@ struct NoBstarHook {
 template <int NT>
 __device__ __forceinline__ void sel_clear(SelScratch& ss) {
   for (int i = threadIdx.x; i < kHistBins; i += NT) ss.hist[i] = 0u;
-  if (threadIdx.x < 8) ss.misc[threadIdx.x] = threadIdx.x == 3 ? 0xFFFFFFFFu : 0u;
+  if (threadIdx.x < 12) ss.misc[threadIdx.x] = threadIdx.x == 3 ? 0xFFFFFFFFu : 0u;
+}
+
+// Radix passes over the key bits of the items in linear bin bstar (clustered
+// or equal scores: too many for the rank count).  On entry r = (smallest key
+// of the bin, largest key of the bin, items still to take from the bin); on
+// return items of the bin with key > e_hi are taken and `need` of those with
+// key in [e_lo, e_hi] (lowest position first).
+template <int NT, int VT, int JMAX, typename Valid>
+__device__ void radix_in_bin(const float* sc, Valid valid, const LinBins& bin, uint32_t bstar,
+                             RegSel& r, SelScratch& ss, uint32_t* scan_tmp) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0u, pmask = 0u;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
+    __syncthreads();
+    for (int i = tid; i < kHistBins; i += NT) ss.hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < JMAX; ++j)
+#pragma unroll
+      for (int e = 0; e < VT; ++e) {
+        if (!valid(j, e)) continue;
+        const float sv = sc[j * VT + e];
+        const uint32_t key = score_key(sv);
+        if ((key & pmask) == prefix && bin(sv) == bstar)
+          atomicAdd(&ss.hist[(key >> shift) & dmask], 1u);
+      }
+    __syncthreads();
+    find_digit<NT>(ss.hist, r.need, ss.misc + 4, scan_tmp);
+    const uint32_t d = ss.misc[4], ab = ss.misc[5], c2 = ss.misc[6];
+    prefix |= d << shift;
+    pmask |= dmask << shift;
+    r.need -= ab;
+    if (c2 == r.need) break;
+  }
+  __syncthreads();
+  r.e_lo = max(r.e_lo, prefix);
+  r.e_hi = min(r.e_hi, prefix | ~pmask);
 }
 
 template <int NT, int VT, int JMAX, bool CLEARED = false, typename Valid, typename Order,
@@ -667,35 +707,7 @@ __device__ RegSel reg_select(const float* sc, Valid valid, Order order, uint32_t
   }
   // Many keys in the boundary bin (clustered or equal scores): radix passes
   // over the key bits inside it.
-  uint32_t prefix = 0u, pmask = 0u;
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
-    __syncthreads();
-    for (int i = tid; i < kHistBins; i += NT) ss.hist[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < JMAX; ++j)
-#pragma unroll
-      for (int e = 0; e < VT; ++e) {
-        if (!valid(j, e)) continue;
-        const float sv = sc[j * VT + e];
-        const uint32_t key = score_key(sv);
-        if ((key & pmask) == prefix && bin(sv) == bstar)
-          atomicAdd(&ss.hist[(key >> shift) & dmask], 1u);
-      }
-    __syncthreads();
-    find_digit<NT>(ss.hist, r.need, ss.misc + 4, scan_tmp);
-    const uint32_t d = ss.misc[4], ab = ss.misc[5], c2 = ss.misc[6];
-    prefix |= d << shift;
-    pmask |= dmask << shift;
-    r.need -= ab;
-    if (c2 == r.need) break;
-  }
-  __syncthreads();
-  r.e_lo = max(r.e_lo, prefix);
-  r.e_hi = min(r.e_hi, prefix | ~pmask);
+  radix_in_bin<NT, VT, JMAX>(sc, valid, bin, bstar, r, ss, scan_tmp);
   return r;
 }
 
@@ -713,7 +725,7 @@ __device__ __forceinline__ void reg_emit(const float* sc, Valid valid, const Reg
                                          uint32_t* tot, Put put) {
   constexpr int W = NT / 64;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = wave_id();
   const float f_lo = key_float(r.e_lo == 0x7FFFFFFFu ? 0x80000000u : r.e_lo);
   const float f_hi = key_float(r.e_hi == 0x7FFFFFFFu ? 0x7FFFFFFEu : r.e_hi);
   uint32_t ex[JMAX];
@@ -785,6 +797,131 @@ __device__ __forceinline__ void reg_emit(const float* sc, Valid valid, const Reg
       eb += E;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Register-resident selection into an unordered token list (for attention,
+// which does not depend on the order of its tokens).  Same item layout,
+// valid/order conventions and result as reg_select; the list holds the
+// positions of the k largest.  Two halves, so that the caller can start
+// reading the first part of the list while the boundary is resolved.
+// ---------------------------------------------------------------------------
+struct ListSel {
+  uint32_t bstar;  // boundary linear bin
+  uint32_t n_a;    // items in higher bins: list[0 .. n_a), all taken
+  uint32_t need;   // items still to take from the boundary bin (>= 1)
+  uint32_t cnt;    // items in the boundary bin
+};
+
+// First half.  The histogram of the linear bins gives the boundary bin b*
+// (the scratch was cleared before one of the caller's barriers); every item
+// of a higher bin is written to list[0 .. n_a) ordered by (wave, lane, round,
+// element) (wave totals exchanged through LDS), and the items of b* are
+// collected as candidates (key, position; when there are at most kRankMax of
+// them) together with the smallest and largest key of the bin.  Ends with a barrier, after which
+// list[0 .. n_a) is complete; its order depends only on the items' places.
+template <int NT, int VT, int JMAX, typename Valid, typename Order>
+__device__ ListSel list_select_a(const float* sc, Valid valid, Order order, uint32_t k,
+                                 const LinBins& bin, SelScratch& ss, uint32_t* scan_tmp,
+                                 int32_t* list) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < JMAX; ++j)
+#pragma unroll
+    for (int e = 0; e < VT; ++e) {
+      const uint32_t bi = bin(sc[j * VT + e]);
+      if (valid(j, e) && bi != 0u) atomicAdd(&ss.hist[bi], 1u);
+    }
+  __syncthreads();
+  find_digit<NT>(ss.hist, k, ss.misc + 4, scan_tmp);
+  ListSel ls;
+  ls.bstar = ss.misc[4];
+  ls.n_a = ss.misc[5];
+  ls.cnt = ss.misc[6];
+  ls.need = k - ls.n_a;
+  const bool few = ls.cnt <= (uint32_t)kRankMax;
+  uint32_t mine = 0u;
+#pragma unroll
+  for (int j = 0; j < JMAX; ++j)
+#pragma unroll
+    for (int e = 0; e < VT; ++e) mine += valid(j, e) && bin(sc[j * VT + e]) > ls.bstar ? 1u : 0u;
+  // positions in (wave, lane, round, element) order: the list and hence
+  // the attention's summation order are the same on every run
+  const int w = wave_id();
+  const uint32_t incl = wave_incl_scan(mine);
+  if (lane == 63) scan_tmp[w] = incl;  // find_digit's reads of scan_tmp are behind its last barrier
+  __syncthreads();
+  uint32_t pos = incl - mine;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) pos += i < w ? scan_tmp[i] : 0u;
+#pragma unroll
+  for (int j = 0; j < JMAX; ++j)
+#pragma unroll
+    for (int e = 0; e < VT; ++e) {
+      if (!valid(j, e)) continue;
+      const float sv = sc[j * VT + e];
+      const uint32_t bi = bin(sv);
+      if (bi > ls.bstar) {
+        list[pos++] = order(j, e);
+      } else if (bi == ls.bstar) {
+        const uint32_t key = score_key(sv);
+        atomicMin(&ss.misc[3], key);
+        atomicMax(&ss.misc[7], key);
+        if (few) {
+          const uint32_t c = atomicAdd(&ss.misc[0], 1u);
+          ss.cand_key[c] = key;
+          ss.cand_idx[c] = order(j, e);
+        }
+      }
+    }
+  __syncthreads();
+  return ls;
+}
+
+// Second half: the `need` items taken from the boundary bin go to
+// list[n_a .. k).  With few candidates each one's rank (key descending, then
+// position ascending) is counted and the first `need` ranks are written;
+// otherwise radix passes inside the bin and an ordered emission of its taken
+// items.  Ends with a barrier (the list is complete) and returns the whole
+// selection characterised as by reg_select, for reg_emit.
+template <int NT, int VT, int JMAX, typename Valid, typename Order>
+__device__ RegSel list_select_b(const float* sc, Valid valid, Order order, const LinBins& bin,
+                                const ListSel& ls, SelScratch& ss, uint32_t* scan_tmp,
+                                uint32_t* tot, int32_t* list) {
+  const int tid = threadIdx.x;
+  RegSel r;
+  if (ls.cnt <= (uint32_t)kRankMax) {
+    for (int i = tid; i < (int)ls.cnt; i += NT) {
+      const uint32_t ki = ss.cand_key[i];
+      const int ti = ss.cand_idx[i];
+      uint32_t above = 0, tied = 0;
+      for (int m = 0; m < (int)ls.cnt; ++m) {
+        const uint32_t km = ss.cand_key[m];
+        above += km > ki;
+        tied += km == ki && ss.cand_idx[m] < ti;
+      }
+      const uint32_t rank = above + tied;
+      if (rank < ls.need) list[ls.n_a + rank] = ti;
+      if (rank == ls.need - 1) {  // the last item taken
+        ss.misc[2] = ki;
+        ss.misc[8] = above;
+      }
+    }
+    __syncthreads();
+    r.e_lo = r.e_hi = ss.misc[2];
+    r.need = ls.need - ss.misc[8];
+    return r;
+  }
+  r.e_lo = ss.misc[3];
+  r.e_hi = ss.misc[7];
+  r.need = ls.need;
+  if (ls.cnt != ls.need) radix_in_bin<NT, VT, JMAX>(sc, valid, bin, ls.bstar, r, ss, scan_tmp);
+  const uint32_t bstar = ls.bstar;
+  reg_emit<NT, VT, JMAX>(
+      sc, [&](int j, int e) { return valid(j, e) && bin(sc[j * VT + e]) == bstar; }, r, tot,
+      [&](uint32_t pos, int j, int e) { list[ls.n_a + pos] = order(j, e); });
+  __syncthreads();
+  return r;
 }
 
 __device__ __forceinline__ int row_len(const ScoreArgs& a, int b) {

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la, 
   const int CH = sa.chunk;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = wave_id();
   const int r = sa.r;
   const int t_beg = c * CH;
   const int t_end = min(S, t_beg + CH);
