@@ -173,10 +173,12 @@ __device__ __forceinline__ void attend_run(const AttnArgs& a, const __half* Kr, 
   };
   for (int base = slot; base < n; base += 2 * kStep) {
     consume(base, L.ka, L.va);
-    if (base + 2 * kStep < n) attn_issue(a, Kr, Vr, kl, base + 2 * kStep, 0, n, tok, L.ka, L.va, false);
+    if (base + 2 * kStep < n)
+      attn_issue(a, Kr, Vr, kl, base + 2 * kStep, 0, n, tok, L.ka, L.va, false);
     if (base + kStep >= n) break;
     consume(base + kStep, L.kb, L.vb);
-    if (base + 3 * kStep < n) attn_issue(a, Kr, Vr, kl, base + 3 * kStep, 0, n, tok, L.kb, L.vb, false);
+    if (base + 3 * kStep < n)
+      attn_issue(a, Kr, Vr, kl, base + 3 * kStep, 0, n, tok, L.kb, L.vb, false);
   }
 }
 

@@ -234,7 +234,12 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
     if (early) attn_issue(aa, Kr, Vr, kl, slot, 0, (int)ls.n_a, tok, L.ka, L.va, false);
     const RegSel rs = list_select_b<kNT, VT, JMAX>(sc, valid, token, bin, ls, f.sel, f.scan_tmp,
                                                    f.tot, f.lidx);
-    attn_issue(aa, Kr, Vr, kl, slot, early ? (int)ls.n_a : 0, sa.k, tok, L.ka, L.va, early);
+    // the rest of the first group (only when it reaches past n_a: filling
+    // registers with loads in flight waits for those loads)
+    if (!early)
+      attn_issue(aa, Kr, Vr, kl, slot, 0, sa.k, tok, L.ka, L.va, false);
+    else if ((int)ls.n_a < kSlots * kUnroll)
+      attn_issue(aa, Kr, Vr, kl, slot, (int)ls.n_a, sa.k, tok, L.ka, L.va, true);
     if (sa.pad_idx) {  // caller asked for the selected set, ascending
       int32_t* out = sa.idx + (int64_t)row * sa.idx_stride;
       reg_emit<kNT, VT, JMAX>(sc, valid, rs, f.tot,

@@ -606,8 +606,9 @@ __device__ __forceinline__ void sel_clear(SelScratch& ss) {
 // return items of the bin with key > e_hi are taken and `need` of those with
 // key in [e_lo, e_hi] (lowest position first).
 template <int NT, int VT, int JMAX, typename Valid>
-__device__ void radix_in_bin(const float* sc, Valid valid, const LinBins& bin, uint32_t bstar,
-                             RegSel& r, SelScratch& ss, uint32_t* scan_tmp) {
+__device__ __forceinline__ void radix_in_bin(const float* sc, Valid valid, const LinBins& bin,
+                                             uint32_t bstar, RegSel& r, SelScratch& ss,
+                                             uint32_t* scan_tmp) {
   const int tid = threadIdx.x;
   uint32_t prefix = 0u, pmask = 0u;
 #pragma unroll 1
@@ -642,9 +643,9 @@ __device__ void radix_in_bin(const float* sc, Valid valid, const LinBins& bin, u
 
 template <int NT, int VT, int JMAX, bool CLEARED = false, typename Valid, typename Order,
           typename OnBstar = NoBstarHook>
-__device__ RegSel reg_select(const float* sc, Valid valid, Order order, uint32_t k, float mn,
-                             float mx, SelScratch& ss, uint32_t* scan_tmp,
-                             OnBstar on_bstar = OnBstar()) {
+__device__ __forceinline__ RegSel reg_select(const float* sc, Valid valid, Order order, uint32_t k,
+                                             float mn, float mx, SelScratch& ss,
+                                             uint32_t* scan_tmp, OnBstar on_bstar = OnBstar()) {
   const int tid = threadIdx.x;
   const LinBins bin(mn, mx);
   if (!CLEARED) {
@@ -815,15 +816,14 @@ struct ListSel {
 
 // First half.  The histogram of the linear bins gives the boundary bin b*
 // (the scratch was cleared before one of the caller's barriers); every item
-// of a higher bin is written to list[0 .. n_a) ordered by (wave, lane, round,
-// element) (wave totals exchanged through LDS), and the items of b* are
-// collected as candidates (key, position; when there are at most kRankMax of
-// them) together with the smallest and largest key of the bin.  Ends with a barrier, after which
-// list[0 .. n_a) is complete; its order depends only on the items' places.
+// of a higher bin is written to list[0 .. n_a) and, when there are at most
+// kRankMax of them, the items of b* to the candidate arrays (key, position),
+// both ordered by (wave, lane, round, element) through one exchange of wave
+// totals.  Ends with a barrier, after which list[0 .. n_a) is complete.
 template <int NT, int VT, int JMAX, typename Valid, typename Order>
-__device__ ListSel list_select_a(const float* sc, Valid valid, Order order, uint32_t k,
-                                 const LinBins& bin, SelScratch& ss, uint32_t* scan_tmp,
-                                 int32_t* list) {
+__device__ __forceinline__ ListSel list_select_a(const float* sc, Valid valid, Order order,
+                                                 uint32_t k, const LinBins& bin, SelScratch& ss,
+                                                 uint32_t* scan_tmp, int32_t* list) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int j = 0; j < JMAX; ++j)
@@ -840,13 +840,17 @@ __device__ ListSel list_select_a(const float* sc, Valid valid, Order order, uint
   ls.cnt = ss.misc[6];
   ls.need = k - ls.n_a;
   const bool few = ls.cnt <= (uint32_t)kRankMax;
+  // per thread: items above b* (low half) and in b* (high half); positions
+  // in (wave, lane, round, element) order, so the list and hence the
+  // attention's summation order are the same on every run
   uint32_t mine = 0u;
 #pragma unroll
   for (int j = 0; j < JMAX; ++j)
 #pragma unroll
-    for (int e = 0; e < VT; ++e) mine += valid(j, e) && bin(sc[j * VT + e]) > ls.bstar ? 1u : 0u;
-  // positions in (wave, lane, round, element) order: the list and hence
-  // the attention's summation order are the same on every run
+    for (int e = 0; e < VT; ++e) {
+      const uint32_t bi = bin(sc[j * VT + e]);
+      if (valid(j, e)) mine += bi > ls.bstar ? 1u : (bi == ls.bstar ? 0x10000u : 0u);
+    }
   const int w = wave_id();
   const uint32_t incl = wave_incl_scan(mine);
   if (lane == 63) scan_tmp[w] = incl;  // find_digit's reads of scan_tmp are behind its last barrier
@@ -854,6 +858,7 @@ __device__ ListSel list_select_a(const float* sc, Valid valid, Order order, uint
   uint32_t pos = incl - mine;
 #pragma unroll
   for (int i = 0; i < NT / 64; ++i) pos += i < w ? scan_tmp[i] : 0u;
+  uint32_t pa = pos & 0xFFFFu, pb = pos >> 16;
 #pragma unroll
   for (int j = 0; j < JMAX; ++j)
 #pragma unroll
@@ -862,16 +867,13 @@ __device__ ListSel list_select_a(const float* sc, Valid valid, Order order, uint
       const float sv = sc[j * VT + e];
       const uint32_t bi = bin(sv);
       if (bi > ls.bstar) {
-        list[pos++] = order(j, e);
+        list[pa++] = order(j, e);
       } else if (bi == ls.bstar) {
-        const uint32_t key = score_key(sv);
-        atomicMin(&ss.misc[3], key);
-        atomicMax(&ss.misc[7], key);
         if (few) {
-          const uint32_t c = atomicAdd(&ss.misc[0], 1u);
-          ss.cand_key[c] = key;
-          ss.cand_idx[c] = order(j, e);
+          ss.cand_key[pb] = score_key(sv);
+          ss.cand_idx[pb] = order(j, e);
         }
+        ++pb;
       }
     }
   __syncthreads();
@@ -885,9 +887,10 @@ __device__ ListSel list_select_a(const float* sc, Valid valid, Order order, uint
 // items.  Ends with a barrier (the list is complete) and returns the whole
 // selection characterised as by reg_select, for reg_emit.
 template <int NT, int VT, int JMAX, typename Valid, typename Order>
-__device__ RegSel list_select_b(const float* sc, Valid valid, Order order, const LinBins& bin,
-                                const ListSel& ls, SelScratch& ss, uint32_t* scan_tmp,
-                                uint32_t* tot, int32_t* list) {
+__device__ __forceinline__ RegSel list_select_b(const float* sc, Valid valid, Order order,
+                                                const LinBins& bin, const ListSel& ls,
+                                                SelScratch& ss, uint32_t* scan_tmp, uint32_t* tot,
+                                                int32_t* list) {
   const int tid = threadIdx.x;
   RegSel r;
   if (ls.cnt <= (uint32_t)kRankMax) {
@@ -912,11 +915,32 @@ __device__ RegSel list_select_b(const float* sc, Valid valid, Order order, const
     r.need = ls.need - ss.misc[8];
     return r;
   }
+  // smallest and largest key of the boundary bin
+  const uint32_t bstar = ls.bstar;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < JMAX; ++j)
+#pragma unroll
+    for (int e = 0; e < VT; ++e)
+      if (valid(j, e) && bin(sc[j * VT + e]) == bstar) {
+        const uint32_t key = score_key(sc[j * VT + e]);
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
+      }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+  }
+  if ((tid & 63) == 0) {
+    atomicMin(&ss.misc[3], kmin);
+    atomicMax(&ss.misc[7], kmax);
+  }
+  __syncthreads();
   r.e_lo = ss.misc[3];
   r.e_hi = ss.misc[7];
   r.need = ls.need;
-  if (ls.cnt != ls.need) radix_in_bin<NT, VT, JMAX>(sc, valid, bin, ls.bstar, r, ss, scan_tmp);
-  const uint32_t bstar = ls.bstar;
+  if (ls.cnt != ls.need) radix_in_bin<NT, VT, JMAX>(sc, valid, bin, bstar, r, ss, scan_tmp);
   reg_emit<NT, VT, JMAX>(
       sc, [&](int j, int e) { return valid(j, e) && bin(sc[j * VT + e]) == bstar; }, r, tot,
       [&](uint32_t pos, int j, int e) { list[ls.n_a + pos] = order(j, e); });
