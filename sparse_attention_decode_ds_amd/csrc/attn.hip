@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   load_query<G>(a, b, g, c, kl, qf);
   AttnAcc<G> acc;
   acc_init<G>(acc);
-  const __half* Kr = a.K + (int64_t)b * a.ks0 + (int64_t)g * a.ks1 + c * 8;
+  const __half* Kr = a.K + (int64_t)b * a.ks0 + (int64_t)g * a.ks1 + min(c, (a.d_k >> 3) - 1) * 8;
   const __half* Vr = a.V + (int64_t)b * a.vs0 + (int64_t)g * a.vs1 + c * 8;
 
   if (a.sparse) {
@@ -41,10 +41,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
       const int32_t* src = a.idx + (int64_t)row * a.idx_stride + t0 + bat;
       for (int i = tid; i < nb; i += kAttnThreads) lidx[i] = src[i];
       __syncthreads();
-      attend<G>(a, Kr, Vr, kl, slot, nb, [&](int i) { return (int64_t)lidx[i]; }, qf, acc);
+      attend<G>(a, Kr, Vr, slot, nb, [&](int i) { return (int64_t)lidx[i]; }, qf, acc);
     }
   } else {
-    attend<G>(a, Kr, Vr, kl, slot, n_here, [&](int i) { return (int64_t)(t0 + i); }, qf, acc);
+    attend<G>(a, Kr, Vr, slot, n_here, [&](int i) { return (int64_t)(t0 + i); }, qf, acc);
   }
   attn_finish<G, FINAL>(a, acc, red, b, g, split);
 }

@@ -84,38 +84,33 @@ struct AttnLoads {
   uint4 ka[kUnroll], va[kUnroll], kb[kUnroll], vb[kUnroll];
 };
 
-// Loads of the tokens tok(i), i = base + 16 u in [lo, hi), into kk/vv; with
-// `fill` the other entries are left as they are, else they are zeroed.
-// Kr, Vr point at channel 8c of the row's token 0.
+// Loads of the tokens tok(i), i = base + 16 u, into kk/vv.  Positions at or
+// past hi load the list's first token tok(0) instead (the row's token 0 if
+// the list is still empty): every load is issued unconditionally, so no
+// register holding a load in flight is ever merged or cleared; the consumer
+// masks those positions out, and their values are finite wherever the
+// selected rows are.  Kr, Vr point at the lane's 16-byte piece of the row's
+// token 0 (lanes past the stored K width read a valid column; their query
+// weights are zero).
 template <typename TokFn>
 __device__ __forceinline__ void attn_issue(const AttnArgs& a, const __half* Kr, const __half* Vr,
-                                           bool kl, int base, int lo, int hi, TokFn tok, uint4* kk,
-                                           uint4* vv, bool fill) {
+                                           int base, int hi, TokFn tok, uint4* kk, uint4* vv) {
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int i = base + u * kSlots;
-    if (!fill) {
-      kk[u] = make_uint4(0, 0, 0, 0);
-      vv[u] = make_uint4(0, 0, 0, 0);
-    }
-    if (i >= lo && i < hi) {
-      const int64_t t = tok(i);
-      if (kl) kk[u] = ld_stream(Kr + t * a.ks2);
-      vv[u] = ld_stream(Vr + t * a.vs2);
-    }
+    const int64_t t = hi > 0 ? tok(i < hi ? i : 0) : 0;
+    kk[u] = ld_stream(Kr + t * a.ks2);
+    vv[u] = ld_stream(Vr + t * a.vs2);
   }
 }
 
-// The first two groups of slot `slot` restricted to list positions [lo, hi):
-// prime (fill = false) zeroes what it does not load; a later call with
-// fill = true loads the positions that were not ready yet.
+// The first two groups of slot `slot`, positions [0, n).
 template <typename TokFn>
 __device__ __forceinline__ void attend_prime(const AttnArgs& a, const __half* Kr, const __half* Vr,
-                                             bool kl, int slot, int lo, int hi, TokFn tok,
-                                             AttnLoads& L, bool fill) {
+                                             int slot, int n, TokFn tok, AttnLoads& L) {
   constexpr int kStep = kSlots * kUnroll;
-  attn_issue(a, Kr, Vr, kl, slot, lo, hi, tok, L.ka, L.va, fill);
-  attn_issue(a, Kr, Vr, kl, slot + kStep, lo, hi, tok, L.kb, L.vb, fill);
+  attn_issue(a, Kr, Vr, slot, n, tok, L.ka, L.va);
+  attn_issue(a, Kr, Vr, slot + kStep, n, tok, L.kb, L.vb);
 }
 
 // Accumulate tokens tok(i), i in [0, n), slot `slot` taking i = slot, slot+16, ...,
@@ -123,9 +118,8 @@ __device__ __forceinline__ void attend_prime(const AttnArgs& a, const __half* Kr
 // reloaded with the group after next as soon as it is consumed.
 template <int G, typename TokFn>
 __device__ __forceinline__ void attend_run(const AttnArgs& a, const __half* Kr, const __half* Vr,
-                                           bool kl, int slot, int n, TokFn tok,
-                                           const float (&qf)[G][8], AttnAcc<G>& acc,
-                                           AttnLoads& L) {
+                                           int slot, int n, TokFn tok, const float (&qf)[G][8],
+                                           AttnAcc<G>& acc, AttnLoads& L) {
   constexpr int kStep = kSlots * kUnroll;
   auto consume = [&](int base, const uint4* kk, const uint4* vv) {
     float s[kUnroll][G];
@@ -173,22 +167,21 @@ __device__ __forceinline__ void attend_run(const AttnArgs& a, const __half* Kr, 
   };
   for (int base = slot; base < n; base += 2 * kStep) {
     consume(base, L.ka, L.va);
-    if (base + 2 * kStep < n)
-      attn_issue(a, Kr, Vr, kl, base + 2 * kStep, 0, n, tok, L.ka, L.va, false);
+    if (base + 2 * kStep < n) attn_issue(a, Kr, Vr, base + 2 * kStep, n, tok, L.ka, L.va);
     if (base + kStep >= n) break;
     consume(base + kStep, L.kb, L.vb);
-    if (base + 3 * kStep < n)
-      attn_issue(a, Kr, Vr, kl, base + 3 * kStep, 0, n, tok, L.kb, L.vb, false);
+    if (base + 3 * kStep < n) attn_issue(a, Kr, Vr, base + 3 * kStep, n, tok, L.kb, L.vb);
   }
 }
 
 template <int G, typename TokFn>
 __device__ __forceinline__ void attend(const AttnArgs& a, const __half* Kr, const __half* Vr,
-                                       bool kl, int slot, int n, TokFn tok,
-                                       const float (&qf)[G][8], AttnAcc<G>& acc) {
+                                       int slot, int n, TokFn tok, const float (&qf)[G][8],
+                                       AttnAcc<G>& acc) {
+  if (n <= 0) return;
   AttnLoads L;
-  attend_prime(a, Kr, Vr, kl, slot, 0, n, tok, L, false);
-  attend_run<G>(a, Kr, Vr, kl, slot, n, tok, qf, acc, L);
+  attend_prime(a, Kr, Vr, slot, n, tok, L);
+  attend_run<G>(a, Kr, Vr, slot, n, tok, qf, acc, L);
 }
 
 template <int G, bool FINAL>

@@ -124,11 +124,16 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
   // The append runs on the last wave: the first one holds the row's tail
   // vectors (round JMAX - 1 when S is just above a multiple of 256 VT).
   constexpr int kAppendWave = kWaves - 1;
-  // Attention: lane c of slot `slot` holds K/V channels [8c, 8c + 8); the
-  // query row at the stored K columns' channels, scaled for exp2.
-  const __half* Kr = aa.K + (int64_t)b * aa.ks0 + (int64_t)g * aa.ks1 + c * 8;
+  // Attention: lane c of slot `slot` holds K/V channels [8c, 8c + 8).  List
+  // position i is token f.lidx[i] on the sparse path and token i on the
+  // dense one; both paths share the attention code below.
+  const __half* Kr =
+      aa.K + (int64_t)b * aa.ks0 + (int64_t)g * aa.ks1 + min(c, (aa.d_k >> 3) - 1) * 8;
   const __half* Vr = aa.V + (int64_t)b * aa.vs0 + (int64_t)g * aa.vs1 + c * 8;
   auto tok = [&](int i) { return sparse ? (int64_t)f.lidx[i] : (int64_t)i; };
+  auto token = [&](int j, int e) { return (j * kNT + tid) * VT + e; };
+  auto valid = [&](int j, int) { return j < jn; };  // empty slots hold -inf
+  const int n_att = sparse ? sa.k : S;  // tokens attended
   AttnLoads L;
   if (!sparse) {
     if (do_append && w == kAppendWave) append_label<R, INT4>(la, row, t_new, f, r, false);
@@ -136,7 +141,10 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
       int32_t* out = sa.idx + (int64_t)row * sa.idx_stride;
       for (int i = tid; i < sa.idx_stride; i += kNT) out[i] = i < S ? i : -1;
     }
-    attend_prime(aa, Kr, Vr, kl, slot, 0, S, tok, L, false);
+    // label loads issued ahead of the row length are not used here; let them
+    // land before the attention loads take their place
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    if (n_att > 0) attend_prime(aa, Kr, Vr, slot, n_att, tok, L);
   } else {
     sel_clear<kNT>(f.sel);  // published by the barrier after the scores
     if (do_append && w == kAppendWave) append_label<R, INT4>(la, row, t_new, f, r, true);
@@ -221,36 +229,34 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
     }
 
     // --- exact select into the LDS token list --------------------------------
-    // Tokens of the bins above the boundary bin are listed first; their K/V
-    // loads go out while the boundary bin is resolved.
-    auto token = [&](int j, int e) { return (j * kNT + tid) * VT + e; };
-    auto valid = [&](int j, int) { return j < jn; };  // empty slots hold -inf
     const LinBins bin(mn, mx);
     const ListSel ls = list_select_a<kNT, VT, JMAX>(sc, valid, token, (uint32_t)sa.k, bin, f.sel,
                                                     f.scan_tmp, f.lidx);
-    // first group of every slot, as far as the list is known (unless the
-    // boundary bin needs radix passes, which want the registers)
-    const bool early = ls.cnt <= (uint32_t)kRankMax;
-    if (early) attn_issue(aa, Kr, Vr, kl, slot, 0, (int)ls.n_a, tok, L.ka, L.va, false);
-    const RegSel rs = list_select_b<kNT, VT, JMAX>(sc, valid, token, bin, ls, f.sel, f.scan_tmp,
-                                                   f.tot, f.lidx);
-    // the rest of the first group (only when it reaches past n_a: filling
-    // registers with loads in flight waits for those loads)
-    if (!early)
-      attn_issue(aa, Kr, Vr, kl, slot, 0, sa.k, tok, L.ka, L.va, false);
-    else if ((int)ls.n_a < kSlots * kUnroll)
-      attn_issue(aa, Kr, Vr, kl, slot, (int)ls.n_a, sa.k, tok, L.ka, L.va, true);
-    if (sa.pad_idx) {  // caller asked for the selected set, ascending
-      int32_t* out = sa.idx + (int64_t)row * sa.idx_stride;
-      reg_emit<kNT, VT, JMAX>(sc, valid, rs, f.tot,
-                              [&](uint32_t pos, int j, int e) { out[pos] = token(j, e); });
-      for (int i = sa.k + tid; i < sa.idx_stride; i += kNT) out[i] = -1;
+    const int n_a = (int)ls.n_a;
+    if (!sa.pad_idx && ls.cnt <= (uint32_t)kRankMax) {
+      // Common case: the tokens of the bins above the boundary bin are
+      // listed; when they cover the first two groups of every slot, those
+      // loads go out while the few boundary candidates are ranked (the
+      // scores are no longer needed).
+      const bool early = n_a >= 2 * kSlots * kUnroll;
+      if (early) attend_prime(aa, Kr, Vr, slot, n_a, tok, L);
+      list_rank<kNT>(ls, f.sel, f.lidx);
+      if (!early) attend_prime(aa, Kr, Vr, slot, n_att, tok, L);
+    } else {
+      const RegSel rs = list_select_b<kNT, VT, JMAX>(sc, valid, token, bin, ls, f.sel,
+                                                     f.scan_tmp, f.tot, f.lidx);
+      if (sa.pad_idx) {  // caller asked for the selected set, ascending
+        int32_t* out = sa.idx + (int64_t)row * sa.idx_stride;
+        reg_emit<kNT, VT, JMAX>(sc, valid, rs, f.tot,
+                                [&](uint32_t pos, int j, int e) { out[pos] = token(j, e); });
+        for (int i = sa.k + tid; i < sa.idx_stride; i += kNT) out[i] = -1;
+      }
+      attend_prime(aa, Kr, Vr, slot, n_att, tok, L);
     }
-    attn_issue(aa, Kr, Vr, kl, slot + kSlots * kUnroll, 0, sa.k, tok, L.kb, L.vb, false);
   }
-  const int n_sel = sparse ? sa.k : S;
 
   // --- attention ---------------------------------------------------------------
+  // the query row at the stored K columns' channels, scaled for exp2
   float qf[1][8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -259,7 +265,7 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
   }
   AttnAcc<1> acc;
   acc_init<1>(acc);
-  attend_run<1>(aa, Kr, Vr, kl, slot, n_sel, tok, qf, acc, L);
+  attend_run<1>(aa, Kr, Vr, slot, n_att, tok, qf, acc, L);
   attn_finish<1, true>(aa, acc, f.red, b, g, 0);
 }
 

@@ -880,6 +880,35 @@ __device__ __forceinline__ ListSel list_select_a(const float* sc, Valid valid, O
   return ls;
 }
 
+// Second half with at most kRankMax candidates (collected by list_select_a):
+// each one's rank (key descending, then position ascending) is counted and
+// the first `need` ranks go to list[n_a .. k).  Ends with a barrier; returns
+// the whole selection characterised as by reg_select (for reg_emit).
+template <int NT>
+__device__ __forceinline__ RegSel list_rank(const ListSel& ls, SelScratch& ss, int32_t* list) {
+  for (int i = threadIdx.x; i < (int)ls.cnt; i += NT) {
+    const uint32_t ki = ss.cand_key[i];
+    const int ti = ss.cand_idx[i];
+    uint32_t above = 0, tied = 0;
+    for (int m = 0; m < (int)ls.cnt; ++m) {
+      const uint32_t km = ss.cand_key[m];
+      above += km > ki;
+      tied += km == ki && ss.cand_idx[m] < ti;
+    }
+    const uint32_t rank = above + tied;
+    if (rank < ls.need) list[ls.n_a + rank] = ti;
+    if (rank == ls.need - 1) {  // the last item taken
+      ss.misc[2] = ki;
+      ss.misc[8] = above;
+    }
+  }
+  __syncthreads();
+  RegSel r;
+  r.e_lo = r.e_hi = ss.misc[2];
+  r.need = ls.need - ss.misc[8];
+  return r;
+}
+
 // Second half: the `need` items taken from the boundary bin go to
 // list[n_a .. k).  With few candidates each one's rank (key descending, then
 // position ascending) is counted and the first `need` ranks are written;
@@ -893,28 +922,7 @@ __device__ __forceinline__ RegSel list_select_b(const float* sc, Valid valid, Or
                                                 int32_t* list) {
   const int tid = threadIdx.x;
   RegSel r;
-  if (ls.cnt <= (uint32_t)kRankMax) {
-    for (int i = tid; i < (int)ls.cnt; i += NT) {
-      const uint32_t ki = ss.cand_key[i];
-      const int ti = ss.cand_idx[i];
-      uint32_t above = 0, tied = 0;
-      for (int m = 0; m < (int)ls.cnt; ++m) {
-        const uint32_t km = ss.cand_key[m];
-        above += km > ki;
-        tied += km == ki && ss.cand_idx[m] < ti;
-      }
-      const uint32_t rank = above + tied;
-      if (rank < ls.need) list[ls.n_a + rank] = ti;
-      if (rank == ls.need - 1) {  // the last item taken
-        ss.misc[2] = ki;
-        ss.misc[8] = above;
-      }
-    }
-    __syncthreads();
-    r.e_lo = r.e_hi = ss.misc[2];
-    r.need = ls.need - ss.misc[8];
-    return r;
-  }
+  if (ls.cnt <= (uint32_t)kRankMax) return list_rank<NT>(ls, ss, list);
   // smallest and largest key of the boundary bin
   const uint32_t bstar = ls.bstar;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
