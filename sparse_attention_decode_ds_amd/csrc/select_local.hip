@@ -64,7 +64,9 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la, 
   using Vec = typename VecSel<R, INT4>::type;
   constexpr int VT = Vec::VT;
   constexpr int JMAX = TPT / VT;
-  constexpr int UNR = 4;
+  // label vectors in flight per thread: all of them when they fit in about
+  // 40 registers (one round trip for the whole chunk), else 4 at a time
+  constexpr int UNR = JMAX * (int)sizeof(Vec) <= 160 ? JMAX : 4;
   constexpr float kEmpty = -__builtin_huge_valf();
   __shared__ LocalScratch<NT, TPT> f;
 

@@ -35,10 +35,10 @@ def prefill(cfg, inp, upto):
     return labels
 
 
-def run(cfg, inp, labels, seq_lens, max_seq, k=None, **kw):
+def run(cfg, inp, labels, seq_lens, max_seq, k=None, want_idx=True, **kw):
     k = cfg.k if k is None else k
     topk = None
-    if k > 0:
+    if k > 0 and want_idx:
         topk = torch.full((cfg.B, cfg.Hkv, k), -7, dtype=torch.int32, device="cuda")
     out = ds.decode_attn(inp.q, inp.K, inp.V, seq_lens, max_seq, k, cfg.sm_scale, chan=inp.chan,
                          labels=labels if k > 0 else None, keep=inp.keep, topk_idx=topk, **kw)
@@ -117,6 +117,20 @@ SMALL = {
     "leank48_ds": dict(B=2, Hq=8, Hkv=2, S0=400, r=8, k=50, int4=True, d_k=48),
     "g8_dense": dict(B=1, Hq=16, Hkv=2, S0=300, r=0, k=0, int4=False),
 }
+
+
+def check_without_idx(cfg, inp, labels, seq, max_seq, out_idx, rows, **kw):
+    """The same decode without the selected-set output (the path that does
+    not order the set): every row's output matches the run that returned
+    the set, and the sampled rows match the oracle."""
+    out, _ = run(cfg, inp, labels, seq, max_seq, want_idx=False, **kw)
+    a = out.float()
+    b = out_idx.float()
+    den = b.abs().amax(dim=-1, keepdim=True).clamp_min(1e-30)
+    diff = ((a - b).abs() / den).max().item()
+    assert diff <= 1e-3, ("output without the set output", diff)
+    ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k, out,
+                        None, rows)
 
 
 def _small_inputs(name, **over):
@@ -233,6 +247,37 @@ def test_fused_row_lengths(S0, r, int4, k):
     out, topk = run(cfg, inp, labels, seq, S, flags=ds.DECODE_APPEND)
     ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k, out,
                         topk, ds_check.sample_rows(cfg, 100), label_upto=S)
+    check_without_idx(cfg, inp, labels, seq, S, out, ds_check.sample_rows(cfg, 4),
+                      flags=ds.DECODE_APPEND)
+
+
+@pytest.mark.parametrize("sign", [1, -1])
+def test_fused_outlier_scores(sign):
+    """Ten outlier tokens per row with scores far above (sign 1) or far below
+    (sign -1) the rest: the linear bins between the row's smallest and
+    largest score crowd the other tokens into a few bins, so the boundary
+    bin is resolved among many candidates."""
+    cfg, inp = _small_inputs("mha_int4_r8", B=2, S0=4096, r=8, int4=True, k=256)
+    _note("fused outlier scores, sign %d" % sign)
+    g = torch.Generator().manual_seed(7 + sign)
+    q = inp.q.float()
+    for b in range(cfg.B):
+        for h in range(cfg.Hkv):
+            ch = inp.chan[h].long()
+            sgn = torch.sign(q[b, h, ch]).to(torch.float16)
+            sgn[sgn == 0] = 1
+            rows = torch.randperm(cfg.S0, generator=g)[:10].to(inp.K.device)
+            inp.K[b, h, rows[:, None], ch[None, :]] = (60 * sign) * sgn
+    S = cfg.S0 + 1
+    seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
+    labels = prefill(cfg, inp, cfg.S0)
+    plan = ds.decode_plan(inp.K, inp.V, cfg.Hq, cfg.D, labels, cfg.k, S)
+    assert plan["path"] == "fused"
+    out, topk = run(cfg, inp, labels, seq, S, flags=ds.DECODE_APPEND)
+    ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k, out,
+                        topk, ds_check.sample_rows(cfg, 8), label_upto=S, strict_sets=True)
+    check_without_idx(cfg, inp, labels, seq, S, out, ds_check.sample_rows(cfg, 4),
+                      flags=ds.DECODE_APPEND)
 
 
 @pytest.mark.parametrize("mode", [0, 1])
@@ -366,6 +411,8 @@ def test_workload_full_size(name, n_rows):
     res = ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k,
                               out, topk, rows)
     _note("workload %s: %s" % (name, res))
+    if cfg.k > 0:
+        check_without_idx(cfg, inp, labels, seq, cfg.cap, out, rows[:2], flags=ds.DECODE_APPEND)
     del inp, labels, out, topk
     gc.collect()
     torch.cuda.empty_cache()
