@@ -197,18 +197,23 @@ __device__ __forceinline__ void attn_finish(const AttnArgs& a, AttnAcc<G>& acc, 
   const int lane = tid & 63;
   const int w = wave_id();
   const int c = lane & 15;
+  // slots 4w + s merge with slot 4w + (s ^ 1), then with 4w + (s ^ 2): the
+  // lanes 16 and 32 apart (both lanes of a pair compute the same state)
 #pragma unroll
   for (int off = 16; off <= 32; off <<= 1) {
+    auto xchg = [&](float x) { return off == 16 ? xchg16(x) : xchg32(x); };
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float m2 = __shfl_xor(acc.m[h], off, 64);
-      const float l2 = __shfl_xor(acc.l[h], off, 64);
+      const LanePair pm = xchg(acc.m[h]);
+      const LanePair pl = xchg(acc.l[h]);
       float w1, w2, mx;
-      merge_weights(acc.m[h], m2, w1, w2, mx);
-      acc.l[h] = acc.l[h] * w1 + l2 * w2;
+      merge_weights(pm.lo, pm.hi, w1, w2, mx);
+      acc.l[h] = pl.lo * w1 + pl.hi * w2;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        acc.o[h][i] = acc.o[h][i] * w1 + __shfl_xor(acc.o[h][i], off, 64) * w2;
+      for (int i = 0; i < 8; ++i) {
+        const LanePair po = xchg(acc.o[h][i]);
+        acc.o[h][i] = po.lo * w1 + po.hi * w2;
+      }
       acc.m[h] = mx;
     }
   }

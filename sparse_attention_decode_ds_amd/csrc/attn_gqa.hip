@@ -138,8 +138,10 @@ __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a) {
         sv[j] = i0 + 4 * kg + j < nb ? acc[j] * a.scale_log2 : kNegInf;
         tm = fmaxf(tm, sv[j]);
       }
-      tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
-      tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+      LanePair pr = xchg16(tm);  // over the four lane groups (tokens 4 kg + j)
+      tm = fmaxf(pr.lo, pr.hi);
+      pr = xchg32(tm);
+      tm = fmaxf(pr.lo, pr.hi);
       const float mnew = fmaxf(m_run, tm);  // finite: token i0 of the tile is real
       const float al = m_run == kNegInf ? 0.0f : exp2f(m_run - mnew);
       float ps = 0.0f;
@@ -149,8 +151,10 @@ __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a) {
         f.p[w][4 * kg + j][m16] = pj;
         ps += pj;
       }
-      ps += __shfl_xor(ps, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
+      pr = xchg16(ps);
+      ps = pr.lo + pr.hi;
+      pr = xchg32(ps);
+      ps = pr.lo + pr.hi;
       l_run = l_run * al + ps;
       m_run = mnew;
       if (kg == 0) f.alpha[w][m16] = al;

@@ -199,11 +199,8 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
     }
     // Row min and max: wave partials, one barrier (which also publishes the
     // appended token's score and the cleared select scratch).
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      mn = fminf(mn, __shfl_xor(mn, o, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
     if (lane == 0) {
       f.mm_tmp[w] = mn;
       f.mm_tmp[kWaves + w] = mx;

@@ -213,6 +213,50 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, u
   return before + x - v;
 }
 
+// Cross-row lane exchange without LDS (v_permlane16_swap / v_permlane32_swap):
+// for lanes l and l ^ 16 (resp. l ^ 32) both get the pair (value of the
+// lower lane, value of the upper lane), so a combination of the two is the
+// same, bit for bit, in both lanes.
+struct LanePair {
+  float lo, hi;
+};
+__device__ __forceinline__ LanePair xchg16(float x) {
+  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return {__uint_as_float(t[0]), __uint_as_float(t[1])};
+}
+__device__ __forceinline__ LanePair xchg32(float x) {
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return {__uint_as_float(t[0]), __uint_as_float(t[1])};
+}
+
+// Butterfly within each row of 16 lanes (swap neighbours, swap pairs,
+// mirror within 8, mirror within 16), then across rows: every lane gets
+// op over the whole wave.  op must be commutative and associative.
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float x, Op op) {
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false)));
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false)));
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false)));
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false)));
+  LanePair p = xchg16(x);
+  x = op(p.lo, p.hi);
+  p = xchg32(x);
+  return op(p.lo, p.hi);
+}
+__device__ __forceinline__ float wave_max(float x) {
+  return wave_reduce(x, [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ float wave_min(float x) {
+  return wave_reduce(x, [](float a, float b) { return fminf(a, b); });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  return __float_as_uint(wave_reduce(__uint_as_float(x), [](float a, float b) {
+    return __uint_as_float(min(__float_as_uint(a), __float_as_uint(b)));
+  }));
+}
+
 // Sum over the 16 lanes of a row (lanes 16i .. 16i+15) with DPP moves:
 // swap neighbours, swap pairs, mirror within 8, mirror within 16.
 __device__ __forceinline__ float row16_sum(float x) {

@@ -341,11 +341,8 @@ __device__ __forceinline__ void score_range(const ScoreArgs& a, const RowPtrs& p
 // Workgroup min and max (two barriers); tmp holds 2 * NT / 64 floats.
 template <int NT>
 __device__ __forceinline__ void block_minmax(float& mn, float& mx, float* tmp) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    mn = fminf(mn, __shfl_xor(mn, o, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
   const int w = wave_id();
   if ((threadIdx.x & 63) == 0) {
     tmp[w] = mn;

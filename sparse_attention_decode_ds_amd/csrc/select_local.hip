@@ -12,7 +12,9 @@
 //
 // k_select_merge: one workgroup per row gathers the candidates (chunk order,
 //   so ascending token order), selects the k largest exactly (linear bins +
-//   exact boundary resolution, score_common.h) and emits them in order.  The
+//   exact boundary resolution, score_common.h) and writes them to the token
+//   list, in ascending order only when the caller asked for the selected set
+//   (the attention pass does not depend on the order).  The
 //   result is exact when every chunk that dropped tokens has theta <= the
 //   smallest selected key (every dropped key is then strictly smaller).  If a
 //   chunk overflowed its slots or that check fails, the workgroup re-scores
@@ -263,8 +265,7 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la, 
     if (lane == 63) f.tot[j][w] = incl;
   }
   if (!keep_all) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) tmin = min(tmin, (uint32_t)__shfl_xor((int)tmin, o, 64));
+    tmin = wave_min_u32(tmin);
     if (lane == 0) atomicMin(&f.theta, tmin);
   }
   __syncthreads();
@@ -395,17 +396,28 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
           sc[j * VTM + e] = -__builtin_huge_valf();
         }
       }
+    sel_clear<kNTM>(f.sel);  // published by block_minmax's barriers
     block_minmax<kNTM>(mn, mx, f.mm_tmp);
     auto valid = [&](int j, int) { return j * kNTM * VTM < slots; };  // empty slots hold -inf
-    auto order = [&](int j, int e) { return (j * kNTM + tid) * VTM + e; };
-    const RegSel rs = reg_select<kNTM, VTM, kMergeJ>(sc, valid, order, (uint32_t)sa.k, mn, mx,
-                                                    f.sel, f.scan_tmp);
+    // slot order is token order, so ties go to the lower token either way
+    auto order = [&](int j, int e) { return tok[j * VTM + e]; };
+    // The selected tokens go straight to the output list, unordered (the
+    // attention pass does not depend on their order), unless the caller
+    // asked for the selected set, which is then written in ascending order.
+    const LinBins bin(mn, mx);
+    const ListSel ls = list_select_a<kNTM, VTM, kMergeJ>(sc, valid, order, (uint32_t)sa.k, bin,
+                                                         f.sel, f.scan_tmp, out);
+    const RegSel rs =
+        ls.cnt <= (uint32_t)kRankMax
+            ? list_rank<kNTM>(ls, f.sel, out)
+            : list_select_b<kNTM, VTM, kMergeJ>(sc, valid, order, bin, ls, f.sel, f.scan_tmp,
+                                                f.tot, out);
     // Complete iff every chunk that dropped tokens (theta != 0) has theta at
     // or below the smallest selected key; e_lo is at or below that key.
     if (tid < min(n_ch, kMaxLocalChunks) && f.ch_theta[tid] > rs.e_lo) atomicOr(&f.flag, 1u);
     __syncthreads();
     full = f.flag != 0u;
-    if (!full)
+    if (!full && sa.pad_idx)
       reg_emit<kNTM, VTM, kMergeJ>(sc, valid, rs, f.tot, [&](uint32_t pos, int j, int e) {
         out[pos] = tok[j * VTM + e];
       });
