@@ -79,6 +79,11 @@ __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a) {
   const int m16 = lane & 15;  // K token of the tile; head of the score and output columns
   const int kg = lane >> 4;   // K channels [32 kg, 32 kg + 32); V tokens 4 kg .. 4 kg + 3
 
+  // The first batch of the token list and the query rows are fetched
+  // together (one round trip, one barrier).
+  const int32_t* src0 = a.idx + (int64_t)row * a.idx_stride + t0;
+  if (a.sparse)
+    for (int i = tid; i < min(n_here, kMaxTokensPerSplit); i += kGT) f.lidx[i] = src0[i];
   // Query operand: q of head m16 (zero past G) at the query channel of each
   // stored K column 32 kg + 4 s + j, staged in LDS per stored column.
   for (int i = tid; i < G * kDv; i += kGT) {
@@ -112,10 +117,9 @@ __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a) {
 
   for (int bat = 0; bat < n_here; bat += kMaxTokensPerSplit) {
     const int nb = min(kMaxTokensPerSplit, n_here - bat);
-    if (a.sparse) {
+    if (a.sparse && bat > 0) {
       __syncthreads();
-      const int32_t* src = a.idx + (int64_t)row * a.idx_stride + t0 + bat;
-      for (int i = tid; i < nb; i += kGT) f.lidx[i] = src[i];
+      for (int i = tid; i < nb; i += kGT) f.lidx[i] = src0[bat + i];
       __syncthreads();
     }
     auto tok = [&](int i) -> int64_t {
