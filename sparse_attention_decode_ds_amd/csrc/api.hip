@@ -189,15 +189,17 @@ AttnArgs attn_args(const ds_kv_desc* kv, const void* q, const void* K, const voi
 }
 
 // Attention partitions per row: about kTargetAttnBlocks workgroups in all,
-// each with at least 64 tokens (128 for query groups, whose workgroups take
-// 16-token tiles per wave).
+// each with at least 64 tokens.  Query groups: about half as many
+// workgroups (the group kernel holds two per compute unit) of at least 256
+// tokens (four 16-token tiles per wave); one split also saves the combine.
 int auto_splits(const Plan& p, int64_t rows, int G, int requested) {
   int ns;
   if (requested > 0) {
     ns = requested;
   } else {
-    const int min_tok = G > 1 ? 2 * kMinTokensPerSplit : kMinTokensPerSplit;
-    ns = (int)ceil_div(kTargetAttnBlocks, std::max<int64_t>(rows, 1));
+    const int min_tok = G > 1 ? 4 * kMinTokensPerSplit : kMinTokensPerSplit;
+    const int target = G > 1 ? kTargetAttnBlocks / 2 : kTargetAttnBlocks;
+    ns = (int)ceil_div(target, std::max<int64_t>(rows, 1));
     ns = (int)std::min<int64_t>(ns, std::max<int64_t>(1, ceil_div(p.kk, min_tok)));
   }
   return std::max(1, std::min(ns, p.split_cap));
