@@ -221,6 +221,9 @@ Route route(const ds_kv_desc* kv, const ds_label_desc* lab, int k, int max_seq, 
   else if (G == 1 && !(flags & (DS_DECODE_UNFUSED | DS_DECODE_STREAM)) &&
            decode_fused_fits(max_seq, k, lab->r, lab->dtype == DS_LABEL_INT4))
     r.path = DS_PATH_FUSED;
+  else if (G > 1 && !(flags & (DS_DECODE_UNFUSED | DS_DECODE_STREAM)) &&
+           decode_fused_g_fits(max_seq, k, lab->r, lab->dtype == DS_LABEL_INT4, G))
+    r.path = DS_PATH_FUSED;
   else if (!(flags & DS_DECODE_STREAM) && p.local_nch <= kMaxLocalChunks)
     r.path = DS_PATH_LOCAL;
   else
@@ -433,17 +436,20 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
     sa.cand_stride = p.cand_stride;
     idx = sa.idx;
     idx_stride = sa.idx_stride;
-    // One kernel for the whole step when the row's keys and token list fit
-    // in LDS and the group is one query head.
+    // One kernel for the whole step when the row's scores fit in one
+    // workgroup's registers and its token list in LDS (256 threads for a
+    // single query head, 1024 for a query group).
     if (fused_step) {
       LabelArgs la = label_args(kv, K, chan, lab);
       AttnArgs aa = attn_args(kv, q, K, V, seq_lens, max_seq_len, keep, sm_scale, out, ws, p);
       aa.n_split = 1;
       mark(DS_STAGE_SELECT);
       mark_attn(DS_STAGE_ATTN);
-      if (launch_decode_fused(sa, aa, la, (flags & DS_DECODE_APPEND) ? 1 : 0, (int)rows, stream,
-                              attn_ev) != hipSuccess)
-        return DS_ERR_HIP;
+      const int app = (flags & DS_DECODE_APPEND) ? 1 : 0;
+      const hipError_t e =
+          G == 1 ? launch_decode_fused(sa, aa, la, app, (int)rows, stream, attn_ev)
+                 : launch_decode_fused_g(sa, aa, la, app, (int)rows, stream, attn_ev);
+      if (e != hipSuccess) return DS_ERR_HIP;
       mark_attn(DS_STAGE_COMBINE);
       mark(DS_STAGE_COUNT);
       return DS_OK;

@@ -34,9 +34,10 @@ struct AttnAcc {
   float l[G];
 };
 
-template <int G>
+// Per wave: final (o, m, l) of each head.
+template <int G, int NW = 4>
 struct AttnRed {
-  float v[4][G][kDv + 2];
+  float v[NW][G][kDv + 2];
 };
 
 // Merge weights of two online-softmax states; either may be empty (m = -inf).
@@ -184,9 +185,9 @@ __device__ __forceinline__ void attend(const AttnArgs& a, const __half* Kr, cons
   attend_run<G>(a, Kr, Vr, slot, n, tok, qf, acc, L);
 }
 
-template <int G, bool FINAL>
-__device__ __forceinline__ void attn_store(const AttnArgs& a, AttnRed<G>& red, int b, int g,
-                                           int split);
+template <int G, bool FINAL, int NW = 4>
+__device__ __forceinline__ void attn_store(const AttnArgs& a, AttnRed<G, NW>& red, int b, int g,
+                                           int split, int ng = G);
 
 // Merge the 16 slot states and write either the fp16 output (FINAL) or the
 // (o, m, l) partial of split `split`.  Every thread of the workgroup calls it.
@@ -233,24 +234,24 @@ __device__ __forceinline__ void attn_finish(const AttnArgs& a, AttnAcc<G>& acc, 
   attn_store<G, FINAL>(a, red, b, g, split);
 }
 
-// Workgroup merge of the four wave states in `red` and the store, by threads
-// (h, c) with h < G (the others do nothing).
-template <int G, bool FINAL>
-__device__ __forceinline__ void attn_store(const AttnArgs& a, AttnRed<G>& red, int b, int g,
-                                           int split) {
+// Workgroup merge of the NW wave states in `red` and the store, by threads
+// (h, c) with h < ng (the others do nothing); ng <= G heads in the group.
+template <int G, bool FINAL, int NW>
+__device__ __forceinline__ void attn_store(const AttnArgs& a, AttnRed<G, NW>& red, int b, int g,
+                                           int split, int ng) {
   const int tid = threadIdx.x;
-  if (tid >= G * 16) return;
+  if (tid >= ng * 16) return;
   const int h = tid >> 4;
   const int cc = tid & 15;
   float M = kNegInf;
 #pragma unroll
-  for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, red.v[ww][h][kDv]);
+  for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, red.v[ww][h][kDv]);
   float L = 0.0f, O[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) O[i] = 0.0f;
   if (M != kNegInf) {
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
       const float mw = red.v[ww][h][kDv];
       if (mw == kNegInf) continue;
       const float sc = exp2f(mw - M);
@@ -259,7 +260,7 @@ __device__ __forceinline__ void attn_store(const AttnArgs& a, AttnRed<G>& red, i
       for (int i = 0; i < 8; ++i) O[i] += sc * red.v[ww][h][cc * 8 + i];
     }
   }
-  const int64_t bh = (int64_t)b * a.Hq + (int64_t)g * G + h;
+  const int64_t bh = (int64_t)b * a.Hq + (int64_t)g * ng + h;
   if (FINAL) {
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     __half2 r2[4];

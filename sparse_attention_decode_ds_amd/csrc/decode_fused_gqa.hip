@@ -1,0 +1,305 @@
+// decode_fused_gqa.hip -- one workgroup of 1024 threads per (batch, KV head)
+// row runs the whole Double Sparsity decode step for a query group of
+// G = 2..8 heads ([DS] "offline calibration": label append; "online forward
+// computation": steps 1-3; [GQA] section 4: the group's heads share the K/V
+// rows, and the label score uses the query summed over the group):
+//
+//   setup    the group's query rows, the heavy-channel table, the kept-column
+//            table and the appended token's K row are fetched ahead of the
+//            label stream; the summed, gathered query and the query rows at
+//            the stored K columns' channels go to LDS;
+//   append   the appended token's label is written and scored from the K row;
+//   score    the label stream is scored into registers (thread tid holds the
+//            vectors v = j * 1024 + tid);
+//   select   exact top-k into an LDS token list (list_select_a, then rank
+//            count or radix passes for the boundary bin);
+//   attend   each of the 16 waves takes every 16th 16-token tile of the list
+//            on the matrix cores (gqa_tile.h; with k <= 256 one tile per
+//            wave, so all K/V loads of the row are in flight at once); the 16
+//            wave states are merged per head through LDS and the fp16 output
+//            written.
+//
+// The rows of a decode batch with few KV heads are long (thousands of
+// tokens), so the workgroup is as wide as a compute unit holds, and one pass
+// replaces the chunked score, the merge and the attention launch.
+#include "gqa_tile.h"
+#include "score_common.h"
+
+namespace ds {
+namespace {
+
+constexpr int kNTG = 1024;
+constexpr int kWG = kNTG / 64;  // waves
+
+template <int JMAX>
+struct FusedGScratch {
+  __half qrows[kMaxGroup][256];  // the group's query rows
+  int32_t chan[128];
+  int32_t keep[128];
+  __half knew[128];  // K row of the appended token
+  float lnew[128];   // its label values (int4: codes)
+  QueryLds q;        // the summed, gathered query
+  float snew;        // the appended token's score
+  float mm_tmp[2 * kWG];
+  uint32_t scan_tmp[kWG];
+  SelScratch sel;
+  uint32_t tot[JMAX * kWG];  // per round and wave: taken | equal << 16
+  alignas(16) __half qk[kMaxGroup][kDv];  // query rows at the stored K columns' channels
+  int32_t lidx[kDecodeFusedMaxK];
+  AttnRed<kMaxGroup, kWG> red;
+};
+
+// TPTC: tokens per thread before rounding up to whole label vectors.
+template <int R, bool INT4, int TPTC>
+__global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs aa, LabelArgs la,
+                                                       int append) {
+  using Vec = typename VecSel<R, INT4>::type;
+  constexpr int VT = Vec::VT;
+  constexpr int JMAX = (TPTC + VT - 1) / VT;  // rounds of vectors per thread
+  constexpr int TPT = JMAX * VT;
+  // label vectors in flight per thread: all of them when they fit in about
+  // 72 registers, else 4 at a time
+  constexpr int UNR = JMAX * (int)sizeof(Vec) <= 288 ? JMAX : 4;
+  __shared__ FusedGScratch<JMAX> f;
+
+  const int row = blockIdx.x;
+  const int b = row / sa.Hkv;
+  const int g = row - b * sa.Hkv;
+  const int S = row_len(sa, b);
+  const int G = sa.G;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = wave_id();
+  const int r = sa.r;
+  const int t_new = S - 1;
+  const bool do_append = append && S >= 1;
+  const bool sparse = sa.k > 0 && S > sa.k;
+
+  // --- setup: small loads first --------------------------------------------
+  {
+    const __half* qh = sa.q + ((int64_t)b * sa.Hq + (int64_t)g * G) * sa.d_q;
+    for (int i = tid; i < G * sa.d_q; i += kNTG) f.qrows[i / sa.d_q][i % sa.d_q] = qh[i];
+    for (int j = tid; j < r; j += kNTG) f.chan[j] = sa.chan[(int64_t)g * r + j];
+    if (sa.keep)
+      for (int i = tid; i < sa.d_k; i += kNTG) f.keep[i] = sa.keep[(int64_t)g * sa.d_k + i];
+    if (do_append && tid < (la.d_k >> 3)) {
+      const __half* kr = la.K + (int64_t)b * la.ks0 + (int64_t)g * la.ks1 + (int64_t)t_new * la.ks2;
+      *reinterpret_cast<uint4*>(&f.knew[tid * 8]) = *reinterpret_cast<const uint4*>(kr + tid * 8);
+    }
+  }
+
+  const RowPtrs p = row_ptrs(sa, row);
+  const int n_vec = sparse ? (S + VT - 1) / VT : 0;
+  const int v_last = n_vec - 1;  // the only vector that may be partial; it holds t_new
+  const int jn = (n_vec + kNTG - 1) / kNTG;  // rounds holding any vector (uniform)
+  // The first label loads go out before the row's length arrives: every
+  // slot below the batch bound max_seq (<= slots, a multiple of 16) is
+  // fetched.
+  const int n_vec_ld =
+      sa.k > 0 && sa.max_seq > sa.k ? (min(sa.max_seq, sa.slots) + VT - 1) / VT : 0;
+  Vec vec[UNR];
+#pragma unroll
+  for (int u = 0; u < UNR; ++u) {
+    const int v = u * kNTG + tid;
+    if (v < n_vec_ld) vec[u].load(p, v);
+  }
+  __syncthreads();
+  {
+    // qg[j] = sum over the group's heads of q[h][keep[chan[j]]], in head order
+    float qgv = 0.0f;
+    if (tid < r) {
+      const int col = f.chan[tid];
+      const int qc = sa.keep ? f.keep[col] : col;
+      for (int h = 0; h < G; ++h) qgv += h2f(f.qrows[h][qc]);
+    }
+    store_query(INT4, r, qgv, f.q);
+    for (int i = tid; i < G * kDv; i += kNTG) {
+      const int h = i / kDv, c = i - h * kDv;
+      f.qk[h][c] = c < aa.d_k ? f.qrows[h][sa.keep ? f.keep[c] : c] : __float2half(0.0f);
+    }
+  }
+  __syncthreads();
+
+  // The append runs on the last wave: the first one holds the row's tail
+  // vectors (round JMAX - 1 when S is just above a multiple of 1024 VT).
+  constexpr int kAppendWave = kWG - 1;
+  // List position i is token f.lidx[i] on the sparse path and token i on the
+  // dense one.
+  auto tok = [&](int i) -> int64_t { return sparse ? (int64_t)f.lidx[i] : (int64_t)i; };
+  auto token = [&](int j, int e) { return (j * kNTG + tid) * VT + e; };
+  auto valid = [&](int j, int) { return j < jn; };  // empty slots hold -inf
+  const int n_att = sparse ? sa.k : S;  // tokens attended
+  if (!sparse) {
+    if (do_append && w == kAppendWave) append_label<R, INT4>(la, row, t_new, f, r, false);
+    if (sa.pad_idx) {
+      int32_t* out = sa.idx + (int64_t)row * sa.idx_stride;
+      for (int i = tid; i < sa.idx_stride; i += kNTG) out[i] = i < S ? i : -1;
+    }
+    // label loads issued ahead of the row length are not used here
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  } else {
+    sel_clear<kNTG>(f.sel);  // published by the barrier after the scores
+    if (do_append && w == kAppendWave) append_label<R, INT4>(la, row, t_new, f, r, true);
+    typename Vec::Q q;
+    q.load(f.q);
+    // --- score into registers ----------------------------------------------
+    constexpr float kEmpty = -__builtin_huge_valf();
+    float sc[TPT];
+    float mn = __builtin_huge_valf(), mx = kEmpty;
+#pragma unroll
+    for (int j0 = 0; j0 < JMAX; j0 += UNR) {
+      if (j0 > 0) {
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+          const int v = (j0 + u) * kNTG + tid;
+          if (j0 + u < JMAX && v < n_vec) vec[u].load(p, v);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int j = j0 + u;
+        if (j >= JMAX) continue;
+        const int v = j * kNTG + tid;
+        float s[VT];
+#pragma unroll
+        for (int e = 0; e < VT; ++e) s[e] = kEmpty;
+        if (v < v_last) {  // a full vector of real tokens
+          vec[u].score(q, r, s);
+#pragma unroll
+          for (int e = 0; e < VT; ++e) {
+            mn = fminf(mn, s[e]);
+            mx = fmaxf(mx, s[e]);
+          }
+        } else if (v == v_last) {
+          vec[u].score(q, r, s);
+#pragma unroll
+          for (int e = 0; e < VT; ++e) {
+            const int t = v * VT + e;
+            if (t >= S || (do_append && t == t_new)) {
+              s[e] = kEmpty;
+            } else {
+              mn = fminf(mn, s[e]);
+              mx = fmaxf(mx, s[e]);
+            }
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < VT; ++e) sc[j * VT + e] = s[e];
+      }
+    }
+    // Row min and max: wave partials, one barrier (which also publishes the
+    // appended token's score and the cleared select scratch).
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane == 0) {
+      f.mm_tmp[w] = mn;
+      f.mm_tmp[kWG + w] = mx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kWG; ++i) {
+      mn = fminf(mn, f.mm_tmp[i]);
+      mx = fmaxf(mx, f.mm_tmp[kWG + i]);
+    }
+    if (do_append) {
+      const float sn = f.snew;
+      if ((v_last & (kNTG - 1)) == tid) {
+        const int jl = v_last / kNTG;
+#pragma unroll
+        for (int j = 0; j < JMAX; ++j)
+#pragma unroll
+          for (int e = 0; e < VT; ++e)
+            if (j == jl && e == t_new - v_last * VT) sc[j * VT + e] = sn;
+      }
+      mn = fminf(mn, sn);
+      mx = fmaxf(mx, sn);
+    }
+
+    // --- exact select into the LDS token list --------------------------------
+    const LinBins bin(mn, mx);
+    const ListSel ls = list_select_a<kNTG, VT, JMAX>(sc, valid, token, (uint32_t)sa.k, bin,
+                                                     f.sel, f.scan_tmp, f.lidx);
+    if (!sa.pad_idx && ls.cnt <= (uint32_t)kRankMax) {
+      list_rank<kNTG>(ls, f.sel, f.lidx);
+    } else {
+      const RegSel rs = list_select_b<kNTG, VT, JMAX>(sc, valid, token, bin, ls, f.sel,
+                                                      f.scan_tmp, f.tot, f.lidx);
+      if (sa.pad_idx) {  // caller asked for the selected set, ascending
+        int32_t* out = sa.idx + (int64_t)row * sa.idx_stride;
+        reg_emit<kNTG, VT, JMAX>(sc, valid, rs, f.tot,
+                                 [&](uint32_t pos, int j, int e) { out[pos] = token(j, e); });
+        for (int i = sa.k + tid; i < sa.idx_stride; i += kNTG) out[i] = -1;
+      }
+    }
+  }
+
+  // --- attention -----------------------------------------------------------------
+  const GqaLane ln(aa, b, g);
+  half4_t qb[8];
+  gqa_query(&f.qk[0][0], G, ln, qb);
+  GqaState st;
+  gqa_init(st);
+  // one tile in registers per wave (k <= 256: one tile per wave)
+  constexpr int kStride = kWG * kGqaTile;
+  for (int i0 = w * kGqaTile; i0 < n_att; i0 += kStride) {
+    GqaTile cur;
+    gqa_load(aa, ln, i0, n_att, tok, cur);
+    gqa_tile(cur, qb, i0, n_att, aa.scale_log2, ln.kg, st);
+  }
+  gqa_to_red(st, ln, G, w, f.red);
+  __syncthreads();
+  attn_store<kMaxGroup, true, kWG>(aa, f.red, b, g, 0, G);
+}
+
+template <int R, bool INT4, int TPTC>
+hipError_t launch_rt(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la, int append,
+                     int rows, hipStream_t s, const KEvents& ev) {
+  return launch_k(k_decode_fused_g<R, INT4, TPTC>, dim3(rows), dim3(kNTG), s, ev, sa, aa, la,
+                  append);
+}
+
+template <int TPTC>
+hipError_t launch_tpt(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la, int append,
+                      int rows, hipStream_t s, const KEvents& ev) {
+  if (sa.is_int4) {
+    if (sa.r == 8) return launch_rt<8, true, TPTC>(sa, aa, la, append, rows, s, ev);
+    if (sa.r == 16) return launch_rt<16, true, TPTC>(sa, aa, la, append, rows, s, ev);
+    return launch_rt<0, true, TPTC>(sa, aa, la, append, rows, s, ev);
+  }
+  if (sa.r == 8) return launch_rt<8, false, TPTC>(sa, aa, la, append, rows, s, ev);
+  if (sa.r == 16) return launch_rt<16, false, TPTC>(sa, aa, la, append, rows, s, ev);
+  return launch_rt<0, false, TPTC>(sa, aa, la, append, rows, s, ev);
+}
+
+// Tokens per thread before rounding up to whole label vectors (1, 2 or 4
+// tokens): the smallest class that holds the longest row.
+constexpr int kTptClass[3] = {4, 9, 16};
+
+int vec_tokens(int r, int is_int4) {
+  if (!is_int4 || (r != 8 && r != 16)) return 1;
+  return r == 8 ? 4 : 2;
+}
+
+int rows_capacity(int tptc, int r, int is_int4) {
+  const int vt = vec_tokens(r, is_int4);
+  return kNTG * ((tptc + vt - 1) / vt) * vt;
+}
+
+}  // namespace
+
+bool decode_fused_g_fits(int max_seq, int k, int r, int is_int4, int G) {
+  return G >= 2 && G <= kMaxGroup && max_seq <= rows_capacity(kTptClass[2], r, is_int4) &&
+         (k >= max_seq || k <= kDecodeFusedMaxK);
+}
+
+hipError_t launch_decode_fused_g(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la,
+                                 int append, int rows, hipStream_t s, const KEvents& ev) {
+  if (rows <= 0) return hipSuccess;
+  if (sa.max_seq <= rows_capacity(kTptClass[0], sa.r, sa.is_int4))
+    return launch_tpt<kTptClass[0]>(sa, aa, la, append, rows, s, ev);
+  if (sa.max_seq <= rows_capacity(kTptClass[1], sa.r, sa.is_int4))
+    return launch_tpt<kTptClass[1]>(sa, aa, la, append, rows, s, ev);
+  return launch_tpt<kTptClass[2]>(sa, aa, la, append, rows, s, ev);
+}
+
+}  // namespace ds

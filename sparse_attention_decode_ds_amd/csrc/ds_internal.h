@@ -136,6 +136,10 @@ hipError_t launch_combine(const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_decode_fused(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la,
                                int append, int rows, hipStream_t s, const KEvents& ev = KEvents());
 bool decode_fused_fits(int max_seq, int k, int r, int is_int4);
+hipError_t launch_decode_fused_g(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la,
+                                 int append, int rows, hipStream_t s,
+                                 const KEvents& ev = KEvents());
+bool decode_fused_g_fits(int max_seq, int k, int r, int is_int4, int G);
 hipError_t launch_score_local(const ScoreArgs& sa, const LabelArgs& la, int append, int rows,
                               hipStream_t s);
 hipError_t launch_select_merge(const ScoreArgs& sa, int rows, hipStream_t s);

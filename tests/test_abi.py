@@ -159,9 +159,14 @@ def test_decode_plan_paths(lib):
     assert rc == 0 and ds.PATHS[pl.path] == "local" and pl.n_split > 1 and pl.kernels == 4
     assert 8192 < pl.chunk <= 10240     # 512-thread chunk workgroups, 20 scores per thread
     assert pl.n_split * pl.tokens_per_split >= 8192
-    # GQA groups (7 query heads per KV head) never take the one-kernel path.
+    # GQA groups (7 query heads per KV head): one 1024-thread kernel for rows
+    # up to 16384 tokens, local top-M + merge beyond.
     rc, pl = _plan(lib, _kv(batch=64, capacity=8224, k_stride=(4 * 8224 * 128, 8224 * 128, 128),
                             v_stride=(4 * 8224 * 128, 8224 * 128, 128)), _lab(slots=8224), 256, 8193)
+    assert rc == 0 and ds.PATHS[pl.path] == "fused" and pl.kernels == 1 and pl.n_split == 1
+    rc, pl = _plan(lib, _kv(batch=8, capacity=32784, k_stride=(4 * 32784 * 128, 32784 * 128, 128),
+                            v_stride=(4 * 32784 * 128, 32784 * 128, 128)), _lab(slots=32784), 1024,
+                   32769)
     assert rc == 0 and ds.PATHS[pl.path] == "local"
     # Flags force the other paths; k <= 0 is dense.
     kv, lab = _mha(32, 32, 4160), _lab(slots=4160, **int4)

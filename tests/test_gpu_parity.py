@@ -280,6 +280,91 @@ def test_fused_outlier_scores(sign):
                       flags=ds.DECODE_APPEND)
 
 
+FUSED_GROUP = {
+    # tokens per thread 4 (rows up to 4096 tokens)
+    "g7_f16_r16_3000": dict(Hq=28, Hkv=4, S0=3000, r=16, int4=False, k=256),
+    # just past 4096: the 9-per-thread class with one token in its last round
+    "g4_int4_r16_4096": dict(Hq=16, Hkv=4, S0=4096, r=16, int4=True, k=300),
+    # the 8K query-group workload's shape, rows nearly filling the class
+    "g7_f16_r16_8223": dict(Hq=28, Hkv=4, S0=8223, r=16, int4=False, k=256),
+    # four tokens per label vector: the class holds 12288 tokens, filled
+    "g2_int4_r8_12287": dict(Hq=4, Hkv=2, S0=12287, r=8, int4=True, k=1024),
+    # the longest rows (16384 tokens) with the largest list
+    "g8_f16_r8_16383": dict(Hq=16, Hkv=2, S0=16383, r=8, int4=False, k=2048),
+    # label width without a specialised vector
+    "g3_f16_r12_5000": dict(Hq=6, Hkv=2, S0=5000, r=12, int4=False, k=300),
+    # LeanK: 32 stored K columns
+    "g7_leank_6000": dict(Hq=28, Hkv=4, S0=6000, r=8, int4=False, k=512, d_k=32),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FUSED_GROUP))
+def test_fused_group_rows(name):
+    """The one-kernel path for query groups at the row lengths of each
+    register budget (4, 9 and 16 tokens per thread), with the label append
+    of the current token, with and without the selected-set output."""
+    cfg, inp = _small_inputs("gqa7_f16_r16", B=2, **FUSED_GROUP[name])
+    _note("fused group %s" % name)
+    S = cfg.S0 + 1
+    seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
+    labels = prefill(cfg, inp, cfg.S0)
+    plan = ds.decode_plan(inp.K, inp.V, cfg.Hq, cfg.D, labels, cfg.k, S)
+    assert plan["path"] == "fused" and plan["kernels"] == 1
+    out, topk = run(cfg, inp, labels, seq, S, flags=ds.DECODE_APPEND)
+    rows = ds_check.sample_rows(cfg, 4)
+    ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k, out,
+                        topk, rows, label_upto=S)
+    check_without_idx(cfg, inp, labels, seq, S, out, ds_check.sample_rows(cfg, 2, seed=1),
+                      flags=ds.DECODE_APPEND)
+
+
+def test_fused_group_ragged_lengths():
+    """Per-row lengths on the query-group kernel: empty, one token, below, at
+    and just above k, and full rows, with and without the set output."""
+    cfg, inp = _small_inputs("gqa7_f16_r16", B=7, S0=5000, k=300)
+    k = cfg.k
+    lens = [0, 1, k - 1, k, k + 1, 2500, cfg.S0 + 1]
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    labels = prefill(cfg, inp, cfg.S0 + 1)
+    plan = ds.decode_plan(inp.K, inp.V, cfg.Hq, cfg.D, labels, k, cfg.S0 + 1)
+    assert plan["path"] == "fused"
+    out, topk = run(cfg, inp, labels, seq, cfg.S0 + 1)
+    assert not out[0].any()
+    rows = ds_check.sample_rows(cfg, 1000)
+    ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, k, out, topk,
+                        rows, label_upto=cfg.S0 + 1)
+    check_without_idx(cfg, inp, labels, seq, cfg.S0 + 1, out, rows)
+
+
+@pytest.mark.parametrize("sign", [1, -1])
+def test_fused_group_outlier_scores(sign):
+    """Outlier tokens on the query-group kernel (as test_fused_outlier_scores:
+    the boundary bin is crowded), the outliers aligned with the query summed
+    over the group."""
+    cfg, inp = _small_inputs("gqa7_f16_r16", B=2, S0=8192, r=16, int4=False, k=256)
+    _note("fused group outlier scores, sign %d" % sign)
+    g = torch.Generator().manual_seed(11 + sign)
+    q = inp.q.float()
+    for b in range(cfg.B):
+        for h in range(cfg.Hkv):
+            ch = inp.chan[h].long()
+            qs = q[b, h * cfg.G:(h + 1) * cfg.G][:, ch].sum(dim=0)
+            sgn = torch.sign(qs).to(torch.float16)
+            sgn[sgn == 0] = 1
+            rows = torch.randperm(cfg.S0, generator=g)[:10].to(inp.K.device)
+            inp.K[b, h, rows[:, None], ch[None, :]] = (8 * sign) * sgn
+    S = cfg.S0 + 1
+    seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
+    labels = prefill(cfg, inp, cfg.S0)
+    plan = ds.decode_plan(inp.K, inp.V, cfg.Hq, cfg.D, labels, cfg.k, S)
+    assert plan["path"] == "fused"
+    out, topk = run(cfg, inp, labels, seq, S, flags=ds.DECODE_APPEND)
+    ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k, out,
+                        topk, ds_check.sample_rows(cfg, 4), label_upto=S, strict_sets=True)
+    check_without_idx(cfg, inp, labels, seq, S, out, ds_check.sample_rows(cfg, 2),
+                      flags=ds.DECODE_APPEND)
+
+
 @pytest.mark.parametrize("mode", [0, 1])
 def test_local_select_fallbacks(mode):
     """Long rows are pre-selected per chunk, then merged.  mode 0: the whole
