@@ -52,11 +52,11 @@ def algorithmic_bytes(cfg, S):
             "out": cfg.B * cfg.Hq * cfg.d_v * 2}
 
 
-def dominant_kernel(plan, ab):
+def dominant_kernel(plan, ab, G):
     """The kernel that takes most of a step on this path, its name prefix in
     profiles, and its algorithmic bytes per launch."""
     if plan["path"] == "fused":
-        return "k_decode_fused", sum(ab.values())
+        return ("k_decode_fused_g" if G > 1 else "k_decode_fused"), sum(ab.values())
     final = plan["n_split"] == 1
     return "k_attn", ab["rows"] + ab["q"] + (ab["out"] if final else 0)
 
@@ -271,7 +271,7 @@ def main():
     S_mid = cfg.S0 + 1 + min(cfg.steps - 1, (args.steps // L) // 2)
     plan = ds.decode_plan(inp.K, inp.V, cfg.Hq, cfg.D, labs[0], cfg.k, S_mid, args.n_split, flags)
     ab = algorithmic_bytes(cfg, S_mid)
-    dom, dom_bytes = dominant_kernel(plan, ab)
+    dom, dom_bytes = dominant_kernel(plan, ab, cfg.G)
     dom_stage = ds.STAGES.index("attn")  # both dominant kernels run in the attention stage
 
     # Pre-marshalled ctypes arguments per (layer, step): the timed loops only

@@ -37,7 +37,7 @@ struct AttnAcc {
 // Per wave: final (o, m, l) of each head.
 template <int G, int NW = 4>
 struct AttnRed {
-  float v[NW][G][kDv + 2];
+  alignas(16) float v[NW][G][kDv + 4];  // o[0 .. kDv), m, l, 2 floats of padding
 };
 
 // Merge weights of two online-softmax states; either may be empty (m = -inf).

@@ -49,6 +49,32 @@ struct FusedGScratch {
   AttnRed<kMaxGroup, kWG> red;
 };
 
+// The wave states merged per head and channel by threads (h, c), h < ng,
+// and the fp16 output written (one channel per thread).
+template <int NW>
+__device__ __forceinline__ void merge_out(const AttnArgs& a, const AttnRed<kMaxGroup, NW>& red,
+                                          int b, int g, int ng) {
+  const int tid = threadIdx.x;
+  if (tid >= ng * kDv) return;
+  const int h = tid / kDv, c = tid - h * kDv;
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, red.v[w][h][kDv]);
+  float L = 0.0f, O = 0.0f;
+  if (M != kNegInf) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = red.v[w][h][kDv];
+      if (mw == kNegInf) continue;
+      const float sc = exp2f(mw - M);
+      L += sc * red.v[w][h][kDv + 1];
+      O += sc * red.v[w][h][c];
+    }
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  a.out[((int64_t)b * a.Hq + (int64_t)g * ng + h) * kDv + c] = __float2half_rn(O * inv);
+}
+
 // TPTC: tokens per thread before rounding up to whole label vectors.
 template <int R, bool INT4, int TPTC>
 __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs aa, LabelArgs la,
@@ -75,34 +101,38 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs 
   const bool do_append = append && S >= 1;
   const bool sparse = sa.k > 0 && S > sa.k;
 
-  // --- setup: small loads first --------------------------------------------
-  {
-    const __half* qh = sa.q + ((int64_t)b * sa.Hq + (int64_t)g * G) * sa.d_q;
-    for (int i = tid; i < G * sa.d_q; i += kNTG) f.qrows[i / sa.d_q][i % sa.d_q] = qh[i];
-    for (int j = tid; j < r; j += kNTG) f.chan[j] = sa.chan[(int64_t)g * r + j];
-    if (sa.keep)
-      for (int i = tid; i < sa.d_k; i += kNTG) f.keep[i] = sa.keep[(int64_t)g * sa.d_k + i];
-    if (do_append && tid < (la.d_k >> 3)) {
-      const __half* kr = la.K + (int64_t)b * la.ks0 + (int64_t)g * la.ks1 + (int64_t)t_new * la.ks2;
-      *reinterpret_cast<uint4*>(&f.knew[tid * 8]) = *reinterpret_cast<const uint4*>(kr + tid * 8);
-    }
-  }
+  // --- setup ----------------------------------------------------------------
+  // The small loads (query rows, heavy channels, kept columns) go out first,
+  // then the whole label stream, and only then are the small values written
+  // to LDS, so their wait does not hold the label loads back.  Every label
+  // load is unconditional (lanes past the batch bound max_seq re-read its
+  // last vector): a path that issued fewer loads after the small ones would
+  // make their wait cover the whole stream.
+  const __half* qh = sa.q + ((int64_t)b * sa.Hq + (int64_t)g * G) * sa.d_q;
+  const int nq = G * sa.d_q;  // <= 2 * kNTG
+  __half qv0 = __float2half(0.0f), qv1 = __float2half(0.0f);
+  int chv = 0, kpv = 0;
+  if (tid < nq) qv0 = qh[tid];
+  if (tid + kNTG < nq) qv1 = qh[tid + kNTG];
+  if (tid < r) chv = sa.chan[(int64_t)g * r + tid];
+  if (sa.keep && tid < sa.d_k) kpv = sa.keep[(int64_t)g * sa.d_k + tid];
 
   const RowPtrs p = row_ptrs(sa, row);
   const int n_vec = sparse ? (S + VT - 1) / VT : 0;
   const int v_last = n_vec - 1;  // the only vector that may be partial; it holds t_new
   const int jn = (n_vec + kNTG - 1) / kNTG;  // rounds holding any vector (uniform)
-  // The first label loads go out before the row's length arrives: every
-  // slot below the batch bound max_seq (<= slots, a multiple of 16) is
-  // fetched.
+  // The label loads go out before the row's length arrives: every slot below
+  // the batch bound max_seq (<= slots, a multiple of 16) is fetched.
   const int n_vec_ld =
       sa.k > 0 && sa.max_seq > sa.k ? (min(sa.max_seq, sa.slots) + VT - 1) / VT : 0;
+  const int v_ld = max(n_vec_ld, 1) - 1;
   Vec vec[UNR];
 #pragma unroll
-  for (int u = 0; u < UNR; ++u) {
-    const int v = u * kNTG + tid;
-    if (v < n_vec_ld) vec[u].load(p, v);
-  }
+  for (int u = 0; u < UNR; ++u) vec[u].load(p, min(u * kNTG + tid, v_ld));
+  if (tid < nq) f.qrows[tid / sa.d_q][tid % sa.d_q] = qv0;
+  if (tid + kNTG < nq) f.qrows[(tid + kNTG) / sa.d_q][(tid + kNTG) % sa.d_q] = qv1;
+  if (tid < r) f.chan[tid] = chv;
+  if (sa.keep && tid < sa.d_k) f.keep[tid] = kpv;
   __syncthreads();
   {
     // qg[j] = sum over the group's heads of q[h][keep[chan[j]]], in head order
@@ -121,8 +151,17 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs 
   __syncthreads();
 
   // The append runs on the last wave: the first one holds the row's tail
-  // vectors (round JMAX - 1 when S is just above a multiple of 1024 VT).
+  // vectors (round JMAX - 1 when S is just above a multiple of 1024 VT).  It
+  // fetches the appended token's K row itself, behind its own label loads.
   constexpr int kAppendWave = kWG - 1;
+  auto append_new = [&](bool with_score) {
+    if (lane < (la.d_k >> 3)) {
+      const __half* kr = la.K + (int64_t)b * la.ks0 + (int64_t)g * la.ks1 + (int64_t)t_new * la.ks2;
+      *reinterpret_cast<uint4*>(&f.knew[lane * 8]) = *reinterpret_cast<const uint4*>(kr + lane * 8);
+    }
+    __builtin_amdgcn_wave_barrier();
+    append_label<R, INT4>(la, row, t_new, f, r, with_score);
+  };
   // List position i is token f.lidx[i] on the sparse path and token i on the
   // dense one.
   auto tok = [&](int i) -> int64_t { return sparse ? (int64_t)f.lidx[i] : (int64_t)i; };
@@ -130,7 +169,7 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs 
   auto valid = [&](int j, int) { return j < jn; };  // empty slots hold -inf
   const int n_att = sparse ? sa.k : S;  // tokens attended
   if (!sparse) {
-    if (do_append && w == kAppendWave) append_label<R, INT4>(la, row, t_new, f, r, false);
+    if (do_append && w == kAppendWave) append_new(false);
     if (sa.pad_idx) {
       int32_t* out = sa.idx + (int64_t)row * sa.idx_stride;
       for (int i = tid; i < sa.idx_stride; i += kNTG) out[i] = i < S ? i : -1;
@@ -139,7 +178,7 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs 
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   } else {
     sel_clear<kNTG>(f.sel);  // published by the barrier after the scores
-    if (do_append && w == kAppendWave) append_label<R, INT4>(la, row, t_new, f, r, true);
+    if (do_append && w == kAppendWave) append_new(true);
     typename Vec::Q q;
     q.load(f.q);
     // --- score into registers ----------------------------------------------
@@ -248,7 +287,7 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs 
   }
   gqa_to_red(st, ln, G, w, f.red);
   __syncthreads();
-  attn_store<kMaxGroup, true, kWG>(aa, f.red, b, g, 0, G);
+  merge_out(aa, f.red, b, g, G);
 }
 
 template <int R, bool INT4, int TPTC>

@@ -168,13 +168,16 @@ template <int G, int NW>
 __device__ __forceinline__ void gqa_to_red(const GqaState& st, const GqaLane& ln, int ng, int w,
                                            AttnRed<G, NW>& red) {
   if (ln.m16 < ng) {
+    float* dst = &red.v[w][ln.m16][0];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-      for (int s = 0; s < 8; ++s) red.v[w][ln.m16][8 * (4 * ln.kg + jj) + s] = st.o[s][jj];
+    for (int jj = 0; jj < 4; ++jj) {
+      float4* d4 = reinterpret_cast<float4*>(dst + 8 * (4 * ln.kg + jj));
+      d4[0] = make_float4(st.o[0][jj], st.o[1][jj], st.o[2][jj], st.o[3][jj]);
+      d4[1] = make_float4(st.o[4][jj], st.o[5][jj], st.o[6][jj], st.o[7][jj]);
+    }
     if (ln.kg == 0) {
-      red.v[w][ln.m16][kDv] = st.m;
-      red.v[w][ln.m16][kDv + 1] = st.l;
+      dst[kDv] = st.m;
+      dst[kDv + 1] = st.l;
     }
   }
 }
