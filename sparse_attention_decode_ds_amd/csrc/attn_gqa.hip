@@ -4,9 +4,10 @@
 // section 2.2: K stored as d_k kept columns, the query read at keep[c]).
 //
 // One workgroup of four waves per (row, split); each wave takes every fourth
-// 16-token tile of the split's token list, with the next tile's loads in
-// flight while the current one is consumed (gqa_tile.h: both products of a
-// tile on the matrix cores).  The four wave states are merged through LDS.
+// 16-token tile of the split's token list, with the loads of its next tile
+// (splits of up to four tiles per wave) or next two tiles in flight while one
+// is consumed (gqa_tile.h: both products of a tile on the matrix cores).  The
+// four wave states are merged through LDS.
 #include "gqa_tile.h"
 
 namespace ds {
@@ -21,7 +22,9 @@ struct GqaLds {
   AttnRed<G> red;  // per wave: final (o, m, l) of each head
 };
 
-template <int G, bool FINAL>
+// RING: splits of more than four tiles per wave (the ring measured faster on
+// long runs, the single prefetch on short ones).
+template <int G, bool FINAL, bool RING>
 __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a) {
   __shared__ GqaLds<G> f;
   const int row = blockIdx.x / a.n_split;
@@ -66,13 +69,35 @@ __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a) {
     auto tok = [&](int i) -> int64_t {
       return a.sparse ? (int64_t)f.lidx[i] : (int64_t)(t0 + bat + i);
     };
-    GqaTile cur, nxt;
-    int i0 = w * kGqaTile;
-    if (i0 < nb) gqa_load(a, ln, i0, nb, tok, nxt);
-    for (; i0 < nb; i0 += 4 * kGqaTile) {
-      cur = nxt;
-      if (i0 + 4 * kGqaTile < nb) gqa_load(a, ln, i0 + 4 * kGqaTile, nb, tok, nxt);
-      gqa_tile(cur, qb, i0, nb, a.scale_log2, ln.kg, st);
+    constexpr int D = 4 * kGqaTile;  // the wave's tiles are D positions apart
+    const int i_first = w * kGqaTile;
+    if (i_first >= nb) continue;
+    if (!RING) {
+      // The next tile's loads in flight while one is consumed.
+      GqaTile cur, nxt;
+      gqa_load(a, ln, i_first, nb, tok, nxt);
+      for (int i0 = i_first; i0 < nb; i0 += D) {
+        cur = nxt;
+        if (i0 + D < nb) gqa_load(a, ln, i0 + D, nb, tok, nxt);
+        gqa_tile(cur, qb, i0, nb, a.scale_log2, ln.kg, st);
+      }
+    } else {
+      // A ring of three tiles: two in flight while one is consumed.  Every
+      // load is issued (up to two past the end read the last token again),
+      // so each wait covers exactly one tile.
+      GqaTile t0, t1, t2;
+      gqa_load(a, ln, i_first, nb, tok, t0);
+      gqa_load(a, ln, i_first + D, nb, tok, t1);
+      for (int i0 = i_first; i0 < nb; i0 += 3 * D) {
+        gqa_load(a, ln, i0 + 2 * D, nb, tok, t2);
+        gqa_tile(t0, qb, i0, nb, a.scale_log2, ln.kg, st);
+        if (i0 + D >= nb) break;
+        gqa_load(a, ln, i0 + 3 * D, nb, tok, t0);
+        gqa_tile(t1, qb, i0 + D, nb, a.scale_log2, ln.kg, st);
+        if (i0 + 2 * D >= nb) break;
+        gqa_load(a, ln, i0 + 4 * D, nb, tok, t1);
+        gqa_tile(t2, qb, i0 + 2 * D, nb, a.scale_log2, ln.kg, st);
+      }
     }
   }
 
@@ -85,8 +110,12 @@ __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a) {
 template <int G>
 hipError_t launch_g(const AttnArgs& a, int rows, bool final_out, hipStream_t s, const KEvents& ev) {
   const dim3 grid(rows * a.n_split);
-  if (final_out) return launch_k(k_attn_gqa<G, true>, grid, dim3(kGT), s, ev, a);
-  return launch_k(k_attn_gqa<G, false>, grid, dim3(kGT), s, ev, a);
+  const bool ring = a.tps > 16 * kGqaTile;  // more than four tiles per wave
+  if (final_out)
+    return ring ? launch_k(k_attn_gqa<G, true, true>, grid, dim3(kGT), s, ev, a)
+                : launch_k(k_attn_gqa<G, true, false>, grid, dim3(kGT), s, ev, a);
+  return ring ? launch_k(k_attn_gqa<G, false, true>, grid, dim3(kGT), s, ev, a)
+              : launch_k(k_attn_gqa<G, false, false>, grid, dim3(kGT), s, ev, a);
 }
 
 }  // namespace

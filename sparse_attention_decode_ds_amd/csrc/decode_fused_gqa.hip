@@ -49,32 +49,6 @@ struct FusedGScratch {
   AttnRed<kMaxGroup, kWG> red;
 };
 
-// The wave states merged per head and channel by threads (h, c), h < ng,
-// and the fp16 output written (one channel per thread).
-template <int NW>
-__device__ __forceinline__ void merge_out(const AttnArgs& a, const AttnRed<kMaxGroup, NW>& red,
-                                          int b, int g, int ng) {
-  const int tid = threadIdx.x;
-  if (tid >= ng * kDv) return;
-  const int h = tid / kDv, c = tid - h * kDv;
-  float M = kNegInf;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) M = fmaxf(M, red.v[w][h][kDv]);
-  float L = 0.0f, O = 0.0f;
-  if (M != kNegInf) {
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float mw = red.v[w][h][kDv];
-      if (mw == kNegInf) continue;
-      const float sc = exp2f(mw - M);
-      L += sc * red.v[w][h][kDv + 1];
-      O += sc * red.v[w][h][c];
-    }
-  }
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  a.out[((int64_t)b * a.Hq + (int64_t)g * ng + h) * kDv + c] = __float2half_rn(O * inv);
-}
-
 // TPTC: tokens per thread before rounding up to whole label vectors.
 template <int R, bool INT4, int TPTC>
 __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs aa, LabelArgs la,
@@ -273,21 +247,21 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs 
   }
 
   // --- attention -----------------------------------------------------------------
+  // Each wave takes every 16th tile of the list, one tile in registers.
   const GqaLane ln(aa, b, g);
   half4_t qb[8];
   gqa_query(&f.qk[0][0], G, ln, qb);
   GqaState st;
   gqa_init(st);
-  // one tile in registers per wave (k <= 256: one tile per wave)
-  constexpr int kStride = kWG * kGqaTile;
-  for (int i0 = w * kGqaTile; i0 < n_att; i0 += kStride) {
+  constexpr int D = kWG * kGqaTile;  // the wave's tiles are D positions apart
+  for (int i0 = w * kGqaTile; i0 < n_att; i0 += D) {
     GqaTile cur;
     gqa_load(aa, ln, i0, n_att, tok, cur);
     gqa_tile(cur, qb, i0, n_att, aa.scale_log2, ln.kg, st);
   }
   gqa_to_red(st, ln, G, w, f.red);
   __syncthreads();
-  merge_out(aa, f.red, b, g, G);
+  gqa_merge_out(aa, f.red, b, g, G);
 }
 
 template <int R, bool INT4, int TPTC>

@@ -59,14 +59,14 @@ __device__ __forceinline__ void gqa_init(GqaState& st) {
 // Lane roles and row bases: m16 = lane % 16 (K token of the tile; head of
 // the score and output columns), kg = lane / 16.
 struct GqaLane {
-  const __half* Kr;  // K of the (batch, KV head) row, at channel 32 kg
+  const __half* Kb;  // K of the (batch, KV head) row
   const __half* Vr;  // V of the row, at channel 8 m16
   int m16, kg;
   __device__ __forceinline__ GqaLane(const AttnArgs& a, int b, int g) {
     const int lane = threadIdx.x & 63;
     m16 = lane & 15;
     kg = lane >> 4;
-    Kr = a.K + (int64_t)b * a.ks0 + (int64_t)g * a.ks1 + 32 * kg;
+    Kb = a.K + (int64_t)b * a.ks0 + (int64_t)g * a.ks1;
     Vr = a.V + (int64_t)b * a.vs0 + (int64_t)g * a.vs1 + 8 * m16;
   }
 };
@@ -86,25 +86,23 @@ __device__ __forceinline__ void gqa_query(const __half* qk, int ng, const GqaLan
   }
 }
 
-// Loads of the tile at list positions [i0, i0 + 16) of nb; tok(i) is the
-// token at position i.  Positions past nb load nothing (zeros).
+// Loads of the tile at list positions [i0, i0 + 16) of nb (nb >= 1); tok(i)
+// is the token at position i.  Every load is issued, without a branch:
+// positions past nb read the token at nb - 1 and K columns past d_k read
+// the last stored column.  Their values never count: the scores of such
+// positions are set to -inf (so P = 0) and the query is zero past d_k.
+// Branch-free loads let the compiler wait for one tile while later tiles are
+// still in flight.
 template <typename TokFn>
 __device__ __forceinline__ void gqa_load(const AttnArgs& a, const GqaLane& ln, int i0, int nb,
                                          TokFn tok, GqaTile& T) {
-  const int ik = i0 + ln.m16;
-  const bool kv_ok = ik < nb;
-  const int64_t tk = kv_ok ? tok(ik) : 0;
+  const int64_t tk = tok(min(i0 + ln.m16, nb - 1));
+  const __half* kr = ln.Kb + tk * a.ks2;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    T.k[u] = make_uint4(0, 0, 0, 0);
-    if (kv_ok && 32 * ln.kg + 8 * u < a.d_k) T.k[u] = ld_stream(ln.Kr + tk * a.ks2 + 8 * u);
-  }
+  for (int u = 0; u < 4; ++u) T.k[u] = ld_stream(kr + min(32 * ln.kg + 8 * u, a.d_k - 8));
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int iv = i0 + 4 * ln.kg + j;
-    T.v[j] = make_uint4(0, 0, 0, 0);
-    if (iv < nb) T.v[j] = ld_stream(ln.Vr + tok(iv) * a.vs2);
-  }
+  for (int j = 0; j < 4; ++j)
+    T.v[j] = ld_stream(ln.Vr + tok(min(i0 + 4 * ln.kg + j, nb - 1)) * a.vs2);
 }
 
 // Half s (0..7) of the four 16-byte pieces x[0..3], as the A operand.
@@ -120,9 +118,34 @@ __device__ __forceinline__ half4_t pick_half(const uint4 (&x)[4], int s) {
   return __builtin_bit_cast(half4_t, u32x2_t{lo, hi});
 }
 
+// Query operand for gqa_tile: the registers gqa_query fills (half4_t[8]), or
+// this view that re-reads the LDS rows for every tile where registers are
+// short.
+struct GqaQLds {
+  const __half* qk;
+  int ng;
+  const GqaLane& ln;
+  __device__ __forceinline__ GqaQLds(const __half* qk_, int ng_, const GqaLane& ln_)
+      : qk(qk_), ng(ng_), ln(ln_) {}
+};
+
+__device__ __forceinline__ void gqa_qop(const half4_t (&q)[8], half4_t (&qb)[8]) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) qb[s] = q[s];
+}
+__device__ __forceinline__ void gqa_qop(const GqaQLds& q, half4_t (&qb)[8]) {
+  // an opaque zero offset keeps the reads inside the caller's loop
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  gqa_query(q.qk + z, q.ng, q.ln, qb);
+}
+
 // One tile (positions [i0, i0 + 16) of nb, i0 < nb) into the state.
-__device__ __forceinline__ void gqa_tile(const GqaTile& cur, const half4_t (&qb)[8], int i0, int nb,
+template <typename QOp>
+__device__ __forceinline__ void gqa_tile(const GqaTile& cur, const QOp& qop, int i0, int nb,
                                          float scale_log2, int kg, GqaState& st) {
+  half4_t qb[8];
+  gqa_qop(qop, qb);
   // scores of the tile: lane holds S[token 4 kg + j][head m16]
   float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -180,6 +203,32 @@ __device__ __forceinline__ void gqa_to_red(const GqaState& st, const GqaLane& ln
       dst[kDv + 1] = st.l;
     }
   }
+}
+
+// The wave states merged per head and channel by threads (h, c), h < ng,
+// and the fp16 output written (one channel per thread).
+template <int NW>
+__device__ __forceinline__ void gqa_merge_out(const AttnArgs& a, const AttnRed<kMaxGroup, NW>& red,
+                                              int b, int g, int ng) {
+  const int tid = threadIdx.x;
+  if (tid >= ng * kDv) return;
+  const int h = tid / kDv, c = tid - h * kDv;
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, red.v[w][h][kDv]);
+  float L = 0.0f, O = 0.0f;
+  if (M != kNegInf) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = red.v[w][h][kDv];
+      if (mw == kNegInf) continue;
+      const float sc = exp2f(mw - M);
+      L += sc * red.v[w][h][kDv + 1];
+      O += sc * red.v[w][h][c];
+    }
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  a.out[((int64_t)b * a.Hq + (int64_t)g * ng + h) * kDv + c] = __float2half_rn(O * inv);
 }
 
 }  // namespace ds

@@ -352,7 +352,7 @@ def test_fused_group_outlier_scores(sign):
             sgn = torch.sign(qs).to(torch.float16)
             sgn[sgn == 0] = 1
             rows = torch.randperm(cfg.S0, generator=g)[:10].to(inp.K.device)
-            inp.K[b, h, rows[:, None], ch[None, :]] = (8 * sign) * sgn
+            inp.K[b, h, rows[:, None], ch[None, :]] = (60 * sign) * sgn
     S = cfg.S0 + 1
     seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
     labels = prefill(cfg, inp, cfg.S0)
@@ -427,6 +427,85 @@ def test_local_select_fallbacks_wide_chunks(mode):
     del inp, labels, out, topk
     gc.collect()
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("want_idx", [True, False])
+def test_local_select_groups(mode, want_idx):
+    """Query groups on the local path (chunk pre-selection, merge, split
+    attention).  mode 0: the top k all in chunk 0 (completeness check fails,
+    full select); mode 1: a chunk of equal scores overflows its slots; mode
+    2: no fallback.  Rows of ragged lengths, one at most k long (every token
+    attended); the result does not depend on the split count."""
+    cfg, inp = _small_inputs("gqa7_f16_r16", B=3, S0=6000, k=100)
+    _note("local select, groups, mode %d, idx %s" % (mode, want_idx))
+    q = inp.q.float()
+    for b in range(cfg.B):
+        for g in range(cfg.Hkv):
+            ch = inp.chan[g].long()
+            if mode == 0:
+                qs = q[b, g * cfg.G:(g + 1) * cfg.G][:, ch].sum(dim=0)
+                sgn = torch.sign(qs).to(torch.float16)
+                sgn[sgn == 0] = 1
+                inp.K[b, g, :150][:, ch] = 60 * sgn
+            elif mode == 1:
+                inp.K[b, g, 1024:3072][:, ch] = 0
+    S = cfg.S0 + 1
+    seq = torch.tensor([S, 3100, cfg.k - 5], dtype=torch.int32, device="cuda")
+    labels = prefill(cfg, inp, S)
+    plan = ds.decode_plan(inp.K, inp.V, cfg.Hq, cfg.D, labels, cfg.k, S, flags=ds.DECODE_UNFUSED)
+    assert plan["path"] == "local" and plan["chunk"] <= 2048
+    out, topk = run(cfg, inp, labels, seq, S, want_idx=want_idx, flags=ds.DECODE_UNFUSED)
+    ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k, out,
+                        topk, ds_check.sample_rows(cfg, 100))
+    if mode == 0 and want_idx:
+        assert (topk[:2] < 150).all()
+    ref, _ = run(cfg, inp, labels, seq, S, want_idx=want_idx, flags=ds.DECODE_UNFUSED, n_split=3)
+    err = ds_check.rel_err_rows(out.float().cpu().numpy(), ref.float().cpu().numpy()).max()
+    assert err <= 1e-3, err
+
+
+def test_local_leank_long_rows():
+    """LeanK + Double Sparsity rows too long for the one-kernel path (17001
+    tokens, 32 stored K columns) on the local path, with the label append."""
+    cfg, inp = _small_inputs("leank_ds", B=2, S0=17000, k=400)
+    S = cfg.S0 + 1
+    seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
+    labels = prefill(cfg, inp, cfg.S0)
+    plan = ds.decode_plan(inp.K, inp.V, cfg.Hq, cfg.D, labels, cfg.k, S)
+    assert plan["path"] == "local"
+    out, topk = run(cfg, inp, labels, seq, S, flags=ds.DECODE_APPEND)
+    ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k, out,
+                        topk, ds_check.sample_rows(cfg, 4), label_upto=S)
+    check_without_idx(cfg, inp, labels, seq, S, out, ds_check.sample_rows(cfg, 2),
+                      flags=ds.DECODE_APPEND)
+
+
+@pytest.mark.parametrize("case", ["dense_5000", "sparse_1500", "leank_dense_3000"])
+def test_group_attention_long_splits(case):
+    """The split attention for query groups with more than four tiles per
+    wave (one split per row: the ring of three tile buffers), including
+    splits longer than one token-list batch (2048 positions) and tails of
+    one to three tiles."""
+    if case == "dense_5000":
+        cfg, inp = _small_inputs("g8_dense", B=2, S0=5000)
+        k, n_split = 0, 1
+    elif case == "sparse_1500":
+        cfg, inp = _small_inputs("gqa7_f16_r16", B=2, S0=4000, k=1500)
+        k, n_split = 1500, 1
+    else:
+        cfg, inp = _small_inputs("leank_dense", B=2, S0=3000)
+        k, n_split = 0, 1
+    _note("group attention, long splits, %s" % case)
+    S = cfg.S0 + 1
+    seq = torch.tensor([S, S - 37], dtype=torch.int32, device="cuda")
+    labels = prefill(cfg, inp, S) if k > 0 else None
+    kw = dict(n_split=n_split, flags=ds.DECODE_UNFUSED)
+    plan = ds.decode_plan(inp.K, inp.V, cfg.Hq, cfg.D, labels, k, S, **kw)
+    assert plan["n_split"] == 1 and plan["tokens_per_split"] > 256
+    out, topk = run(cfg, inp, labels, seq, S, k=k, **kw)
+    ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, k, out, topk,
+                        ds_check.sample_rows(cfg, 100))
 
 
 def test_split_count_invariance_and_determinism():
