@@ -276,24 +276,24 @@ template <bool INT4>
 struct LabelVec0 {  // generic r: 1 token, scalar loads, qg read from LDS
   static constexpr int VT = 1;
   using Q = QPtr;
-  const RowPtrs* p;
+  RowPtrs p;  // by value: the caller's RowPtrs may go out of scope before score()
   int t;
   __device__ __forceinline__ void load(const RowPtrs& pp, int v) {
-    p = &pp;
+    p = pp;
     t = v;
   }
   __device__ __forceinline__ void score(const Q& q, int r, float* out) const {
     float acc = 0.0f;
     if (INT4) {
-      const uint8_t* c = p->codes + (int64_t)t * (r >> 1);
+      const uint8_t* c = p.codes + (int64_t)t * (r >> 1);
       for (int j = 0; j < r; ++j) {
         const int byte = c[j >> 1];
         const int v = (j & 1) ? (byte >> 4) : (byte & 0xF);
         acc = fmaf(q.qg[j], (float)(v >= 8 ? v - 16 : v), acc);
       }
-      out[0] = h2f(p->scales[t]) * acc;
+      out[0] = h2f(p.scales[t]) * acc;
     } else {
-      const __half* c = p->lab16 + (int64_t)t * r;
+      const __half* c = p.lab16 + (int64_t)t * r;
       for (int j = 0; j < r; ++j) acc = fmaf(q.qg[j], h2f(c[j]), acc);
       out[0] = acc;
     }
