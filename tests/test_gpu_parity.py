@@ -51,7 +51,7 @@ def run(cfg, inp, labels, seq_lens, max_seq, k=None, want_idx=True, **kw):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("r,int4", [(8, True), (16, True), (6, True), (16, False), (8, False),
-                                    (5, False)])
+                                    (5, False), (128, False), (64, True)])
 def test_label_build_and_append_bitexact(r, int4):
     cfg = synth.small("lab", B=3, Hq=4, Hkv=4, S0=197, steps=5, r=r, int4=int4, seed=31)
     _note("label r=%d int4=%d" % (r, int4))
@@ -506,6 +506,37 @@ def test_group_attention_long_splits(case):
     out, topk = run(cfg, inp, labels, seq, S, k=k, **kw)
     ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, k, out, topk,
                         ds_check.sample_rows(cfg, 100))
+
+
+WIDE = {
+    # 256-channel queries, 128 stored K columns chosen by the keep table,
+    # every stored column a heavy channel (fp16 labels of generic width)
+    "mha_q256_r128_f16": dict(B=2, Hq=4, Hkv=4, D=256, d_k=128, S0=1500, r=128, k=64,
+                              int4=False),
+    # the same for a query group with 64 int4 heavy channels
+    "g4_q256_r64_int4": dict(B=2, Hq=16, Hkv=4, D=256, d_k=128, S0=2000, r=64, k=100,
+                             int4=True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(WIDE))
+@pytest.mark.parametrize("mode", ["default", "unfused", "stream"])
+def test_wide_query_and_widest_labels(name, mode):
+    """The widest query (256 channels, read through the keep table) and the
+    widest labels (every stored column), on the one-kernel, local and
+    streaming paths, with the label append."""
+    cfg, inp = _small_inputs("mha_f16_r16", **WIDE[name])
+    _note("wide %s %s" % (name, mode))
+    S = cfg.S0 + 1
+    seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
+    labels = prefill(cfg, inp, cfg.S0)
+    flags = ds.DECODE_APPEND | {"default": 0, "unfused": ds.DECODE_UNFUSED,
+                                "stream": ds.DECODE_STREAM}[mode]
+    plan = ds.decode_plan(inp.K, inp.V, cfg.Hq, cfg.D, labels, cfg.k, S, flags=flags)
+    assert plan["path"] == {"default": "fused", "unfused": "local", "stream": "stream"}[mode]
+    out, topk = run(cfg, inp, labels, seq, S, flags=flags)
+    ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k, out,
+                        topk, ds_check.sample_rows(cfg, 100), label_upto=S)
 
 
 def test_split_count_invariance_and_determinism():
