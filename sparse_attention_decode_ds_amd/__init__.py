@@ -159,6 +159,31 @@ class LabelCache:
         return d
 
 
+def check_tables(chan, d_k: int, r: int | None = None, keep=None, d_q: int | None = None,
+                 n_kv_heads: int | None = None):
+    """Check the contents of the index tables, which the C ABI does not read
+    on the host: chan [H_kv][r] holds distinct stored-K columns in [0, d_k)
+    per KV head; keep [H_kv][d_k] holds query channels in [0, d_q).  Copies
+    the tables to the host (a synchronisation), so it suits set-up time, not
+    every decode step.  Raises ValueError."""
+    if chan is not None:
+        c = chan.detach().to("cpu", torch.int64)
+        if c.dim() != 2 or (n_kv_heads is not None and c.shape[0] != n_kv_heads) or (
+                r is not None and c.shape[1] != r):
+            raise ValueError("chan: expected shape [n_kv_heads][r], got %s" % (tuple(c.shape),))
+        if c.numel() and (int(c.min()) < 0 or int(c.max()) >= d_k):
+            raise ValueError("chan: column outside [0, %d)" % d_k)
+        if c.shape[1] > 1 and bool((c.sort(dim=1).values.diff(dim=1) == 0).any()):
+            raise ValueError("chan: repeated column in a KV head's table")
+    if keep is not None:
+        k = keep.detach().to("cpu", torch.int64)
+        if k.dim() != 2 or k.shape[1] != d_k or (n_kv_heads is not None and k.shape[0] != n_kv_heads):
+            raise ValueError("keep: expected shape [n_kv_heads][%d], got %s" % (d_k, tuple(k.shape)))
+        hi = d_q if d_q is not None else d_k
+        if k.numel() and (int(k.min()) < 0 or int(k.max()) >= hi):
+            raise ValueError("keep: query channel outside [0, %d)" % hi)
+
+
 def label_build(K, chan, labels: LabelCache, t_begin: int, t_end: int, stream=None):
     kv = kv_desc(K, K, 1)
     lab = labels.desc()
@@ -201,10 +226,14 @@ def decode_plan(K, V, n_q_heads, d_q, labels: LabelCache | None, k, max_seq_len,
 def decode_attn(q, K, V, seq_lens, max_seq_len: int, k: int, sm_scale: float,
                 chan=None, labels: LabelCache | None = None, keep=None, out=None,
                 topk_idx=None, workspace=None, n_split: int = 0, flags: int = 0,
-                stage_events=None, stream=None):
+                stage_events=None, stream=None, validate_tables: bool = False):
     """One decode step (ds_decode_attn).  Returns ``out`` fp16 [B][H_q][d_v].
-    ``stage_events``: optional ctypes array of STAGE_COUNT + 1 hipEvent_t."""
+    ``stage_events``: optional ctypes array of STAGE_COUNT + 1 hipEvent_t.
+    ``validate_tables``: check chan and keep first (check_tables; synchronises)."""
     B, Hq, d_q = q.shape
+    if validate_tables:
+        check_tables(chan if k > 0 else None, K.shape[3], labels.r if labels is not None else None,
+                     keep, d_q, K.shape[1])
     kv = kv_desc(K, V, Hq, d_q)
     lab = labels.desc() if labels is not None else None
     lib = load()

@@ -209,3 +209,24 @@ def test_product_has_no_fallback():
     src = open(mod.__file__).read()
     assert "oracle" not in src.replace("there is no fallback", "")
     assert "import oracle" not in src and "numpy" not in src
+
+
+def test_check_tables_host_logic():
+    """The binding's index-table check (CPU tensors, no GPU needed)."""
+    import torch
+    chan = torch.tensor([[0, 3, 7], [1, 2, 31]], dtype=torch.int32)
+    ds.check_tables(chan, d_k=32, r=3, n_kv_heads=2)
+    keep = torch.arange(64, dtype=torch.int32).reshape(2, 32) * 2
+    ds.check_tables(chan, d_k=32, r=3, keep=keep, d_q=128, n_kv_heads=2)
+    bad = [
+        dict(chan=torch.tensor([[0, 3, 32], [1, 2, 3]], dtype=torch.int32), d_k=32),   # column >= d_k
+        dict(chan=torch.tensor([[0, -1, 5], [1, 2, 3]], dtype=torch.int32), d_k=32),   # negative
+        dict(chan=torch.tensor([[4, 3, 4], [1, 2, 3]], dtype=torch.int32), d_k=32),    # repeated
+        dict(chan=chan, d_k=32, r=4),                                                 # wrong r
+        dict(chan=chan, d_k=32, n_kv_heads=3),                                        # wrong heads
+        dict(chan=chan, d_k=32, keep=keep, d_q=100),                                  # keep >= d_q
+        dict(chan=chan, d_k=32, keep=keep[:, :16], d_q=128),                          # keep width
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            ds.check_tables(**kw)

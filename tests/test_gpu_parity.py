@@ -40,6 +40,7 @@ def run(cfg, inp, labels, seq_lens, max_seq, k=None, want_idx=True, **kw):
     topk = None
     if k > 0 and want_idx:
         topk = torch.full((cfg.B, cfg.Hkv, k), -7, dtype=torch.int32, device="cuda")
+    kw.setdefault("validate_tables", True)
     out = ds.decode_attn(inp.q, inp.K, inp.V, seq_lens, max_seq, k, cfg.sm_scale, chan=inp.chan,
                          labels=labels if k > 0 else None, keep=inp.keep, topk_idx=topk, **kw)
     torch.cuda.synchronize()
