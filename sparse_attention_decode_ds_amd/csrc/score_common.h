@@ -844,12 +844,20 @@ template <int NT, int VT, int JMAX, typename Valid, typename Order>
 __device__ __forceinline__ ListSel list_select_a(const float* sc, Valid valid, Order order,
                                                  uint32_t k, const LinBins& bin, SelScratch& ss,
                                                  uint32_t* scan_tmp, int32_t* list) {
+  constexpr int N = JMAX * VT;
+  static_assert(N <= 32, "one bit per item");
   const int lane = threadIdx.x & 63;
+  // the items' bins, two 16-bit halves per word, computed once
+  uint32_t bp[(N + 1) / 2];
+#pragma unroll
+  for (int i = 0; i < (N + 1) / 2; ++i) bp[i] = 0u;
 #pragma unroll
   for (int j = 0; j < JMAX; ++j)
 #pragma unroll
     for (int e = 0; e < VT; ++e) {
-      const uint32_t bi = bin(sc[j * VT + e]);
+      const int i = j * VT + e;
+      const uint32_t bi = bin(sc[i]);
+      bp[i >> 1] |= bi << (16 * (i & 1));
       if (valid(j, e) && bi != 0u) atomicAdd(&ss.hist[bi], 1u);
     }
   __syncthreads();
@@ -860,17 +868,23 @@ __device__ __forceinline__ ListSel list_select_a(const float* sc, Valid valid, O
   ls.cnt = ss.misc[6];
   ls.need = k - ls.n_a;
   const bool few = ls.cnt <= (uint32_t)kRankMax;
-  // per thread: items above b* (low half) and in b* (high half); positions
-  // in (wave, lane, round, element) order, so the list and hence the
+  // per thread: items above b* and in b* (bit i: item i); positions in
+  // (wave, lane, round, element) order, so the list and hence the
   // attention's summation order are the same on every run
-  uint32_t mine = 0u;
+  uint32_t above = 0u, equal = 0u;
 #pragma unroll
   for (int j = 0; j < JMAX; ++j)
 #pragma unroll
     for (int e = 0; e < VT; ++e) {
-      const uint32_t bi = bin(sc[j * VT + e]);
-      if (valid(j, e)) mine += bi > ls.bstar ? 1u : (bi == ls.bstar ? 0x10000u : 0u);
+      const int i = j * VT + e;
+      const uint32_t bi = (bp[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      if (valid(j, e)) {
+        above |= (bi > ls.bstar ? 1u : 0u) << i;
+        equal |= (bi == ls.bstar ? 1u : 0u) << i;
+      }
     }
+  const uint32_t mine = (uint32_t)__builtin_popcount(above) |
+                        ((uint32_t)__builtin_popcount(equal) << 16);
   const int w = wave_id();
   const uint32_t incl = wave_incl_scan(mine);
   if (lane == 63) scan_tmp[w] = incl;  // find_digit's reads of scan_tmp are behind its last barrier
@@ -883,14 +897,12 @@ __device__ __forceinline__ ListSel list_select_a(const float* sc, Valid valid, O
   for (int j = 0; j < JMAX; ++j)
 #pragma unroll
     for (int e = 0; e < VT; ++e) {
-      if (!valid(j, e)) continue;
-      const float sv = sc[j * VT + e];
-      const uint32_t bi = bin(sv);
-      if (bi > ls.bstar) {
+      const int i = j * VT + e;
+      if ((above >> i) & 1u) {
         list[pa++] = order(j, e);
-      } else if (bi == ls.bstar) {
+      } else if ((equal >> i) & 1u) {
         if (few) {
-          ss.cand_key[pb] = score_key(sv);
+          ss.cand_key[pb] = score_key(sc[i]);
           ss.cand_idx[pb] = order(j, e);
         }
         ++pb;
