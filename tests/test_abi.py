@@ -230,3 +230,24 @@ def test_check_tables_host_logic():
     for kw in bad:
         with pytest.raises(ValueError):
             ds.check_tables(**kw)
+
+
+@pytest.mark.parametrize("G,max_seq,path", [
+    (1, 6144, "fused"), (1, 6145, "local"),        # 256 threads x 24 scores
+    (7, 16384, "fused"), (7, 16385, "local"),      # 1024 threads x 16 scores
+    (2, 12288, "fused"), (8, 4096, "fused"),
+])
+def test_one_kernel_path_bounds(lib, G, max_seq, path):
+    """The one-kernel paths hold rows up to their register budget: 6144
+    tokens for a single query head, 16384 for a query group."""
+    Hkv = 4
+    cap = (max_seq + 63) // 64 * 64
+    kv = _kv(batch=8, n_q_heads=G * Hkv, n_kv_heads=Hkv, capacity=cap,
+             k_stride=(Hkv * cap * 128, cap * 128, 128), v_stride=(Hkv * cap * 128, cap * 128, 128))
+    rc, pl = _plan(lib, kv, _lab(slots=cap), 256, max_seq)
+    assert rc == 0 and ds.PATHS[pl.path] == path
+    if path == "fused":
+        assert pl.kernels == 1 and pl.n_split == 1
+    # k beyond the LDS token list (2048) leaves the one-kernel path
+    rc, pl = _plan(lib, kv, _lab(slots=cap), 2049, max_seq)
+    assert rc == 0 and ds.PATHS[pl.path] != "fused"
