@@ -62,15 +62,19 @@ def dominant_kernel(plan, ab, G):
 
 
 def source_hash():
-    """Hash of the kernel sources: a stored counter record is only used while
-    the kernels it was taken on are unchanged."""
+    """Hash of the kernel sources, comments and blank space left out: a stored
+    counter record is only used while the code it was taken on is unchanged."""
     import hashlib
+    import re
     h = hashlib.sha256()
     d = os.path.join(ROOT, "sparse_attention_decode_ds_amd", "csrc")
     for f in sorted(os.listdir(d)):
         if f.endswith((".hip", ".h")):
+            text = open(os.path.join(d, f), encoding="utf-8").read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
             h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+            h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

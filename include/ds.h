@@ -164,8 +164,9 @@ typedef struct {
 enum {
   DS_PATH_DENSE = 0,  /* k <= 0: attention over every token, no label read */
   DS_PATH_FUSED = 1,  /* one kernel per step: one workgroup per (batch, KV head)
-                         row appends, scores, selects and attends (single
-                         query head per group, rows short enough for LDS) */
+                         row appends, scores, selects and attends (rows of up
+                         to 6144 tokens for single-head groups, 16384 for
+                         groups of 2 to 8 query heads; k <= 2048) */
   DS_PATH_LOCAL = 2,  /* chunked scores with a local top-M per chunk, an exact
                          merge per row, split attention, merge of splits */
   DS_PATH_STREAM = 3  /* every score streamed to the workspace, a radix select

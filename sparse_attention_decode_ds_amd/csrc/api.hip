@@ -375,9 +375,9 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
   };
 
   mark(DS_STAGE_APPEND);
-  // Paths for the score and select: one kernel for the whole step (single
-  // query head, short rows), local top-M + exact merge, or a full streaming
-  // select over every score.
+  // Paths for the score and select: one kernel for the whole step (rows
+  // whose scores fit in one workgroup's registers), local top-M + exact
+  // merge, or a full streaming select over every score.
   const Route rt = route(kv, lab, k, max_seq_len, flags, opts ? opts->n_split : 0, p);
   const bool fused_step = rt.path == DS_PATH_FUSED;
   const bool local_path = rt.path == DS_PATH_LOCAL;
