@@ -311,9 +311,15 @@ struct MergeScratch {
   uint32_t total; // candidates of the row
 };
 
+// Token lists up to this long are built in LDS and copied out in one
+// coalesced pass (placing them straight into global memory scatters 4-byte
+// stores over the list).
+constexpr int kMergeLdsList = 8192;
+
 template <int R, bool INT4>
 __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
   __shared__ MergeScratch f;
+  __shared__ int32_t lds_list[kMergeLdsList];
   const int row = blockIdx.x;
   const int b = row / sa.Hkv;
   const int g = row - b * sa.Hkv;
@@ -405,22 +411,27 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
     // attention pass does not depend on their order), unless the caller
     // asked for the selected set, which is then written in ascending order.
     const LinBins bin(mn, mx);
+    const bool in_lds = sa.k <= kMergeLdsList;
+    int32_t* list = in_lds ? lds_list : out;
     const ListSel ls = list_select_a<kNTM, VTM, kMergeJ>(sc, valid, order, (uint32_t)sa.k, bin,
-                                                         f.sel, f.scan_tmp, out);
+                                                         f.sel, f.scan_tmp, list);
     const RegSel rs =
         ls.cnt <= (uint32_t)kRankMax
-            ? list_rank<kNTM>(ls, f.sel, out)
+            ? list_rank<kNTM>(ls, f.sel, list)
             : list_select_b<kNTM, VTM, kMergeJ>(sc, valid, order, bin, ls, f.sel, f.scan_tmp,
-                                                f.tot, out);
+                                                f.tot, list);
     // Complete iff every chunk that dropped tokens (theta != 0) has theta at
     // or below the smallest selected key; e_lo is at or below that key.
     if (tid < min(n_ch, kMaxLocalChunks) && f.ch_theta[tid] > rs.e_lo) atomicOr(&f.flag, 1u);
     __syncthreads();
     full = f.flag != 0u;
-    if (!full && sa.pad_idx)
+    if (!full && sa.pad_idx) {
       reg_emit<kNTM, VTM, kMergeJ>(sc, valid, rs, f.tot, [&](uint32_t pos, int j, int e) {
         out[pos] = tok[j * VTM + e];
       });
+    } else if (!full && in_lds) {
+      for (int i = tid; i < sa.k; i += kNTM) out[i] = lds_list[i];
+    }
   }
 
   if (full) {
