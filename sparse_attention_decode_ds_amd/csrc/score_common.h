@@ -918,14 +918,27 @@ __device__ __forceinline__ ListSel list_select_a(const float* sc, Valid valid, O
 // the whole selection characterised as by reg_select (for reg_emit).
 template <int NT>
 __device__ __forceinline__ RegSel list_rank(const ListSel& ls, SelScratch& ss, int32_t* list) {
-  for (int i = threadIdx.x; i < (int)ls.cnt; i += NT) {
+  const int cnt = (int)ls.cnt;
+  for (int i = threadIdx.x; i < cnt; i += NT) {
     const uint32_t ki = ss.cand_key[i];
     const int ti = ss.cand_idx[i];
     uint32_t above = 0, tied = 0;
-    for (int m = 0; m < (int)ls.cnt; ++m) {
-      const uint32_t km = ss.cand_key[m];
-      above += km > ki;
-      tied += km == ki && ss.cand_idx[m] < ti;
+    // eight candidates per step, their LDS reads in flight together (slots
+    // past cnt read as key 0 with index INT_MAX: never above or tied-below)
+    for (int m = 0; m < cnt; m += 8) {
+      uint32_t km[8];
+      int tm[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool in = m + u < cnt;
+        km[u] = in ? ss.cand_key[m + u] : 0u;
+        tm[u] = in ? ss.cand_idx[m + u] : 0x7FFFFFFF;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        above += km[u] > ki;
+        tied += km[u] == ki && tm[u] < ti;
+      }
     }
     const uint32_t rank = above + tied;
     if (rank < ls.need) list[ls.n_a + rank] = ti;
