@@ -118,34 +118,9 @@ __device__ __forceinline__ half4_t pick_half(const uint4 (&x)[4], int s) {
   return __builtin_bit_cast(half4_t, u32x2_t{lo, hi});
 }
 
-// Query operand for gqa_tile: the registers gqa_query fills (half4_t[8]), or
-// this view that re-reads the LDS rows for every tile where registers are
-// short.
-struct GqaQLds {
-  const __half* qk;
-  int ng;
-  const GqaLane& ln;
-  __device__ __forceinline__ GqaQLds(const __half* qk_, int ng_, const GqaLane& ln_)
-      : qk(qk_), ng(ng_), ln(ln_) {}
-};
-
-__device__ __forceinline__ void gqa_qop(const half4_t (&q)[8], half4_t (&qb)[8]) {
-#pragma unroll
-  for (int s = 0; s < 8; ++s) qb[s] = q[s];
-}
-__device__ __forceinline__ void gqa_qop(const GqaQLds& q, half4_t (&qb)[8]) {
-  // an opaque zero offset keeps the reads inside the caller's loop
-  int z;
-  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-  gqa_query(q.qk + z, q.ng, q.ln, qb);
-}
-
 // One tile (positions [i0, i0 + 16) of nb, i0 < nb) into the state.
-template <typename QOp>
-__device__ __forceinline__ void gqa_tile(const GqaTile& cur, const QOp& qop, int i0, int nb,
+__device__ __forceinline__ void gqa_tile(const GqaTile& cur, const half4_t (&qb)[8], int i0, int nb,
                                          float scale_log2, int kg, GqaState& st) {
-  half4_t qb[8];
-  gqa_qop(qop, qb);
   // scores of the tile: lane holds S[token 4 kg + j][head m16]
   float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
