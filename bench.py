@@ -213,8 +213,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs the decode path on one GPU only; "
-              "--gpus %d (WORLD_SIZE %d) is not supported" % (args.gpus, world), file=sys.stderr)
+        print("bench.py: the decode path runs on one GPU; --gpus %d (WORLD_SIZE %d) is not "
+              "supported (one GPU holds a whole row set; see the sharding notes)" % (args.gpus, world),
+              file=sys.stderr)
         return 2
     if args.traffic_from:
         return write_traffic(args)
