@@ -61,6 +61,35 @@ def dominant_kernel(plan, ab, G):
     return "k_attn", ab["rows"] + ab["q"] + (ab["out"] if final else 0)
 
 
+def pct_us(ms_list):
+    """[median, 90th percentile] of a list of durations in ms, in µs."""
+    if not ms_list:
+        return None
+    st = sorted(ms_list)
+    return [round(st[len(st) // 2] * 1e3, 3), round(st[min(len(st) - 1, (9 * len(st)) // 10)] * 1e3, 3)]
+
+
+def copy_ceiling_gbs(torch, mib=1024, reps=5):
+    """A plain device copy of `mib` MiB (torch's copy kernel): bytes read plus
+    written per second, the box's practical streaming ceiling beside the
+    8 TB/s peak."""
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(2):
+        y.copy_(x)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del x, y
+    return 2.0 * mib * (1 << 20) / (ms * 1e-3) / 1e9
+
+
 def source_hash():
     """Hash of the kernel sources, comments and blank space left out: a stored
     counter record is only used while the code it was taken on is unchanged."""
@@ -344,6 +373,8 @@ def main():
                 step_ms.append(events.elapsed_ms(b, b + ds.STAGE_COUNT))
     mean = {k: (sum(v) / len(v) if v else None) for k, v in stage_ms.items()}
 
+    copy_gbs = copy_ceiling_gbs(torch)
+
     value = cfg.B * args.steps / wall
     ms_step = wall / args.steps * 1e3
     dom_ms = mean["attn"]
@@ -375,6 +406,9 @@ def main():
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": dom_bytes,
                      "avg_launch_us": round(dom_ms * 1e3, 3) if dom_ms else None,
+                     "launch_us_p50_p90": pct_us(stage_ms["attn"]),
+                     "copy_gbs": round(copy_gbs, 1),
+                     "frac_of_copy": round(achieved / copy_gbs, 4) if achieved else None,
                      "timing": "HIP events recorded by the kernel's own launch at its start "
                                "and end, in a second pass of the same %d steps" % args.steps},
         "step": {"algorithmic_bytes": step_bytes,
@@ -385,8 +419,7 @@ def main():
                                    for k, v in mean.items()}},
     }
     if step_ms:
-        st = sorted(step_ms)
-        result["step"]["median_us_events"] = round(st[len(st) // 2] * 1e3, 3)
+        result["step"]["us_p50_p90_events"] = pct_us(step_ms)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     events.close()
