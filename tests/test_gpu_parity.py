@@ -540,6 +540,22 @@ def test_wide_query_and_widest_labels(name, mode):
                         topk, ds_check.sample_rows(cfg, 100), label_upto=S)
 
 
+@pytest.mark.parametrize("name", ["mha_int4_r8", "gqa7_f16_r16"])
+@pytest.mark.parametrize("k", [1, 2, 17])
+@pytest.mark.parametrize("mode", ["default", "unfused", "stream"])
+def test_smallest_k(name, k, mode):
+    """One, two or seventeen heavy tokens per row on every path (the boundary
+    bin then holds the whole quota or one item), with the set output."""
+    cfg, inp = _small_inputs(name, k=k)
+    S = cfg.S0 + 1
+    seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
+    labels = prefill(cfg, inp, S)
+    flags = {"default": 0, "unfused": ds.DECODE_UNFUSED, "stream": ds.DECODE_STREAM}[mode]
+    out, topk = run(cfg, inp, labels, seq, S, flags=flags)
+    ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, k, out, topk,
+                        ds_check.sample_rows(cfg, 100))
+
+
 def test_split_count_invariance_and_determinism():
     cfg, inp = _small_inputs("mha_int4_r8")
     S = cfg.S0 + 1
