@@ -21,10 +21,7 @@ namespace ds {
 
 constexpr int kAttnThreads = 256;
 constexpr int kSlots = 16;
-#ifndef DS_ATTN_UNROLL
-#define DS_ATTN_UNROLL 4
-#endif
-constexpr int kUnroll = DS_ATTN_UNROLL;  // tokens per slot and group
+constexpr int kUnroll = 4;  // tokens per slot and group
 constexpr float kNegInf = -__builtin_huge_valf();
 
 template <int G>

@@ -27,10 +27,6 @@
 #include "attn_common.h"
 #include "score_common.h"
 
-#ifndef DS_FUSED_ALL_LOADS
-#define DS_FUSED_ALL_LOADS 1
-#endif
-
 namespace ds {
 namespace {
 
@@ -64,7 +60,7 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
   constexpr int JMAX = TPT / VT;  // rounds of vectors per thread
   // label vectors in flight per thread: all of them when they fit in about
   // 40 registers, else 4 at a time
-  constexpr int UNR = DS_FUSED_ALL_LOADS && JMAX * (int)sizeof(Vec) <= 160 ? JMAX : 4;
+  constexpr int UNR = JMAX * (int)sizeof(Vec) <= 160 ? JMAX : 4;
   __shared__ FusedScratch<TPT> f;
 
   const int row = blockIdx.x;

@@ -153,12 +153,8 @@ __device__ __forceinline__ float h2f(__half h) { return __half2float(h); }
 // labels) streams through the caches instead of displacing reused lines.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld_stream(const void* p) {
-#ifdef DS_NO_NT_LOADS
-  return *reinterpret_cast<const uint4*>(p);
-#else
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
-#endif
 }
 
 __device__ __forceinline__ void unpack8(const uint4 v, float* f) {
