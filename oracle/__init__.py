@@ -11,8 +11,9 @@ marshals numpy arrays into it.  Pages (cited by title and section):
 * "Double Sparsity" article (joto.ai blog archive 2025060420469), sections
   "offline calibration" (label cache, 4-bit labels) and "online forward
   computation" (gather, approximate score, top-k + exact attention);
-* LeanK article (aitangshan.cn news 1293675), section 2.2 (static K-channel
-  mask) -- the ``keep`` table;
+* LeanK article (aitangshan.cn news 1293675), section 1.1 (channel importance
+  from the query-key product) -- the calibration criteria; section 2.2 (static
+  K-channel mask) -- the ``keep`` table;
 * grouped-query attention article (trdm.cn news 80600), section 4 -- groups of
   query heads sharing a K/V head.
 """
@@ -68,6 +69,8 @@ def _load():
         lib.oracle_decode.restype = I
         lib.oracle_attend_sets.argtypes = [P, P, P, P, P, P, I, ctypes.c_double, P, I, P, I]
         lib.oracle_attend_sets.restype = I
+        lib.oracle_calibrate.argtypes = [P, P, I, I, I, I, P, I, I, I, P, I, I, P, P]
+        lib.oracle_calibrate.restype = I
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = I
         _lib = lib
@@ -248,3 +251,35 @@ def attend_sets(q, K, V, sets, sm_scale, keep=None, rows=None, n_threads=0):
 
 def max_threads() -> int:
     return _load().oracle_max_threads()
+
+
+CALIB_K, CALIB_Q, CALIB_QK = 0, 1, 2
+
+
+def calibrate(K, criterion, r, qwin=None, Hq=None, keep=None, n_tok=None):
+    """Heavy channels per KV head from sample tokens ("Double Sparsity",
+    section "offline calibration"; LeanK section 1.1).
+
+    K: fp16 [B][Hkv][cap][d_k] (any token/head/batch strides); qwin: fp16
+    [B][n_win][Hq][d_q] or None; keep: int32 [Hkv][d_k] or None.  Returns
+    (chan int32 [Hkv][r] ascending, norms float64 [Hkv][3][d_k]: K column
+    sums of squares, window query sums of squares, criterion score)."""
+    Ku = _kv(K)
+    B, Hkv, cap, d_k = Ku.shape
+    n_tok = cap if n_tok is None else int(n_tok)
+    ks = np.array([s // Ku.itemsize for s in Ku.strides[:3]], np.int64)
+    if qwin is not None:
+        qu = np.ascontiguousarray(_u16(qwin))
+        n_win, d_q = qu.shape[1], qu.shape[3]
+        Hq = qu.shape[2]
+    else:
+        qu, n_win, d_q, Hq = None, 0, 0, Hq or Hkv
+    keep_a = _i32(keep)
+    chan = np.zeros((Hkv, r), np.int32)
+    norms = np.zeros((Hkv, 3, d_k), np.float64)
+    rc = _load().oracle_calibrate(_ptr(Ku), _ptr(ks), B, Hkv, d_k, n_tok, _ptr(qu), n_win, Hq,
+                                  d_q, _ptr(keep_a), int(criterion), int(r), _ptr(chan),
+                                  _ptr(norms))
+    if rc != 0:
+        raise ValueError("oracle_calibrate: status %d" % rc)
+    return chan, norms

@@ -10,7 +10,8 @@
  *   [DS]    "Double Sparsity" article, joto.ai blog archive 2025060420469:
  *           section "offline calibration" (label cache; 4-bit labels) and
  *           section "online forward computation" (steps 1-3).
- *   [LeanK] LeanK article, aitangshan.cn news 1293675: section 2.2 (static
+ *   [LeanK] LeanK article, aitangshan.cn news 1293675: section 1.1 (channel
+ *           importance from the query-key product), section 2.2 (static
  *           hardware-aligned K-channel mask), section 3.2 (kernel speed).
  *   [GQA]   grouped-query attention article, trdm.cn news 80600: section 4
  *           (query heads split into groups sharing one K/V head).
@@ -424,4 +425,93 @@ int oracle_max_threads(void) {
 #else
   return 1;
 #endif
+}
+
+/* ------------------------------------------------------------------------ */
+/* Offline heavy-channel calibration ([DS] "offline calibration": the        */
+/* channels that move the attention scores most are found once, from a few  */
+/* sample tokens, by one of the K-, Q- or QK-outlier criteria; [LeanK]       */
+/* section 1.1: the importance of channel i is the L2 norm of Q[i] K[i]^T,   */
+/* Q the queries of an observation window, K the whole key matrix).          */
+/* ------------------------------------------------------------------------ */
+
+/* For KV head g and stored K column c (query channel qc = keep[g][c], or c):
+ *   kn_b = sum_{t < n_tok} K[b][g][t][c]^2                 (sample b's K column)
+ *   qn_b = sum_{w < n_win} sum_{h in group g} q[b][w][h][qc]^2
+ *   K-outlier  (criterion 0): score = sum_b kn_b
+ *   Q-outlier  (criterion 1): score = sum_b qn_b
+ *   QK-outlier (criterion 2): score = sqrt(sum_b qn_b * kn_b), the Frobenius
+ *     norm of the per-sample products Q_b[c] K_b[c]^T (column c of the
+ *     window's query rows times column c of K; a rank-one matrix, whose norm
+ *     is the product of the two column norms), taken together over samples.
+ * chan[g] = the r columns with the largest score, ties to the lower column,
+ * listed in ascending column order.  norms (optional): [Hkv][3][d_k] holding
+ * sum_b kn_b, sum_b qn_b and the criterion's score.
+ * K: fp16 bits with element strides ks = {batch, head, token}, unit channel
+ * stride; qwin: fp16 bits [B][n_win][Hq][d_q]; keep: [Hkv][d_k] or NULL.
+ * Returns ORC_OK, ORC_ERR_ARG or ORC_ERR_NONFINITE (a non-finite input). */
+int oracle_calibrate(const uint16_t* K, const int64_t* ks, int B, int Hkv, int d_k, int n_tok,
+                     const uint16_t* qwin, int n_win, int Hq, int d_q, const int32_t* keep,
+                     int criterion, int r, int32_t* chan, double* norms) {
+  if (B < 1 || Hkv < 1 || d_k < 1 || n_tok < 0 || n_win < 0 || r < 1 || r > d_k || !chan)
+    return ORC_ERR_ARG;
+  if (criterion < 0 || criterion > 2) return ORC_ERR_ARG;
+  if (n_win > 0 && (!qwin || Hq < Hkv || Hq % Hkv || d_q < 1)) return ORC_ERR_ARG;
+  if (n_tok > 0 && !K) return ORC_ERR_ARG;
+  const int G = n_win > 0 ? Hq / Hkv : 1;
+  orc_pair* p = (orc_pair*)malloc(sizeof(orc_pair) * (size_t)d_k);
+  int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)r);
+  if (!p || !sel) {
+    free(p);
+    free(sel);
+    return ORC_ERR_NOMEM;
+  }
+  int rc = ORC_OK;
+  for (int g = 0; g < Hkv && rc == ORC_OK; ++g) {
+    for (int c = 0; c < d_k; ++c) {
+      const int qc = keep ? keep[(size_t)g * d_k + c] : c;
+      if (n_win > 0 && (qc < 0 || qc >= d_q)) {
+        rc = ORC_ERR_ARG;
+        break;
+      }
+      double kn = 0.0, qn = 0.0, qk = 0.0;
+      for (int b = 0; b < B; ++b) {
+        double knb = 0.0, qnb = 0.0;
+        for (int t = 0; t < n_tok; ++t) {
+          const double x = oracle_half_to_double(K[b * ks[0] + g * ks[1] + t * ks[2] + c]);
+          knb += x * x;
+        }
+        for (int w = 0; w < n_win; ++w)
+          for (int h = 0; h < G; ++h) {
+            const double x = oracle_half_to_double(
+                qwin[(((size_t)b * n_win + w) * Hq + (size_t)g * G + h) * d_q + qc]);
+            qnb += x * x;
+          }
+        kn += knb;
+        qn += qnb;
+        qk += qnb * knb;
+      }
+      if (!isfinite(kn) || !isfinite(qn) || !isfinite(qk)) {
+        rc = ORC_ERR_NONFINITE;
+        break;
+      }
+      const double s = criterion == 0 ? kn : criterion == 1 ? qn : sqrt(qk);
+      p[c].s = s;
+      p[c].t = c;
+      if (norms) {
+        double* nd = norms + (size_t)g * 3 * d_k;
+        nd[c] = kn;
+        nd[d_k + c] = qn;
+        nd[2 * d_k + c] = s;
+      }
+    }
+    if (rc != ORC_OK) break;
+    qsort(p, (size_t)d_k, sizeof(orc_pair), cmp_desc_score_asc_index);
+    for (int j = 0; j < r; ++j) sel[j] = p[j].t;
+    qsort(sel, (size_t)r, sizeof(int32_t), cmp_int32);
+    memcpy(chan + (size_t)g * r, sel, sizeof(int32_t) * (size_t)r);
+  }
+  free(p);
+  free(sel);
+  return rc;
 }
