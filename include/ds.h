@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define DS_ABI_VERSION 1
+#define DS_ABI_VERSION 2
 
 typedef enum {
   DS_OK = 0,
@@ -234,6 +234,48 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
 ds_status ds_decode_attn_plan(const ds_kv_desc* kv, const ds_label_desc* lab, int32_t k,
                               int32_t max_seq_len, const ds_decode_opts* opts,
                               ds_decode_plan* plan);
+
+/* Heavy-channel calibration criteria ([DS] offline calibration: channels
+ * found from outliers of K, of the query, or of their product). */
+typedef enum { DS_CALIB_K = 0, DS_CALIB_Q = 1, DS_CALIB_QK = 2 } ds_calib_criterion;
+
+/* Workspace bytes that ds_calibrate_channels needs for kv's batch, KV heads
+ * and d_k and n_tok sample tokens (0 if the arguments are invalid). */
+size_t ds_calibrate_workspace_size(const ds_kv_desc* kv, int32_t n_tok);
+
+/* Heavy-channel calibration ([DS] offline calibration: the channels that
+ * move the attention scores most are chosen once from a few samples;
+ * [LeanK] section 1.1: a channel's importance is the L2 norm of the product
+ * of the observation window's query column and the key column).  For KV
+ * head g and stored K column c, with query channel qc = keep[g][c] (or c):
+ *   kn_b = sum_{t < n_tok} K[b][g][t][c]^2       (sample b = batch row b)
+ *   qn_b = sum_{w < n_win} sum_{h of group g} qwin[b][w][h][qc]^2
+ *   DS_CALIB_K:  score = sum_b kn_b
+ *   DS_CALIB_Q:  score = sum_b qn_b
+ *   DS_CALIB_QK: score = sqrt(sum_b qn_b kn_b), the Frobenius norm of the
+ *                per-sample rank-one products Q_b[c] K_b[c]^T taken together.
+ * chan[g] receives the r columns with the largest score (ties to the lower
+ * column) in ascending order: a table ds_label_build accepts.  Sums are fp32
+ * in a fixed order, so a call repeats bit for bit.
+ *   K       fp16 K cache (kv: batch, n_kv_heads, d_k, capacity, k_stride are
+ *           read); tokens t < n_tok <= capacity count.
+ *   qwin    fp16 [batch][n_win][n_q_heads][d_q] window queries, contiguous
+ *           (kv's n_q_heads and d_q are read when n_win > 0); n_win may be 0
+ *           (then qn = 0).
+ *   keep    int32 [n_kv_heads][d_k] device array with entries in [0, d_q),
+ *           or NULL (then d_k <= d_q); entries are not checked on the device.
+ *   chan    int32 [n_kv_heads][r] device output, 1 <= r <= d_k.
+ *   norms   NULL, or fp32 [n_kv_heads][3][d_k] device output: sum_b kn_b,
+ *           sum_b qn_b and the score (a NaN score is reported as -1 and
+ *           ranks last).
+ *   workspace  device scratch of ds_calibrate_workspace_size() bytes.
+ * Errors: DS_ERR_ARG (null pointer, n_tok, n_win, r or criterion out of
+ * range), DS_ERR_SHAPE, DS_ERR_ALIGN (K not 16-byte aligned, stride not a
+ * multiple of 8), DS_ERR_WORKSPACE, DS_ERR_HIP. */
+ds_status ds_calibrate_channels(const ds_kv_desc* kv, const void* K, int32_t n_tok,
+                                const void* qwin, int32_t n_win, const int32_t* keep,
+                                int32_t criterion, int32_t r, int32_t* chan, float* norms,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static text for a status code (never NULL). */
 const char* ds_status_str(ds_status s);

@@ -35,7 +35,8 @@ DECODE_UNFUSED = 4
 DECODE_STREAM = 8
 PATHS = ("dense", "fused", "local", "stream")
 EXPORTS = ("ds_label_build", "ds_label_append", "ds_decode_attn_workspace_size",
-           "ds_decode_attn_plan", "ds_decode_attn", "ds_status_str", "ds_abi_version")
+           "ds_decode_attn_plan", "ds_decode_attn", "ds_calibrate_workspace_size",
+           "ds_calibrate_channels", "ds_status_str", "ds_abi_version")
 
 
 class DsError(RuntimeError):
@@ -93,6 +94,11 @@ def load() -> ctypes.CDLL:
         lib.ds_decode_attn.argtypes = [P, P, P, P, P, I32, P, P, P, I32, ctypes.c_float, P, P, P,
                                        ctypes.c_size_t, P, P]
         lib.ds_decode_attn.restype = ctypes.c_int
+        lib.ds_calibrate_workspace_size.argtypes = [P, I32]
+        lib.ds_calibrate_workspace_size.restype = ctypes.c_size_t
+        lib.ds_calibrate_channels.argtypes = [P, P, I32, P, I32, P, I32, I32, P, P, P,
+                                              ctypes.c_size_t, P]
+        lib.ds_calibrate_channels.restype = ctypes.c_int
         lib.ds_status_str.argtypes = [ctypes.c_int]
         lib.ds_status_str.restype = ctypes.c_char_p
         lib.ds_abi_version.argtypes = []
@@ -197,6 +203,48 @@ def label_append(K, chan, labels: LabelCache, pos, stream=None):
     lab = labels.desc()
     _check("ds_label_append", load().ds_label_append(
         ctypes.byref(kv), _p(K), _p(chan), ctypes.byref(lab), _p(pos), _stream(stream)))
+
+
+CALIB_K, CALIB_Q, CALIB_QK = 0, 1, 2
+CALIB_CRITERIA = {"k": CALIB_K, "q": CALIB_Q, "qk": CALIB_QK}
+
+
+def calibrate_workspace_size(K, n_tok: int) -> int:
+    kv = kv_desc(K, K, 1)
+    return int(load().ds_calibrate_workspace_size(ctypes.byref(kv), int(n_tok)))
+
+
+def calibrate_channels(K, r: int, criterion="qk", qwin=None, keep=None, n_tok: int | None = None,
+                       norms=None, workspace=None, validate_tables: bool = True, stream=None):
+    """Heavy channels per KV head (ds_calibrate_channels; "Double Sparsity",
+    section "offline calibration"; LeanK section 1.1).
+
+    K: fp16 cache [B][Hkv][capacity][d_k]; qwin: fp16 [B][n_win][Hq][d_q]
+    window queries or None; keep: int32 [Hkv][d_k] or None; criterion "k",
+    "q" or "qk".  Returns chan, int32 [Hkv][r] on K's device (ascending
+    columns); fills ``norms`` (fp32 [Hkv][3][d_k]) when given."""
+    import torch
+    crit = CALIB_CRITERIA[criterion] if isinstance(criterion, str) else int(criterion)
+    B, Hkv, cap, d_k = K.shape
+    n_tok = cap if n_tok is None else int(n_tok)
+    if qwin is not None:
+        assert qwin.dtype == torch.float16 and qwin.is_contiguous() and qwin.dim() == 4
+        n_win, Hq, d_q = qwin.shape[1], qwin.shape[2], qwin.shape[3]
+    else:
+        n_win, Hq, d_q = 0, Hkv, d_k
+    if validate_tables and keep is not None:
+        check_tables(None, d_k, keep=keep, d_q=d_q, n_kv_heads=Hkv)
+    kv = kv_desc(K, K, Hq, d_q)
+    need = int(load().ds_calibrate_workspace_size(ctypes.byref(kv), n_tok))
+    if need == 0:
+        raise DsError("ds_calibrate_workspace_size", -2)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=K.device)
+    chan = torch.empty((Hkv, int(r)), dtype=torch.int32, device=K.device)
+    _check("ds_calibrate_channels", load().ds_calibrate_channels(
+        ctypes.byref(kv), _p(K), n_tok, _p(qwin), int(n_win), _p(keep), crit, int(r), _p(chan),
+        _p(norms), _p(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return chan
 
 
 def workspace_size(K, V, n_q_heads, d_q, labels: LabelCache | None, k, max_seq_len) -> int:

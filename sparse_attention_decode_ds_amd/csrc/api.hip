@@ -489,4 +489,53 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
   return DS_OK;
 }
 
+size_t ds_calibrate_workspace_size(const ds_kv_desc* kv, int32_t n_tok) {
+  if (check_kv(kv, false) || n_tok < 0 || n_tok > kv->capacity) return 0;
+  return std::max<size_t>(256, calib_plan(kv->batch, kv->n_kv_heads, n_tok, kv->d_k).part_bytes);
+}
+
+ds_status ds_calibrate_channels(const ds_kv_desc* kv, const void* K, int32_t n_tok,
+                                const void* qwin, int32_t n_win, const int32_t* keep,
+                                int32_t criterion, int32_t r, int32_t* chan, float* norms,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  ds_status st = check_kv(kv, false);
+  if (st) return st;
+  if (n_tok < 0 || n_tok > kv->capacity || n_win < 0) return DS_ERR_ARG;
+  if (criterion < DS_CALIB_K || criterion > DS_CALIB_QK) return DS_ERR_ARG;
+  if (r < 1 || r > kv->d_k || !chan) return DS_ERR_ARG;
+  if (n_tok > 0 && !K) return DS_ERR_ARG;
+  if (n_win > 0) {
+    if (!qwin) return DS_ERR_ARG;
+    if (kv->n_q_heads < 1 || kv->n_q_heads % kv->n_kv_heads) return DS_ERR_SHAPE;
+    if (kv->d_q < 1 || kv->d_q > 256) return DS_ERR_SHAPE;
+    if (!keep && kv->d_k > kv->d_q) return DS_ERR_SHAPE;
+  }
+  if (K && !aligned16(K)) return DS_ERR_ALIGN;
+  const CalibPlan pl = calib_plan(kv->batch, kv->n_kv_heads, n_tok, kv->d_k);
+  if (pl.part_bytes > 0 && (!workspace || workspace_bytes < pl.part_bytes)) return DS_ERR_WORKSPACE;
+  if (pl.blocks > INT32_MAX) return DS_ERR_SHAPE;
+  CalibArgs a{};
+  a.K = static_cast<const __half*>(K);
+  a.ks0 = kv->k_stride[0];
+  a.ks1 = kv->k_stride[1];
+  a.ks2 = kv->k_stride[2];
+  a.B = kv->batch;
+  a.Hkv = kv->n_kv_heads;
+  a.d_k = kv->d_k;
+  a.n_tok = n_tok;
+  a.n_cpr = pl.n_cpr;
+  a.chunk = pl.chunk;
+  a.part = static_cast<float*>(workspace);
+  a.q = static_cast<const __half*>(qwin);
+  a.n_win = n_win;
+  a.Hq = n_win > 0 ? kv->n_q_heads : kv->n_kv_heads;
+  a.d_q = n_win > 0 ? kv->d_q : kv->d_k;
+  a.keep = keep;
+  a.criterion = criterion;
+  a.r = r;
+  a.chan = chan;
+  a.norms = norms;
+  return launch_calib(a, pl.blocks, stream) == hipSuccess ? DS_OK : DS_ERR_HIP;
+}
+
 }  // extern "C"

@@ -124,8 +124,31 @@ inline hipError_t launch_k(F kernel, dim3 grid, dim3 block, hipStream_t s, const
   return hipGetLastError();
 }
 
+// Heavy-channel calibration ([DS] "offline calibration"; [LeanK] section 1.1).
+constexpr int kMaxDk = 128;  // stored K columns at most
+struct CalibArgs {
+  const __half* K;
+  int64_t ks0, ks1, ks2;
+  int B, Hkv, d_k, n_tok;
+  int n_cpr, chunk;  // token chunks per (KV head, sample) and tokens per chunk
+  float* part;       // [Hkv][B][n_cpr][d_k] column sums of squares per chunk
+  const __half* q;   // [B][n_win][Hq][d_q] window queries
+  int n_win, Hq, d_q;
+  const int32_t* keep;  // [Hkv][d_k] or null
+  int criterion, r;
+  int32_t* chan;  // [Hkv][r]
+  float* norms;   // [Hkv][3][d_k] or null
+};
+struct CalibPlan {
+  int n_cpr = 0, chunk = 0;
+  int64_t blocks = 0;
+  size_t part_bytes = 0;
+};
+CalibPlan calib_plan(int B, int Hkv, int n_tok, int d_k);
+
 // Launchers (return the launch status of the last kernel they enqueue).
 hipError_t launch_label(const LabelArgs& a, int n_blocks, hipStream_t s);
+hipError_t launch_calib(const CalibArgs& a, int64_t blocks, hipStream_t s);
 hipError_t launch_score_chunks(const ScoreArgs& a, int rows, hipStream_t s);
 hipError_t launch_select_stream(const ScoreArgs& a, int rows, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int rows, int G, bool final_out, hipStream_t s,

@@ -32,7 +32,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ds_abi_version() == 1
+    assert lib.ds_abi_version() == 2
     for code in range(0, -7, -1):
         s = lib.ds_status_str(code).decode()
         assert s and s != "unknown status"
@@ -251,3 +251,39 @@ def test_one_kernel_path_bounds(lib, G, max_seq, path):
     # k beyond the LDS token list (2048) leaves the one-kernel path
     rc, pl = _plan(lib, kv, _lab(slots=cap), 2049, max_seq)
     assert rc == 0 and ds.PATHS[pl.path] != "fused"
+
+
+def test_calibrate_workspace_and_argument_errors(lib):
+    """Host-side checks of ds_calibrate_channels: every case returns before
+    anything is enqueued, so no GPU is needed."""
+    P = ctypes.c_void_p
+    kv = _kv()
+    need = lib.ds_calibrate_workspace_size(ctypes.byref(kv), 900)
+    assert need >= 2 * 4 * 128 * 4 and need % 4 == 0
+    assert lib.ds_calibrate_workspace_size(ctypes.byref(kv), 0) == 256
+    assert lib.ds_calibrate_workspace_size(ctypes.byref(kv), 1001) == 0
+    assert lib.ds_calibrate_workspace_size(ctypes.byref(_kv(d_k=12)), 10) == 0
+
+    def call(kv=kv, K=FAKE, n_tok=900, q=FAKE, n_win=4, keep=None, crit=2, r=16, chan=FAKE,
+             ws=FAKE, ws_bytes=need):
+        return lib.ds_calibrate_channels(ctypes.byref(kv), P(K), n_tok, P(q), n_win,
+                                         P(keep) if keep else None, crit, r, P(chan), None,
+                                         P(ws) if ws else None, ws_bytes, None)
+
+    assert call(r=0) == -1
+    assert call(r=129) == -1
+    assert call(crit=3) == -1
+    assert call(crit=-1) == -1
+    assert call(n_tok=1001) == -1
+    assert call(n_tok=-1) == -1
+    assert call(n_win=-1) == -1
+    assert call(chan=0) == -1
+    assert call(q=0) == -1
+    assert call(K=0) == -1
+    assert call(K=FAKE + 8) == -4
+    assert call(ws=0) == -5
+    assert call(ws_bytes=need - 4) == -5
+    assert call(kv=_kv(n_q_heads=30)) == -2
+    assert call(kv=_kv(d_q=64)) == -2  # no keep table and d_k > d_q
+    assert call(kv=_kv(d_k=12)) == -2
+    assert call(kv=_kv(k_stride=(4 * 1000 * 128, 1000 * 128, 132))) == -4

@@ -1,0 +1,148 @@
+"""GPU parity of heavy-channel calibration (ds_calibrate_channels) against the
+oracle ("Double Sparsity", section "offline calibration"; LeanK section 1.1).
+
+Norms are fp32 sums on the GPU and fp64 in the oracle: relative error within
+1e-5 (at most ~2^-24 per addition over sums of non-negative terms, with
+partial sums of at most a few thousand terms).  The chosen columns must equal
+the oracle's, except that columns whose oracle scores lie within 1e-5
+(relative) of the r-th largest may trade places."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+ds = pytest.importorskip("sparse_attention_decode_ds_amd")
+CRIT = {"k": oracle.CALIB_K, "q": oracle.CALIB_Q, "qk": oracle.CALIB_QK}
+RTOL = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ds.load()
+    yield
+    torch.cuda.empty_cache()
+
+
+def _inputs(seed, B, Hkv, G, cap, d_k, W, d_q=None, keep=False, outliers=()):
+    g = torch.Generator().manual_seed(seed)
+    d_q = d_q or d_k
+    K = torch.randn((B, Hkv, cap, d_k), generator=g)
+    q = torch.randn((B, W, Hkv * G, d_q), generator=g)
+    for c, fk, fq in outliers:
+        K[..., c] *= fk
+        q[..., c] *= fq
+    kp = None
+    if keep:
+        kp = torch.stack([torch.randperm(d_q, generator=g)[:d_k].sort().values for _ in range(Hkv)])
+        kp = kp.to(torch.int32)
+    return K.half(), q.half(), kp
+
+
+def _check(K, q, keep, crit, r, n_tok=None, note=""):
+    print("calib %s crit=%s r=%d K=%s q=%s keep=%s n_tok=%s" % (
+        note, crit, r, tuple(K.shape), None if q is None else tuple(q.shape), keep is not None,
+        n_tok), flush=True)
+    Hkv, d_k = K.shape[1], K.shape[3]
+    Kd = K.cuda()
+    qd = q.cuda() if q is not None else None
+    kd = keep.cuda() if keep is not None else None
+    norms = torch.full((Hkv, 3, d_k), float("nan"), device="cuda")
+    chan = ds.calibrate_channels(Kd, r, crit, qwin=qd, keep=kd, n_tok=n_tok, norms=norms)
+    torch.cuda.synchronize()
+    ch_o, nr_o = oracle.calibrate(K.numpy(), CRIT[crit], r,
+                                  qwin=q.numpy() if q is not None else None,
+                                  keep=keep.numpy() if keep is not None else None, n_tok=n_tok)
+    nr = norms.cpu().double().numpy()
+    np.testing.assert_allclose(nr, nr_o, rtol=RTOL, atol=1e-30)
+    ch = chan.cpu().numpy()
+    for gg in range(Hkv):
+        got = ch[gg].tolist()
+        assert got == sorted(set(got)) and len(got) == r, got
+        if got == ch_o[gg].tolist():
+            continue
+        s = nr_o[gg, 2]
+        kth = np.sort(s)[::-1][r - 1]
+        for c in set(got) ^ set(ch_o[gg].tolist()):
+            assert abs(s[c] - kth) <= RTOL * abs(kth), (gg, c, s[c], kth)
+    return chan, norms
+
+
+@pytest.mark.parametrize("crit", ["k", "q", "qk"])
+@pytest.mark.parametrize("shape", [
+    dict(B=1, Hkv=2, G=1, cap=300, d_k=128, W=4),
+    dict(B=3, Hkv=4, G=7, cap=1111, d_k=128, W=16),
+    dict(B=2, Hkv=3, G=2, cap=257, d_k=32, W=5, d_q=128, keep=True),
+    dict(B=2, Hkv=2, G=4, cap=70, d_k=24, W=3, d_q=64, keep=True),
+])
+def test_calibrate_matches_oracle(crit, shape):
+    K, q, keep = _inputs(11, **shape)
+    _check(K, q, keep, crit, r=min(16, shape["d_k"]), note=str(shape))
+
+
+@pytest.mark.parametrize("r", [1, 7, 32, 128])
+def test_calibrate_r_range(r):
+    K, q, _ = _inputs(12, B=2, Hkv=4, G=2, cap=600, d_k=128, W=8)
+    _check(K, q, None, "qk", r)
+
+
+def test_calibrate_planted_outliers_exact():
+    K, q, _ = _inputs(13, B=2, Hkv=8, G=4, cap=2048, d_k=128, W=32,
+                      outliers=[(3, 6.0, 0.05), (40, 0.05, 6.0), (77, 3.0, 3.0), (101, 2.5, 2.5)])
+    for crit, want in (("k", 3), ("q", 40), ("qk", 77)):
+        chan, _ = _check(K, q, None, crit, 1)
+        assert chan.cpu().tolist() == [[want]] * 8
+    chan, _ = _check(K, q, None, "qk", 2)
+    assert chan.cpu().tolist() == [[77, 101]] * 8
+
+
+def test_calibrate_token_prefix_and_strided_cache():
+    # the sample is the first n_tok tokens of a larger cache viewed with strides
+    K, q, _ = _inputs(14, B=2, Hkv=4, G=2, cap=900, d_k=128, W=4)
+    big = torch.zeros((2, 4, 1000, 128), dtype=torch.float16)
+    big[:, :, :900] = K
+    big[:, :, 500:, 9] = 30.0  # past n_tok: must not count
+    _check(big, q, None, "k", 8, n_tok=500, note="prefix")
+    perm = K.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)  # token-major layout
+    _check(perm, q, None, "qk", 8, note="strided")
+
+
+def test_calibrate_degenerate_inputs():
+    K, q, _ = _inputs(15, B=1, Hkv=2, G=2, cap=64, d_k=64, W=2)
+    chan, norms = _check(K, q, None, "k", 5, n_tok=0, note="no tokens")
+    assert chan.cpu().tolist() == [[0, 1, 2, 3, 4]] * 2
+    assert float(norms[:, 0].abs().max()) == 0.0
+    chan, _ = _check(K, None, None, "q", 3, note="no window")
+    assert chan.cpu().tolist() == [[0, 1, 2]] * 2
+    ones = torch.ones((1, 2, 64, 64), dtype=torch.float16)
+    chan, _ = _check(ones, q, None, "k", 4, note="all columns equal")
+    assert chan.cpu().tolist() == [[0, 1, 2, 3]] * 2
+
+
+def test_calibrate_repeats_bit_for_bit_and_feeds_the_label_build():
+    K, q, _ = _inputs(16, B=4, Hkv=8, G=4, cap=4096, d_k=128, W=64)
+    Kd, qd = K.cuda(), q.cuda()
+    n1 = torch.empty((8, 3, 128), device="cuda")
+    n2 = torch.empty_like(n1)
+    c1 = ds.calibrate_channels(Kd, 16, "qk", qwin=qd, norms=n1)
+    c2 = ds.calibrate_channels(Kd, 16, "qk", qwin=qd, norms=n2)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2) and torch.equal(n1, n2)
+    ds.check_tables(c1, 128, 16, n_kv_heads=8)
+    labels = ds.LabelCache.allocate(4, 8, 4096, 16, False)
+    ds.label_build(Kd, c1, labels, 0, 4096)
+    torch.cuda.synchronize()
+    idx = c1.long().cpu()
+    want = torch.stack([K[:, g][:, :, idx[g]] for g in range(8)], dim=1)  # [B][Hkv][tok][r]
+    assert torch.equal(labels.codes[:, :, :4096].cpu(), want)
+
+
+def test_calibrate_full_size_layer():
+    # Llama-2-7B-shaped layer sample: 4 sequences x 32 KV heads x 4096 tokens,
+    # a 64-query observation window (the calibration workload of the bench)
+    K, q, _ = _inputs(17, B=4, Hkv=32, G=1, cap=4096, d_k=128, W=64)
+    _check(K, q, None, "qk", 16, note="full size")
