@@ -214,6 +214,94 @@ def cpu_baseline(cfg, inp, seconds):
                       % (n_b, cfg.B, cfg.Hkv, S, reps, el)}
 
 
+CALIB = dict(name="calib_llama2_7b_4k", B=4, Hkv=32, Hq=32, N=4096, D=128, W=64, r=16,
+             criterion="qk",
+             note="heavy-channel calibration of one Llama-2-7B-shaped layer: 4 sample sequences "
+                  "of 4096 tokens, 32 KV heads, a 64-query observation window, QK-outlier, r 16")
+
+
+def run_calibration(args):
+    """Times ds_calibrate_channels on the calibration workload: K of one layer's
+    samples and the window queries already in HBM, a rotation of K copies that
+    moves well over the Infinity Cache, HIP events on the call's stream."""
+    import torch
+
+    import oracle
+    import sparse_attention_decode_ds_amd as ds
+
+    c = CALIB
+    torch.cuda.set_device(0)
+    ds.load()
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    B, Hkv, N, D, W = c["B"], c["Hkv"], c["N"], c["D"], c["W"]
+    k_bytes = B * Hkv * N * D * 2
+    L = max(2, int(math.ceil(1.5e9 / k_bytes)))
+    Ks = [torch.randn((B, Hkv, N, D), generator=g, device="cuda").half() for _ in range(L)]
+    q = torch.randn((B, W, c["Hq"], D), generator=g, device="cuda").half()
+    need = ds.calibrate_workspace_size(Ks[0], N, q)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    norms = torch.empty((Hkv, 3, D), device="cuda")
+    print("bench: calibration workload %s, %d K copies" % (c["name"], L), flush=True)
+
+    def call(i):
+        return ds.calibrate_channels(Ks[i % L], c["r"], c["criterion"], qwin=q, norms=norms,
+                                     workspace=ws, validate_tables=False)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record()
+        call(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    call_ms = [a.elapsed_time(b) for a, b in ev]
+    call_mean = sum(call_ms) / len(call_ms)
+    alg = k_bytes + q.numel() * 2 + Hkv * c["r"] * 4 + norms.numel() * 4
+    achieved = alg / (call_mean * 1e-3) / 1e9
+    result = {
+        "metric": "heavy-channel calibration layers/s + achieved HBM GB/s",
+        "value": round(1e3 / ms, 1), "unit": "layers/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": c["name"], "samples": B, "kv_heads": Hkv, "tokens": N,
+                   "head_dim": D, "window": W, "r": c["r"], "criterion": c["criterion"],
+                   "k_copies": L, "note": c["note"]},
+        "roofline": {"bound": "hbm", "kernel": "k_calib_cols + k_calib_select",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": alg,
+                     "avg_launch_us": round(call_mean * 1e3, 3),
+                     "launch_us_p50_p90": pct_us(call_ms),
+                     "timing": "torch events on the call's stream around each call (both "
+                               "kernels), in a second pass of the same %d calls" % args.steps},
+    }
+    if not args.no_cpu_baseline:
+        # the oracle on a bounded sample: one sequence and four KV heads
+        Kc = Ks[0][:1, :4].cpu().numpy()
+        qc = q[:1, :, :4].cpu().numpy()
+        n, t1 = 0, time.perf_counter()
+        while True:
+            oracle.calibrate(Kc, oracle.CALIB_QK, c["r"], qwin=qc)
+            n += 1
+            if time.perf_counter() - t1 > min(args.cpu_seconds, 10.0):
+                break
+        per = (time.perf_counter() - t1) / n * (B * Hkv / 4)
+        result["cpu_baseline"] = {"value": round(1.0 / per, 3), "unit": "layers/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": "1 of 4 sequences x 4 of 32 KV heads, %d calls, "
+                                            "scaled by 32" % n}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,6 +326,9 @@ def main():
     ap.add_argument("--traffic-kernel", default="k_decode_fused")
     ap.add_argument("--traffic-cmd", action="append", help="command recorded with the counters")
     ap.add_argument("--traffic-out", default=None, help="record path (default: under profiles/)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="time heavy-channel calibration (%s) instead of the decode step" %
+                         CALIB["name"])
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -248,6 +339,8 @@ def main():
         return 2
     if args.traffic_from:
         return write_traffic(args)
+    if args.calibrate:
+        return run_calibration(args)
 
     import torch
 

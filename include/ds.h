@@ -240,8 +240,9 @@ ds_status ds_decode_attn_plan(const ds_kv_desc* kv, const ds_label_desc* lab, in
 typedef enum { DS_CALIB_K = 0, DS_CALIB_Q = 1, DS_CALIB_QK = 2 } ds_calib_criterion;
 
 /* Workspace bytes that ds_calibrate_channels needs for kv's batch, KV heads
- * and d_k and n_tok sample tokens (0 if the arguments are invalid). */
-size_t ds_calibrate_workspace_size(const ds_kv_desc* kv, int32_t n_tok);
+ * and d_k (and n_q_heads when n_win > 0), n_tok sample tokens and n_win
+ * window queries (0 if the arguments are invalid). */
+size_t ds_calibrate_workspace_size(const ds_kv_desc* kv, int32_t n_tok, int32_t n_win);
 
 /* Heavy-channel calibration ([DS] offline calibration: the channels that
  * move the attention scores most are chosen once from a few samples;

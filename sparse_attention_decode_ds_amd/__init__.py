@@ -94,7 +94,7 @@ def load() -> ctypes.CDLL:
         lib.ds_decode_attn.argtypes = [P, P, P, P, P, I32, P, P, P, I32, ctypes.c_float, P, P, P,
                                        ctypes.c_size_t, P, P]
         lib.ds_decode_attn.restype = ctypes.c_int
-        lib.ds_calibrate_workspace_size.argtypes = [P, I32]
+        lib.ds_calibrate_workspace_size.argtypes = [P, I32, I32]
         lib.ds_calibrate_workspace_size.restype = ctypes.c_size_t
         lib.ds_calibrate_channels.argtypes = [P, P, I32, P, I32, P, I32, I32, P, P, P,
                                               ctypes.c_size_t, P]
@@ -209,9 +209,11 @@ CALIB_K, CALIB_Q, CALIB_QK = 0, 1, 2
 CALIB_CRITERIA = {"k": CALIB_K, "q": CALIB_Q, "qk": CALIB_QK}
 
 
-def calibrate_workspace_size(K, n_tok: int) -> int:
-    kv = kv_desc(K, K, 1)
-    return int(load().ds_calibrate_workspace_size(ctypes.byref(kv), int(n_tok)))
+def calibrate_workspace_size(K, n_tok: int, qwin=None) -> int:
+    n_win, Hq, d_q = (qwin.shape[1], qwin.shape[2], qwin.shape[3]) if qwin is not None else (
+        0, K.shape[1], K.shape[3])
+    kv = kv_desc(K, K, Hq, d_q)
+    return int(load().ds_calibrate_workspace_size(ctypes.byref(kv), int(n_tok), int(n_win)))
 
 
 def calibrate_channels(K, r: int, criterion="qk", qwin=None, keep=None, n_tok: int | None = None,
@@ -235,7 +237,7 @@ def calibrate_channels(K, r: int, criterion="qk", qwin=None, keep=None, n_tok: i
     if validate_tables and keep is not None:
         check_tables(None, d_k, keep=keep, d_q=d_q, n_kv_heads=Hkv)
     kv = kv_desc(K, K, Hq, d_q)
-    need = int(load().ds_calibrate_workspace_size(ctypes.byref(kv), n_tok))
+    need = int(load().ds_calibrate_workspace_size(ctypes.byref(kv), n_tok, int(n_win)))
     if need == 0:
         raise DsError("ds_calibrate_workspace_size", -2)
     if workspace is None:

@@ -489,9 +489,12 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
   return DS_OK;
 }
 
-size_t ds_calibrate_workspace_size(const ds_kv_desc* kv, int32_t n_tok) {
-  if (check_kv(kv, false) || n_tok < 0 || n_tok > kv->capacity) return 0;
-  return std::max<size_t>(256, calib_plan(kv->batch, kv->n_kv_heads, n_tok, kv->d_k).part_bytes);
+size_t ds_calibrate_workspace_size(const ds_kv_desc* kv, int32_t n_tok, int32_t n_win) {
+  if (check_kv(kv, false) || n_tok < 0 || n_tok > kv->capacity || n_win < 0) return 0;
+  if (n_win > 0 && (kv->n_q_heads < 1 || kv->n_q_heads % kv->n_kv_heads)) return 0;
+  const int G = n_win > 0 ? kv->n_q_heads / kv->n_kv_heads : 1;
+  const CalibPlan pl = calib_plan(kv->batch, kv->n_kv_heads, n_tok, kv->d_k, n_win * G);
+  return std::max<size_t>(256, pl.ws_bytes);
 }
 
 ds_status ds_calibrate_channels(const ds_kv_desc* kv, const void* K, int32_t n_tok,
@@ -511,8 +514,10 @@ ds_status ds_calibrate_channels(const ds_kv_desc* kv, const void* K, int32_t n_t
     if (!keep && kv->d_k > kv->d_q) return DS_ERR_SHAPE;
   }
   if (K && !aligned16(K)) return DS_ERR_ALIGN;
-  const CalibPlan pl = calib_plan(kv->batch, kv->n_kv_heads, n_tok, kv->d_k);
-  if (pl.part_bytes > 0 && (!workspace || workspace_bytes < pl.part_bytes)) return DS_ERR_WORKSPACE;
+  const int G = n_win > 0 ? kv->n_q_heads / kv->n_kv_heads : 1;
+  if ((int64_t)n_win * G > INT32_MAX / 2) return DS_ERR_SHAPE;
+  const CalibPlan pl = calib_plan(kv->batch, kv->n_kv_heads, n_tok, kv->d_k, n_win * G);
+  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return DS_ERR_WORKSPACE;
   if (pl.blocks > INT32_MAX) return DS_ERR_SHAPE;
   CalibArgs a{};
   a.K = static_cast<const __half*>(K);
@@ -526,6 +531,9 @@ ds_status ds_calibrate_channels(const ds_kv_desc* kv, const void* K, int32_t n_t
   a.n_cpr = pl.n_cpr;
   a.chunk = pl.chunk;
   a.part = static_cast<float*>(workspace);
+  a.qpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.qpart_off);
+  a.n_qch = pl.n_qch;
+  a.q_blocks = (int)pl.q_blocks;
   a.q = static_cast<const __half*>(qwin);
   a.n_win = n_win;
   a.Hq = n_win > 0 ? kv->n_q_heads : kv->n_kv_heads;

@@ -126,12 +126,15 @@ inline hipError_t launch_k(F kernel, dim3 grid, dim3 block, hipStream_t s, const
 
 // Heavy-channel calibration ([DS] "offline calibration"; [LeanK] section 1.1).
 constexpr int kMaxDk = 128;  // stored K columns at most
+constexpr int kQRows = 32;   // window-query rows per calibration workgroup
 struct CalibArgs {
   const __half* K;
   int64_t ks0, ks1, ks2;
   int B, Hkv, d_k, n_tok;
   int n_cpr, chunk;  // token chunks per (KV head, sample) and tokens per chunk
   float* part;       // [Hkv][B][n_cpr][d_k] column sums of squares per chunk
+  float* qpart;      // [Hkv][B][n_qch][d_k] the same over window-query rows
+  int n_qch, q_blocks;
   const __half* q;   // [B][n_win][Hq][d_q] window queries
   int n_win, Hq, d_q;
   const int32_t* keep;  // [Hkv][d_k] or null
@@ -140,11 +143,11 @@ struct CalibArgs {
   float* norms;   // [Hkv][3][d_k] or null
 };
 struct CalibPlan {
-  int n_cpr = 0, chunk = 0;
-  int64_t blocks = 0;
-  size_t part_bytes = 0;
+  int n_cpr = 0, chunk = 0, n_qch = 0;
+  int64_t blocks = 0, q_blocks = 0;  // all workgroups; the window-query ones first
+  size_t part_bytes = 0, qpart_off = 0, ws_bytes = 0;
 };
-CalibPlan calib_plan(int B, int Hkv, int n_tok, int d_k);
+CalibPlan calib_plan(int B, int Hkv, int n_tok, int d_k, int n_qrows);
 
 // Launchers (return the launch status of the last kernel they enqueue).
 hipError_t launch_label(const LabelArgs& a, int n_blocks, hipStream_t s);

@@ -258,11 +258,14 @@ def test_calibrate_workspace_and_argument_errors(lib):
     anything is enqueued, so no GPU is needed."""
     P = ctypes.c_void_p
     kv = _kv()
-    need = lib.ds_calibrate_workspace_size(ctypes.byref(kv), 900)
-    assert need >= 2 * 4 * 128 * 4 and need % 4 == 0
-    assert lib.ds_calibrate_workspace_size(ctypes.byref(kv), 0) == 256
-    assert lib.ds_calibrate_workspace_size(ctypes.byref(kv), 1001) == 0
-    assert lib.ds_calibrate_workspace_size(ctypes.byref(_kv(d_k=12)), 10) == 0
+    need = lib.ds_calibrate_workspace_size(ctypes.byref(kv), 900, 4)
+    assert need >= 2 * 4 * 128 * 4 * 2 and need % 4 == 0
+    assert lib.ds_calibrate_workspace_size(ctypes.byref(kv), 0, 0) == 256
+    assert lib.ds_calibrate_workspace_size(ctypes.byref(kv), 0, 4) > 256
+    assert lib.ds_calibrate_workspace_size(ctypes.byref(kv), 1001, 4) == 0
+    assert lib.ds_calibrate_workspace_size(ctypes.byref(kv), 900, -1) == 0
+    assert lib.ds_calibrate_workspace_size(ctypes.byref(_kv(n_q_heads=30)), 900, 4) == 0
+    assert lib.ds_calibrate_workspace_size(ctypes.byref(_kv(d_k=12)), 10, 0) == 0
 
     def call(kv=kv, K=FAKE, n_tok=900, q=FAKE, n_win=4, keep=None, crit=2, r=16, chan=FAKE,
              ws=FAKE, ws_bytes=need):

@@ -78,6 +78,7 @@ def _check(K, q, keep, crit, r, n_tok=None, note=""):
     dict(B=3, Hkv=4, G=7, cap=1111, d_k=128, W=16),
     dict(B=2, Hkv=3, G=2, cap=257, d_k=32, W=5, d_q=128, keep=True),
     dict(B=2, Hkv=2, G=4, cap=70, d_k=24, W=3, d_q=64, keep=True),
+    dict(B=9, Hkv=2, G=3, cap=200, d_k=64, W=7),  # samples in three rounds of four
 ])
 def test_calibrate_matches_oracle(crit, shape):
     K, q, keep = _inputs(11, **shape)
