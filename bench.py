@@ -146,7 +146,7 @@ def write_traffic(args):
     import sparse_attention_decode_ds_amd as ds
     import synth
     fetch_csv, write_csv = args.traffic_from
-    cfg = synth.CONFIGS[args.workload]
+    name = synth.CONFIGS[args.workload].name if args.workload in synth.CONFIGS else args.workload
     kern = args.traffic_kernel
     calib_kib = args.calib_copy_mb * 1024.0
     cf, ncf = _pmc_mean(fetch_csv, "FETCH_SIZE", "neg_kernel")
@@ -158,7 +158,7 @@ def write_traffic(args):
               file=sys.stderr)
         return 1
     f_fetch, f_write = calib_kib / cf, calib_kib / cw
-    rec = {"workload": cfg.name, "kernel": kern, "source_hash": source_hash(),
+    rec = {"workload": name, "kernel": kern, "source_hash": source_hash(),
            "fetch_kib_per_launch": round(kf, 1), "write_kib_per_launch": round(kw, 1),
            "dispatches": [nkf, nkw],
            "calibration": {"copy_mib": args.calib_copy_mb, "fetch_kib": round(cf, 1),
@@ -166,7 +166,7 @@ def write_traffic(args):
                            "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4)},
            "bytes_per_launch": int(round((kf * f_fetch + kw * f_write) * 1024.0)),
            "commands": args.traffic_cmd or []}
-    dst = args.traffic_out or traffic_path(cfg.name)
+    dst = args.traffic_out or traffic_path(name)
     os.makedirs(os.path.dirname(os.path.abspath(dst)), exist_ok=True)
     with open(dst, "w") as f:
         json.dump(rec, f, indent=1)
@@ -214,6 +214,18 @@ def cpu_baseline(cfg, inp, seconds):
                       % (n_b, cfg.B, cfg.Hkv, S, reps, el)}
 
 
+def counter_reference_copy(torch, mib):
+    """A plain streaming kernel of known size (reads and writes mib MiB, five
+    times), the reference for the HBM byte counters."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 CALIB = dict(name="calib_llama2_7b_4k", B=4, Hkv=32, Hq=32, N=4096, D=128, W=64, r=16,
              criterion="qk",
              note="heavy-channel calibration of one Llama-2-7B-shaped layer: 4 sample sequences "
@@ -232,6 +244,8 @@ def run_calibration(args):
     c = CALIB
     torch.cuda.set_device(0)
     ds.load()
+    if args.calib_copy_mb > 0:
+        counter_reference_copy(torch, args.calib_copy_mb)
     g = torch.Generator(device="cuda").manual_seed(1234)
     B, Hkv, N, D, W = c["B"], c["Hkv"], c["N"], c["D"], c["W"]
     k_bytes = B * Hkv * N * D * 2
@@ -276,7 +290,9 @@ def run_calibration(args):
                    "k_copies": L, "note": c["note"]},
         "roofline": {"bound": "hbm", "kernel": "k_calib_cols + k_calib_select",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": stored_traffic(c["name"], "k_calib_cols"),
+                     "traffic_kernel": "k_calib_cols",
                      "algorithmic_bytes_per_launch": alg,
                      "avg_launch_us": round(call_mean * 1e3, 3),
                      "launch_us_p50_p90": pct_us(call_ms),
@@ -358,15 +374,7 @@ def main():
     L = args.layers if args.layers > 0 else max(2, min(8, int(math.ceil(1.5e9 / step0))))
 
     if args.calib_copy_mb > 0:
-        # A plain streaming kernel of known size (reads and writes n bytes),
-        # the reference for the HBM byte counters.
-        n = args.calib_copy_mb * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        counter_reference_copy(torch, args.calib_copy_mb)
 
     print("bench: workload %s (%s), %d layer caches" % (cfg.name, cfg.note, L), flush=True)
     inp = synth.make_inputs(cfg, dev)
