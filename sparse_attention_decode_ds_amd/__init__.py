@@ -249,6 +249,19 @@ def calibrate_channels(K, r: int, criterion="qk", qwin=None, keep=None, n_tok: i
     return chan
 
 
+def channel_overlap(chan_a, chan_b):
+    """Per KV head, the fraction of heavy channels two tables share: the check
+    of offline-calibrated channels against those found online at decode time
+    ("Double Sparsity", section "offline calibration").  Host computation on
+    [H_kv][r] tables (copies them to the host); returns a list of floats."""
+    a = chan_a.detach().to("cpu", torch.int64) if hasattr(chan_a, "detach") else torch.as_tensor(chan_a)
+    b = chan_b.detach().to("cpu", torch.int64) if hasattr(chan_b, "detach") else torch.as_tensor(chan_b)
+    if a.dim() != 2 or a.shape != b.shape or a.shape[1] == 0:
+        raise ValueError("channel_overlap: two [n_kv_heads][r] tables of one shape expected")
+    r = a.shape[1]
+    return [len(set(a[g].tolist()) & set(b[g].tolist())) / r for g in range(a.shape[0])]
+
+
 def workspace_size(K, V, n_q_heads, d_q, labels: LabelCache | None, k, max_seq_len) -> int:
     kv = kv_desc(K, V, n_q_heads, d_q)
     lab = labels.desc() if labels is not None else None

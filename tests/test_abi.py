@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ds = pytest.importorskip("sparse_attention_decode_ds_amd")
@@ -290,3 +291,13 @@ def test_calibrate_workspace_and_argument_errors(lib):
     assert call(kv=_kv(d_q=64)) == -2  # no keep table and d_k > d_q
     assert call(kv=_kv(d_k=12)) == -2
     assert call(kv=_kv(k_stride=(4 * 1000 * 128, 1000 * 128, 132))) == -4
+
+
+def test_channel_overlap_host_logic():
+    a = torch.tensor([[0, 1, 2, 3], [4, 5, 6, 7]], dtype=torch.int32)
+    b = torch.tensor([[3, 2, 9, 8], [4, 5, 6, 7]], dtype=torch.int32)
+    assert ds.channel_overlap(a, b) == [0.5, 1.0]
+    assert ds.channel_overlap(a, a) == [1.0, 1.0]
+    assert ds.channel_overlap([[1, 2]], [[3, 4]]) == [0.0]
+    with pytest.raises(ValueError):
+        ds.channel_overlap(a, b[:, :2])

@@ -147,3 +147,28 @@ def test_calibrate_full_size_layer():
     # a 64-query observation window (the calibration workload of the bench)
     K, q, _ = _inputs(17, B=4, Hkv=32, G=1, cap=4096, d_k=128, W=64)
     _check(K, q, None, "qk", 16, note="full size")
+
+
+def test_offline_and_online_channels_overlap_on_static_outliers():
+    # Synthetic heads whose heavy channels are static (a fixed quarter of the
+    # columns carries 3x larger q and K): channels calibrated offline on sample
+    # sequences agree with those found online from one decode query and its
+    # own row, as the pages report for real models at r/d = 0.25.
+    g = torch.Generator().manual_seed(18)
+    Hkv, G, d, r = 4, 2, 128, 32
+    heavy = torch.stack([torch.randperm(d, generator=g)[:r] for _ in range(Hkv)])
+    def sample(B, N, W):
+        K = torch.randn((B, Hkv, N, d), generator=g)
+        q = torch.randn((B, W, Hkv * G, d), generator=g)
+        for h in range(Hkv):
+            K[:, h, :, heavy[h]] *= 3.0
+            q[:, :, h * G:(h + 1) * G, heavy[h]] *= 3.0
+        return K.half().cuda(), q.half().cuda()
+    Ks, qs = sample(4, 1024, 16)
+    off = ds.calibrate_channels(Ks, r, "qk", qwin=qs)
+    Kd, qd = sample(1, 2048, 1)
+    on = ds.calibrate_channels(Kd, r, "qk", qwin=qd)
+    torch.cuda.synchronize()
+    want = heavy.sort(dim=1).values.to(torch.int32)
+    assert torch.equal(off.cpu(), want)
+    assert min(ds.channel_overlap(off, on)) >= 0.9
