@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 METRIC = "sparse decode-attn queries/s + achieved HBM GB/s, Llama-2-7B-shaped @4K–128K"
 HBM_PEAK_GBS = 8000.0
+HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction
 
 
 def algorithmic_bytes(cfg, S):
@@ -342,6 +343,8 @@ def main():
     ap.add_argument("--traffic-kernel", default="k_decode_fused")
     ap.add_argument("--traffic-cmd", action="append", help="command recorded with the counters")
     ap.add_argument("--traffic-out", default=None, help="record path (default: under profiles/)")
+    ap.add_argument("--offload", action="store_true",
+                    help="K/V in pinned host memory, read over the host link (labels in HBM)")
     ap.add_argument("--calibrate", action="store_true",
                     help="time heavy-channel calibration (%s) instead of the decode step" %
                          CALIB["name"])
@@ -372,6 +375,8 @@ def main():
     # Infinity Cache (about 1.5 GB of step bytes), 2 to 8 copies.
     step0 = sum(algorithmic_bytes(cfg, cfg.S0 + 1).values())
     L = args.layers if args.layers > 0 else max(2, min(8, int(math.ceil(1.5e9 / step0))))
+    if args.offload:
+        L = 1  # one K/V copy in pinned host memory; host reads never sit in the Infinity Cache
 
     if args.calib_copy_mb > 0:
         counter_reference_copy(torch, args.calib_copy_mb)
@@ -389,6 +394,18 @@ def main():
             labs.append(lab)
         else:
             labs.append(None)
+    if args.offload:
+        # K and V in pinned host memory (mapped into the GPU's address space);
+        # the labels and everything else stay in HBM
+        Ks = [torch.empty(inp.K.shape, dtype=inp.K.dtype, pin_memory=True)]
+        Vs = [torch.empty(inp.V.shape, dtype=inp.V.dtype, pin_memory=True)]
+        Ks[0].copy_(inp.K)
+        Vs[0].copy_(inp.V)
+        hip = ctypes.CDLL("libamdhip64.so")
+        for t in (Ks[0], Vs[0]):
+            dptr = ctypes.c_void_p()
+            rc = hip.hipHostGetDevicePointer(ctypes.byref(dptr), ctypes.c_void_p(t.data_ptr()), 0)
+            assert rc == 0 and dptr.value == t.data_ptr(), "pinned memory not mapped for the GPU"
     n_q = 16
     qs = [synth.make_q(cfg, dev, s) for s in range(n_q)]
     seqs = [torch.full((cfg.B,), cfg.S0 + j + 1, dtype=torch.int32, device=dev)
@@ -521,6 +538,20 @@ def main():
     }
     if step_ms:
         result["step"]["us_p50_p90_events"] = pct_us(step_ms)
+    if args.offload:
+        # the selected K/V rows (and the appended token's K row) cross the host
+        # link; the dominant kernel is priced against the link, not HBM
+        link = ab["rows"] + (cfg.B * cfg.Hkv * cfg.d_k * 2 if cfg.k > 0 else 0)
+        dom_link = ab["rows"]  # the dominant kernel is the one that reads the rows
+        ach = dom_link / (dom_ms * 1e-3) / 1e9 if dom_ms else None
+        result["config"]["kv_memory"] = "pinned host"
+        result["roofline"].update({
+            "bound": "host_link", "achieved": round(ach, 2) if ach else None,
+            "peak": HOST_LINK_PEAK_GBS, "frac": round(ach / HOST_LINK_PEAK_GBS, 4) if ach else None,
+            "traffic": None, "algorithmic_bytes_per_launch": dom_link,
+            "copy_gbs": None, "frac_of_copy": None})
+        result["offload"] = {"link_bytes_per_step": link,
+                             "link_gbs": round(link / (ms_step * 1e-3) / 1e9, 2)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     events.close()
