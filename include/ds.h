@@ -203,8 +203,10 @@ size_t ds_decode_attn_workspace_size(const ds_kv_desc* kv, const ds_label_desc* 
  *      o_h = sum_{t in T} softmax_t(sm_scale * q_h . K_t) V_t, with q_h read at
  *      keep[g][c] for stored K column c ([LeanK] section 2.2).
  * With k <= 0 every row attends all S tokens and no label is read (chan and
- * lab may be NULL); with k >= S that row attends all its tokens (the dense
- * fallback of [DS] "use in SGLang").  A row with S = 0 gets a zero output.
+ * lab may be NULL, unless DS_DECODE_APPEND is set: a dense step still appends
+ * the current token's label, so later sparse steps find the cache current);
+ * with k >= S that row attends all its tokens (the dense fallback of [DS]
+ * "use in SGLang").  A row with S = 0 gets a zero output.
  *   q           fp16 [batch][n_q_heads][d_q].
  *   K, V        the caches (kv); the current token must already be written.
  *   seq_lens    int32 [batch] device array: tokens per row, current included.
@@ -234,6 +236,14 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
 ds_status ds_decode_attn_plan(const ds_kv_desc* kv, const ds_label_desc* lab, int32_t k,
                               int32_t max_seq_len, const ds_decode_opts* opts,
                               ds_decode_plan* plan);
+
+/* Batch policy of [DS] "use in SGLang" (the sparse-decode threshold): a
+ * batch decodes with Double Sparsity only when k > 0, its longest sequence
+ * has at least `threshold` tokens and its shortest at least k; otherwise the
+ * whole batch decodes densely (ds_decode_attn with k <= 0, which may still
+ * append labels).  Host-only; returns 1 (sparse) or 0 (dense). */
+int32_t ds_sparse_decode_enabled(int32_t max_seq_len, int32_t min_seq_len, int32_t k,
+                                 int32_t threshold);
 
 /* Heavy-channel calibration criteria ([DS] offline calibration: channels
  * found from outliers of K, of the query, or of their product). */

@@ -36,7 +36,8 @@ DECODE_STREAM = 8
 PATHS = ("dense", "fused", "local", "stream")
 EXPORTS = ("ds_label_build", "ds_label_append", "ds_decode_attn_workspace_size",
            "ds_decode_attn_plan", "ds_decode_attn", "ds_calibrate_workspace_size",
-           "ds_calibrate_channels", "ds_status_str", "ds_abi_version")
+           "ds_calibrate_channels", "ds_sparse_decode_enabled", "ds_status_str",
+           "ds_abi_version")
 
 
 class DsError(RuntimeError):
@@ -99,6 +100,8 @@ def load() -> ctypes.CDLL:
         lib.ds_calibrate_channels.argtypes = [P, P, I32, P, I32, P, I32, I32, P, P, P,
                                               ctypes.c_size_t, P]
         lib.ds_calibrate_channels.restype = ctypes.c_int
+        lib.ds_sparse_decode_enabled.argtypes = [I32, I32, I32, I32]
+        lib.ds_sparse_decode_enabled.restype = I32
         lib.ds_status_str.argtypes = [ctypes.c_int]
         lib.ds_status_str.restype = ctypes.c_char_p
         lib.ds_abi_version.argtypes = []
@@ -286,19 +289,35 @@ def decode_plan(K, V, n_q_heads, d_q, labels: LabelCache | None, k, max_seq_len,
             "workspace_bytes": int(pl.workspace_bytes)}
 
 
+def sparse_decode_enabled(max_seq_len: int, min_seq_len: int, k: int, threshold: int) -> bool:
+    """The batch policy of the sparse-decode threshold (ds_sparse_decode_enabled)."""
+    return bool(load().ds_sparse_decode_enabled(int(max_seq_len), int(min_seq_len), int(k),
+                                                int(threshold)))
+
+
 def decode_attn(q, K, V, seq_lens, max_seq_len: int, k: int, sm_scale: float,
                 chan=None, labels: LabelCache | None = None, keep=None, out=None,
                 topk_idx=None, workspace=None, n_split: int = 0, flags: int = 0,
-                stage_events=None, stream=None, validate_tables: bool = False):
+                stage_events=None, stream=None, validate_tables: bool = False,
+                sparse_decode_threshold: int | None = None, min_seq_len: int | None = None):
     """One decode step (ds_decode_attn).  Returns ``out`` fp16 [B][H_q][d_v].
     ``stage_events``: optional ctypes array of STAGE_COUNT + 1 hipEvent_t.
-    ``validate_tables``: check chan and keep first (check_tables; synchronises)."""
+    ``validate_tables``: check chan and keep first (check_tables; synchronises).
+    ``sparse_decode_threshold``: apply the batch policy (needs ``min_seq_len``,
+    the host's shortest sequence); a dense step then runs with k = 0 (and
+    still appends labels when DECODE_APPEND is set), and ``topk_idx`` is left
+    untouched."""
+    if sparse_decode_threshold is not None and k > 0:
+        if min_seq_len is None:
+            raise ValueError("sparse_decode_threshold needs min_seq_len")
+        if not sparse_decode_enabled(max_seq_len, min_seq_len, k, sparse_decode_threshold):
+            k, topk_idx = 0, None
     B, Hq, d_q = q.shape
     if validate_tables:
         check_tables(chan if k > 0 else None, K.shape[3], labels.r if labels is not None else None,
                      keep, d_q, K.shape[1])
     kv = kv_desc(K, V, Hq, d_q)
-    lab = labels.desc() if labels is not None else None
+    lab = labels.desc() if labels is not None and (k > 0 or flags & DECODE_APPEND) else None
     lib = load()
     need = int(lib.ds_decode_attn_workspace_size(
         ctypes.byref(kv), ctypes.byref(lab) if lab is not None else None, int(k),

@@ -319,6 +319,7 @@ ds_status ds_decode_attn_plan(const ds_kv_desc* kv, const ds_label_desc* lab, in
   int n = 1;  // the attention pass, or the fused kernel
   if (r.path == DS_PATH_LOCAL) n += 2;
   if (r.path == DS_PATH_STREAM) n += 2 + ((flags & DS_DECODE_APPEND) ? 1 : 0);
+  if (r.path == DS_PATH_DENSE && (flags & DS_DECODE_APPEND)) ++n;
   if (r.path != DS_PATH_FUSED && r.n_split > 1) ++n;
   plan->kernels = n;
   plan->chunk = r.path == DS_PATH_LOCAL ? p.local_chunk : (r.path == DS_PATH_STREAM ? kScoreChunk : 0);
@@ -335,7 +336,8 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
   ds_status st = check_kv(kv, true);
   if (st) return st;
   const bool sparse = k > 0;
-  if (sparse) {
+  const uint32_t flags = opts ? opts->flags : 0u;
+  if (sparse || (flags & DS_DECODE_APPEND)) {  // a dense step may still append labels
     if ((st = check_lab(kv, lab))) return st;
     if (!chan) return DS_ERR_ARG;
   }
@@ -343,11 +345,9 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
   if (!aligned16(K) || !aligned16(V) || !aligned16(out)) return DS_ERR_ALIGN;
   if (!keep && kv->d_k != kv->d_q) return DS_ERR_SHAPE;
   if (max_seq_len < 0 || max_seq_len > kv->capacity) return DS_ERR_ARG;
-  const uint32_t flags = opts ? opts->flags : 0u;
   if (flags & ~(DS_DECODE_APPEND | DS_DECODE_VALIDATE_ONLY | DS_DECODE_UNFUSED | DS_DECODE_STREAM))
     return DS_ERR_ARG;
   if (opts && opts->n_split < 0) return DS_ERR_ARG;
-  if ((flags & DS_DECODE_APPEND) && !sparse) return DS_ERR_ARG;
   if (!std::isfinite(sm_scale)) return DS_ERR_ARG;
 
   const Plan p = make_plan(kv, k, max_seq_len);
@@ -487,6 +487,11 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
   if (!final_out && launch_combine(aa, B, stream) != hipSuccess) return DS_ERR_HIP;
   mark(DS_STAGE_COUNT);
   return DS_OK;
+}
+
+int32_t ds_sparse_decode_enabled(int32_t max_seq_len, int32_t min_seq_len, int32_t k,
+                                 int32_t threshold) {
+  return (k > 0 && max_seq_len >= threshold && min_seq_len >= k) ? 1 : 0;
 }
 
 size_t ds_calibrate_workspace_size(const ds_kv_desc* kv, int32_t n_tok, int32_t n_win) {

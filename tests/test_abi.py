@@ -85,6 +85,8 @@ def test_validate_only_accepts_good_arguments(lib):
     assert _decode(lib, lab=_lab(dtype=ds.LABEL_INT4, r=8, scales=FAKE)) == 0
     kv = _kv(d_k=32, k_stride=(4 * 1000 * 32, 1000 * 32, 32))
     assert _decode(lib, kv=kv, keep=FAKE, lab=_lab(r=8)) == 0                # LeanK
+    # a dense step that still appends the current token's label
+    assert _decode(lib, k=0, flags=ds.DECODE_VALIDATE_ONLY | ds.DECODE_APPEND) == 0
 
 
 @pytest.mark.parametrize("case,code", [
@@ -301,3 +303,16 @@ def test_channel_overlap_host_logic():
     assert ds.channel_overlap([[1, 2]], [[3, 4]]) == [0.0]
     with pytest.raises(ValueError):
         ds.channel_overlap(a, b[:, :2])
+
+
+def test_sparse_decode_threshold_policy(lib):
+    """[DS] "use in SGLang": Double Sparsity decodes a batch only when its
+    longest sequence reaches the threshold and its shortest reaches k."""
+    en = lib.ds_sparse_decode_enabled
+    assert en(4096, 4096, 256, 0) == 1
+    assert en(4096, 300, 256, 0) == 1
+    assert en(4096, 255, 256, 0) == 0      # a sequence shorter than k
+    assert en(4095, 4095, 256, 4096) == 0  # longest below the threshold
+    assert en(4096, 1000, 256, 4096) == 1
+    assert en(4096, 4096, 0, 0) == 0       # k <= 0 is dense
+    assert ds.sparse_decode_enabled(8192, 8192, 256, 8192) is True
