@@ -217,9 +217,10 @@ def decode(q, K, V, seq_lens, k, sm_scale, chan=None, lab: Labels | None = None,
     tk = np.full((B, Hkv, k_cap), -1, np.int32)
     sc = np.zeros((B, Hkv, cap), np.float64) if (want_scores and k > 0) else None
     use_lab = k > 0
+    keep_a, chan_a = _i32(keep), _i32(chan)  # held here: the C call reads them
     rc = _load().oracle_decode(
-        ctypes.byref(sh), _ptr(q), _ptr(K), _ptr(V), _ptr(seq), _ptr(_i32(keep)),
-        _ptr(_i32(chan)) if use_lab else None,
+        ctypes.byref(sh), _ptr(q), _ptr(K), _ptr(V), _ptr(seq), _ptr(keep_a),
+        _ptr(chan_a) if use_lab else None,
         _ptr(lab.f16) if use_lab else None, _ptr(lab.codes) if use_lab else None,
         _ptr(lab.scales) if use_lab else None, int(k), float(sm_scale), _ptr(rows_a),
         len(rows_a), _ptr(out), _ptr(tk), k_cap, _ptr(sc), cap, int(n_threads))
@@ -241,7 +242,8 @@ def attend_sets(q, K, V, sets, sm_scale, keep=None, rows=None, n_threads=0):
     rows_a = np.ascontiguousarray(np.array(rows, np.int32).reshape(-1, 2))
     sets = _i32(sets)
     out = np.zeros((B, Hq, V.shape[3]), np.float64)
-    rc = _load().oracle_attend_sets(ctypes.byref(sh), _ptr(q), _ptr(K), _ptr(V), _ptr(_i32(keep)),
+    keep_a = _i32(keep)  # held here: the C call reads it
+    rc = _load().oracle_attend_sets(ctypes.byref(sh), _ptr(q), _ptr(K), _ptr(V), _ptr(keep_a),
                                     _ptr(sets), sets.shape[2], float(sm_scale), _ptr(rows_a),
                                     len(rows_a), _ptr(out), int(n_threads))
     if rc:
