@@ -233,7 +233,9 @@ def calibrate_channels(K, r: int, criterion="qk", qwin=None, keep=None, n_tok: i
     B, Hkv, cap, d_k = K.shape
     n_tok = cap if n_tok is None else int(n_tok)
     if qwin is not None:
-        assert qwin.dtype == torch.float16 and qwin.is_contiguous() and qwin.dim() == 4
+        if qwin.dtype != torch.float16 or not qwin.is_contiguous() or qwin.dim() != 4 or \
+                qwin.shape[0] != B:
+            raise ValueError("qwin: expected a contiguous fp16 [batch][n_win][n_q_heads][d_q] tensor")
         n_win, Hq, d_q = qwin.shape[1], qwin.shape[2], qwin.shape[3]
     else:
         n_win, Hq, d_q = 0, Hkv, d_k

@@ -316,3 +316,11 @@ def test_sparse_decode_threshold_policy(lib):
     assert en(4096, 1000, 256, 4096) == 1
     assert en(4096, 4096, 0, 0) == 0       # k <= 0 is dense
     assert ds.sparse_decode_enabled(8192, 8192, 256, 8192) is True
+
+
+def test_calibrate_binding_rejects_a_bad_window():
+    K = torch.zeros((2, 4, 16, 128), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        ds.calibrate_channels(K, 8, "qk", qwin=torch.zeros((2, 3, 4, 128), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        ds.calibrate_channels(K, 8, "qk", qwin=torch.zeros((3, 3, 4, 128), dtype=torch.float16))
