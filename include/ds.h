@@ -209,6 +209,11 @@ size_t ds_decode_attn_workspace_size(const ds_kv_desc* kv, const ds_label_desc* 
  * "use in SGLang").  A row with S = 0 gets a zero output.
  *   q           fp16 [batch][n_q_heads][d_q].
  *   K, V        the caches (kv); the current token must already be written.
+ *               They may be device memory or pinned host memory that HIP maps
+ *               into the device's address space at its host address
+ *               (hipHostMalloc): the kernels then read only the selected rows
+ *               (and the appended token's K row) over the host link ([DS]
+ *               "experiment details": the offloading variant).
  *   seq_lens    int32 [batch] device array: tokens per row, current included.
  *   max_seq_len host upper bound of seq_lens (sizes the grid), <= capacity.
  *   keep        int32 [n_kv_heads][d_k] device array: query channel of each
