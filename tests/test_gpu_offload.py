@@ -81,3 +81,27 @@ def test_offloaded_kv_equals_device_kv(name):
         assert torch.equal(labs[0].codes, labs[1].codes)
         if labs[0].scales is not None:
             assert torch.equal(labs[0].scales, labs[1].scales)
+
+
+def test_offloaded_kv_full_size_128k():
+    # the 128K workload at full size (B4 x 32 KV heads, 131072 + 1 tokens,
+    # int4 labels r 8, k 8192): 8.6 GB of K/V in pinned host memory
+    cfg = synth.CONFIGS["long_128k"]
+    inp = synth.make_inputs(cfg, "cuda")
+    print("offload full size %s" % cfg.name, flush=True)
+    Kh, Vh = _pinned_copy(inp.K), _pinned_copy(inp.V)
+    S = cfg.S0 + 1
+    seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
+    res = []
+    for K, V in ((inp.K, inp.V), (Kh, Vh)):
+        lab = ds.LabelCache.allocate(cfg.B, cfg.Hkv, cfg.cap, cfg.r, cfg.int4)
+        ds.label_build(inp.K, inp.chan, lab, 0, cfg.S0)
+        idx = torch.full((cfg.B, cfg.Hkv, cfg.k), -7, dtype=torch.int32, device="cuda")
+        out = ds.decode_attn(inp.q, K, V, seq, S, cfg.k, cfg.sm_scale, chan=inp.chan, labels=lab,
+                             keep=inp.keep, topk_idx=idx, flags=ds.DECODE_APPEND)
+        torch.cuda.synchronize()
+        res.append((out, idx, lab))
+    assert torch.equal(res[0][0], res[1][0])
+    assert torch.equal(res[0][1], res[1][1])
+    assert torch.equal(res[0][2].codes, res[1][2].codes)
+    assert torch.equal(res[0][2].scales, res[1][2].scales)
