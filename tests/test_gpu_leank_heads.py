@@ -77,3 +77,41 @@ def test_per_head_kept_counts(flags):
             o, w = out[b, g * G:(g + 1) * G], res["out"][b]
             err = (np.abs(o - w).max(axis=1) / np.abs(w).max(axis=1)).max()
             assert err <= 2e-3, (g, b, err)
+
+
+def test_fully_pruned_head_and_pruned_v_columns():
+    # LeanK section 4.4: a head may lose every channel, and V may be pruned
+    # too.  With the same zero-padding layout a fully pruned head (K and V all
+    # zero) outputs zeros, and pruned V columns give zero output channels;
+    # the rest matches the oracle on the same cache.
+    g0 = torch.Generator().manual_seed(43)
+    B, Hkv, G, D, cap, S, r, k, d_k = 2, 3, 2, 128, 512, 480, 8, 40, 32
+    K = torch.randn((B, Hkv, cap, d_k), generator=g0)
+    V = torch.randn((B, Hkv, cap, D), generator=g0)
+    K[:, 1] = 0.0
+    V[:, 1] = 0.0                    # head 1: fully pruned
+    V[:, 2, :, 64:] = 0.0            # head 2: V keeps 64 of 128 channels
+    K, V = K.half(), V.half()
+    q = torch.randn((B, Hkv * G, D), generator=g0).half()
+    keep = torch.stack([torch.randperm(D, generator=g0)[:d_k].sort().values
+                        for _ in range(Hkv)]).to(torch.int32)
+    chan = torch.stack([torch.randperm(d_k, generator=g0)[:r].sort().values
+                        for _ in range(Hkv)]).to(torch.int32)
+    scale = 1.0 / np.sqrt(D)
+    labels = ds.LabelCache.allocate(B, Hkv, cap, r, False)
+    ds.label_build(K.cuda(), chan.cuda(), labels, 0, S)
+    seq = torch.full((B,), S, dtype=torch.int32, device="cuda")
+    out = ds.decode_attn(q.cuda(), K.cuda(), V.cuda(), seq, S, k, scale, chan=chan.cuda(),
+                         labels=labels, keep=keep.cuda(), validate_tables=True)
+    torch.cuda.synchronize()
+    out = out.cpu().double().numpy()
+    assert np.all(out[:, 2:4] == 0.0)
+    assert np.all(out[:, 4:6, 64:] == 0.0)
+    lab = oracle.Labels.empty(B, Hkv, cap, r, False)
+    oracle.label_build(K.numpy(), chan.numpy(), lab, 0, S)
+    res = oracle.decode(q.numpy(), K.numpy(), V.numpy(), np.full(B, S, np.int32), k, scale,
+                        chan=chan.numpy(), lab=lab, keep=keep.numpy())
+    for h in (0, 1, 4, 5):
+        w = res["out"][:, h, :64]
+        err = (np.abs(out[:, h, :64] - w).max(axis=1) / np.abs(w).max(axis=1)).max()
+        assert err <= 2e-3, (h, err)
