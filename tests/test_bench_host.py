@@ -1,6 +1,7 @@
 """bench.py host logic without a GPU: the algorithmic byte counts of the
 workloads, the dominant-kernel choice per path, the one-GPU contract and the
-source hash that keys the stored counter records."""
+source hash that keys the stored counter records, and the counter record of
+the calibration workload."""
 import os
 import subprocess
 import sys
@@ -50,3 +51,31 @@ def test_source_hash_ignores_comments(tmp_path, monkeypatch):
     assert bench.source_hash() == h1
     (d / "k.hip").write_text("int f() { return 2; }\n")
     assert bench.source_hash() != h1
+
+
+def test_traffic_record_for_the_calibration_workload(tmp_path):
+    # two synthetic counter files: the reference copy (neg_kernel) and the
+    # calibration column kernel, two dispatches each, values split over XCDs
+    def csv(path, counter, copy_kib, kern_kib):
+        rows = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+        for d in (1, 2):
+            for half in (0.25, 0.75):
+                rows.append("%d,neg_kernel,%s,%.1f" % (d, counter, copy_kib * half))
+        for d in (3, 4):
+            rows.append("%d,ds::k_calib_cols(ds::CalibArgs),%s,%.1f" % (d, counter, kern_kib))
+        path.write_text("\n".join(rows) + "\n")
+    f, w = tmp_path / "f.csv", tmp_path / "w.csv"
+    csv(f, "FETCH_SIZE", 131072.0, 66000.0)   # FETCH_SIZE reads half of a 256 MiB copy
+    csv(w, "WRITE_SIZE", 262144.0, 1000.0)
+    out = tmp_path / "rec.json"
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload",
+                        "calib_llama2_7b_4k", "--calib-copy-mb", "256", "--traffic-from", str(f),
+                        str(w), "--traffic-kernel", "k_calib_cols", "--traffic-out", str(out)],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    import json
+    rec = json.loads(out.read_text())
+    assert rec["workload"] == "calib_llama2_7b_4k" and rec["kernel"] == "k_calib_cols"
+    assert rec["calibration"]["fetch_factor"] == 2.0 and rec["calibration"]["write_factor"] == 1.0
+    assert rec["bytes_per_launch"] == int(round((66000.0 * 2 + 1000.0) * 1024))
+    assert rec["dispatches"] == [2, 2]
