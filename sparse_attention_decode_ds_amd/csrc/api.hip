@@ -115,8 +115,9 @@ Plan make_plan(const ds_kv_desc* kv, int k, int max_seq) {
   // Local top-M chunks (at least 1024 tokens unless the row is shorter).  A
   // chunk workgroup costs a fixed latency plus its tokens per thread, and the
   // chunks run in rounds of as many workgroups as the chip holds at once
-  // (1024 of 512 threads, 2048 of 256): a last round with a few workgroups
-  // costs as much as a full one.  The merge then costs about its candidates
+  // (1024 of 512 threads, 2048 of 256): a single round costs its latency
+  // however full it is, while beyond one round workgroups start as others
+  // finish, so the rounds count in proportion to the workgroups.  The merge then costs about its candidates
   // (quota per chunk, twice the expected share of k) per merge thread.  Pick
   // the chunk count with the lowest total.
   {
@@ -129,7 +130,7 @@ Plan make_plan(const ds_kv_desc* kv, int k, int max_seq) {
       const int64_t nch = ceil_div(S, chunk);
       const int threads = chunk > 4096 ? 512 : 256;
       const int64_t slots = kLocalSlotsPerCu * (2048 / threads);
-      const double rounds = (double)ceil_div(rows * nch, slots);
+      const double rounds = std::max(1.0, (double)(rows * nch) / (double)slots);
       const double quota = std::min<double>((double)chunk,
                                             std::max(64.0, 2.0 * std::max(k, 0) * chunk / S + 1));
       const double cost = rounds * (16.0 + (double)ceil_div(chunk, threads)) + nch * quota / 1024.0;
