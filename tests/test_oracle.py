@@ -403,3 +403,99 @@ def test_synth_config_inputs_are_consistent():
                 assert len(ht[g]) == cfg.r == len(set(ht[g])) and ht[g] == sorted(ht[g])
                 cols = [kt[g][c] for c in ht[g]] if kt is not None else ht[g]
                 assert set(out[: cfg.r]) <= set(cols)
+
+
+def _golden_int4_scores():
+    with open(os.path.join(GOLDEN, "int4_score_cases.json")) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_int4_scores_with_per_token_scales_golden(G):
+    """Hand-worked int4 scores ("online forward computation", step 2, on the
+    4-bit labels of "offline calibration"): tokens whose scales differ and are
+    not 1, so dropping the scale, or taking another token's, changes the
+    scores and the top-k set.  Values in non-heavy channels of K and q are
+    large distractors that must not enter the labels or the gathered query.
+    G = 2 splits the gathered query evenly over two query heads of a group."""
+    gd = _golden_int4_scores()
+    chan = np.array(gd["chan"], np.int32)
+    qg = np.array(gd["qg"], np.float64)
+    toks = gd["tokens"]
+    S, D, r = len(toks), 128, len(chan)
+    K = np.full((1, 1, S, D), gd["distractor_k"], np.float16)
+    K[0, 0][:, chan] = np.array([t["x"] for t in toks], np.float16)
+    q = np.full((1, G, D), gd["distractor_q"], np.float16)
+    q[0][:, chan] = (qg / G).astype(np.float16)[None, :].repeat(G, 0)
+    assert np.array_equal(q[0][:, chan].astype(np.float64).sum(0), qg)   # exact split
+    lab = oracle.label_build(K.view(np.uint16), chan[None], oracle.Labels.empty(1, 1, S, r, True),
+                             0, S)
+    assert lab.scales[0, 0].tolist() == [t["scale_bits"] for t in toks]
+    assert lab.codes[0, 0].tolist() == [t["bytes"] for t in toks]
+    V = np.zeros((1, 1, S, D), np.float16)
+    for k_str, expect in gd["topk"].items():
+        res = oracle.decode(q, K, V, np.array([S], np.int32), int(k_str), 0.1, chan=chan[None],
+                            lab=lab, want_scores=True)
+        assert res["scores"][0, 0, :S].tolist() == [t["score"] for t in toks]
+        assert res["topk"][0, 0].tolist() == expect
+
+
+# --------------------------------------------------------------------------
+# attention over a caller-given token set ("online forward computation",
+# step 3: exact softmax attention over the selected tokens' full rows), the
+# reference the parity checks fall back to when two selections differ in
+# near-ties
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("Hq,Hkv,leank", [(4, 4, False), (6, 2, False), (8, 2, True)])
+def test_attend_sets_is_masked_attention(Hq, Hkv, leank):
+    """attend_sets over sets padded with -1 and holding out-of-range entries
+    (>= capacity, which are ignored) equals textbook attention masked to the
+    valid entries; an all-padding set gives zeros.  Under LeanK the pruned K
+    is the full K with the query zeroed outside the kept channels."""
+    rng = np.random.default_rng(23)
+    B, S, D, dk, k_cap = 3, 41, 128, 32, 12
+    G = Hq // Hkv
+    q, Kfull, V = _tensors(rng, B, Hq, Hkv, S)
+    keep = None
+    K = Kfull
+    qref = q
+    if leank:
+        keep = np.stack([np.sort(rng.choice(D, dk, replace=False)) for _ in range(Hkv)]).astype(np.int32)
+        K = np.ascontiguousarray(np.stack([Kfull[:, g][..., keep[g]] for g in range(Hkv)], 1))
+        qref = np.zeros_like(q)
+        for h in range(Hq):
+            qref[:, h, keep[h // G]] = q[:, h, keep[h // G]]
+    sets = np.full((B, Hkv, k_cap), -1, np.int32)
+    mask = np.zeros((B, Hkv, S), bool)
+    for b in range(B):
+        for g in range(Hkv):
+            if (b, g) == (B - 1, Hkv - 1):
+                continue                                   # all padding
+            n = int(rng.integers(1, k_cap - 2))
+            sel = rng.choice(S, n, replace=False)
+            mask[b, g, sel] = True
+            row = np.concatenate([sel, [S + 3, 10 ** 6, -5]]).astype(np.int32)  # junk entries
+            rng.shuffle(row)
+            sets[b, g, :len(row)] = row
+    got = oracle.attend_sets(q, K, V, sets, 0.09, keep=keep)
+    m = np.repeat(mask, G, 1)
+    ref = sdpa(qref, np.repeat(Kfull, G, 1), np.repeat(V, G, 1), 0.09,
+               mask=np.where(m.any(-1, keepdims=True), m, True))
+    live = m.any(-1)
+    np.testing.assert_allclose(got[live], ref[live], rtol=1e-12, atol=1e-12)
+    assert not got[~live].any()
+    assert (~live).sum() == G
+
+
+def test_attend_sets_agrees_with_decode_on_its_own_selection():
+    """Fed the oracle's own top-k sets, attend_sets reproduces the decode
+    output exactly (same summation)."""
+    rng = np.random.default_rng(24)
+    B, Hq, Hkv, S, D, r, k = 2, 6, 3, 90, 128, 8, 13
+    q, K, V = _tensors(rng, B, Hq, Hkv, S)
+    chan = np.stack([np.sort(rng.choice(D, r, replace=False)) for _ in range(Hkv)]).astype(np.int32)
+    lab = oracle.label_build(K.view(np.uint16), chan, oracle.Labels.empty(B, Hkv, S, r, True), 0, S)
+    res = oracle.decode(q, K, V, np.full(B, S, np.int32), k, 0.1, chan=chan, lab=lab)
+    got = oracle.attend_sets(q, K, V, res["topk"], 0.1)
+    np.testing.assert_array_equal(got, res["out"])
