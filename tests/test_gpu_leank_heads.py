@@ -67,14 +67,20 @@ def test_per_head_kept_counts(flags):
                             want_scores=True)
         for b in range(B):
             got, want = set(topk[b, g].tolist()), set(res["topk"][b, 0].tolist())
+            w = res["out"][b]
             if got != want:
                 s = res["scores"][b, 0, :S]
                 sk = np.sort(s)[::-1][k - 1]
                 tol = 1e-3 * abs(sk) + 1e-6 * np.abs(s).max()
                 for t in got ^ want:
                     assert abs(s[t] - sk) <= tol, (g, b, t, s[t], sk)
-                continue
-            o, w = out[b, g * G:(g + 1) * G], res["out"][b]
+                # near-tie swap: the reference is the oracle's attention over
+                # the GPU's own set, so the arithmetic is still checked
+                sets = np.full((B, 1, k), -1, np.int32)
+                sets[b, 0] = topk[b, g]
+                w = oracle.attend_sets(qg, Kg, Vg, sets, scale, keep=keep[g:g + 1, :n].numpy(),
+                                       rows=[(b, 0)])[b]
+            o = out[b, g * G:(g + 1) * G]
             err = (np.abs(o - w).max(axis=1) / np.abs(w).max(axis=1)).max()
             assert err <= 2e-3, (g, b, err)
 

@@ -7,13 +7,16 @@ and the kernels read the selected rows from there directly: the labels, the
 query, the workspace and the output stay on the GPU.  Each step must equal,
 bit for bit, the same call with K and V in device memory (the kernels and
 their summation order are the same), including the label append, which reads
-the current token's K row from host memory."""
+the current token's K row from host memory.  The offloaded results are also
+checked against the CPU oracle on the same bytes: labels bit-exact, selected
+sets up to near-ties of the k-th score, attention within 2e-3 per row."""
 import ctypes
 
 import pytest
 import torch
 
 import synth
+from tests import ds_check
 
 pytestmark = pytest.mark.gpu
 
@@ -81,6 +84,10 @@ def test_offloaded_kv_equals_device_kv(name):
         assert torch.equal(labs[0].codes, labs[1].codes)
         if labs[0].scales is not None:
             assert torch.equal(labs[0].scales, labs[1].scales)
+    # the offloaded step against the oracle, on the host copies it read
+    res = ds_check.check_rows(cfg, inp.q, Kh, Vh, inp.chan, inp.keep, labs[1], seq, cfg.k,
+                              outs[1], idxs[1], ds_check.sample_rows(cfg, 8))
+    print("offload %s vs oracle: %s" % (name, res), flush=True)
 
 
 def test_offloaded_kv_full_size_128k():
@@ -105,3 +112,7 @@ def test_offloaded_kv_full_size_128k():
     assert torch.equal(res[0][1], res[1][1])
     assert torch.equal(res[0][2].codes, res[1][2].codes)
     assert torch.equal(res[0][2].scales, res[1][2].scales)
+    # sampled rows of the offloaded step against the oracle
+    chk = ds_check.check_rows(cfg, inp.q, Kh, Vh, inp.chan, inp.keep, res[1][2], seq, cfg.k,
+                              res[1][0], res[1][1], ds_check.sample_rows(cfg, 4, seed=5))
+    print("offload full size vs oracle: %s" % chk, flush=True)

@@ -2,11 +2,13 @@
 a batch whose longest sequence is below the threshold, or whose shortest is
 below k, decodes densely.  Such a step equals the dense decode bit for bit
 and still appends the current token's label, which then equals what a label
-build over the same tokens writes."""
+build over the same tokens writes.  Both the dense-by-policy step and the
+sparse step at the threshold are checked against the CPU oracle."""
 import pytest
 import torch
 
 import synth
+from tests import ds_check
 
 pytestmark = pytest.mark.gpu
 
@@ -58,3 +60,17 @@ def test_threshold_policy(over):
         assert torch.equal(lab_a.scales, full.scales)
     assert torch.equal(out_b, out_c)
     assert not torch.equal(out_b, dense)  # k = 64 of 601 tokens: a different result
+    rows = ds_check.sample_rows(cfg, 8)
+    # dense by policy: every token attended (the oracle with k <= 0)
+    ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, None, seq, 0, out_a, None,
+                        rows)
+    # at the threshold: the sparse step, with its appended labels
+    idx = torch.full((cfg.B, cfg.Hkv, cfg.k), -7, dtype=torch.int32, device="cuda")
+    lab_d = prefilled()
+    out_d = ds.decode_attn(*args, chan=inp.chan, labels=lab_d, flags=ds.DECODE_APPEND,
+                           sparse_decode_threshold=S, min_seq_len=S, topk_idx=idx,
+                           validate_tables=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out_d, out_b)
+    ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, lab_d, seq, cfg.k, out_d,
+                        idx, rows)
