@@ -21,7 +21,8 @@
  *
  * Conventions for every call:
  *   - Pointers are device memory owned by the caller unless marked "host".
- *     The library allocates nothing, keeps no state between calls and never
+ *     The library allocates nothing, keeps no state between calls (except
+ *     the per-GPU scratch array of ds_decode_attn_noalloc) and never
  *     synchronises the stream.
  *   - fp16 is IEEE binary16.  All arrays are row-major, last index fastest.
  *   - Work is enqueued asynchronously on `stream`.  Arguments are validated on
@@ -233,6 +234,32 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
                          const int32_t* chan, const ds_label_desc* lab, int32_t k, float sm_scale,
                          void* out, int32_t* topk_idx, void* workspace, size_t workspace_bytes,
                          const ds_decode_opts* opts, hipStream_t stream);
+
+/* Scratch bytes of ds_decode_attn_noalloc (per GPU). */
+#define DS_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* ds_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It takes the same arguments, launches
+ * the same kernels and gives the same results as ds_decode_attn; the scratch
+ * that ds_decode_attn takes from the caller's workspace comes instead from a
+ * device array of DS_NOALLOC_SCRATCH_BYTES that the library holds on each GPU
+ * from the first use of the library there until the process ends.  The call
+ * allocates nothing.  Its first call on a device (the device current at the
+ * call, which must be the device of `stream`) looks up that array's address.
+ * Every call on a GPU shares the one array: calls that overlap on one GPU
+ * (other streams, other threads) race on it and give undefined results; the
+ * caller orders them.  The scratch needs no clearing between calls (each call
+ * writes what it reads).
+ * Errors: those of ds_decode_attn; DS_ERR_WORKSPACE when these shapes need
+ * more than DS_NOALLOC_SCRATCH_BYTES (as ds_decode_attn_workspace_size
+ * reports); DS_ERR_HIP when the array's address cannot be found. */
+ds_status ds_decode_attn_noalloc(const ds_kv_desc* kv, const void* q, const void* K,
+                                 const void* V, const int32_t* seq_lens, int32_t max_seq_len,
+                                 const int32_t* keep, const int32_t* chan,
+                                 const ds_label_desc* lab, int32_t k, float sm_scale, void* out,
+                                 int32_t* topk_idx, const ds_decode_opts* opts,
+                                 hipStream_t stream);
 
 /* Host-only query: fills *plan for a ds_decode_attn call with these shapes,
  * k, max_seq_len and options (no device pointer is read and nothing is

@@ -33,9 +33,11 @@ DECODE_APPEND = 1
 DECODE_VALIDATE_ONLY = 2
 DECODE_UNFUSED = 4
 DECODE_STREAM = 8
+NOALLOC_SCRATCH_BYTES = 128 << 20  # DS_NOALLOC_SCRATCH_BYTES
 PATHS = ("dense", "fused", "local", "stream")
 EXPORTS = ("ds_label_build", "ds_label_append", "ds_decode_attn_workspace_size",
-           "ds_decode_attn_plan", "ds_decode_attn", "ds_calibrate_workspace_size",
+           "ds_decode_attn_plan", "ds_decode_attn", "ds_decode_attn_noalloc",
+           "ds_calibrate_workspace_size",
            "ds_calibrate_channels", "ds_sparse_decode_enabled", "ds_status_str",
            "ds_abi_version")
 
@@ -95,6 +97,9 @@ def load() -> ctypes.CDLL:
         lib.ds_decode_attn.argtypes = [P, P, P, P, P, I32, P, P, P, I32, ctypes.c_float, P, P, P,
                                        ctypes.c_size_t, P, P]
         lib.ds_decode_attn.restype = ctypes.c_int
+        lib.ds_decode_attn_noalloc.argtypes = [P, P, P, P, P, I32, P, P, P, I32, ctypes.c_float,
+                                               P, P, P, P]
+        lib.ds_decode_attn_noalloc.restype = ctypes.c_int
         lib.ds_calibrate_workspace_size.argtypes = [P, I32, I32]
         lib.ds_calibrate_workspace_size.restype = ctypes.c_size_t
         lib.ds_calibrate_channels.argtypes = [P, P, I32, P, I32, P, I32, I32, P, P, P,
@@ -336,6 +341,26 @@ def decode_attn(q, K, V, seq_lens, max_seq_len: int, k: int, sm_scale: float,
         ctypes.byref(lab) if lab is not None else None, int(k), float(sm_scale), _p(out),
         _p(topk_idx), _p(workspace), workspace.numel() * workspace.element_size(),
         ctypes.byref(opts), _stream(stream)))
+    return out
+
+
+def decode_attn_noalloc(q, K, V, seq_lens, max_seq_len: int, k: int, sm_scale: float,
+                        chan=None, labels: LabelCache | None = None, keep=None, out=None,
+                        topk_idx=None, n_split: int = 0, flags: int = 0, stream=None):
+    """ds_decode_attn_noalloc: the same step as decode_attn with the library's
+    per-GPU scratch in place of a workspace (calls on one GPU must not
+    overlap).  ``out`` must be given: this call allocates nothing."""
+    if out is None:
+        raise ValueError("decode_attn_noalloc: pass out (this call allocates nothing)")
+    B, Hq, d_q = q.shape
+    kv = kv_desc(K, V, Hq, d_q)
+    lab = labels.desc() if labels is not None and (k > 0 or flags & DECODE_APPEND) else None
+    opts = DecodeOpts()
+    opts.n_split, opts.flags = int(n_split), int(flags)
+    _check("ds_decode_attn_noalloc", load().ds_decode_attn_noalloc(
+        ctypes.byref(kv), _p(q), _p(K), _p(V), _p(seq_lens), int(max_seq_len), _p(keep), _p(chan),
+        ctypes.byref(lab) if lab is not None else None, int(k), float(sm_scale), _p(out),
+        _p(topk_idx), ctypes.byref(opts), _stream(stream)))
     return out
 
 

@@ -11,6 +11,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "ds_internal.h"
 
@@ -329,11 +330,17 @@ ds_status ds_decode_attn_plan(const ds_kv_desc* kv, const ds_label_desc* lab, in
   return DS_OK;
 }
 
-ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, const void* V,
-                         const int32_t* seq_lens, int32_t max_seq_len, const int32_t* keep,
-                         const int32_t* chan, const ds_label_desc* lab, int32_t k, float sm_scale,
-                         void* out, int32_t* topk_idx, void* workspace, size_t workspace_bytes,
-                         const ds_decode_opts* opts, hipStream_t stream) {
+}  // extern "C"
+
+namespace ds {
+namespace {
+
+// The decode step behind both decode entry points: validation, plan, launches.
+ds_status decode_impl(const ds_kv_desc* kv, const void* q, const void* K, const void* V,
+                      const int32_t* seq_lens, int32_t max_seq_len, const int32_t* keep,
+                      const int32_t* chan, const ds_label_desc* lab, int32_t k, float sm_scale,
+                      void* out, int32_t* topk_idx, void* workspace, size_t workspace_bytes,
+                      const ds_decode_opts* opts, hipStream_t stream) {
   ds_status st = check_kv(kv, true);
   if (st) return st;
   const bool sparse = k > 0;
@@ -488,6 +495,56 @@ ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, con
   if (!final_out && launch_combine(aa, B, stream) != hipSuccess) return DS_ERR_HIP;
   mark(DS_STAGE_COUNT);
   return DS_OK;
+}
+
+// Scratch of ds_decode_attn_noalloc: one array per device, held from the
+// code object's load until the process ends.  In host code its name is only
+// a stand-in; the device address comes from hipGetSymbolAddress, once per
+// device, and only that address is handed to the kernels.
+static __device__ __align__(256) char scratch[DS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+ds_status scratch_ptr(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DS_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DS_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return DS_OK;
+}
+
+}  // namespace
+}  // namespace ds
+
+extern "C" {
+
+ds_status ds_decode_attn(const ds_kv_desc* kv, const void* q, const void* K, const void* V,
+                         const int32_t* seq_lens, int32_t max_seq_len, const int32_t* keep,
+                         const int32_t* chan, const ds_label_desc* lab, int32_t k, float sm_scale,
+                         void* out, int32_t* topk_idx, void* workspace, size_t workspace_bytes,
+                         const ds_decode_opts* opts, hipStream_t stream) {
+  return decode_impl(kv, q, K, V, seq_lens, max_seq_len, keep, chan, lab, k, sm_scale, out,
+                     topk_idx, workspace, workspace_bytes, opts, stream);
+}
+
+ds_status ds_decode_attn_noalloc(const ds_kv_desc* kv, const void* q, const void* K,
+                                 const void* V, const int32_t* seq_lens, int32_t max_seq_len,
+                                 const int32_t* keep, const int32_t* chan,
+                                 const ds_label_desc* lab, int32_t k, float sm_scale, void* out,
+                                 int32_t* topk_idx, const ds_decode_opts* opts,
+                                 hipStream_t stream) {
+  void* ws = nullptr;
+  const ds_status st = scratch_ptr(&ws);
+  if (st != DS_OK) return st;
+  return decode_impl(kv, q, K, V, seq_lens, max_seq_len, keep, chan, lab, k, sm_scale, out,
+                     topk_idx, ws, DS_NOALLOC_SCRATCH_BYTES, opts, stream);
 }
 
 int32_t ds_sparse_decode_enabled(int32_t max_seq_len, int32_t min_seq_len, int32_t k,
