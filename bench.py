@@ -53,13 +53,46 @@ def algorithmic_bytes(cfg, S):
             "out": cfg.B * cfg.Hq * cfg.d_v * 2}
 
 
-def dominant_kernel(plan, ab, G):
-    """The kernel that takes most of a step on this path, its name prefix in
-    profiles, and its algorithmic bytes per launch."""
-    if plan["path"] == "fused":
-        return ("k_decode_fused_g" if G > 1 else "k_decode_fused"), sum(ab.values())
+def stage_kernels(plan, cfg, append):
+    """The kernel each stage of a step launches on this path (stage name ->
+    kernel name prefix in profiles), and each kernel's algorithmic bytes per
+    launch from the step's byte counts ``ab`` (selection moves no algorithmic
+    bytes: its reads and writes are intermediate data)."""
+    attn = "k_attn_gqa" if cfg.G > 1 else "k_attn"
     final = plan["n_split"] == 1
-    return "k_attn", ab["rows"] + ab["q"] + (ab["out"] if final else 0)
+    if plan["path"] == "fused":
+        return {"attn": "k_decode_fused_g" if cfg.G > 1 else "k_decode_fused"}
+    st = {}
+    if plan["path"] == "local":
+        st["score"] = "k_score_local"
+        st["select"] = "k_select_merge"
+    elif plan["path"] == "stream":
+        if append:
+            st["append"] = "k_label"
+        st["score"] = "k_score_chunk"
+        st["select"] = "k_select_stream"
+    elif append and cfg.k > 0:
+        st["append"] = "k_label"
+    st["attn"] = attn
+    if not final:
+        st["combine"] = "k_combine"
+    return st
+
+
+def kernel_bytes(stage, kernel, ab, final):
+    if kernel.startswith("k_decode_fused"):
+        return sum(ab.values())
+    if stage == "append":
+        return ab["append"]
+    if stage == "score":
+        return ab["labels"] + (ab["append"] if kernel == "k_score_local" else 0)
+    if stage == "select":
+        return 0
+    if stage == "attn":
+        return ab["rows"] + ab["q"] + (ab["out"] if final else 0)
+    if stage == "combine":
+        return ab["out"]
+    return 0
 
 
 def pct_us(ms_list):
@@ -176,9 +209,10 @@ def write_traffic(args):
     return 0
 
 
-def cpu_baseline(cfg, inp, seconds):
+def cpu_baseline(cfg, inp, seconds, threads=None):
     """The oracle (as it stands) on a bounded sample of the workload: a few
-    whole batch rows of one decode step, repeated for about `seconds`."""
+    whole batch rows of one decode step (one row with a single thread),
+    repeated for about `seconds`; all host threads unless `threads` is given."""
     import numpy as np
 
     import oracle
@@ -186,6 +220,8 @@ def cpu_baseline(cfg, inp, seconds):
     S = cfg.S0 + 1
     per_row = cfg.Hkv * (S * (cfg.r + 8) + min(cfg.k if cfg.k > 0 else S, S) * 600)
     n_b = max(1, min(cfg.B, int(2e8 // max(per_row, 1))))
+    if threads == 1:
+        n_b = 1
     q = inp.q[:n_b].cpu().numpy()
     K = inp.K[:n_b].cpu().numpy()
     V = inp.V[:n_b].cpu().numpy()
@@ -197,7 +233,7 @@ def cpu_baseline(cfg, inp, seconds):
         oracle.label_build(K, chan, lab, 0, cfg.S0)
     seq = np.full(n_b, S, np.int32)
     pos = seq - 1
-    threads = oracle.max_threads()
+    threads = threads or oracle.max_threads()
     reps = 0
     t0 = time.perf_counter()
     while True:
@@ -210,9 +246,9 @@ def cpu_baseline(cfg, inp, seconds):
         if el >= seconds:
             break
     return {"value": n_b * reps / el, "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d batch rows (all %d KV heads each), one decode step at S=%d "
+            "sample": "%s: %d of %d batch rows (all %d KV heads each), one decode step at S=%d "
                       "(label append + scores + top-k + attention), repeated %d times in %.1f s"
-                      % (n_b, cfg.B, cfg.Hkv, S, reps, el)}
+                      % (cfg.name, n_b, cfg.B, cfg.Hkv, S, reps, el)}
 
 
 def counter_reference_copy(torch, mib):
@@ -319,22 +355,222 @@ def run_calibration(args):
     return 0
 
 
+def measure(cfg, args, torch, ds, lib, layers=0, offload=False, cpu=True):
+    """Times `args.steps` decode steps of workload `cfg` (inputs resident in
+    HBM, `layers` rotated layer caches), then one more pass of the same steps
+    per kernel of the step with HIP events that the kernel's own launch
+    records.  Returns the result fields for the JSON line."""
+    import synth
+    dev = "cuda"
+    # Enough layer copies that one rotation moves well over the 256 MB
+    # Infinity Cache (about 1.5 GB of step bytes), 2 to 8 copies.
+    step0 = sum(algorithmic_bytes(cfg, cfg.S0 + 1).values())
+    L = layers if layers > 0 else max(2, min(8, int(math.ceil(1.5e9 / step0))))
+    if offload:
+        L = 1  # one K/V copy in pinned host memory; host reads never sit in the Infinity Cache
+    print("bench: workload %s (%s), %d layer caches" % (cfg.name, cfg.note, L), flush=True)
+    inp = synth.make_inputs(cfg, dev)
+    Ks, Vs, labs = [inp.K], [inp.V], []
+    for _ in range(1, L):
+        Ks.append(inp.K.clone())
+        Vs.append(inp.V.clone())
+    for l in range(L):
+        if cfg.k > 0:
+            lab = ds.LabelCache.allocate(cfg.B, cfg.Hkv, cfg.cap, cfg.r, cfg.int4, dev)
+            ds.label_build(Ks[l], inp.chan, lab, 0, cfg.S0)
+            labs.append(lab)
+        else:
+            labs.append(None)
+    if offload:
+        # K and V in pinned host memory (mapped into the GPU's address space);
+        # the labels and everything else stay in HBM
+        Ks = [torch.empty(inp.K.shape, dtype=inp.K.dtype, pin_memory=True)]
+        Vs = [torch.empty(inp.V.shape, dtype=inp.V.dtype, pin_memory=True)]
+        Ks[0].copy_(inp.K)
+        Vs[0].copy_(inp.V)
+        hip = ctypes.CDLL("libamdhip64.so")
+        for t in (Ks[0], Vs[0]):
+            dptr = ctypes.c_void_p()
+            rc = hip.hipHostGetDevicePointer(ctypes.byref(dptr), ctypes.c_void_p(t.data_ptr()), 0)
+            assert rc == 0 and dptr.value == t.data_ptr(), "pinned memory not mapped for the GPU"
+    n_q = 16
+    qs = [synth.make_q(cfg, dev, s) for s in range(n_q)]
+    seqs = [torch.full((cfg.B,), cfg.S0 + j + 1, dtype=torch.int32, device=dev)
+            for j in range(cfg.steps)]
+    out = torch.empty((cfg.B, cfg.Hq, cfg.d_v), dtype=torch.float16, device=dev)
+    ws_bytes = ds.workspace_size(inp.K, inp.V, cfg.Hq, cfg.D, labs[0], cfg.k, cfg.cap)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    print("bench: inputs ready (%.1f GB of K/V)" % (
+        L * (inp.K.numel() + inp.V.numel()) * 2 / 1e9), flush=True)
+
+    flags = ds.DECODE_APPEND if cfg.k > 0 else 0
+    if args.unfused:
+        flags |= ds.DECODE_UNFUSED
+    S_mid = cfg.S0 + 1 + min(cfg.steps - 1, (args.steps // L) // 2)
+    plan = ds.decode_plan(inp.K, inp.V, cfg.Hq, cfg.D, labs[0], cfg.k, S_mid, args.n_split, flags)
+    ab = algorithmic_bytes(cfg, S_mid)
+    kernels = stage_kernels(plan, cfg, bool(flags & ds.DECODE_APPEND))
+    final = plan["n_split"] == 1
+
+    # Pre-marshalled ctypes arguments per (layer, step): the timed loops only
+    # call into the library.
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    n_ev = ds.STAGE_COUNT + 1
+    P = ctypes.c_void_p
+    keep = []  # keeps ctypes objects alive
+
+    def make_call(i, events=None):
+        l = i % L
+        j = (i // L) % cfg.steps
+        kv = ds.kv_desc(Ks[l], Vs[l], cfg.Hq, cfg.D)
+        lab = labs[l].desc() if labs[l] is not None else None
+        opts = ds.DecodeOpts()
+        opts.n_split, opts.flags = args.n_split, flags
+        if events is not None:
+            opts.stage_events = events.slot_address((i - args.warmup) * n_ev)
+        keep.append((kv, lab, opts))
+        return (ctypes.byref(kv), P(qs[i % n_q].data_ptr()), P(Ks[l].data_ptr()),
+                P(Vs[l].data_ptr()), P(seqs[j].data_ptr()), cfg.S0 + j + 1,
+                P(inp.keep.data_ptr()) if inp.keep is not None else None,
+                P(inp.chan.data_ptr()) if inp.chan is not None else None,
+                ctypes.byref(lab) if lab is not None else None, cfg.k, cfg.sm_scale,
+                P(out.data_ptr()), None, P(ws.data_ptr()), ws.numel(), ctypes.byref(opts),
+                stream)
+
+    fn = lib.ds_decode_attn
+    for c in [make_call(i) for i in range(args.warmup)]:
+        rc = fn(*c)
+        assert rc == 0, ds.STATUS.get(rc, rc)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, nothing but the library calls.
+    timed = [make_call(args.warmup + i) for i in range(args.steps)]
+    t0 = time.perf_counter()
+    for c in timed:
+        fn(*c)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+
+    # Kernel-timing passes: the same K steps again, once per kernel of the
+    # step, with events recorded by that kernel's own launch (stage slots i
+    # and i + 1 only); or one pass with events between every stage.
+    per_kernel = []
+    stage_ms = {}
+    step_ms = []
+    if args.stage_events == "kernel":
+        for stage, kname in kernels.items():
+            si = ds.STAGES.index(stage)
+            skip = [x for x in range(args.steps * n_ev) if x % n_ev not in (si, si + 1)]
+            events = ds.HipEvents(args.steps * n_ev, skip=skip)
+            calls = [make_call(args.warmup + i, events) for i in range(args.steps)]
+            for c in calls:
+                fn(*c)
+            torch.cuda.synchronize()
+            ms = [events.elapsed_ms(i * n_ev + si, i * n_ev + si + 1) for i in range(args.steps)]
+            events.close()
+            stage_ms[stage] = ms
+            mean = sum(ms) / len(ms)
+            nbytes = kernel_bytes(stage, kname, ab, final)
+            gbs = nbytes / (mean * 1e-3) / 1e9
+            per_kernel.append({"kernel": kname, "stage": stage, "avg_us": round(mean * 1e3, 3),
+                               "us_p50_p90": pct_us(ms), "algorithmic_bytes": nbytes,
+                               "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    elif args.stage_events == "all":
+        events = ds.HipEvents(args.steps * n_ev)
+        calls = [make_call(args.warmup + i, events) for i in range(args.steps)]
+        for c in calls:
+            fn(*c)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            b = i * n_ev
+            for si, name in enumerate(ds.STAGES):
+                stage_ms.setdefault(name, []).append(events.elapsed_ms(b + si, b + si + 1))
+            step_ms.append(events.elapsed_ms(b, b + ds.STAGE_COUNT))
+        events.close()
+
+    step_bytes = sum(ab.values())
+    dom_stage = max(per_kernel, key=lambda d: d["avg_us"])["stage"] if per_kernel else "attn"
+    dom = kernels.get(dom_stage, kernels.get("attn"))
+    dom_bytes = kernel_bytes(dom_stage, dom, ab, final)
+    dom_ms = (sum(stage_ms[dom_stage]) / len(stage_ms[dom_stage])) if stage_ms.get(dom_stage) else None
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9 if dom_ms else None
+    res = {
+        "cfg": cfg, "inp": inp, "plan": plan, "L": L, "ms_step": ms_step,
+        "value": cfg.B * args.steps / wall,
+        "roofline": {"bound": "hbm", "kernel": dom,
+                     "achieved": round(achieved, 1) if achieved else None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
+                     "traffic": stored_traffic(cfg.name, dom),
+                     "algorithmic_bytes_per_launch": dom_bytes,
+                     "avg_launch_us": round(dom_ms * 1e3, 3) if dom_ms else None,
+                     "launch_us_p50_p90": pct_us(stage_ms.get(dom_stage)),
+                     "timing": "HIP events recorded by the kernel's own launch at its start "
+                               "and end, in a pass of the same %d steps of its own" % args.steps},
+        "step": {"algorithmic_bytes": step_bytes,
+                 "us": round(ms_step * 1e3, 3),
+                 "hbm_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+                 "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "bytes": ab, "kernels": per_kernel},
+        "config": {"workload": cfg.name, "batch": cfg.B, "q_heads": cfg.Hq,
+                   "kv_heads": cfg.Hkv, "head_dim": cfg.D, "k_cols": cfg.d_k, "prefill": cfg.S0,
+                   "r": cfg.r, "k": cfg.k,
+                   "labels": ("int4" if cfg.int4 else "fp16") if cfg.k > 0 else None,
+                   "storage": "fp16 q/K/V", "layer_caches": L, "path": plan["path"],
+                   "n_split": plan["n_split"], "note": cfg.note},
+    }
+    if step_ms:
+        res["step"]["us_p50_p90_events"] = pct_us(step_ms)
+        res["step"]["stage_mean_us_events"] = {k: round(sum(v) / len(v) * 1e3, 3)
+                                               for k, v in stage_ms.items()}
+    if offload:
+        # the selected K/V rows (and the appended token's K row) cross the host
+        # link; the attention kernel is priced against the link, not HBM
+        link = ab["rows"] + (cfg.B * cfg.Hkv * cfg.d_k * 2 if cfg.k > 0 else 0)
+        at_ms = (sum(stage_ms["attn"]) / len(stage_ms["attn"])) if stage_ms.get("attn") else None
+        ach = ab["rows"] / (at_ms * 1e-3) / 1e9 if at_ms else None
+        res["config"]["kv_memory"] = "pinned host"
+        res["roofline"].update({
+            "bound": "host_link", "kernel": kernels["attn"],
+            "achieved": round(ach, 2) if ach else None,
+            "peak": HOST_LINK_PEAK_GBS, "frac": round(ach / HOST_LINK_PEAK_GBS, 4) if ach else None,
+            "traffic": None, "algorithmic_bytes_per_launch": ab["rows"],
+            "avg_launch_us": round(at_ms * 1e3, 3) if at_ms else None})
+        res["offload"] = {"link_bytes_per_step": link,
+                          "link_gbs": round(link / (ms_step * 1e-3) / 1e9, 2)}
+    return res
+
+
+def release(torch, res):
+    """Drop a measured workload's tensors before the next one is built."""
+    res.pop("inp", None)
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="llama2_7b_4k")
+    ap.add_argument("--also", default=None,
+                    help="comma-separated further workloads measured in the same run and "
+                         "reported under 'also' (default: long_128k beside the 4K headline; "
+                         "'none' for none)")
     ap.add_argument("--layers", type=int, default=0,
                     help="independent layer caches rotated per step (0: enough that one "
                          "rotation is far larger than the Infinity Cache, 2 to 8)")
     ap.add_argument("--n-split", type=int, default=0)
     ap.add_argument("--unfused", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-events", choices=["kernel", "all", "none"], default="kernel",
-                    help="second pass of --steps steps with HIP events around the dominant "
-                         "kernel only, around every stage, or no second pass")
+                    help="per kernel of the step, a pass with events recorded by that kernel's "
+                         "own launch; or one pass with events between every stage; or none")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -370,191 +606,58 @@ def main():
     torch.cuda.set_device(0)
     lib = ds.load()
     cfg = synth.CONFIGS[args.workload]
-    dev = "cuda"
-    # Enough layer copies that one rotation moves well over the 256 MB
-    # Infinity Cache (about 1.5 GB of step bytes), 2 to 8 copies.
-    step0 = sum(algorithmic_bytes(cfg, cfg.S0 + 1).values())
-    L = args.layers if args.layers > 0 else max(2, min(8, int(math.ceil(1.5e9 / step0))))
-    if args.offload:
-        L = 1  # one K/V copy in pinned host memory; host reads never sit in the Infinity Cache
+    if args.also is None:
+        also = ["long_128k"] if args.workload == "llama2_7b_4k" and not args.offload else []
+    else:
+        also = [w for w in args.also.split(",") if w and w != "none"]
 
     if args.calib_copy_mb > 0:
         counter_reference_copy(torch, args.calib_copy_mb)
 
-    print("bench: workload %s (%s), %d layer caches" % (cfg.name, cfg.note, L), flush=True)
-    inp = synth.make_inputs(cfg, dev)
-    Ks, Vs, labs = [inp.K], [inp.V], []
-    for _ in range(1, L):
-        Ks.append(inp.K.clone())
-        Vs.append(inp.V.clone())
-    for l in range(L):
-        if cfg.k > 0:
-            lab = ds.LabelCache.allocate(cfg.B, cfg.Hkv, cfg.cap, cfg.r, cfg.int4, dev)
-            ds.label_build(Ks[l], inp.chan, lab, 0, cfg.S0)
-            labs.append(lab)
-        else:
-            labs.append(None)
-    if args.offload:
-        # K and V in pinned host memory (mapped into the GPU's address space);
-        # the labels and everything else stay in HBM
-        Ks = [torch.empty(inp.K.shape, dtype=inp.K.dtype, pin_memory=True)]
-        Vs = [torch.empty(inp.V.shape, dtype=inp.V.dtype, pin_memory=True)]
-        Ks[0].copy_(inp.K)
-        Vs[0].copy_(inp.V)
-        hip = ctypes.CDLL("libamdhip64.so")
-        for t in (Ks[0], Vs[0]):
-            dptr = ctypes.c_void_p()
-            rc = hip.hipHostGetDevicePointer(ctypes.byref(dptr), ctypes.c_void_p(t.data_ptr()), 0)
-            assert rc == 0 and dptr.value == t.data_ptr(), "pinned memory not mapped for the GPU"
-    n_q = 16
-    qs = [synth.make_q(cfg, dev, s) for s in range(n_q)]
-    seqs = [torch.full((cfg.B,), cfg.S0 + j + 1, dtype=torch.int32, device=dev)
-            for j in range(cfg.steps)]
-    out = torch.empty((cfg.B, cfg.Hq, cfg.d_v), dtype=torch.float16, device=dev)
-    ws_bytes = ds.workspace_size(inp.K, inp.V, cfg.Hq, cfg.D, labs[0], cfg.k, cfg.cap)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-    print("bench: inputs ready (%.1f GB of K/V)" % (
-        L * (inp.K.numel() + inp.V.numel()) * 2 / 1e9), flush=True)
-
-    flags = ds.DECODE_APPEND if cfg.k > 0 else 0
-    if args.unfused:
-        flags |= ds.DECODE_UNFUSED
-    S_mid = cfg.S0 + 1 + min(cfg.steps - 1, (args.steps // L) // 2)
-    plan = ds.decode_plan(inp.K, inp.V, cfg.Hq, cfg.D, labs[0], cfg.k, S_mid, args.n_split, flags)
-    ab = algorithmic_bytes(cfg, S_mid)
-    dom, dom_bytes = dominant_kernel(plan, ab, cfg.G)
-    dom_stage = ds.STAGES.index("attn")  # both dominant kernels run in the attention stage
-
-    # Pre-marshalled ctypes arguments per (layer, step): the timed loops only
-    # call into the library.
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    n_ev = ds.STAGE_COUNT + 1
-    total = args.warmup + 2 * args.steps
-    if args.stage_events == "all":
-        skip = ()
-    else:
-        skip = [i for i in range(args.steps * n_ev) if i % n_ev not in (dom_stage, dom_stage + 1)]
-    events = ds.HipEvents(args.steps * n_ev, skip=skip)
-    P = ctypes.c_void_p
-    keep = []  # keeps ctypes objects alive
-
-    def make_call(i, ev_base):
-        l = i % L
-        j = (i // L) % cfg.steps
-        kv = ds.kv_desc(Ks[l], Vs[l], cfg.Hq, cfg.D)
-        lab = labs[l].desc() if labs[l] is not None else None
-        opts = ds.DecodeOpts()
-        opts.n_split, opts.flags = args.n_split, flags
-        if ev_base is not None:
-            opts.stage_events = events.slot_address(ev_base)
-        keep.append((kv, lab, opts))
-        return (ctypes.byref(kv), P(qs[i % n_q].data_ptr()), P(Ks[l].data_ptr()),
-                P(Vs[l].data_ptr()), P(seqs[j].data_ptr()), cfg.S0 + j + 1,
-                P(inp.keep.data_ptr()) if inp.keep is not None else None,
-                P(inp.chan.data_ptr()) if inp.chan is not None else None,
-                ctypes.byref(lab) if lab is not None else None, cfg.k, cfg.sm_scale,
-                P(out.data_ptr()), None, P(ws.data_ptr()), ws.numel(), ctypes.byref(opts),
-                stream)
-
-    warm = [make_call(i, None) for i in range(args.warmup)]
-    timed = [make_call(args.warmup + i, None) for i in range(args.steps)]
-    kpass = [make_call(args.warmup + i, i * n_ev) for i in range(args.steps)]
-    fn = lib.ds_decode_attn
-
-    for c in warm:
-        rc = fn(*c)
-        assert rc == 0, ds.STATUS.get(rc, rc)
-    torch.cuda.synchronize()
-
-    # Timed region: K steps, nothing but the library calls.
-    t0 = time.perf_counter()
-    for c in timed:
-        fn(*c)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    # Kernel-timing pass: the same K steps again, HIP events recorded on the
-    # library's stream around the dominant kernel (or every stage).
-    stage_ms = {name: [] for name in ds.STAGES}
-    step_ms = []
-    if args.stage_events != "none":
-        for c in kpass:
-            fn(*c)
-        torch.cuda.synchronize()
-        for i in range(args.steps):
-            b = i * n_ev
-            for si, name in enumerate(ds.STAGES):
-                if events.handles[b + si] and events.handles[b + si + 1]:
-                    stage_ms[name].append(events.elapsed_ms(b + si, b + si + 1))
-            if events.handles[b] and events.handles[b + ds.STAGE_COUNT]:
-                step_ms.append(events.elapsed_ms(b, b + ds.STAGE_COUNT))
-    mean = {k: (sum(v) / len(v) if v else None) for k, v in stage_ms.items()}
-
+    res = measure(cfg, args, torch, ds, lib, args.layers, args.offload)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, res["inp"], args.cpu_seconds)
+        # single-thread figures beside it: this workload and the tiny one
+        one = [cpu_baseline(cfg, res["inp"], 4.0, threads=1)]
+        if cfg.name != "tiny":
+            tiny = synth.CONFIGS["tiny"]
+            one.append(cpu_baseline(tiny, synth.make_inputs(tiny, "cpu"), 3.0, threads=1))
+        cpu["one_thread"] = [{k: v for k, v in o.items() if k != "kind"} for o in one]
+    release(torch, res)
+    others = {}
+    for w in also:
+        r2 = measure(synth.CONFIGS[w], args, torch, ds, lib)
+        release(torch, r2)
+        others[w] = {"queries_per_s": round(r2["value"], 1), "ms_per_step": round(r2["ms_step"], 5),
+                     "config": r2["config"], "step": r2["step"], "roofline": r2["roofline"]}
     copy_gbs = copy_ceiling_gbs(torch)
-
-    value = cfg.B * args.steps / wall
-    ms_step = wall / args.steps * 1e3
-    dom_ms = mean["attn"]
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9 if dom_ms else None
-    traffic = stored_traffic(cfg.name, dom)
-    step_bytes = sum(ab.values())
+    rf = res["roofline"]
+    rf["copy_gbs"] = round(copy_gbs, 1)
+    rf["frac_of_copy"] = round(rf["achieved"] / copy_gbs, 4) if rf.get("achieved") else None
     result = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": round(res["value"], 1),
         "unit": "queries/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": round(res["ms_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "batch": cfg.B, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv,
-                   "head_dim": cfg.D, "k_cols": cfg.d_k, "prefill": cfg.S0, "r": cfg.r,
-                   "k": cfg.k, "labels": ("int4" if cfg.int4 else "fp16") if cfg.k > 0 else None,
-                   "storage": "fp16 q/K/V", "layer_caches": L, "path": plan["path"],
-                   "n_split": plan["n_split"], "note": cfg.note},
-        "roofline": {"bound": "hbm", "kernel": dom,
-                     "achieved": round(achieved, 1) if achieved else None,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
-                     "traffic": traffic,
-                     "algorithmic_bytes_per_launch": dom_bytes,
-                     "avg_launch_us": round(dom_ms * 1e3, 3) if dom_ms else None,
-                     "launch_us_p50_p90": pct_us(stage_ms["attn"]),
-                     "copy_gbs": round(copy_gbs, 1),
-                     "frac_of_copy": round(achieved / copy_gbs, 4) if achieved else None,
-                     "timing": "HIP events recorded by the kernel's own launch at its start "
-                               "and end, in a second pass of the same %d steps" % args.steps},
-        "step": {"algorithmic_bytes": step_bytes,
-                 "hbm_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
-                 "hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                 "bytes": ab,
-                 "stage_mean_us": {k: (round(v * 1e3, 3) if v is not None else None)
-                                   for k, v in mean.items()}},
+        "config": res["config"],
+        "roofline": rf,
+        "step": res["step"],
     }
-    if step_ms:
-        result["step"]["us_p50_p90_events"] = pct_us(step_ms)
-    if args.offload:
-        # the selected K/V rows (and the appended token's K row) cross the host
-        # link; the dominant kernel is priced against the link, not HBM
-        link = ab["rows"] + (cfg.B * cfg.Hkv * cfg.d_k * 2 if cfg.k > 0 else 0)
-        dom_link = ab["rows"]  # the dominant kernel is the one that reads the rows
-        ach = dom_link / (dom_ms * 1e-3) / 1e9 if dom_ms else None
-        result["config"]["kv_memory"] = "pinned host"
-        result["roofline"].update({
-            "bound": "host_link", "achieved": round(ach, 2) if ach else None,
-            "peak": HOST_LINK_PEAK_GBS, "frac": round(ach / HOST_LINK_PEAK_GBS, 4) if ach else None,
-            "traffic": None, "algorithmic_bytes_per_launch": dom_link,
-            "copy_gbs": None, "frac_of_copy": None})
-        result["offload"] = {"link_bytes_per_step": link,
-                             "link_gbs": round(link / (ms_step * 1e-3) / 1e9, 2)}
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
-    events.close()
+    if "offload" in res:
+        result["offload"] = res["offload"]
+    if others:
+        result["also"] = others
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
     return 0
 

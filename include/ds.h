@@ -151,14 +151,16 @@ typedef struct {
                         row's selected tokens in the attention pass (clamped to
                         the range the workspace was sized for) */
   uint32_t flags;    /* DS_DECODE_* */
-  hipEvent_t* stage_events; /* NULL, or DS_STAGE_COUNT + 1 event slots: event i
-                               is recorded on `stream` before stage i, the last
-                               one after the final stage (stages that launch
-                               nothing give empty intervals); NULL slots are
-                               skipped.  The attention stage is one kernel:
-                               when slots DS_STAGE_ATTN and DS_STAGE_COMBINE
-                               are both given, that launch records them at the
-                               kernel's own start and end */
+  hipEvent_t* stage_events; /* NULL, or DS_STAGE_COUNT + 1 event slots (NULL
+                               slots are skipped).  When exactly two adjacent
+                               slots i and i + 1 are given, stage i's kernel
+                               launch records them at the kernel's own start
+                               and end (a stage that launches nothing records
+                               them back to back); on the one-kernel path that
+                               launch is the attention stage's.  Otherwise
+                               event i is recorded on `stream` before stage i
+                               and the last one after the final stage (stages
+                               that launch nothing give empty intervals). */
 } ds_decode_opts;
 
 /* Kernel paths of ds_decode_attn. */

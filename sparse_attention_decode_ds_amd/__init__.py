@@ -321,8 +321,11 @@ def decode_attn(q, K, V, seq_lens, max_seq_len: int, k: int, sm_scale: float,
             k, topk_idx = 0, None
     B, Hq, d_q = q.shape
     if validate_tables:
-        check_tables(chan if k > 0 else None, K.shape[3], labels.r if labels is not None else None,
-                     keep, d_q, K.shape[1])
+        # chan is read by the sparse path and by the label append (a dense
+        # step with DECODE_APPEND still appends the current token's label)
+        uses_chan = k > 0 or bool(flags & DECODE_APPEND)
+        check_tables(chan if uses_chan else None, K.shape[3],
+                     labels.r if labels is not None else None, keep, d_q, K.shape[1])
     kv = kv_desc(K, V, Hq, d_q)
     lab = labels.desc() if labels is not None and (k > 0 or flags & DECODE_APPEND) else None
     lib = load()

@@ -368,18 +368,39 @@ ds_status decode_impl(const ds_kv_desc* kv, const void* q, const void* K, const 
   const int64_t rows = (int64_t)B * Hkv;
   char* ws = static_cast<char*>(workspace);
   hipEvent_t* ev = opts ? opts->stage_events : nullptr;
-  auto mark = [&](int i) {
-    if (ev && ev[i]) (void)hipEventRecord(ev[i], stream);
-  };
-  // The attention stage is one kernel: when both of its events are given,
-  // the launch records them at the kernel's own start and end.
-  KEvents attn_ev;
-  if (ev && ev[DS_STAGE_ATTN] && ev[DS_STAGE_COMBINE]) {
-    attn_ev.start = ev[DS_STAGE_ATTN];
-    attn_ev.stop = ev[DS_STAGE_COMBINE];
+  // Kernel timing: when exactly two adjacent slots i and i + 1 are given,
+  // stage i's launch records them at the kernel's own start and end (a stage
+  // that launches nothing records them back to back); otherwise every given
+  // slot is recorded on the stream between the stages.
+  int own = -1;
+  if (ev) {
+    int n = 0, first = -1;
+    for (int i = 0; i <= DS_STAGE_COUNT; ++i)
+      if (ev[i]) {
+        ++n;
+        if (first < 0) first = i;
+      }
+    if (n == 2 && first < DS_STAGE_COUNT && ev[first + 1]) own = first;
   }
-  auto mark_attn = [&](int i) {
-    if (!attn_ev.start) mark(i);
+  bool own_done = false;
+  auto kev = [&](int i) {
+    KEvents e;
+    if (own == i) {
+      e.start = ev[i];
+      e.stop = ev[i + 1];
+      own_done = true;
+    }
+    return e;
+  };
+  auto mark = [&](int i) {
+    if (own < 0 && ev && ev[i]) (void)hipEventRecord(ev[i], stream);
+  };
+  auto mark_end = [&]() {
+    if (own >= 0 && !own_done) {
+      (void)hipEventRecord(ev[own], stream);
+      (void)hipEventRecord(ev[own + 1], stream);
+    }
+    mark(DS_STAGE_COUNT);
   };
 
   mark(DS_STAGE_APPEND);
@@ -394,7 +415,8 @@ ds_status decode_impl(const ds_kv_desc* kv, const void* q, const void* K, const 
     la.pos = seq_lens;
     la.pos_minus_one = 1;
     la.n_items = (int)rows;
-    if (launch_label(la, (int)ceil_div(rows, 64), stream) != hipSuccess) return DS_ERR_HIP;
+    if (launch_label(la, (int)ceil_div(rows, 64), stream, kev(DS_STAGE_APPEND)) != hipSuccess)
+      return DS_ERR_HIP;
   }
 
   const int32_t* idx = nullptr;
@@ -452,29 +474,32 @@ ds_status decode_impl(const ds_kv_desc* kv, const void* q, const void* K, const 
       AttnArgs aa = attn_args(kv, q, K, V, seq_lens, max_seq_len, keep, sm_scale, out, ws, p);
       aa.n_split = 1;
       mark(DS_STAGE_SELECT);
-      mark_attn(DS_STAGE_ATTN);
+      mark(DS_STAGE_ATTN);
       const int app = (flags & DS_DECODE_APPEND) ? 1 : 0;
       const hipError_t e =
-          G == 1 ? launch_decode_fused(sa, aa, la, app, (int)rows, stream, attn_ev)
-                 : launch_decode_fused_g(sa, aa, la, app, (int)rows, stream, attn_ev);
+          G == 1 ? launch_decode_fused(sa, aa, la, app, (int)rows, stream, kev(DS_STAGE_ATTN))
+                 : launch_decode_fused_g(sa, aa, la, app, (int)rows, stream, kev(DS_STAGE_ATTN));
       if (e != hipSuccess) return DS_ERR_HIP;
-      mark_attn(DS_STAGE_COMBINE);
-      mark(DS_STAGE_COUNT);
+      mark(DS_STAGE_COMBINE);
+      mark_end();
       return DS_OK;
     }
     if (local_path) {
       LabelArgs la = label_args(kv, K, chan, lab);
       sa.chunk = p.local_chunk;
       sa.n_chunks = p.local_nch;
-      if (launch_score_local(sa, la, (flags & DS_DECODE_APPEND) ? 1 : 0, (int)rows, stream) !=
-          hipSuccess)
+      if (launch_score_local(sa, la, (flags & DS_DECODE_APPEND) ? 1 : 0, (int)rows, stream,
+                             kev(DS_STAGE_SCORE)) != hipSuccess)
         return DS_ERR_HIP;
       mark(DS_STAGE_SELECT);
-      if (launch_select_merge(sa, (int)rows, stream) != hipSuccess) return DS_ERR_HIP;
+      if (launch_select_merge(sa, (int)rows, stream, kev(DS_STAGE_SELECT)) != hipSuccess)
+        return DS_ERR_HIP;
     } else {
-      if (launch_score_chunks(sa, (int)rows, stream) != hipSuccess) return DS_ERR_HIP;
+      if (launch_score_chunks(sa, (int)rows, stream, kev(DS_STAGE_SCORE)) != hipSuccess)
+        return DS_ERR_HIP;
       mark(DS_STAGE_SELECT);
-      if (launch_select_stream(sa, (int)rows, stream) != hipSuccess) return DS_ERR_HIP;
+      if (launch_select_stream(sa, (int)rows, stream, kev(DS_STAGE_SELECT)) != hipSuccess)
+        return DS_ERR_HIP;
     }
   } else {
     mark(DS_STAGE_SELECT);
@@ -488,12 +513,14 @@ ds_status decode_impl(const ds_kv_desc* kv, const void* q, const void* K, const 
   aa.n_split = rt.n_split;
   aa.tps = rt.tps;
 
-  mark_attn(DS_STAGE_ATTN);
+  mark(DS_STAGE_ATTN);
   const bool final_out = aa.n_split == 1;
-  if (launch_attn(aa, (int)rows, G, final_out, stream, attn_ev) != hipSuccess) return DS_ERR_HIP;
-  mark_attn(DS_STAGE_COMBINE);
-  if (!final_out && launch_combine(aa, B, stream) != hipSuccess) return DS_ERR_HIP;
-  mark(DS_STAGE_COUNT);
+  if (launch_attn(aa, (int)rows, G, final_out, stream, kev(DS_STAGE_ATTN)) != hipSuccess)
+    return DS_ERR_HIP;
+  mark(DS_STAGE_COMBINE);
+  if (!final_out && launch_combine(aa, B, stream, kev(DS_STAGE_COMBINE)) != hipSuccess)
+    return DS_ERR_HIP;
+  mark_end();
   return DS_OK;
 }
 

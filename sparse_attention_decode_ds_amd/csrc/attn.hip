@@ -74,12 +74,11 @@ hipError_t launch_attn(const AttnArgs& a, int rows, int G, bool final_out, hipSt
   return launch_attn_gqa(a, rows, G, final_out, s, ev);
 }
 
-hipError_t launch_combine(const AttnArgs& a, int B, hipStream_t s) {
+hipError_t launch_combine(const AttnArgs& a, int B, hipStream_t s, const KEvents& ev) {
   const int n_rows = B * a.Hq;
   if (n_rows <= 0) return hipSuccess;
   const int per = kAttnThreads / 16;
-  hipLaunchKernelGGL(k_combine, dim3((n_rows + per - 1) / per), dim3(kAttnThreads), 0, s, a, n_rows);
-  return hipGetLastError();
+  return launch_k(k_combine, dim3((n_rows + per - 1) / per), dim3(kAttnThreads), s, ev, a, n_rows);
 }
 
 }  // namespace ds

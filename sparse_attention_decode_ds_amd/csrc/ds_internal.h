@@ -150,15 +150,18 @@ struct CalibPlan {
 CalibPlan calib_plan(int B, int Hkv, int n_tok, int d_k, int n_qrows);
 
 // Launchers (return the launch status of the last kernel they enqueue).
-hipError_t launch_label(const LabelArgs& a, int n_blocks, hipStream_t s);
+hipError_t launch_label(const LabelArgs& a, int n_blocks, hipStream_t s,
+                        const KEvents& ev = KEvents());
 hipError_t launch_calib(const CalibArgs& a, int64_t blocks, hipStream_t s);
-hipError_t launch_score_chunks(const ScoreArgs& a, int rows, hipStream_t s);
-hipError_t launch_select_stream(const ScoreArgs& a, int rows, hipStream_t s);
+hipError_t launch_score_chunks(const ScoreArgs& a, int rows, hipStream_t s,
+                               const KEvents& ev = KEvents());
+hipError_t launch_select_stream(const ScoreArgs& a, int rows, hipStream_t s,
+                                const KEvents& ev = KEvents());
 hipError_t launch_attn(const AttnArgs& a, int rows, int G, bool final_out, hipStream_t s,
                        const KEvents& ev = KEvents());
 hipError_t launch_attn_gqa(const AttnArgs& a, int rows, int G, bool final_out, hipStream_t s,
                            const KEvents& ev = KEvents());
-hipError_t launch_combine(const AttnArgs& a, int B, hipStream_t s);
+hipError_t launch_combine(const AttnArgs& a, int B, hipStream_t s, const KEvents& ev = KEvents());
 hipError_t launch_decode_fused(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la,
                                int append, int rows, hipStream_t s, const KEvents& ev = KEvents());
 bool decode_fused_fits(int max_seq, int k, int r, int is_int4);
@@ -167,8 +170,9 @@ hipError_t launch_decode_fused_g(const ScoreArgs& sa, const AttnArgs& aa, const 
                                  const KEvents& ev = KEvents());
 bool decode_fused_g_fits(int max_seq, int k, int r, int is_int4, int G);
 hipError_t launch_score_local(const ScoreArgs& sa, const LabelArgs& la, int append, int rows,
-                              hipStream_t s);
-hipError_t launch_select_merge(const ScoreArgs& sa, int rows, hipStream_t s);
+                              hipStream_t s, const KEvents& ev = KEvents());
+hipError_t launch_select_merge(const ScoreArgs& sa, int rows, hipStream_t s,
+                               const KEvents& ev = KEvents());
 
 // ---------------------------------------------------------------------------
 // Device helpers.

@@ -120,10 +120,9 @@ __global__ __launch_bounds__(kThreads) void k_label(LabelArgs a) {
 
 }  // namespace
 
-hipError_t launch_label(const LabelArgs& a, int n_blocks, hipStream_t s) {
+hipError_t launch_label(const LabelArgs& a, int n_blocks, hipStream_t s, const KEvents& ev) {
   if (n_blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_label, dim3(n_blocks), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  return launch_k(k_label, dim3(n_blocks), dim3(kThreads), s, ev, a);
 }
 
 }  // namespace ds

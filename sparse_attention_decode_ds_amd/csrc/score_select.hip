@@ -89,17 +89,19 @@ struct ChunkK {
 
 }  // namespace
 
-hipError_t launch_score_chunks(const ScoreArgs& a, int rows, hipStream_t s) {
+hipError_t launch_score_chunks(const ScoreArgs& a, int rows, hipStream_t s, const KEvents& ev) {
   if (rows <= 0 || a.n_chunks <= 0) return hipSuccess;
   void* fn = Pick<ChunkK, kChunkThreads>::get(a.r, a.is_int4 != 0);
   void* args[] = {const_cast<ScoreArgs*>(&a)};
+  if (ev.start && ev.stop)
+    return hipExtLaunchKernel(fn, dim3(rows * a.n_chunks), dim3(kChunkThreads), args, 0, s,
+                              ev.start, ev.stop, 0);
   return hipLaunchKernel(fn, dim3(rows * a.n_chunks), dim3(kChunkThreads), args, 0, s);
 }
 
-hipError_t launch_select_stream(const ScoreArgs& a, int rows, hipStream_t s) {
+hipError_t launch_select_stream(const ScoreArgs& a, int rows, hipStream_t s, const KEvents& ev) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_select_stream<kSelectThreads>, dim3(rows), dim3(kSelectThreads), 0, s, a);
-  return hipGetLastError();
+  return launch_k(k_select_stream<kSelectThreads>, dim3(rows), dim3(kSelectThreads), s, ev, a);
 }
 
 }  // namespace ds

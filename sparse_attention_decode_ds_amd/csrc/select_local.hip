@@ -458,48 +458,45 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
 
 template <int R, bool INT4>
 hipError_t launch_local_rt(const ScoreArgs& sa, const LabelArgs& la, int append, int rows,
-                           hipStream_t s) {
+                           hipStream_t s, const KEvents& ev) {
   const dim3 grid(rows * sa.n_chunks);
   if (sa.chunk > 512 * 16)
-    hipLaunchKernelGGL((k_score_local<512, 20, R, INT4>), grid, dim3(512), 0, s, sa, la, append);
-  else if (sa.chunk > 256 * 16)
-    hipLaunchKernelGGL((k_score_local<512, 16, R, INT4>), grid, dim3(512), 0, s, sa, la, append);
-  else
-    hipLaunchKernelGGL((k_score_local<256, 16, R, INT4>), grid, dim3(256), 0, s, sa, la, append);
-  return hipGetLastError();
+    return launch_k(k_score_local<512, 20, R, INT4>, grid, dim3(512), s, ev, sa, la, append);
+  if (sa.chunk > 256 * 16)
+    return launch_k(k_score_local<512, 16, R, INT4>, grid, dim3(512), s, ev, sa, la, append);
+  return launch_k(k_score_local<256, 16, R, INT4>, grid, dim3(256), s, ev, sa, la, append);
 }
 
 template <int R, bool INT4>
-hipError_t launch_merge_rt(const ScoreArgs& sa, int rows, hipStream_t s) {
-  hipLaunchKernelGGL((k_select_merge<R, INT4>), dim3(rows), dim3(kNTM), 0, s, sa);
-  return hipGetLastError();
+hipError_t launch_merge_rt(const ScoreArgs& sa, int rows, hipStream_t s, const KEvents& ev) {
+  return launch_k(k_select_merge<R, INT4>, dim3(rows), dim3(kNTM), s, ev, sa);
 }
 
 }  // namespace
 
 hipError_t launch_score_local(const ScoreArgs& sa, const LabelArgs& la, int append, int rows,
-                              hipStream_t s) {
+                              hipStream_t s, const KEvents& ev) {
   if (rows <= 0) return hipSuccess;
   if (sa.is_int4) {
-    if (sa.r == 8) return launch_local_rt<8, true>(sa, la, append, rows, s);
-    if (sa.r == 16) return launch_local_rt<16, true>(sa, la, append, rows, s);
-    return launch_local_rt<0, true>(sa, la, append, rows, s);
+    if (sa.r == 8) return launch_local_rt<8, true>(sa, la, append, rows, s, ev);
+    if (sa.r == 16) return launch_local_rt<16, true>(sa, la, append, rows, s, ev);
+    return launch_local_rt<0, true>(sa, la, append, rows, s, ev);
   }
-  if (sa.r == 8) return launch_local_rt<8, false>(sa, la, append, rows, s);
-  if (sa.r == 16) return launch_local_rt<16, false>(sa, la, append, rows, s);
-  return launch_local_rt<0, false>(sa, la, append, rows, s);
+  if (sa.r == 8) return launch_local_rt<8, false>(sa, la, append, rows, s, ev);
+  if (sa.r == 16) return launch_local_rt<16, false>(sa, la, append, rows, s, ev);
+  return launch_local_rt<0, false>(sa, la, append, rows, s, ev);
 }
 
-hipError_t launch_select_merge(const ScoreArgs& sa, int rows, hipStream_t s) {
+hipError_t launch_select_merge(const ScoreArgs& sa, int rows, hipStream_t s, const KEvents& ev) {
   if (rows <= 0) return hipSuccess;
   if (sa.is_int4) {
-    if (sa.r == 8) return launch_merge_rt<8, true>(sa, rows, s);
-    if (sa.r == 16) return launch_merge_rt<16, true>(sa, rows, s);
-    return launch_merge_rt<0, true>(sa, rows, s);
+    if (sa.r == 8) return launch_merge_rt<8, true>(sa, rows, s, ev);
+    if (sa.r == 16) return launch_merge_rt<16, true>(sa, rows, s, ev);
+    return launch_merge_rt<0, true>(sa, rows, s, ev);
   }
-  if (sa.r == 8) return launch_merge_rt<8, false>(sa, rows, s);
-  if (sa.r == 16) return launch_merge_rt<16, false>(sa, rows, s);
-  return launch_merge_rt<0, false>(sa, rows, s);
+  if (sa.r == 8) return launch_merge_rt<8, false>(sa, rows, s, ev);
+  if (sa.r == 16) return launch_merge_rt<16, false>(sa, rows, s, ev);
+  return launch_merge_rt<0, false>(sa, rows, s, ev);
 }
 
 }  // namespace ds

@@ -235,6 +235,24 @@ def test_check_tables_host_logic():
             ds.check_tables(**kw)
 
 
+def test_dense_append_step_checks_the_channel_table():
+    """A dense step (k <= 0) with DECODE_APPEND still appends the current
+    token's label, which reads the heavy-channel table: validate_tables must
+    reject a bad table there before anything reaches the library (CPU
+    tensors; the check raises before any call)."""
+    import torch
+    B, Hq, Hkv, cap, D = 1, 2, 2, 64, 128
+    q = torch.zeros((B, Hq, D), dtype=torch.float16)
+    K = torch.zeros((B, Hkv, cap, D), dtype=torch.float16)
+    bad = torch.tensor([[0, 200], [1, 2]], dtype=torch.int32)   # column 200 >= d_k
+    lab = ds.LabelCache(2, ds.LABEL_F16, cap, torch.zeros((B, Hkv, cap, 2), dtype=torch.float16),
+                        None)
+    seq = torch.full((B,), 10, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        ds.decode_attn(q, K, K, seq, 10, 0, 0.088, chan=bad, labels=lab,
+                       flags=ds.DECODE_APPEND, validate_tables=True)
+
+
 @pytest.mark.parametrize("G,max_seq,path", [
     (1, 6144, "fused"), (1, 6145, "local"),        # 256 threads x 24 scores
     (7, 16384, "fused"), (7, 16385, "local"),      # 1024 threads x 16 scores

@@ -1,5 +1,5 @@
 """bench.py host logic without a GPU: the algorithmic byte counts of the
-workloads, the dominant-kernel choice per path, the one-GPU contract and the
+workloads, the kernels of each path and their bytes, the one-GPU contract and the
 source hash that keys the stored counter records, and the counter record of
 the calibration workload."""
 import os
@@ -27,12 +27,33 @@ def test_algorithmic_bytes_of_the_workloads():
     assert ab["labels"] == 0 and ab["rows"] == 32 * 4 * 32769 * (32 + 128) * 2
 
 
-def test_dominant_kernel_per_path():
+def test_kernels_of_each_path_and_their_bytes():
+    """Every kernel a step launches, per path, with its algorithmic bytes: the
+    one-kernel step owns all of them; the label stream belongs to the score
+    kernel, the selected rows, query and (with one split) the output to the
+    attention kernel, the output to the merge of splits, none to the select."""
     ab = {"labels": 10, "append": 1, "rows": 100, "q": 2, "out": 3}
-    assert bench.dominant_kernel({"path": "fused", "n_split": 1}, ab, 1) == ("k_decode_fused", 116)
-    assert bench.dominant_kernel({"path": "fused", "n_split": 1}, ab, 7)[0] == "k_decode_fused_g"
-    assert bench.dominant_kernel({"path": "local", "n_split": 8}, ab, 1) == ("k_attn", 102)
-    assert bench.dominant_kernel({"path": "dense", "n_split": 1}, ab, 7) == ("k_attn", 105)
+    mha, gqa = synth.CONFIGS["llama2_7b_4k"], synth.CONFIGS["qwen25_7b_gqa_8k"]
+    assert bench.stage_kernels({"path": "fused", "n_split": 1}, mha, True) == {"attn": "k_decode_fused"}
+    assert bench.stage_kernels({"path": "fused", "n_split": 1}, gqa, True) == {"attn": "k_decode_fused_g"}
+    loc = bench.stage_kernels({"path": "local", "n_split": 8}, mha, True)
+    assert loc == {"score": "k_score_local", "select": "k_select_merge", "attn": "k_attn",
+                   "combine": "k_combine"}
+    st = bench.stage_kernels({"path": "stream", "n_split": 1}, gqa, True)
+    assert st == {"append": "k_label", "score": "k_score_chunk", "select": "k_select_stream",
+                  "attn": "k_attn_gqa"}
+    dense = bench.stage_kernels({"path": "dense", "n_split": 4}, synth.CONFIGS["leank_dense"], False)
+    assert dense == {"attn": "k_attn_gqa", "combine": "k_combine"}
+    kb = bench.kernel_bytes
+    assert kb("attn", "k_decode_fused", ab, True) == 116
+    assert kb("score", "k_score_local", ab, False) == 11
+    assert kb("score", "k_score_chunk", ab, False) == 10
+    assert kb("append", "k_label", ab, False) == 1
+    assert kb("select", "k_select_merge", ab, False) == 0
+    assert kb("attn", "k_attn", ab, False) == 102 and kb("attn", "k_attn", ab, True) == 105
+    assert kb("combine", "k_combine", ab, False) == 3
+    # the kernels of a local step together own every algorithmic byte once
+    assert sum(kb(s, k, ab, False) for s, k in loc.items()) == sum(ab.values())
 
 
 def test_more_than_one_gpu_is_refused():
