@@ -355,6 +355,22 @@ def run_calibration(args):
     return 0
 
 
+def to_page_pool(torch, X, P, seed):
+    """A contiguous cache [B][H][cap][d] scattered into a pool of P-token
+    pages under a shuffled page table (logical page p of row b at page
+    table[b][p]); returns (pool [n_pages][H][P][d], table int32 [B][pages])."""
+    B, H, cap, d = X.shape
+    mp = (cap + P - 1) // P
+    g = torch.Generator().manual_seed(seed)
+    table = torch.randperm(B * mp, generator=g).view(B, mp).to(torch.int32)
+    pool = torch.zeros((B * mp, H, P, d), dtype=X.dtype, device=X.device)
+    Xp = torch.zeros((B, H, mp * P, d), dtype=X.dtype, device=X.device)
+    Xp[:, :, :cap] = X
+    pool[table.reshape(-1).long().to(X.device)] = (
+        Xp.view(B, H, mp, P, d).permute(0, 2, 1, 3, 4).reshape(B * mp, H, P, d))
+    return pool, table.to(X.device)
+
+
 def measure(cfg, args, torch, ds, lib, layers=0, offload=False, cpu=True):
     """Times `args.steps` decode steps of workload `cfg` (inputs resident in
     HBM, `layers` rotated layer caches), then one more pass of the same steps
@@ -374,10 +390,20 @@ def measure(cfg, args, torch, ds, lib, layers=0, offload=False, cpu=True):
     for _ in range(1, L):
         Ks.append(inp.K.clone())
         Vs.append(inp.V.clone())
+    pages = [None] * L
+    cap = cfg.cap
+    if args.page_size > 0:
+        # K/V of every layer in a pool of page_size-token pages under its own
+        # shuffled page table (the serving system's token pool)
+        for l in range(L):
+            Ks[l], table = to_page_pool(torch, Ks[l], args.page_size, 11 + l)
+            Vs[l], _ = to_page_pool(torch, Vs[l], args.page_size, 11 + l)
+            pages[l] = ds.Pages(table, args.page_size)
+        cap = pages[0].table.shape[1] * args.page_size
     for l in range(L):
         if cfg.k > 0:
-            lab = ds.LabelCache.allocate(cfg.B, cfg.Hkv, cfg.cap, cfg.r, cfg.int4, dev)
-            ds.label_build(Ks[l], inp.chan, lab, 0, cfg.S0)
+            lab = ds.LabelCache.allocate(cfg.B, cfg.Hkv, cap, cfg.r, cfg.int4, dev)
+            ds.label_build(Ks[l], inp.chan, lab, 0, cfg.S0, pages=pages[l])
             labs.append(lab)
         else:
             labs.append(None)
@@ -398,7 +424,8 @@ def measure(cfg, args, torch, ds, lib, layers=0, offload=False, cpu=True):
     seqs = [torch.full((cfg.B,), cfg.S0 + j + 1, dtype=torch.int32, device=dev)
             for j in range(cfg.steps)]
     out = torch.empty((cfg.B, cfg.Hq, cfg.d_v), dtype=torch.float16, device=dev)
-    ws_bytes = ds.workspace_size(inp.K, inp.V, cfg.Hq, cfg.D, labs[0], cfg.k, cfg.cap)
+    ws_bytes = ds.workspace_size(Ks[0], Vs[0], cfg.Hq, cfg.D, labs[0], cfg.k, cap,
+                                 pages=pages[0])
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     print("bench: inputs ready (%.1f GB of K/V)" % (
@@ -408,7 +435,8 @@ def measure(cfg, args, torch, ds, lib, layers=0, offload=False, cpu=True):
     if args.unfused:
         flags |= ds.DECODE_UNFUSED
     S_mid = cfg.S0 + 1 + min(cfg.steps - 1, (args.steps // L) // 2)
-    plan = ds.decode_plan(inp.K, inp.V, cfg.Hq, cfg.D, labs[0], cfg.k, S_mid, args.n_split, flags)
+    plan = ds.decode_plan(Ks[0], Vs[0], cfg.Hq, cfg.D, labs[0], cfg.k, S_mid, args.n_split, flags,
+                          pages=pages[0])
     ab = algorithmic_bytes(cfg, S_mid)
     kernels = stage_kernels(plan, cfg, bool(flags & ds.DECODE_APPEND))
     final = plan["n_split"] == 1
@@ -423,7 +451,7 @@ def measure(cfg, args, torch, ds, lib, layers=0, offload=False, cpu=True):
     def make_call(i, events=None):
         l = i % L
         j = (i // L) % cfg.steps
-        kv = ds.kv_desc(Ks[l], Vs[l], cfg.Hq, cfg.D)
+        kv = ds.kv_desc(Ks[l], Vs[l], cfg.Hq, cfg.D, pages=pages[l])
         lab = labs[l].desc() if labs[l] is not None else None
         opts = ds.DecodeOpts()
         opts.n_split, opts.flags = args.n_split, flags
@@ -518,7 +546,9 @@ def measure(cfg, args, torch, ds, lib, layers=0, offload=False, cpu=True):
                    "kv_heads": cfg.Hkv, "head_dim": cfg.D, "k_cols": cfg.d_k, "prefill": cfg.S0,
                    "r": cfg.r, "k": cfg.k,
                    "labels": ("int4" if cfg.int4 else "fp16") if cfg.k > 0 else None,
-                   "storage": "fp16 q/K/V", "layer_caches": L, "path": plan["path"],
+                   "storage": ("fp16 q, fp16 K/V in a pool of %d-token pages" % args.page_size
+                               if args.page_size > 0 else "fp16 q/K/V"),
+                   "layer_caches": L, "path": plan["path"],
                    "n_split": plan["n_split"], "note": cfg.note},
     }
     if step_ms:
@@ -579,6 +609,9 @@ def main():
     ap.add_argument("--traffic-kernel", default="k_decode_fused")
     ap.add_argument("--traffic-cmd", action="append", help="command recorded with the counters")
     ap.add_argument("--traffic-out", default=None, help="record path (default: under profiles/)")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="K/V in a pool of pages of this many tokens under shuffled page tables "
+                         "(0: contiguous rows)")
     ap.add_argument("--offload", action="store_true",
                     help="K/V in pinned host memory, read over the host link (labels in HBM)")
     ap.add_argument("--calibrate", action="store_true",

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define DS_ABI_VERSION 2
+#define DS_ABI_VERSION 3
 
 typedef enum {
   DS_OK = 0,
@@ -63,9 +63,23 @@ typedef enum {
 typedef enum { DS_LABEL_F16 = 0, DS_LABEL_INT4 = 1 } ds_label_dtype;
 
 /* K/V cache description (host struct).
+ * Contiguous rows (page_size == 0):
  *   K: fp16 [batch][n_kv_heads][capacity][d_k], element strides k_stride =
  *      {batch, kv head, token}; channel stride 1.
  *   V: fp16 [batch][n_kv_heads][capacity][d_v], strides v_stride likewise.
+ * Paged token pool (page_size > 0; the serving form of [DS] "use in
+ * SGLang", where the K/V cache is a pool of token slots shared by all
+ * sequences):
+ *   K: fp16 [n_pages][n_kv_heads][page_size][d_k], k_stride = {page, kv
+ *      head, token}; V likewise.  Token t of batch row b lives in page
+ *      page_table[b][t / page_size] at slot t % page_size.
+ *   page_size is a power of two in [16, 65536]; page_table is a device int32
+ *   array [batch][max_pages] whose entries for the tokens in use lie in
+ *   [0, n_pages) (entries are not read on the host; out-of-range ones are
+ *   undefined behaviour); capacity == max_pages * page_size; n_pages *
+ *   page_size < 2^31.  The label cache stays one contiguous stream per
+ *   (batch row, KV head) (ds_label_desc): its contiguity is what the
+ *   approximate scores read.
  * Query head h belongs to KV head h / G with G = n_q_heads / n_kv_heads
  * ([GQA] section 4: consecutive query heads form a group).
  * d_q is the query width (the model's head dim); d_k is the stored K width,
@@ -77,9 +91,12 @@ typedef struct {
   int32_t batch, n_q_heads, n_kv_heads;
   int32_t d_q, d_k, d_v;
   int32_t capacity;
-  int32_t reserved0; /* must be 0 */
+  int32_t page_size;  /* 0: contiguous rows; else tokens per page of the pool */
   int64_t k_stride[3];
   int64_t v_stride[3];
+  const int32_t* page_table; /* paged: [batch][max_pages]; contiguous: NULL */
+  int32_t max_pages;  /* paged: page-table entries per batch row; else 0 */
+  int32_t n_pages;    /* paged: pages in the pool; else 0 */
 } ds_kv_desc;
 
 /* Label cache description (host struct) ([DS] offline calibration).
@@ -108,12 +125,16 @@ typedef struct {
 /* Label-cache build at prefill ([DS] offline calibration: every prefill
  * token's heavy-channel values go from the K cache into the label cache).
  * Writes label slots t in [t_begin, t_end) of every (batch, KV head) row.
- *   K     fp16 K cache as described by kv (read only).
+ *   K     fp16 K cache as described by kv (read only; contiguous rows or a
+ *         paged pool, whose page table gives each token's K row).
  *   chan  int32 [n_kv_heads][r]: heavy channels, indices into the stored K
  *         columns (0 <= chan < d_k); any order, duplicates allowed.
- * Only batch, n_kv_heads, d_k, capacity and k_stride of kv are read.
+ * Only batch, n_kv_heads, d_k, capacity, k_stride and the paging fields of
+ * kv are read.
  * Errors: DS_ERR_ARG (null pointer, 0 <= t_begin <= t_end <= capacity
- * violated), DS_ERR_SHAPE, DS_ERR_DTYPE, DS_ERR_ALIGN, DS_ERR_HIP. */
+ * violated, paging fields given with page_size 0 or a missing page table),
+ * DS_ERR_SHAPE (also a bad page size or page count), DS_ERR_DTYPE,
+ * DS_ERR_ALIGN, DS_ERR_HIP. */
 ds_status ds_label_build(const ds_kv_desc* kv, const void* K, const int32_t* chan,
                          const ds_label_desc* lab, int32_t t_begin, int32_t t_end,
                          hipStream_t stream);
@@ -314,9 +335,10 @@ size_t ds_calibrate_workspace_size(const ds_kv_desc* kv, int32_t n_tok, int32_t 
  *           sum_b qn_b and the score (a NaN score is reported as -1 and
  *           ranks last).
  *   workspace  device scratch of ds_calibrate_workspace_size() bytes.
+ * K must be contiguous rows (page_size 0).
  * Errors: DS_ERR_ARG (null pointer, n_tok, n_win, r or criterion out of
- * range), DS_ERR_SHAPE, DS_ERR_ALIGN (K not 16-byte aligned, stride not a
- * multiple of 8), DS_ERR_WORKSPACE, DS_ERR_HIP. */
+ * range, a paged kv), DS_ERR_SHAPE, DS_ERR_ALIGN (K not 16-byte aligned,
+ * stride not a multiple of 8), DS_ERR_WORKSPACE, DS_ERR_HIP. */
 ds_status ds_calibrate_channels(const ds_kv_desc* kv, const void* K, int32_t n_tok,
                                 const void* qwin, int32_t n_win, const int32_t* keep,
                                 int32_t criterion, int32_t r, int32_t* chan, float* norms,

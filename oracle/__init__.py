@@ -251,6 +251,28 @@ def attend_sets(q, K, V, sets, sm_scale, keep=None, rows=None, n_threads=0):
     return out
 
 
+def gather_pages(pool, table, page_size: int):
+    """The rows of a paged K/V pool as a contiguous cache: out[b][g][t] =
+    pool[table[b][t // page_size]][g][t % page_size] ("Double Sparsity",
+    section "use in SGLang": the K/V cache is a pool of token slots shared by
+    the sequences, and a table maps each sequence's tokens to slots).  pool:
+    [n_pages][H_kv][page_size][d]; table: int [B][max_pages]; entries < 0
+    (pages not in use) give zero rows.  Returns [B][H_kv][max_pages *
+    page_size][d], the layout every other oracle function reads."""
+    pool = np.asarray(pool)
+    table = np.asarray(table, dtype=np.int64)
+    B, max_pages = table.shape
+    n_pages, H, P, d = pool.shape
+    assert P == page_size
+    out = np.zeros((B, H, max_pages * P, d), dtype=pool.dtype)
+    for b in range(B):
+        for p in range(max_pages):
+            pg = int(table[b, p])
+            if pg >= 0:
+                out[b, :, p * P:(p + 1) * P, :] = pool[pg]
+    return out
+
+
 def max_threads() -> int:
     return _load().oracle_max_threads()
 

@@ -52,8 +52,10 @@ class KVDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("d_q", ctypes.c_int32),
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
-                ("capacity", ctypes.c_int32), ("reserved0", ctypes.c_int32),
-                ("k_stride", ctypes.c_int64 * 3), ("v_stride", ctypes.c_int64 * 3)]
+                ("capacity", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("k_stride", ctypes.c_int64 * 3), ("v_stride", ctypes.c_int64 * 3),
+                ("page_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32),
+                ("n_pages", ctypes.c_int32)]
 
 
 class LabelDesc(ctypes.Structure):
@@ -132,13 +134,33 @@ def _check(fn, code):
         raise DsError(fn, code)
 
 
-def kv_desc(K, V, n_q_heads: int, d_q: int | None = None) -> KVDesc:
-    """Describe K [B][H_kv][cap][d_k] and V [B][H_kv][cap][d_v] (fp16, unit channel stride)."""
-    B, Hkv, cap, d_k = K.shape
+@dataclass
+class Pages:
+    """A paged K/V pool: ``table`` int32 [batch][max_pages] on the device
+    (physical page of each logical page of a batch row); the K and V tensors
+    are then pools [n_pages][H_kv][page_size][d]."""
+    table: torch.Tensor
+    page_size: int
+
+
+def kv_desc(K, V, n_q_heads: int, d_q: int | None = None, pages: Pages | None = None) -> KVDesc:
+    """Describe K [B][H_kv][cap][d_k] and V [B][H_kv][cap][d_v] (fp16, unit
+    channel stride), or with ``pages`` the pools K [n_pages][H_kv][P][d_k] and
+    V [n_pages][H_kv][P][d_v]."""
+    d0, Hkv, d2, d_k = K.shape
     d = KVDesc()
-    d.batch, d.n_q_heads, d.n_kv_heads = B, n_q_heads, Hkv
+    if pages is not None:
+        B, max_pages = pages.table.shape
+        d.batch, d.capacity = B, max_pages * pages.page_size
+        d.page_size, d.page_table = pages.page_size, pages.table.data_ptr()
+        d.max_pages, d.n_pages = max_pages, d0
+        if d2 != pages.page_size:
+            raise ValueError("pool pages hold %d tokens, page_size is %d" % (d2, pages.page_size))
+    else:
+        d.batch, d.capacity = d0, d2
+    d.n_q_heads, d.n_kv_heads = n_q_heads, Hkv
     d.d_q = d_k if d_q is None else d_q
-    d.d_k, d.d_v, d.capacity = d_k, V.shape[3], cap
+    d.d_k, d.d_v = d_k, V.shape[3]
     for i in range(3):
         d.k_stride[i] = K.stride(i)
         d.v_stride[i] = V.stride(i)
@@ -198,16 +220,17 @@ def check_tables(chan, d_k: int, r: int | None = None, keep=None, d_q: int | Non
             raise ValueError("keep: query channel outside [0, %d)" % hi)
 
 
-def label_build(K, chan, labels: LabelCache, t_begin: int, t_end: int, stream=None):
-    kv = kv_desc(K, K, 1)
+def label_build(K, chan, labels: LabelCache, t_begin: int, t_end: int, stream=None,
+                pages: Pages | None = None):
+    kv = kv_desc(K, K, 1, pages=pages)
     lab = labels.desc()
     _check("ds_label_build", load().ds_label_build(
         ctypes.byref(kv), _p(K), _p(chan), ctypes.byref(lab), int(t_begin), int(t_end),
         _stream(stream)))
 
 
-def label_append(K, chan, labels: LabelCache, pos, stream=None):
-    kv = kv_desc(K, K, 1)
+def label_append(K, chan, labels: LabelCache, pos, stream=None, pages: Pages | None = None):
+    kv = kv_desc(K, K, 1, pages=pages)
     lab = labels.desc()
     _check("ds_label_append", load().ds_label_append(
         ctypes.byref(kv), _p(K), _p(chan), ctypes.byref(lab), _p(pos), _stream(stream)))
@@ -272,18 +295,19 @@ def channel_overlap(chan_a, chan_b):
     return [len(set(a[g].tolist()) & set(b[g].tolist())) / r for g in range(a.shape[0])]
 
 
-def workspace_size(K, V, n_q_heads, d_q, labels: LabelCache | None, k, max_seq_len) -> int:
-    kv = kv_desc(K, V, n_q_heads, d_q)
+def workspace_size(K, V, n_q_heads, d_q, labels: LabelCache | None, k, max_seq_len,
+                   pages: Pages | None = None) -> int:
+    kv = kv_desc(K, V, n_q_heads, d_q, pages=pages)
     lab = labels.desc() if labels is not None else None
     return int(load().ds_decode_attn_workspace_size(
         ctypes.byref(kv), ctypes.byref(lab) if lab is not None else None, int(k), int(max_seq_len)))
 
 
 def decode_plan(K, V, n_q_heads, d_q, labels: LabelCache | None, k, max_seq_len,
-                n_split: int = 0, flags: int = 0) -> dict:
+                n_split: int = 0, flags: int = 0, pages: Pages | None = None) -> dict:
     """What ds_decode_attn runs for these shapes (ds_decode_attn_plan): the
     path name, attention splits, tokens per split, kernel launches, workspace."""
-    kv = kv_desc(K, V, n_q_heads, d_q)
+    kv = kv_desc(K, V, n_q_heads, d_q, pages=pages)
     lab = labels.desc() if labels is not None else None
     opts = DecodeOpts()
     opts.n_split, opts.flags = int(n_split), int(flags)
@@ -306,14 +330,15 @@ def decode_attn(q, K, V, seq_lens, max_seq_len: int, k: int, sm_scale: float,
                 chan=None, labels: LabelCache | None = None, keep=None, out=None,
                 topk_idx=None, workspace=None, n_split: int = 0, flags: int = 0,
                 stage_events=None, stream=None, validate_tables: bool = False,
-                sparse_decode_threshold: int | None = None, min_seq_len: int | None = None):
+                sparse_decode_threshold: int | None = None, min_seq_len: int | None = None,
+                pages: Pages | None = None):
     """One decode step (ds_decode_attn).  Returns ``out`` fp16 [B][H_q][d_v].
     ``stage_events``: optional ctypes array of STAGE_COUNT + 1 hipEvent_t.
     ``validate_tables``: check chan and keep first (check_tables; synchronises).
     ``sparse_decode_threshold``: apply the batch policy (needs ``min_seq_len``,
     the host's shortest sequence); a dense step then runs with k = 0 (and
     still appends labels when DECODE_APPEND is set), and ``topk_idx`` is left
-    untouched."""
+    untouched.  ``pages``: K and V are paged pools addressed through its table."""
     if sparse_decode_threshold is not None and k > 0:
         if min_seq_len is None:
             raise ValueError("sparse_decode_threshold needs min_seq_len")
@@ -326,7 +351,7 @@ def decode_attn(q, K, V, seq_lens, max_seq_len: int, k: int, sm_scale: float,
         uses_chan = k > 0 or bool(flags & DECODE_APPEND)
         check_tables(chan if uses_chan else None, K.shape[3],
                      labels.r if labels is not None else None, keep, d_q, K.shape[1])
-    kv = kv_desc(K, V, Hq, d_q)
+    kv = kv_desc(K, V, Hq, d_q, pages=pages)
     lab = labels.desc() if labels is not None and (k > 0 or flags & DECODE_APPEND) else None
     lib = load()
     need = int(lib.ds_decode_attn_workspace_size(
@@ -349,14 +374,15 @@ def decode_attn(q, K, V, seq_lens, max_seq_len: int, k: int, sm_scale: float,
 
 def decode_attn_noalloc(q, K, V, seq_lens, max_seq_len: int, k: int, sm_scale: float,
                         chan=None, labels: LabelCache | None = None, keep=None, out=None,
-                        topk_idx=None, n_split: int = 0, flags: int = 0, stream=None):
+                        topk_idx=None, n_split: int = 0, flags: int = 0, stream=None,
+                        pages: Pages | None = None):
     """ds_decode_attn_noalloc: the same step as decode_attn with the library's
     per-GPU scratch in place of a workspace (calls on one GPU must not
     overlap).  ``out`` must be given: this call allocates nothing."""
     if out is None:
         raise ValueError("decode_attn_noalloc: pass out (this call allocates nothing)")
     B, Hq, d_q = q.shape
-    kv = kv_desc(K, V, Hq, d_q)
+    kv = kv_desc(K, V, Hq, d_q, pages=pages)
     lab = labels.desc() if labels is not None and (k > 0 or flags & DECODE_APPEND) else None
     opts = DecodeOpts()
     opts.n_split, opts.flags = int(n_split), int(flags)

@@ -28,9 +28,29 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Paged pool: page size a power of two in [16, 65536], table given, the
+// capacity exactly max_pages pages, physical token ids (page << log2(page
+// size) | slot) below 2^31.  Contiguous rows: no paging fields.
+ds_status check_pages(const ds_kv_desc* kv) {
+  const int P = kv->page_size;
+  if (P == 0) return (kv->page_table || kv->max_pages || kv->n_pages) ? DS_ERR_ARG : DS_OK;
+  if (P < 16 || P > 65536 || (P & (P - 1))) return DS_ERR_SHAPE;
+  if (!kv->page_table) return DS_ERR_ARG;
+  if (kv->max_pages < 1 || kv->n_pages < 1) return DS_ERR_SHAPE;
+  if ((int64_t)kv->max_pages * P != kv->capacity) return DS_ERR_SHAPE;
+  if ((int64_t)kv->n_pages * P > INT32_MAX) return DS_ERR_SHAPE;
+  return DS_OK;
+}
+
+int log2i(int v) {
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
 // K-side fields (all calls) and, for decode, the query and V fields.
 ds_status check_kv(const ds_kv_desc* kv, bool decode) {
-  if (!kv || kv->reserved0 != 0) return DS_ERR_ARG;
+  if (!kv) return DS_ERR_ARG;
   if (kv->batch < 1 || kv->n_kv_heads < 1) return DS_ERR_SHAPE;
   if (kv->d_k < 8 || kv->d_k > 128 || kv->d_k % 8) return DS_ERR_SHAPE;
   if (kv->capacity < 1 || kv->capacity > kMaxCapacity) return DS_ERR_SHAPE;
@@ -38,6 +58,7 @@ ds_status check_kv(const ds_kv_desc* kv, bool decode) {
     if (kv->k_stride[i] < 0) return DS_ERR_SHAPE;
     if (kv->k_stride[i] % 8) return DS_ERR_ALIGN;
   }
+  if (ds_status st = check_pages(kv)) return st;
   if (!decode) return DS_OK;
   if (kv->n_q_heads < 1 || kv->n_q_heads % kv->n_kv_heads) return DS_ERR_SHAPE;
   if (kv->n_q_heads / kv->n_kv_heads > kMaxGroup) return DS_ERR_SHAPE;
@@ -77,6 +98,11 @@ LabelArgs label_args(const ds_kv_desc* kv, const void* K, const int32_t* chan,
   a.d_k = kv->d_k;
   a.cap = kv->capacity;
   a.chan = chan;
+  if (kv->page_size) {
+    a.ptab = kv->page_table;
+    a.pshift = log2i(kv->page_size);
+    a.max_pages = kv->max_pages;
+  }
   a.r = lab->r;
   a.is_int4 = lab->dtype == DS_LABEL_INT4;
   a.slots = lab->slots;
@@ -187,6 +213,12 @@ AttnArgs attn_args(const ds_kv_desc* kv, const void* q, const void* K, const voi
   aa.scale_log2 = sm_scale * 1.4426950408889634f;
   aa.out = static_cast<__half*>(out);
   aa.part = reinterpret_cast<float*>(ws + p.off_part);
+  if (kv->page_size) {
+    aa.ptab = kv->page_table;
+    aa.pshift = log2i(kv->page_size);
+    aa.pmask = kv->page_size - 1;
+    aa.max_pages = kv->max_pages;
+  }
   return aa;
 }
 
@@ -580,7 +612,7 @@ int32_t ds_sparse_decode_enabled(int32_t max_seq_len, int32_t min_seq_len, int32
 }
 
 size_t ds_calibrate_workspace_size(const ds_kv_desc* kv, int32_t n_tok, int32_t n_win) {
-  if (check_kv(kv, false) || n_tok < 0 || n_tok > kv->capacity || n_win < 0) return 0;
+  if (check_kv(kv, false) || kv->page_size || n_tok < 0 || n_tok > kv->capacity || n_win < 0) return 0;
   if (n_win > 0 && (kv->n_q_heads < 1 || kv->n_q_heads % kv->n_kv_heads)) return 0;
   const int G = n_win > 0 ? kv->n_q_heads / kv->n_kv_heads : 1;
   const CalibPlan pl = calib_plan(kv->batch, kv->n_kv_heads, n_tok, kv->d_k, n_win * G);
@@ -593,6 +625,7 @@ ds_status ds_calibrate_channels(const ds_kv_desc* kv, const void* K, int32_t n_t
                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
   ds_status st = check_kv(kv, false);
   if (st) return st;
+  if (kv->page_size) return DS_ERR_ARG;  // calibration samples are contiguous rows
   if (n_tok < 0 || n_tok > kv->capacity || n_win < 0) return DS_ERR_ARG;
   if (criterion < DS_CALIB_K || criterion > DS_CALIB_QK) return DS_ERR_ARG;
   if (r < 1 || r > kv->d_k || !chan) return DS_ERR_ARG;

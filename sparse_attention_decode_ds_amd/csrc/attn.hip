@@ -7,7 +7,9 @@
 namespace ds {
 namespace {
 
-template <int G, bool FINAL>
+// PAGED: K/V in a paged pool; the staged list holds physical token ids (the
+// dense path stages its positions too).
+template <int G, bool FINAL, bool PAGED>
 __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   __shared__ int32_t lidx[kMaxTokensPerSplit];
   __shared__ AttnRed<G> red;
@@ -31,20 +33,25 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   load_query<G>(a, b, g, c, kl, qf);
   AttnAcc<G> acc;
   acc_init<G>(acc);
-  const __half* Kr = a.K + (int64_t)b * a.ks0 + (int64_t)g * a.ks1 + min(c, (a.d_k >> 3) - 1) * 8;
-  const __half* Vr = a.V + (int64_t)b * a.vs0 + (int64_t)g * a.vs1 + c * 8;
+  const __half* Kr = a.K + (PAGED ? 0 : (int64_t)b * a.ks0) + (int64_t)g * a.ks1 +
+                     min(c, (a.d_k >> 3) - 1) * 8;
+  const __half* Vr = a.V + (PAGED ? 0 : (int64_t)b * a.vs0) + (int64_t)g * a.vs1 + c * 8;
+  const int32_t* ptab = PAGED ? a.ptab + (int64_t)b * a.max_pages : nullptr;
 
-  if (a.sparse) {
+  if (a.sparse || PAGED) {
     for (int bat = 0; bat < n_here; bat += kMaxTokensPerSplit) {
       const int nb = min(kMaxTokensPerSplit, n_here - bat);
       __syncthreads();
       const int32_t* src = a.idx + (int64_t)row * a.idx_stride + t0 + bat;
-      for (int i = tid; i < nb; i += kAttnThreads) lidx[i] = src[i];
+      for (int i = tid; i < nb; i += kAttnThreads) {
+        const int t = a.sparse ? src[i] : t0 + bat + i;
+        lidx[i] = PAGED ? phys_tok(ptab, a.pshift, t) : t;
+      }
       __syncthreads();
-      attend<G>(a, Kr, Vr, slot, nb, [&](int i) { return (int64_t)lidx[i]; }, qf, acc);
+      attend<G, PAGED>(a, Kr, Vr, slot, nb, [&](int i) { return (int64_t)lidx[i]; }, qf, acc);
     }
   } else {
-    attend<G>(a, Kr, Vr, slot, n_here, [&](int i) { return (int64_t)(t0 + i); }, qf, acc);
+    attend<G, false>(a, Kr, Vr, slot, n_here, [&](int i) { return (int64_t)(t0 + i); }, qf, acc);
   }
   attn_finish<G, FINAL>(a, acc, red, b, g, split);
 }
@@ -59,8 +66,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_combine(AttnArgs a, int n_rows
 template <int G>
 hipError_t launch_g(const AttnArgs& a, int rows, bool final_out, hipStream_t s, const KEvents& ev) {
   const dim3 grid(rows * a.n_split);
-  if (final_out) return launch_k(k_attn<G, true>, grid, dim3(kAttnThreads), s, ev, a);
-  return launch_k(k_attn<G, false>, grid, dim3(kAttnThreads), s, ev, a);
+  if (a.ptab) {
+    if (final_out) return launch_k(k_attn<G, true, true>, grid, dim3(kAttnThreads), s, ev, a);
+    return launch_k(k_attn<G, false, true>, grid, dim3(kAttnThreads), s, ev, a);
+  }
+  if (final_out) return launch_k(k_attn<G, true, false>, grid, dim3(kAttnThreads), s, ev, a);
+  return launch_k(k_attn<G, false, false>, grid, dim3(kAttnThreads), s, ev, a);
 }
 
 }  // namespace

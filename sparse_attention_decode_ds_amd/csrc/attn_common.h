@@ -82,6 +82,18 @@ struct AttnLoads {
   uint4 ka[kUnroll], va[kUnroll], kb[kUnroll], vb[kUnroll];
 };
 
+// Element offsets of token t's K and V rows from the row's base pointers:
+// t * stride for contiguous rows; for a paged pool t is a physical id
+// (page << pshift | slot) and the base pointers exclude the batch row.
+template <bool PAGED>
+__device__ __forceinline__ int64_t k_off(const AttnArgs& a, int64_t t) {
+  return PAGED ? (t >> a.pshift) * a.ks0 + (t & a.pmask) * a.ks2 : t * a.ks2;
+}
+template <bool PAGED>
+__device__ __forceinline__ int64_t v_off(const AttnArgs& a, int64_t t) {
+  return PAGED ? (t >> a.pshift) * a.vs0 + (t & a.pmask) * a.vs2 : t * a.vs2;
+}
+
 // Loads of the tokens tok(i), i = base + 16 u, into kk/vv.  Positions at or
 // past hi load the list's first token tok(0) instead (the row's token 0 if
 // the list is still empty): every load is issued unconditionally, so no
@@ -89,32 +101,33 @@ struct AttnLoads {
 // masks those positions out, and their values are finite wherever the
 // selected rows are.  Kr, Vr point at the lane's 16-byte piece of the row's
 // token 0 (lanes past the stored K width read a valid column; their query
-// weights are zero).
-template <typename TokFn>
+// weights are zero); for a paged pool, at page 0's and tok gives physical
+// ids.
+template <bool PAGED, typename TokFn>
 __device__ __forceinline__ void attn_issue(const AttnArgs& a, const __half* Kr, const __half* Vr,
                                            int base, int hi, TokFn tok, uint4* kk, uint4* vv) {
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int i = base + u * kSlots;
-    const int64_t t = hi > 0 ? tok(i < hi ? i : 0) : 0;
-    kk[u] = ld_stream(Kr + t * a.ks2);
-    vv[u] = ld_stream(Vr + t * a.vs2);
+    const int64_t t = hi > 0 ? tok(i < hi ? i : 0) : 0;  // (paged: page 0, slot 0)
+    kk[u] = ld_stream(Kr + k_off<PAGED>(a, t));
+    vv[u] = ld_stream(Vr + v_off<PAGED>(a, t));
   }
 }
 
 // The first two groups of slot `slot`, positions [0, n).
-template <typename TokFn>
+template <bool PAGED, typename TokFn>
 __device__ __forceinline__ void attend_prime(const AttnArgs& a, const __half* Kr, const __half* Vr,
                                              int slot, int n, TokFn tok, AttnLoads& L) {
   constexpr int kStep = kSlots * kUnroll;
-  attn_issue(a, Kr, Vr, slot, n, tok, L.ka, L.va);
-  attn_issue(a, Kr, Vr, slot + kStep, n, tok, L.kb, L.vb);
+  attn_issue<PAGED>(a, Kr, Vr, slot, n, tok, L.ka, L.va);
+  attn_issue<PAGED>(a, Kr, Vr, slot + kStep, n, tok, L.kb, L.vb);
 }
 
 // Accumulate tokens tok(i), i in [0, n), slot `slot` taking i = slot, slot+16, ...,
 // with the first two groups already in L (attend_prime); each group is
 // reloaded with the group after next as soon as it is consumed.
-template <int G, typename TokFn>
+template <int G, bool PAGED, typename TokFn>
 __device__ __forceinline__ void attend_run(const AttnArgs& a, const __half* Kr, const __half* Vr,
                                            int slot, int n, TokFn tok, const float (&qf)[G][8],
                                            AttnAcc<G>& acc, AttnLoads& L) {
@@ -165,21 +178,21 @@ __device__ __forceinline__ void attend_run(const AttnArgs& a, const __half* Kr, 
   };
   for (int base = slot; base < n; base += 2 * kStep) {
     consume(base, L.ka, L.va);
-    if (base + 2 * kStep < n) attn_issue(a, Kr, Vr, base + 2 * kStep, n, tok, L.ka, L.va);
+    if (base + 2 * kStep < n) attn_issue<PAGED>(a, Kr, Vr, base + 2 * kStep, n, tok, L.ka, L.va);
     if (base + kStep >= n) break;
     consume(base + kStep, L.kb, L.vb);
-    if (base + 3 * kStep < n) attn_issue(a, Kr, Vr, base + 3 * kStep, n, tok, L.kb, L.vb);
+    if (base + 3 * kStep < n) attn_issue<PAGED>(a, Kr, Vr, base + 3 * kStep, n, tok, L.kb, L.vb);
   }
 }
 
-template <int G, typename TokFn>
+template <int G, bool PAGED, typename TokFn>
 __device__ __forceinline__ void attend(const AttnArgs& a, const __half* Kr, const __half* Vr,
                                        int slot, int n, TokFn tok, const float (&qf)[G][8],
                                        AttnAcc<G>& acc) {
   if (n <= 0) return;
   AttnLoads L;
-  attend_prime(a, Kr, Vr, slot, n, tok, L);
-  attend_run<G>(a, Kr, Vr, slot, n, tok, qf, acc, L);
+  attend_prime<PAGED>(a, Kr, Vr, slot, n, tok, L);
+  attend_run<G, PAGED>(a, Kr, Vr, slot, n, tok, qf, acc, L);
 }
 
 template <int G, bool FINAL, int NW = 4>

@@ -23,8 +23,10 @@ struct GqaLds {
 };
 
 // RING: splits of more than four tiles per wave (the ring measured faster on
-// long runs, the single prefetch on short ones).
-template <int G, bool FINAL, bool RING>
+// long runs, the single prefetch on short ones).  PAGED: K/V in a paged pool;
+// the staged list holds physical token ids (the dense path stages its
+// positions too).
+template <int G, bool FINAL, bool RING, bool PAGED>
 __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a) {
   __shared__ GqaLds<G> f;
   const int row = blockIdx.x / a.n_split;
@@ -37,13 +39,19 @@ __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a) {
   const int n_here = max(0, min(n_tok - t0, a.tps));
   const int tid = threadIdx.x;
   const int w = wave_id();
-  const GqaLane ln(a, b, g);
+  const GqaLane ln(a, b, g, PAGED);
+  const int32_t* ptab = PAGED ? a.ptab + (int64_t)b * a.max_pages : nullptr;
+  // list position -> token (physical id in a paged pool), staged in LDS
+  auto stage = [&](int pos) -> int32_t {
+    const int t = a.sparse ? a.idx[(int64_t)row * a.idx_stride + pos] : pos;
+    return PAGED ? phys_tok(ptab, a.pshift, t) : t;
+  };
+  constexpr bool kStaged = PAGED;  // dense positions are staged too when paged
 
   // The first batch of the token list and the query rows are fetched
   // together (one round trip, one barrier).
-  const int32_t* src0 = a.idx + (int64_t)row * a.idx_stride + t0;
-  if (a.sparse)
-    for (int i = tid; i < min(n_here, kMaxTokensPerSplit); i += kGT) f.lidx[i] = src0[i];
+  if (a.sparse || kStaged)
+    for (int i = tid; i < min(n_here, kMaxTokensPerSplit); i += kGT) f.lidx[i] = stage(t0 + i);
   for (int i = tid; i < G * kDv; i += kGT) {
     const int h = i / kDv, c = i - h * kDv;
     __half v = __float2half(0.0f);
@@ -61,13 +69,13 @@ __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a) {
   gqa_init(st);
   for (int bat = 0; bat < n_here; bat += kMaxTokensPerSplit) {
     const int nb = min(kMaxTokensPerSplit, n_here - bat);
-    if (a.sparse && bat > 0) {
+    if ((a.sparse || kStaged) && bat > 0) {
       __syncthreads();
-      for (int i = tid; i < nb; i += kGT) f.lidx[i] = src0[bat + i];
+      for (int i = tid; i < nb; i += kGT) f.lidx[i] = stage(t0 + bat + i);
       __syncthreads();
     }
     auto tok = [&](int i) -> int64_t {
-      return a.sparse ? (int64_t)f.lidx[i] : (int64_t)(t0 + bat + i);
+      return (a.sparse || kStaged) ? (int64_t)f.lidx[i] : (int64_t)(t0 + bat + i);
     };
     constexpr int D = 4 * kGqaTile;  // the wave's tiles are D positions apart
     const int i_first = w * kGqaTile;
@@ -75,10 +83,10 @@ __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a) {
     if (!RING) {
       // The next tile's loads in flight while one is consumed.
       GqaTile cur, nxt;
-      gqa_load(a, ln, i_first, nb, tok, nxt);
+      gqa_load<PAGED>(a, ln, i_first, nb, tok, nxt);
       for (int i0 = i_first; i0 < nb; i0 += D) {
         cur = nxt;
-        if (i0 + D < nb) gqa_load(a, ln, i0 + D, nb, tok, nxt);
+        if (i0 + D < nb) gqa_load<PAGED>(a, ln, i0 + D, nb, tok, nxt);
         gqa_tile(cur, qb, i0, nb, a.scale_log2, ln.kg, st);
       }
     } else {
@@ -86,16 +94,16 @@ __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a) {
       // load is issued (up to two past the end read the last token again),
       // so each wait covers exactly one tile.
       GqaTile t0, t1, t2;
-      gqa_load(a, ln, i_first, nb, tok, t0);
-      gqa_load(a, ln, i_first + D, nb, tok, t1);
+      gqa_load<PAGED>(a, ln, i_first, nb, tok, t0);
+      gqa_load<PAGED>(a, ln, i_first + D, nb, tok, t1);
       for (int i0 = i_first; i0 < nb; i0 += 3 * D) {
-        gqa_load(a, ln, i0 + 2 * D, nb, tok, t2);
+        gqa_load<PAGED>(a, ln, i0 + 2 * D, nb, tok, t2);
         gqa_tile(t0, qb, i0, nb, a.scale_log2, ln.kg, st);
         if (i0 + D >= nb) break;
-        gqa_load(a, ln, i0 + 3 * D, nb, tok, t0);
+        gqa_load<PAGED>(a, ln, i0 + 3 * D, nb, tok, t0);
         gqa_tile(t1, qb, i0 + D, nb, a.scale_log2, ln.kg, st);
         if (i0 + 2 * D >= nb) break;
-        gqa_load(a, ln, i0 + 4 * D, nb, tok, t1);
+        gqa_load<PAGED>(a, ln, i0 + 4 * D, nb, tok, t1);
         gqa_tile(t2, qb, i0 + 2 * D, nb, a.scale_log2, ln.kg, st);
       }
     }
@@ -107,15 +115,21 @@ __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a) {
   attn_store<G, FINAL>(a, f.red, b, g, split);
 }
 
-template <int G>
-hipError_t launch_g(const AttnArgs& a, int rows, bool final_out, hipStream_t s, const KEvents& ev) {
+template <int G, bool PAGED>
+hipError_t launch_gp(const AttnArgs& a, int rows, bool final_out, hipStream_t s, const KEvents& ev) {
   const dim3 grid(rows * a.n_split);
   const bool ring = a.tps > 16 * kGqaTile;  // more than four tiles per wave
   if (final_out)
-    return ring ? launch_k(k_attn_gqa<G, true, true>, grid, dim3(kGT), s, ev, a)
-                : launch_k(k_attn_gqa<G, true, false>, grid, dim3(kGT), s, ev, a);
-  return ring ? launch_k(k_attn_gqa<G, false, true>, grid, dim3(kGT), s, ev, a)
-              : launch_k(k_attn_gqa<G, false, false>, grid, dim3(kGT), s, ev, a);
+    return ring ? launch_k(k_attn_gqa<G, true, true, PAGED>, grid, dim3(kGT), s, ev, a)
+                : launch_k(k_attn_gqa<G, true, false, PAGED>, grid, dim3(kGT), s, ev, a);
+  return ring ? launch_k(k_attn_gqa<G, false, true, PAGED>, grid, dim3(kGT), s, ev, a)
+              : launch_k(k_attn_gqa<G, false, false, PAGED>, grid, dim3(kGT), s, ev, a);
+}
+
+template <int G>
+hipError_t launch_g(const AttnArgs& a, int rows, bool final_out, hipStream_t s, const KEvents& ev) {
+  return a.ptab ? launch_gp<G, true>(a, rows, final_out, s, ev)
+                : launch_gp<G, false>(a, rows, final_out, s, ev);
 }
 
 }  // namespace

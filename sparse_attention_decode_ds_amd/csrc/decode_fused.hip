@@ -32,8 +32,10 @@ namespace {
 
 constexpr int kNT = 256;
 constexpr int kWaves = kNT / 64;
+// page-table entries of the longest row (pages of at least 16 tokens)
+constexpr int kFusedPages = kNT * kDecodeFusedTPT / 16;
 
-template <int TPT>
+template <int TPT, bool PAGED>
 struct FusedScratch {
   __half qrow[256];
   int32_t chan[128];
@@ -48,11 +50,15 @@ struct FusedScratch {
   uint32_t tot[TPT * kWaves];  // per round and wave: taken | equal << 16
   int32_t lidx[kDecodeFusedMaxK];
   AttnRed<1> red;
+  int32_t ptab[PAGED ? kFusedPages : 1];  // the row's page-table entries (paged pool)
 };
 
 
 
-template <int R, bool INT4, int TPT>
+// PAGED: K/V in a paged pool; the row's page-table entries are staged in
+// LDS with the other small loads, and list tokens become physical ids at
+// the K/V loads.
+template <int R, bool INT4, int TPT, bool PAGED>
 __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs aa, LabelArgs la,
                                                       int append) {
   using Vec = typename VecSel<R, INT4>::type;
@@ -61,7 +67,7 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
   // label vectors in flight per thread: all of them when they fit in about
   // 40 registers, else 4 at a time
   constexpr int UNR = JMAX * (int)sizeof(Vec) <= 160 ? JMAX : 4;
-  __shared__ FusedScratch<TPT> f;
+  __shared__ FusedScratch<TPT, PAGED> f;
 
   const int row = blockIdx.x;
   const int b = row / sa.Hkv;
@@ -86,8 +92,13 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
     if (sa.keep)
       for (int i = tid; i < sa.d_k; i += kNT) f.keep[i] = sa.keep[(int64_t)g * sa.d_k + i];
     if (do_append && tid < (la.d_k >> 3)) {
-      const __half* kr = la.K + (int64_t)b * la.ks0 + (int64_t)g * la.ks1 + (int64_t)t_new * la.ks2;
+      const __half* kr = la.K + kv_off(la.ptab, la.pshift, la.max_pages, b, t_new, la.ks0, la.ks2) +
+                         (int64_t)g * la.ks1;
       *reinterpret_cast<uint4*>(&f.knew[tid * 8]) = *reinterpret_cast<const uint4*>(kr + tid * 8);
+    }
+    if (PAGED) {
+      const int npg = (sa.max_seq + (1 << aa.pshift) - 1) >> aa.pshift;
+      for (int i = tid; i < npg; i += kNT) f.ptab[i] = aa.ptab[(int64_t)b * aa.max_pages + i];
     }
   }
 
@@ -123,10 +134,13 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
   // Attention: lane c of slot `slot` holds K/V channels [8c, 8c + 8).  List
   // position i is token f.lidx[i] on the sparse path and token i on the
   // dense one; both paths share the attention code below.
-  const __half* Kr =
-      aa.K + (int64_t)b * aa.ks0 + (int64_t)g * aa.ks1 + min(c, (aa.d_k >> 3) - 1) * 8;
-  const __half* Vr = aa.V + (int64_t)b * aa.vs0 + (int64_t)g * aa.vs1 + c * 8;
-  auto tok = [&](int i) { return sparse ? (int64_t)f.lidx[i] : (int64_t)i; };
+  const __half* Kr = aa.K + (PAGED ? 0 : (int64_t)b * aa.ks0) + (int64_t)g * aa.ks1 +
+                     min(c, (aa.d_k >> 3) - 1) * 8;
+  const __half* Vr = aa.V + (PAGED ? 0 : (int64_t)b * aa.vs0) + (int64_t)g * aa.vs1 + c * 8;
+  auto tok = [&](int i) -> int64_t {
+    const int t = sparse ? f.lidx[i] : i;
+    return PAGED ? (int64_t)phys_tok(f.ptab, aa.pshift, t) : (int64_t)t;
+  };
   auto token = [&](int j, int e) { return (j * kNT + tid) * VT + e; };
   auto valid = [&](int j, int) { return j < jn; };  // empty slots hold -inf
   const int n_att = sparse ? sa.k : S;  // tokens attended
@@ -140,7 +154,7 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
     // label loads issued ahead of the row length are not used here; let them
     // land before the attention loads take their place
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    if (n_att > 0) attend_prime(aa, Kr, Vr, slot, n_att, tok, L);
+    if (n_att > 0) attend_prime<PAGED>(aa, Kr, Vr, slot, n_att, tok, L);
   } else {
     sel_clear<kNT>(f.sel);  // published by the barrier after the scores
     if (do_append && w == kAppendWave) append_label<R, INT4>(la, row, t_new, f, r, true);
@@ -232,9 +246,9 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
       // loads go out while the few boundary candidates are ranked (the
       // scores are no longer needed).
       const bool early = n_a >= 2 * kSlots * kUnroll;
-      if (early) attend_prime(aa, Kr, Vr, slot, n_a, tok, L);
+      if (early) attend_prime<PAGED>(aa, Kr, Vr, slot, n_a, tok, L);
       list_rank<kNT>(ls, f.sel, f.lidx);
-      if (!early) attend_prime(aa, Kr, Vr, slot, n_att, tok, L);
+      if (!early) attend_prime<PAGED>(aa, Kr, Vr, slot, n_att, tok, L);
     } else {
       const RegSel rs = list_select_b<kNT, VT, JMAX>(sc, valid, token, bin, ls, f.sel,
                                                      f.scan_tmp, f.tot, f.lidx);
@@ -244,7 +258,7 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
                                 [&](uint32_t pos, int j, int e) { out[pos] = token(j, e); });
         for (int i = sa.k + tid; i < sa.idx_stride; i += kNT) out[i] = -1;
       }
-      attend_prime(aa, Kr, Vr, slot, n_att, tok, L);
+      attend_prime<PAGED>(aa, Kr, Vr, slot, n_att, tok, L);
     }
   }
 
@@ -258,14 +272,18 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
   }
   AttnAcc<1> acc;
   acc_init<1>(acc);
-  attend_run<1>(aa, Kr, Vr, slot, n_att, tok, qf, acc, L);
+  attend_run<1, PAGED>(aa, Kr, Vr, slot, n_att, tok, qf, acc, L);
   attn_finish<1, true>(aa, acc, f.red, b, g, 0);
 }
 
 template <int R, bool INT4, int TPT>
 hipError_t launch_rt(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la, int append,
                      int rows, hipStream_t s, const KEvents& ev) {
-  return launch_k(k_decode_fused<R, INT4, TPT>, dim3(rows), dim3(kNT), s, ev, sa, aa, la, append);
+  if (aa.ptab)
+    return launch_k(k_decode_fused<R, INT4, TPT, true>, dim3(rows), dim3(kNT), s, ev, sa, aa, la,
+                    append);
+  return launch_k(k_decode_fused<R, INT4, TPT, false>, dim3(rows), dim3(kNT), s, ev, sa, aa, la,
+                  append);
 }
 
 template <int TPT>

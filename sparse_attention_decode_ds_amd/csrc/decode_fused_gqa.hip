@@ -30,8 +30,9 @@ namespace {
 
 constexpr int kNTG = 1024;
 constexpr int kWG = kNTG / 64;  // waves
+constexpr int kFusedGPages = 16384 / 16;  // page-table entries of the longest row
 
-template <int JMAX>
+template <int JMAX, bool PAGED>
 struct FusedGScratch {
   __half qrows[kMaxGroup][256];  // the group's query rows
   int32_t chan[128];
@@ -47,10 +48,12 @@ struct FusedGScratch {
   alignas(16) __half qk[kMaxGroup][kDv];  // query rows at the stored K columns' channels
   int32_t lidx[kDecodeFusedMaxK];
   AttnRed<kMaxGroup, kWG> red;
+  int32_t ptab[PAGED ? kFusedGPages : 1];  // the row's page-table entries (paged pool)
 };
 
 // TPTC: tokens per thread before rounding up to whole label vectors.
-template <int R, bool INT4, int TPTC>
+// PAGED: K/V in a paged pool (the row's page-table entries staged in LDS).
+template <int R, bool INT4, int TPTC, bool PAGED>
 __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs aa, LabelArgs la,
                                                        int append) {
   using Vec = typename VecSel<R, INT4>::type;
@@ -60,7 +63,7 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs 
   // label vectors in flight per thread: all of them when they fit in about
   // 72 registers, else 4 at a time
   constexpr int UNR = JMAX * (int)sizeof(Vec) <= 288 ? JMAX : 4;
-  __shared__ FusedGScratch<JMAX> f;
+  __shared__ FusedGScratch<JMAX, PAGED> f;
 
   const int row = blockIdx.x;
   const int b = row / sa.Hkv;
@@ -103,6 +106,10 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs 
   Vec vec[UNR];
 #pragma unroll
   for (int u = 0; u < UNR; ++u) vec[u].load(p, min(u * kNTG + tid, v_ld));
+  if (PAGED) {
+    const int npg = (sa.max_seq + (1 << aa.pshift) - 1) >> aa.pshift;
+    for (int i = tid; i < npg; i += kNTG) f.ptab[i] = aa.ptab[(int64_t)b * aa.max_pages + i];
+  }
   if (tid < nq) f.qrows[tid / sa.d_q][tid % sa.d_q] = qv0;
   if (tid + kNTG < nq) f.qrows[(tid + kNTG) / sa.d_q][(tid + kNTG) % sa.d_q] = qv1;
   if (tid < r) f.chan[tid] = chv;
@@ -130,7 +137,8 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs 
   constexpr int kAppendWave = kWG - 1;
   auto append_new = [&](bool with_score) {
     if (lane < (la.d_k >> 3)) {
-      const __half* kr = la.K + (int64_t)b * la.ks0 + (int64_t)g * la.ks1 + (int64_t)t_new * la.ks2;
+      const __half* kr = la.K + kv_off(la.ptab, la.pshift, la.max_pages, b, t_new, la.ks0, la.ks2) +
+                         (int64_t)g * la.ks1;
       *reinterpret_cast<uint4*>(&f.knew[lane * 8]) = *reinterpret_cast<const uint4*>(kr + lane * 8);
     }
     __builtin_amdgcn_wave_barrier();
@@ -138,7 +146,10 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs 
   };
   // List position i is token f.lidx[i] on the sparse path and token i on the
   // dense one.
-  auto tok = [&](int i) -> int64_t { return sparse ? (int64_t)f.lidx[i] : (int64_t)i; };
+  auto tok = [&](int i) -> int64_t {
+    const int t = sparse ? f.lidx[i] : i;
+    return PAGED ? (int64_t)phys_tok(f.ptab, aa.pshift, t) : (int64_t)t;
+  };
   auto token = [&](int j, int e) { return (j * kNTG + tid) * VT + e; };
   auto valid = [&](int j, int) { return j < jn; };  // empty slots hold -inf
   const int n_att = sparse ? sa.k : S;  // tokens attended
@@ -248,7 +259,7 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs 
 
   // --- attention -----------------------------------------------------------------
   // Each wave takes every 16th tile of the list, one tile in registers.
-  const GqaLane ln(aa, b, g);
+  const GqaLane ln(aa, b, g, PAGED);
   half4_t qb[8];
   gqa_query(&f.qk[0][0], G, ln, qb);
   GqaState st;
@@ -256,7 +267,7 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs 
   constexpr int D = kWG * kGqaTile;  // the wave's tiles are D positions apart
   for (int i0 = w * kGqaTile; i0 < n_att; i0 += D) {
     GqaTile cur;
-    gqa_load(aa, ln, i0, n_att, tok, cur);
+    gqa_load<PAGED>(aa, ln, i0, n_att, tok, cur);
     gqa_tile(cur, qb, i0, n_att, aa.scale_log2, ln.kg, st);
   }
   gqa_to_red(st, ln, G, w, f.red);
@@ -267,8 +278,11 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs 
 template <int R, bool INT4, int TPTC>
 hipError_t launch_rt(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la, int append,
                      int rows, hipStream_t s, const KEvents& ev) {
-  return launch_k(k_decode_fused_g<R, INT4, TPTC>, dim3(rows), dim3(kNTG), s, ev, sa, aa, la,
-                  append);
+  if (aa.ptab)
+    return launch_k(k_decode_fused_g<R, INT4, TPTC, true>, dim3(rows), dim3(kNTG), s, ev, sa, aa,
+                    la, append);
+  return launch_k(k_decode_fused_g<R, INT4, TPTC, false>, dim3(rows), dim3(kNTG), s, ev, sa, aa,
+                  la, append);
 }
 
 template <int TPTC>

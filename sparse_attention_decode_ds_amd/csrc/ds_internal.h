@@ -56,6 +56,9 @@ struct LabelArgs {
   int32_t n_items;
   // append driven by seq_lens (pos = seq_lens, token = seq_lens[b] - 1)
   int32_t pos_minus_one;
+  // paged K pool (ptab != nullptr): ks0 is the page stride
+  const int32_t* ptab;
+  int32_t pshift, max_pages;
 };
 
 struct ScoreArgs {
@@ -106,6 +109,10 @@ struct AttnArgs {
   float scale_log2;
   __half* out;
   float* part;
+  // paged K/V pool (ptab != nullptr): ks0 / vs0 are page strides, and the
+  // kernels address tokens by physical id (page << pshift | slot)
+  const int32_t* ptab;
+  int32_t pshift, pmask, max_pages;
 };
 
 // Optional timing events recorded by a launch itself, at the kernel's start
@@ -195,6 +202,23 @@ __device__ __forceinline__ void unpack8(const uint4 v, float* f) {
     f[2 * i] = x.x;
     f[2 * i + 1] = x.y;
   }
+}
+
+// K rows of the label kernels: token t of batch row b at b * s0 + t * s2
+// (contiguous rows, ptab == nullptr) or, in a paged pool, at page * s0 +
+// (t mod 2^pshift) * s2 with page = ptab[b][t >> pshift].
+__device__ __forceinline__ int64_t kv_off(const int32_t* ptab, int pshift, int max_pages, int b,
+                                          int64_t t, int64_t s0, int64_t s2) {
+  if (!ptab) return (int64_t)b * s0 + t * s2;
+  const int64_t pg = ptab[(int64_t)b * max_pages + (t >> pshift)];
+  return pg * s0 + (t & ((int64_t(1) << pshift) - 1)) * s2;
+}
+
+// Physical id (page << pshift | slot) of token t of batch row b in a paged
+// pool, from a page table (global memory or a row's slice staged in LDS
+// with first = the batch row's entry 0).
+__device__ __forceinline__ int32_t phys_tok(const int32_t* row_tab, int pshift, int t) {
+  return (row_tab[t >> pshift] << pshift) | (t & ((1 << pshift) - 1));
 }
 
 // Order-preserving map from fp32 to uint32 (larger value -> larger key);

@@ -62,12 +62,13 @@ struct GqaLane {
   const __half* Kb;  // K of the (batch, KV head) row
   const __half* Vr;  // V of the row, at channel 8 m16
   int m16, kg;
-  __device__ __forceinline__ GqaLane(const AttnArgs& a, int b, int g) {
+  // paged: the bases exclude the batch row (tokens are physical ids)
+  __device__ __forceinline__ GqaLane(const AttnArgs& a, int b, int g, bool paged) {
     const int lane = threadIdx.x & 63;
     m16 = lane & 15;
     kg = lane >> 4;
-    Kb = a.K + (int64_t)b * a.ks0 + (int64_t)g * a.ks1;
-    Vr = a.V + (int64_t)b * a.vs0 + (int64_t)g * a.vs1 + 8 * m16;
+    Kb = a.K + (paged ? 0 : (int64_t)b * a.ks0) + (int64_t)g * a.ks1;
+    Vr = a.V + (paged ? 0 : (int64_t)b * a.vs0) + (int64_t)g * a.vs1 + 8 * m16;
   }
 };
 
@@ -93,16 +94,16 @@ __device__ __forceinline__ void gqa_query(const __half* qk, int ng, const GqaLan
 // positions are set to -inf (so P = 0) and the query is zero past d_k.
 // Branch-free loads let the compiler wait for one tile while later tiles are
 // still in flight.
-template <typename TokFn>
+template <bool PAGED, typename TokFn>
 __device__ __forceinline__ void gqa_load(const AttnArgs& a, const GqaLane& ln, int i0, int nb,
                                          TokFn tok, GqaTile& T) {
   const int64_t tk = tok(min(i0 + ln.m16, nb - 1));
-  const __half* kr = ln.Kb + tk * a.ks2;
+  const __half* kr = ln.Kb + k_off<PAGED>(a, tk);
 #pragma unroll
   for (int u = 0; u < 4; ++u) T.k[u] = ld_stream(kr + min(32 * ln.kg + 8 * u, a.d_k - 8));
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    T.v[j] = ld_stream(ln.Vr + tok(min(i0 + 4 * ln.kg + j, nb - 1)) * a.vs2);
+    T.v[j] = ld_stream(ln.Vr + v_off<PAGED>(a, tok(min(i0 + 4 * ln.kg + j, nb - 1))));
 }
 
 // Half s (0..7) of the four 16-byte pieces x[0..3], as the A operand.

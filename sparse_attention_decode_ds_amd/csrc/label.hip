@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void k_label(LabelArgs a) {
     if (t >= 0 && t < a.cap) {
       const int b = row / a.Hkv;
       const int g = row - b * a.Hkv;
-      so = (int64_t)b * a.ks0 + (int64_t)g * a.ks1 + (int64_t)t * a.ks2;
+      so = kv_off(a.ptab, a.pshift, a.max_pages, b, t, a.ks0, a.ks2) + (int64_t)g * a.ks1;
       dt = (int64_t)row * a.slots + t;
     }
     src_off[tid] = so;

@@ -98,7 +98,8 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la, 
   }
   for (int j = tid; j < r; j += NT) f.chan[j] = sa.chan[(int64_t)g * r + j];
   if (has_new && tid < (la.d_k >> 3)) {
-    const __half* kr = la.K + (int64_t)b * la.ks0 + (int64_t)g * la.ks1 + (int64_t)t_new * la.ks2;
+    const __half* kr = la.K + kv_off(la.ptab, la.pshift, la.max_pages, b, t_new, la.ks0, la.ks2) +
+                       (int64_t)g * la.ks1;
     *reinterpret_cast<uint4*>(&f.knew[tid * 8]) = *reinterpret_cast<const uint4*>(kr + tid * 8);
   }
   if (!sparse) {  // the row attends every token; only the label append is due

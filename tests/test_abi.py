@@ -33,7 +33,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ds_abi_version() == 2
+    assert lib.ds_abi_version() == 3
     for code in range(0, -7, -1):
         s = lib.ds_status_str(code).decode()
         assert s and s != "unknown status"
@@ -81,6 +81,11 @@ def _decode(lib, kv=None, lab=None, k=64, max_seq=900, ws_bytes=1 << 30, flags=d
 
 def test_validate_only_accepts_good_arguments(lib):
     assert _decode(lib) == 0
+    # a paged pool: 64 pages of 16 tokens per batch row, 50 pages in the pool
+    paged = _kv(page_size=16, capacity=1024, max_pages=64, n_pages=50, page_table=FAKE,
+                k_stride=(4 * 16 * 128, 16 * 128, 128), v_stride=(4 * 16 * 128, 16 * 128, 128))
+    assert _decode(lib, kv=paged) == 0
+    assert _decode(lib, kv=paged, k=0, lab=False, chan=None) == 0
     assert _decode(lib, k=0, lab=False, chan=None) == 0                    # dense, no labels
     assert _decode(lib, lab=_lab(dtype=ds.LABEL_INT4, r=8, scales=FAKE)) == 0
     kv = _kv(d_k=32, k_stride=(4 * 1000 * 32, 1000 * 32, 32))
@@ -95,7 +100,14 @@ def test_validate_only_accepts_good_arguments(lib):
     (dict(kv=_kv(d_v=64)), -2),
     (dict(kv=_kv(d_k=36)), -2),
     (dict(kv=_kv(capacity=0)), -2),
-    (dict(kv=_kv(reserved0=1)), -1),
+    (dict(kv=_kv(page_size=16)), -1),                 # paged without a page table
+    (dict(kv=_kv(max_pages=3)), -1),                  # paging fields on contiguous rows
+    (dict(kv=_kv(page_size=24, capacity=960, max_pages=40, n_pages=50, page_table=FAKE)), -2),
+    (dict(kv=_kv(page_size=8, capacity=1024, max_pages=128, n_pages=50, page_table=FAKE)), -2),
+    (dict(kv=_kv(page_size=16, capacity=1024, max_pages=63, n_pages=50, page_table=FAKE)), -2),
+    (dict(kv=_kv(page_size=16, capacity=1024, max_pages=64, n_pages=0, page_table=FAKE)), -2),
+    (dict(kv=_kv(page_size=65536, capacity=65536, max_pages=1, n_pages=32768,
+                 page_table=FAKE)), -2),                # physical ids past 2^31
     (dict(kv=_kv(k_stride=(4 * 1000 * 128, 1000 * 128, 132))), -4),
     (dict(lab=_lab(r=0)), -2),
     (dict(lab=_lab(r=129)), -2),
@@ -272,6 +284,16 @@ def test_one_kernel_path_bounds(lib, G, max_seq, path):
     # k beyond the LDS token list (2048) leaves the one-kernel path
     rc, pl = _plan(lib, kv, _lab(slots=cap), 2049, max_seq)
     assert rc == 0 and ds.PATHS[pl.path] != "fused"
+
+
+def test_calibration_rejects_a_paged_pool(lib):
+    kv = _kv(page_size=16, capacity=1024, max_pages=64, n_pages=50, page_table=FAKE,
+             k_stride=(4 * 16 * 128, 16 * 128, 128))
+    assert lib.ds_calibrate_workspace_size(ctypes.byref(kv), 64, 0) == 0
+    P = ctypes.c_void_p
+    rc = lib.ds_calibrate_channels(ctypes.byref(kv), P(FAKE), 64, None, 0, None, 0, 8, P(FAKE),
+                                   None, P(FAKE), 1 << 20, None)
+    assert rc == -1
 
 
 def test_calibrate_workspace_and_argument_errors(lib):

@@ -499,3 +499,34 @@ def test_attend_sets_agrees_with_decode_on_its_own_selection():
     res = oracle.decode(q, K, V, np.full(B, S, np.int32), k, 0.1, chan=chan, lab=lab)
     got = oracle.attend_sets(q, K, V, res["topk"], 0.1)
     np.testing.assert_array_equal(got, res["out"])
+
+
+# --------------------------------------------------------------------------
+# paged token pool ("use in SGLang": K/V slots pooled across sequences)
+# --------------------------------------------------------------------------
+
+def test_gather_pages_inverts_a_page_scatter():
+    """A contiguous cache scattered into a pool page by page under a random
+    page assignment (written out here slot by slot) is gathered back
+    unchanged, and decoding from the gathered cache is decoding the original;
+    unused table entries (-1) give zero rows."""
+    rng = np.random.default_rng(25)
+    B, H, P, max_pages, D = 3, 2, 16, 5, 128
+    cap = P * max_pages
+    K = rand_f16(rng, (B, H, cap, D))
+    n_pages = B * max_pages + 4
+    perm = rng.permutation(n_pages)[:B * max_pages].reshape(B, max_pages)
+    pool = np.zeros((n_pages, H, P, D), np.float16)
+    for b in range(B):
+        for t in range(cap):
+            pool[perm[b, t // P], :, t % P, :] = K[b, :, t, :]
+    back = oracle.gather_pages(pool, perm, P)
+    assert np.array_equal(back, K)
+    table = perm.copy()
+    table[1, 3:] = -1
+    part = oracle.gather_pages(pool, table, P)
+    assert np.array_equal(part[1, :, :3 * P], K[1, :, :3 * P]) and not part[1, :, 3 * P:].any()
+    q = rand_f16(rng, (B, H, D))
+    ref = oracle.decode(q, K, K, np.full(B, cap, np.int32), 0, 0.1)["out"]
+    got = oracle.decode(q, back, back, np.full(B, cap, np.int32), 0, 0.1)["out"]
+    np.testing.assert_array_equal(got, ref)
