@@ -35,7 +35,7 @@ HBM_PEAK_GBS = 8000.0
 HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction
 
 
-def algorithmic_bytes(cfg, S):
+def algorithmic_bytes(cfg, S, head_cols=None):
     """Bytes one step must move for one layer at length S (all rows): the
     label stream (S * lam per (b, g) row, lam = 2r for fp16 labels, r/2 + 2 for
     int4 codes + fp16 scale), the min(k, S) selected K/V rows of
@@ -46,9 +46,12 @@ def algorithmic_bytes(cfg, S):
     if cfg.k > 0:
         lam = cfg.r // 2 + 2 if cfg.int4 else 2 * cfg.r
     kk = min(cfg.k, S) if cfg.k > 0 else S
+    # per-head layout: each head's own kept K columns, V only for stored heads
+    row_b = (cfg.d_k + cfg.d_v) * 2 * cfg.Hkv if head_cols is None else sum(
+        (c + cfg.d_v) * 2 for c in head_cols if c > 0)
     return {"labels": rows * S * lam,
             "append": rows * (2 * cfg.r + lam) if cfg.k > 0 else 0,
-            "rows": rows * kk * (cfg.d_k + cfg.d_v) * 2,
+            "rows": cfg.B * kk * row_b,
             "q": cfg.B * cfg.Hq * cfg.D * 2,
             "out": cfg.B * cfg.Hq * cfg.d_v * 2}
 
@@ -391,7 +394,23 @@ def measure(cfg, args, torch, ds, lib, layers=0, offload=False, cpu=True):
         Ks.append(inp.K.clone())
         Vs.append(inp.V.clone())
     pages = [None] * L
+    heads = None
     cap = cfg.cap
+    if args.head_cols:
+        # LeanK heads with their own kept counts (the first c of the
+        # workload's kept columns; 0: a fully pruned head, no K or V stored)
+        assert cfg.k <= 0 and args.page_size == 0, "--head-cols: dense workloads, contiguous rows"
+        hc = [int(x) for x in args.head_cols.split(",")]
+        assert len(hc) == cfg.Hkv and max(hc) <= cfg.d_k
+        heads = ds.HeadLayout.packed(hc, cfg.cap, cfg.d_v, dev)
+        for l in range(L):
+            Kb = torch.zeros((cfg.B, heads.k_row), dtype=torch.float16, device=dev)
+            Vb = torch.zeros((cfg.B, max(heads.v_row, 8)), dtype=torch.float16, device=dev)
+            for g, c in enumerate(hc):
+                if c:
+                    heads.head_k(Kb, g).copy_(Ks[l][:, g, :, :c])
+                    heads.head_v(Vb, g).copy_(Vs[l][:, g])
+            Ks[l], Vs[l] = Kb, Vb
     if args.page_size > 0:
         # K/V of every layer in a pool of page_size-token pages under its own
         # shuffled page table (the serving system's token pool)
@@ -403,7 +422,7 @@ def measure(cfg, args, torch, ds, lib, layers=0, offload=False, cpu=True):
     for l in range(L):
         if cfg.k > 0:
             lab = ds.LabelCache.allocate(cfg.B, cfg.Hkv, cap, cfg.r, cfg.int4, dev)
-            ds.label_build(Ks[l], inp.chan, lab, 0, cfg.S0, pages=pages[l])
+            ds.label_build(Ks[l], inp.chan, lab, 0, cfg.S0, pages=pages[l], heads=heads)
             labs.append(lab)
         else:
             labs.append(None)
@@ -425,7 +444,7 @@ def measure(cfg, args, torch, ds, lib, layers=0, offload=False, cpu=True):
             for j in range(cfg.steps)]
     out = torch.empty((cfg.B, cfg.Hq, cfg.d_v), dtype=torch.float16, device=dev)
     ws_bytes = ds.workspace_size(Ks[0], Vs[0], cfg.Hq, cfg.D, labs[0], cfg.k, cap,
-                                 pages=pages[0])
+                                 pages=pages[0], heads=heads)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     print("bench: inputs ready (%.1f GB of K/V)" % (
@@ -436,8 +455,8 @@ def measure(cfg, args, torch, ds, lib, layers=0, offload=False, cpu=True):
         flags |= ds.DECODE_UNFUSED
     S_mid = cfg.S0 + 1 + min(cfg.steps - 1, (args.steps // L) // 2)
     plan = ds.decode_plan(Ks[0], Vs[0], cfg.Hq, cfg.D, labs[0], cfg.k, S_mid, args.n_split, flags,
-                          pages=pages[0])
-    ab = algorithmic_bytes(cfg, S_mid)
+                          pages=pages[0], heads=heads)
+    ab = algorithmic_bytes(cfg, S_mid, heads.k_cols if heads is not None else None)
     kernels = stage_kernels(plan, cfg, bool(flags & ds.DECODE_APPEND))
     final = plan["n_split"] == 1
 
@@ -451,7 +470,7 @@ def measure(cfg, args, torch, ds, lib, layers=0, offload=False, cpu=True):
     def make_call(i, events=None):
         l = i % L
         j = (i // L) % cfg.steps
-        kv = ds.kv_desc(Ks[l], Vs[l], cfg.Hq, cfg.D, pages=pages[l])
+        kv = ds.kv_desc(Ks[l], Vs[l], cfg.Hq, cfg.D, pages=pages[l], heads=heads)
         lab = labs[l].desc() if labs[l] is not None else None
         opts = ds.DecodeOpts()
         opts.n_split, opts.flags = args.n_split, flags
@@ -548,6 +567,7 @@ def measure(cfg, args, torch, ds, lib, layers=0, offload=False, cpu=True):
                    "labels": ("int4" if cfg.int4 else "fp16") if cfg.k > 0 else None,
                    "storage": ("fp16 q, fp16 K/V in a pool of %d-token pages" % args.page_size
                                if args.page_size > 0 else "fp16 q/K/V"),
+                   "head_k_cols": heads.k_cols if heads is not None else None,
                    "layer_caches": L, "path": plan["path"],
                    "n_split": plan["n_split"], "note": cfg.note},
     }
@@ -609,6 +629,9 @@ def main():
     ap.add_argument("--traffic-kernel", default="k_decode_fused")
     ap.add_argument("--traffic-cmd", action="append", help="command recorded with the counters")
     ap.add_argument("--traffic-out", default=None, help="record path (default: under profiles/)")
+    ap.add_argument("--head-cols", default=None,
+                    help="comma-separated kept K columns per KV head (LeanK per-head storage; "
+                         "0: a fully pruned head); dense workloads")
     ap.add_argument("--page-size", type=int, default=0,
                     help="K/V in a pool of pages of this many tokens under shuffled page tables "
                          "(0: contiguous rows)")

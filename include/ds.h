@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define DS_ABI_VERSION 3
+#define DS_ABI_VERSION 4
 
 typedef enum {
   DS_OK = 0,
@@ -61,6 +61,23 @@ typedef enum {
 
 /* Label cache element type ([DS] offline calibration: 4-bit labels). */
 typedef enum { DS_LABEL_F16 = 0, DS_LABEL_INT4 = 1 } ds_label_dtype;
+
+/* Per-KV-head layout of a LeanK cache whose heads keep different numbers of
+ * K columns ([LeanK] section 2.2: each head keeps a hardware-aligned count;
+ * section 4.4: heads whose K channels are all pruned drop their V cache as
+ * well).  Device array [n_kv_heads] (ds_kv_desc.heads).
+ *   k_cols  kept K columns of the head: a multiple of 8 up to d_k, or 0 for a
+ *           fully pruned head, which stores neither K nor V, selects no token
+ *           and outputs zeros;
+ *   k_off   element offset of the head's K block from its batch row's (or
+ *           page's) K base; the block's token stride is k_cols (rows packed);
+ *   v_off   element offset of the head's V block from its batch row's (or
+ *           page's) V base; token stride v_stride[2].
+ * Offsets are multiples of 8 elements.  Entries are not read on the host;
+ * bad ones are undefined behaviour. */
+typedef struct {
+  int64_t k_cols, k_off, v_off;
+} ds_head_layout;
 
 /* K/V cache description (host struct).
  * Contiguous rows (page_size == 0):
@@ -80,6 +97,10 @@ typedef enum { DS_LABEL_F16 = 0, DS_LABEL_INT4 = 1 } ds_label_dtype;
  *   page_size < 2^31.  The label cache stays one contiguous stream per
  *   (batch row, KV head) (ds_label_desc): its contiguity is what the
  *   approximate scores read.
+ * Per-head layout (heads != NULL, either form): K and V of KV head g sit at
+ * heads[g].k_off / v_off from the batch row's (page's) base, K rows of
+ * heads[g].k_cols columns; k_stride[1], k_stride[2] and v_stride[1] are not
+ * used; d_k is the widest kept count (the row width of the keep table).
  * Query head h belongs to KV head h / G with G = n_q_heads / n_kv_heads
  * ([GQA] section 4: consecutive query heads form a group).
  * d_q is the query width (the model's head dim); d_k is the stored K width,
@@ -97,6 +118,7 @@ typedef struct {
   const int32_t* page_table; /* paged: [batch][max_pages]; contiguous: NULL */
   int32_t max_pages;  /* paged: page-table entries per batch row; else 0 */
   int32_t n_pages;    /* paged: pages in the pool; else 0 */
+  const ds_head_layout* heads; /* device [n_kv_heads] per-head layout, or NULL */
 } ds_kv_desc;
 
 /* Label cache description (host struct) ([DS] offline calibration).
@@ -335,7 +357,7 @@ size_t ds_calibrate_workspace_size(const ds_kv_desc* kv, int32_t n_tok, int32_t 
  *           sum_b qn_b and the score (a NaN score is reported as -1 and
  *           ranks last).
  *   workspace  device scratch of ds_calibrate_workspace_size() bytes.
- * K must be contiguous rows (page_size 0).
+ * K must be plain contiguous rows (page_size 0, no per-head layout).
  * Errors: DS_ERR_ARG (null pointer, n_tok, n_win, r or criterion out of
  * range, a paged kv), DS_ERR_SHAPE, DS_ERR_ALIGN (K not 16-byte aligned,
  * stride not a multiple of 8), DS_ERR_WORKSPACE, DS_ERR_HIP. */

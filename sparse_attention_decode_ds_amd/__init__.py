@@ -55,7 +55,7 @@ class KVDesc(ctypes.Structure):
                 ("capacity", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("k_stride", ctypes.c_int64 * 3), ("v_stride", ctypes.c_int64 * 3),
                 ("page_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32),
-                ("n_pages", ctypes.c_int32)]
+                ("n_pages", ctypes.c_int32), ("heads", ctypes.c_void_p)]
 
 
 class LabelDesc(ctypes.Structure):
@@ -77,6 +77,10 @@ class DecodePlan(ctypes.Structure):
 
 
 _lib = None
+
+
+# DS_ABI_VERSION of include/ds.h this binding's structures follow
+ABI_VERSION = 4
 
 
 def load() -> ctypes.CDLL:
@@ -113,6 +117,9 @@ def load() -> ctypes.CDLL:
         lib.ds_status_str.restype = ctypes.c_char_p
         lib.ds_abi_version.argtypes = []
         lib.ds_abi_version.restype = I32
+        if lib.ds_abi_version() != ABI_VERSION:
+            raise ImportError("libds.so has ABI %d, this binding expects %d (rebuild)" %
+                              (lib.ds_abi_version(), ABI_VERSION))
         _lib = lib
     return _lib
 
@@ -143,10 +150,70 @@ class Pages:
     page_size: int
 
 
-def kv_desc(K, V, n_q_heads: int, d_q: int | None = None, pages: Pages | None = None) -> KVDesc:
+@dataclass
+class HeadLayout:
+    """LeanK cache whose KV heads keep different numbers of K columns (LeanK
+    section 2.2; a head with none is fully pruned and stores no V either,
+    section 4.4).  ``table``: int64 [H_kv][3] on the device (k_cols, k_off,
+    v_off); every batch row (or page) of ``tokens`` token slots holds the
+    heads' K blocks back to back in ``k_row`` halves (rows of k_cols columns)
+    and the stored heads' V blocks in ``v_row`` halves (rows of d_v)."""
+    table: torch.Tensor
+    k_cols: list
+    tokens: int
+    k_row: int
+    v_row: int
+    d_v: int = 128
+
+    @staticmethod
+    def packed(k_cols, tokens: int, d_v: int = 128, device="cuda"):
+        k_cols = [int(c) for c in k_cols]
+        if any(c < 0 or c % 8 or c > 128 for c in k_cols):
+            raise ValueError("k_cols: multiples of 8 in [0, 128]")
+        rows, ko, vo = [], 0, 0
+        for c in k_cols:
+            rows.append((c, ko, vo if c > 0 else 0))
+            ko += tokens * c
+            vo += tokens * d_v if c > 0 else 0
+        t = torch.tensor(rows, dtype=torch.int64, device=device)
+        return HeadLayout(t, k_cols, tokens, ko, vo, d_v)
+
+    def head_k(self, Kbuf, g):
+        """Head g's K [B][tokens][k_cols] (a view of the batch-row buffer)."""
+        c = self.k_cols[g]
+        off = int(self.table[g, 1])
+        return Kbuf[:, off:off + self.tokens * c].view(Kbuf.shape[0], self.tokens, c)
+
+    def head_v(self, Vbuf, g):
+        off = int(self.table[g, 2])
+        return Vbuf[:, off:off + self.tokens * self.d_v].view(Vbuf.shape[0], self.tokens, self.d_v)
+
+
+def kv_desc(K, V, n_q_heads: int, d_q: int | None = None, pages: Pages | None = None,
+            heads: HeadLayout | None = None) -> KVDesc:
     """Describe K [B][H_kv][cap][d_k] and V [B][H_kv][cap][d_v] (fp16, unit
     channel stride), or with ``pages`` the pools K [n_pages][H_kv][P][d_k] and
-    V [n_pages][H_kv][P][d_v]."""
+    V [n_pages][H_kv][P][d_v].  With ``heads``, K and V are the per-head
+    buffers [B or n_pages][k_row] and [..][v_row] of that layout."""
+    if heads is not None:
+        d = KVDesc()
+        d0 = K.shape[0]
+        Hkv = len(heads.k_cols)
+        d_k = max(max(heads.k_cols), 8)
+        if pages is not None:
+            B, max_pages = pages.table.shape
+            d.batch, d.capacity = B, max_pages * pages.page_size
+            d.page_size, d.page_table = pages.page_size, pages.table.data_ptr()
+            d.max_pages, d.n_pages = max_pages, d0
+        else:
+            d.batch, d.capacity = d0, heads.tokens
+        d.n_q_heads, d.n_kv_heads = n_q_heads, Hkv
+        d.d_q = d_k if d_q is None else d_q
+        d.d_k, d.d_v = d_k, heads.d_v
+        d.k_stride[0], d.k_stride[1], d.k_stride[2] = K.stride(0), 0, d_k
+        d.v_stride[0], d.v_stride[1], d.v_stride[2] = V.stride(0), 0, heads.d_v
+        d.heads = heads.table.data_ptr()
+        return d
     d0, Hkv, d2, d_k = K.shape
     d = KVDesc()
     if pages is not None:
@@ -196,18 +263,25 @@ class LabelCache:
 
 
 def check_tables(chan, d_k: int, r: int | None = None, keep=None, d_q: int | None = None,
-                 n_kv_heads: int | None = None):
+                 n_kv_heads: int | None = None, head_cols=None):
     """Check the contents of the index tables, which the C ABI does not read
     on the host: chan [H_kv][r] holds distinct stored-K columns in [0, d_k)
-    per KV head; keep [H_kv][d_k] holds query channels in [0, d_q).  Copies
-    the tables to the host (a synchronisation), so it suits set-up time, not
-    every decode step.  Raises ValueError."""
+    per KV head (with ``head_cols``, a per-head layout: in [0, head_cols[g])
+    and not read for a fully pruned head); keep [H_kv][d_k] holds query
+    channels in [0, d_q).  Copies the tables to the host (a synchronisation),
+    so it suits set-up time, not every decode step.  Raises ValueError."""
     if chan is not None:
         c = chan.detach().to("cpu", torch.int64)
         if c.dim() != 2 or (n_kv_heads is not None and c.shape[0] != n_kv_heads) or (
                 r is not None and c.shape[1] != r):
             raise ValueError("chan: expected shape [n_kv_heads][r], got %s" % (tuple(c.shape),))
-        if c.numel() and (int(c.min()) < 0 or int(c.max()) >= d_k):
+        if head_cols is not None:
+            live = [g for g, n in enumerate(head_cols) if n > 0]
+            for g in live:
+                if int(c[g].min()) < 0 or int(c[g].max()) >= head_cols[g]:
+                    raise ValueError("chan: head %d column outside [0, %d)" % (g, head_cols[g]))
+            c = c[live] if live else c[:0]
+        elif c.numel() and (int(c.min()) < 0 or int(c.max()) >= d_k):
             raise ValueError("chan: column outside [0, %d)" % d_k)
         if c.shape[1] > 1 and bool((c.sort(dim=1).values.diff(dim=1) == 0).any()):
             raise ValueError("chan: repeated column in a KV head's table")
@@ -221,16 +295,17 @@ def check_tables(chan, d_k: int, r: int | None = None, keep=None, d_q: int | Non
 
 
 def label_build(K, chan, labels: LabelCache, t_begin: int, t_end: int, stream=None,
-                pages: Pages | None = None):
-    kv = kv_desc(K, K, 1, pages=pages)
+                pages: Pages | None = None, heads: HeadLayout | None = None):
+    kv = kv_desc(K, K, 1, pages=pages, heads=heads)
     lab = labels.desc()
     _check("ds_label_build", load().ds_label_build(
         ctypes.byref(kv), _p(K), _p(chan), ctypes.byref(lab), int(t_begin), int(t_end),
         _stream(stream)))
 
 
-def label_append(K, chan, labels: LabelCache, pos, stream=None, pages: Pages | None = None):
-    kv = kv_desc(K, K, 1, pages=pages)
+def label_append(K, chan, labels: LabelCache, pos, stream=None, pages: Pages | None = None,
+                 heads: HeadLayout | None = None):
+    kv = kv_desc(K, K, 1, pages=pages, heads=heads)
     lab = labels.desc()
     _check("ds_label_append", load().ds_label_append(
         ctypes.byref(kv), _p(K), _p(chan), ctypes.byref(lab), _p(pos), _stream(stream)))
@@ -296,18 +371,19 @@ def channel_overlap(chan_a, chan_b):
 
 
 def workspace_size(K, V, n_q_heads, d_q, labels: LabelCache | None, k, max_seq_len,
-                   pages: Pages | None = None) -> int:
-    kv = kv_desc(K, V, n_q_heads, d_q, pages=pages)
+                   pages: Pages | None = None, heads: HeadLayout | None = None) -> int:
+    kv = kv_desc(K, V, n_q_heads, d_q, pages=pages, heads=heads)
     lab = labels.desc() if labels is not None else None
     return int(load().ds_decode_attn_workspace_size(
         ctypes.byref(kv), ctypes.byref(lab) if lab is not None else None, int(k), int(max_seq_len)))
 
 
 def decode_plan(K, V, n_q_heads, d_q, labels: LabelCache | None, k, max_seq_len,
-                n_split: int = 0, flags: int = 0, pages: Pages | None = None) -> dict:
+                n_split: int = 0, flags: int = 0, pages: Pages | None = None,
+                heads: HeadLayout | None = None) -> dict:
     """What ds_decode_attn runs for these shapes (ds_decode_attn_plan): the
     path name, attention splits, tokens per split, kernel launches, workspace."""
-    kv = kv_desc(K, V, n_q_heads, d_q, pages=pages)
+    kv = kv_desc(K, V, n_q_heads, d_q, pages=pages, heads=heads)
     lab = labels.desc() if labels is not None else None
     opts = DecodeOpts()
     opts.n_split, opts.flags = int(n_split), int(flags)
@@ -331,14 +407,15 @@ def decode_attn(q, K, V, seq_lens, max_seq_len: int, k: int, sm_scale: float,
                 topk_idx=None, workspace=None, n_split: int = 0, flags: int = 0,
                 stage_events=None, stream=None, validate_tables: bool = False,
                 sparse_decode_threshold: int | None = None, min_seq_len: int | None = None,
-                pages: Pages | None = None):
+                pages: Pages | None = None, heads: HeadLayout | None = None):
     """One decode step (ds_decode_attn).  Returns ``out`` fp16 [B][H_q][d_v].
     ``stage_events``: optional ctypes array of STAGE_COUNT + 1 hipEvent_t.
     ``validate_tables``: check chan and keep first (check_tables; synchronises).
     ``sparse_decode_threshold``: apply the batch policy (needs ``min_seq_len``,
     the host's shortest sequence); a dense step then runs with k = 0 (and
     still appends labels when DECODE_APPEND is set), and ``topk_idx`` is left
-    untouched.  ``pages``: K and V are paged pools addressed through its table."""
+    untouched.  ``pages``: K and V are paged pools addressed through its table;
+    ``heads``: K and V are the buffers of a per-head LeanK layout."""
     if sparse_decode_threshold is not None and k > 0:
         if min_seq_len is None:
             raise ValueError("sparse_decode_threshold needs min_seq_len")
@@ -349,9 +426,14 @@ def decode_attn(q, K, V, seq_lens, max_seq_len: int, k: int, sm_scale: float,
         # chan is read by the sparse path and by the label append (a dense
         # step with DECODE_APPEND still appends the current token's label)
         uses_chan = k > 0 or bool(flags & DECODE_APPEND)
-        check_tables(chan if uses_chan else None, K.shape[3],
-                     labels.r if labels is not None else None, keep, d_q, K.shape[1])
-    kv = kv_desc(K, V, Hq, d_q, pages=pages)
+        if heads is not None:
+            check_tables(chan if uses_chan else None, max(heads.k_cols),
+                         labels.r if labels is not None else None, keep, d_q,
+                         len(heads.k_cols), head_cols=heads.k_cols)
+        else:
+            check_tables(chan if uses_chan else None, K.shape[3],
+                         labels.r if labels is not None else None, keep, d_q, K.shape[1])
+    kv = kv_desc(K, V, Hq, d_q, pages=pages, heads=heads)
     lab = labels.desc() if labels is not None and (k > 0 or flags & DECODE_APPEND) else None
     lib = load()
     need = int(lib.ds_decode_attn_workspace_size(
@@ -360,7 +442,7 @@ def decode_attn(q, K, V, seq_lens, max_seq_len: int, k: int, sm_scale: float,
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     if out is None:
-        out = torch.empty((B, Hq, V.shape[3]), dtype=torch.float16, device=q.device)
+        out = torch.empty((B, Hq, kv.d_v), dtype=torch.float16, device=q.device)
     opts = DecodeOpts()
     opts.n_split, opts.flags = int(n_split), int(flags)
     opts.stage_events = ctypes.cast(stage_events, ctypes.c_void_p) if stage_events is not None else None
@@ -375,14 +457,14 @@ def decode_attn(q, K, V, seq_lens, max_seq_len: int, k: int, sm_scale: float,
 def decode_attn_noalloc(q, K, V, seq_lens, max_seq_len: int, k: int, sm_scale: float,
                         chan=None, labels: LabelCache | None = None, keep=None, out=None,
                         topk_idx=None, n_split: int = 0, flags: int = 0, stream=None,
-                        pages: Pages | None = None):
+                        pages: Pages | None = None, heads: HeadLayout | None = None):
     """ds_decode_attn_noalloc: the same step as decode_attn with the library's
     per-GPU scratch in place of a workspace (calls on one GPU must not
     overlap).  ``out`` must be given: this call allocates nothing."""
     if out is None:
         raise ValueError("decode_attn_noalloc: pass out (this call allocates nothing)")
     B, Hq, d_q = q.shape
-    kv = kv_desc(K, V, Hq, d_q, pages=pages)
+    kv = kv_desc(K, V, Hq, d_q, pages=pages, heads=heads)
     lab = labels.desc() if labels is not None and (k > 0 or flags & DECODE_APPEND) else None
     opts = DecodeOpts()
     opts.n_split, opts.flags = int(n_split), int(flags)

@@ -103,6 +103,7 @@ LabelArgs label_args(const ds_kv_desc* kv, const void* K, const int32_t* chan,
     a.pshift = log2i(kv->page_size);
     a.max_pages = kv->max_pages;
   }
+  a.heads = kv->heads;
   a.r = lab->r;
   a.is_int4 = lab->dtype == DS_LABEL_INT4;
   a.slots = lab->slots;
@@ -219,6 +220,8 @@ AttnArgs attn_args(const ds_kv_desc* kv, const void* q, const void* K, const voi
     aa.pmask = kv->page_size - 1;
     aa.max_pages = kv->max_pages;
   }
+  aa.heads = kv->heads;
+  aa.keep_ld = kv->d_k;
   return aa;
 }
 
@@ -464,6 +467,8 @@ ds_status decode_impl(const ds_kv_desc* kv, const void* q, const void* K, const 
     sa.Hkv = Hkv;
     sa.G = G;
     sa.d_k = kv->d_k;
+    sa.keep_ld = kv->d_k;
+    sa.heads = kv->heads;
     sa.keep = keep;
     sa.chan = chan;
     sa.r = lab->r;
@@ -612,7 +617,7 @@ int32_t ds_sparse_decode_enabled(int32_t max_seq_len, int32_t min_seq_len, int32
 }
 
 size_t ds_calibrate_workspace_size(const ds_kv_desc* kv, int32_t n_tok, int32_t n_win) {
-  if (check_kv(kv, false) || kv->page_size || n_tok < 0 || n_tok > kv->capacity || n_win < 0) return 0;
+  if (check_kv(kv, false) || kv->page_size || kv->heads || n_tok < 0 || n_tok > kv->capacity || n_win < 0) return 0;
   if (n_win > 0 && (kv->n_q_heads < 1 || kv->n_q_heads % kv->n_kv_heads)) return 0;
   const int G = n_win > 0 ? kv->n_q_heads / kv->n_kv_heads : 1;
   const CalibPlan pl = calib_plan(kv->batch, kv->n_kv_heads, n_tok, kv->d_k, n_win * G);
@@ -625,7 +630,7 @@ ds_status ds_calibrate_channels(const ds_kv_desc* kv, const void* K, int32_t n_t
                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
   ds_status st = check_kv(kv, false);
   if (st) return st;
-  if (kv->page_size) return DS_ERR_ARG;  // calibration samples are contiguous rows
+  if (kv->page_size || kv->heads) return DS_ERR_ARG;  // calibration samples: plain contiguous rows
   if (n_tok < 0 || n_tok > kv->capacity || n_win < 0) return DS_ERR_ARG;
   if (criterion < DS_CALIB_K || criterion > DS_CALIB_QK) return DS_ERR_ARG;
   if (r < 1 || r > kv->d_k || !chan) return DS_ERR_ARG;

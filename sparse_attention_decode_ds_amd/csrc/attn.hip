@@ -10,16 +10,18 @@ namespace {
 // PAGED: K/V in a paged pool; the staged list holds physical token ids (the
 // dense path stages its positions too).
 template <int G, bool FINAL, bool PAGED>
-__global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a_in) {
   __shared__ int32_t lidx[kMaxTokensPerSplit];
   __shared__ AttnRed<G> red;
 
-  const int row = blockIdx.x / a.n_split;
-  const int split = blockIdx.x - row * a.n_split;
-  const int b = row / a.Hkv;
-  const int g = row - b * a.Hkv;
+  const int row = blockIdx.x / a_in.n_split;
+  const int split = blockIdx.x - row * a_in.n_split;
+  const int b = row / a_in.Hkv;
+  const int g = row - b * a_in.Hkv;
+  const AttnArgs a = with_head(a_in, g);
   const int S = min(max(a.seq_lens[b], 0), a.max_seq);
-  const int n_tok = a.sparse ? min(a.count[row], S) : S;
+  // a fully pruned head (no K columns) attends nothing: zero output
+  const int n_tok = a.d_k == 0 ? 0 : (a.sparse ? min(a.count[row], S) : S);
   const int t0 = split * a.tps;
   const int n_here = max(0, min(n_tok - t0, a.tps));
 

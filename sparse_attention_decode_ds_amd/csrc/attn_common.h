@@ -57,7 +57,7 @@ __device__ __forceinline__ void load_query(const AttnArgs& a, int b, int g, int 
       float v = 0.0f;
       if (kl) {
         const int ch = c * 8 + i;
-        const int qc = a.keep ? a.keep[(int64_t)g * a.d_k + ch] : ch;
+        const int qc = a.keep ? a.keep[(int64_t)g * a.keep_ld + ch] : ch;
         v = h2f(qh[qc]) * a.scale_log2;
       }
       qf[h][i] = v;

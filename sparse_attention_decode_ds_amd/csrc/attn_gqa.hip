@@ -27,14 +27,16 @@ struct GqaLds {
 // the staged list holds physical token ids (the dense path stages its
 // positions too).
 template <int G, bool FINAL, bool RING, bool PAGED>
-__global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a) {
+__global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a_in) {
   __shared__ GqaLds<G> f;
-  const int row = blockIdx.x / a.n_split;
-  const int split = blockIdx.x - row * a.n_split;
-  const int b = row / a.Hkv;
-  const int g = row - b * a.Hkv;
+  const int row = blockIdx.x / a_in.n_split;
+  const int split = blockIdx.x - row * a_in.n_split;
+  const int b = row / a_in.Hkv;
+  const int g = row - b * a_in.Hkv;
+  const AttnArgs a = with_head(a_in, g);
   const int S = min(max(a.seq_lens[b], 0), a.max_seq);
-  const int n_tok = a.sparse ? min(a.count[row], S) : S;
+  // a fully pruned head (no K columns) attends nothing: zero output
+  const int n_tok = a.d_k == 0 ? 0 : (a.sparse ? min(a.count[row], S) : S);
   const int t0 = split * a.tps;
   const int n_here = max(0, min(n_tok - t0, a.tps));
   const int tid = threadIdx.x;
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a) {
     __half v = __float2half(0.0f);
     if (c < a.d_k) {
       const __half* qh = a.q + ((int64_t)b * a.Hq + (int64_t)g * G + h) * a.d_q;
-      v = qh[a.keep ? a.keep[(int64_t)g * a.d_k + c] : c];
+      v = qh[a.keep ? a.keep[(int64_t)g * a.keep_ld + c] : c];
     }
     f.q[h][c] = v;
   }

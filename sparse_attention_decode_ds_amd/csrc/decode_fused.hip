@@ -58,9 +58,9 @@ struct FusedScratch {
 // PAGED: K/V in a paged pool; the row's page-table entries are staged in
 // LDS with the other small loads, and list tokens become physical ids at
 // the K/V loads.
-template <int R, bool INT4, int TPT, bool PAGED>
-__global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs aa, LabelArgs la,
-                                                      int append) {
+template <int R, bool INT4, int TPT, bool PAGED, bool HEADS>
+__global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa_in, AttnArgs aa_in,
+                                                      LabelArgs la_in, int append) {
   using Vec = typename VecSel<R, INT4>::type;
   constexpr int VT = Vec::VT;
   constexpr int JMAX = TPT / VT;  // rounds of vectors per thread
@@ -70,10 +70,25 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
   __shared__ FusedScratch<TPT, PAGED> f;
 
   const int row = blockIdx.x;
-  const int b = row / sa.Hkv;
-  const int g = row - b * sa.Hkv;
+  const int b = row / sa_in.Hkv;
+  const int g = row - b * sa_in.Hkv;
+  // HEADS: a per-head layout; the plain instantiation reads none of its
+  // fields (each argument read or rewritten here lengthens the chain of
+  // scalar loads before the first label load)
+  ScoreArgs sa = sa_in;
+  if (!HEADS) sa.keep_ld = sa.d_k;
+  const AttnArgs aa = HEADS ? with_head(aa_in, g) : aa_in;
+  const LabelArgs la = HEADS ? with_head(la_in, g) : la_in;
   const int S = row_len(sa, b);
   const int tid = threadIdx.x;
+  if (HEADS && aa.d_k == 0) {  // a fully pruned head: no token, zero output
+    if (sa.pad_idx)
+      for (int i = tid; i < sa.idx_stride; i += kNT) sa.idx[(int64_t)row * sa.idx_stride + i] = -1;
+    if (tid < kDv / 8)
+      *reinterpret_cast<uint4*>(aa.out + ((int64_t)b * aa.Hq + g) * kDv + tid * 8) =
+          make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
   const int lane = tid & 63;
   const int w = wave_id();
   const int c = lane & 15;
@@ -90,7 +105,7 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
     for (int i = tid; i < sa.d_q; i += kNT) f.qrow[i] = qh[i];
     for (int j = tid; j < r; j += kNT) f.chan[j] = sa.chan[(int64_t)g * r + j];
     if (sa.keep)
-      for (int i = tid; i < sa.d_k; i += kNT) f.keep[i] = sa.keep[(int64_t)g * sa.d_k + i];
+      for (int i = tid; i < sa.keep_ld; i += kNT) f.keep[i] = sa.keep[(int64_t)g * sa.keep_ld + i];
     if (do_append && tid < (la.d_k >> 3)) {
       const __half* kr = la.K + kv_off(la.ptab, la.pshift, la.max_pages, b, t_new, la.ks0, la.ks2) +
                          (int64_t)g * la.ks1;
@@ -276,27 +291,27 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa, AttnArgs 
   attn_finish<1, true>(aa, acc, f.red, b, g, 0);
 }
 
-template <int R, bool INT4, int TPT>
+template <int R, bool INT4, int TPT, bool HEADS>
 hipError_t launch_rt(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la, int append,
                      int rows, hipStream_t s, const KEvents& ev) {
   if (aa.ptab)
-    return launch_k(k_decode_fused<R, INT4, TPT, true>, dim3(rows), dim3(kNT), s, ev, sa, aa, la,
-                    append);
-  return launch_k(k_decode_fused<R, INT4, TPT, false>, dim3(rows), dim3(kNT), s, ev, sa, aa, la,
-                  append);
+    return launch_k(k_decode_fused<R, INT4, TPT, true, HEADS>, dim3(rows), dim3(kNT), s, ev, sa,
+                    aa, la, append);
+  return launch_k(k_decode_fused<R, INT4, TPT, false, HEADS>, dim3(rows), dim3(kNT), s, ev, sa, aa,
+                  la, append);
 }
 
-template <int TPT>
+template <int TPT, bool HEADS>
 hipError_t launch_tpt(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la, int append,
                       int rows, hipStream_t s, const KEvents& ev) {
   if (sa.is_int4) {
-    if (sa.r == 8) return launch_rt<8, true, TPT>(sa, aa, la, append, rows, s, ev);
-    if (sa.r == 16) return launch_rt<16, true, TPT>(sa, aa, la, append, rows, s, ev);
-    return launch_rt<0, true, TPT>(sa, aa, la, append, rows, s, ev);
+    if (sa.r == 8) return launch_rt<8, true, TPT, HEADS>(sa, aa, la, append, rows, s, ev);
+    if (sa.r == 16) return launch_rt<16, true, TPT, HEADS>(sa, aa, la, append, rows, s, ev);
+    return launch_rt<0, true, TPT, HEADS>(sa, aa, la, append, rows, s, ev);
   }
-  if (sa.r == 8) return launch_rt<8, false, TPT>(sa, aa, la, append, rows, s, ev);
-  if (sa.r == 16) return launch_rt<16, false, TPT>(sa, aa, la, append, rows, s, ev);
-  return launch_rt<0, false, TPT>(sa, aa, la, append, rows, s, ev);
+  if (sa.r == 8) return launch_rt<8, false, TPT, HEADS>(sa, aa, la, append, rows, s, ev);
+  if (sa.r == 16) return launch_rt<16, false, TPT, HEADS>(sa, aa, la, append, rows, s, ev);
+  return launch_rt<0, false, TPT, HEADS>(sa, aa, la, append, rows, s, ev);
 }
 
 }  // namespace
@@ -309,13 +324,15 @@ bool decode_fused_fits(int max_seq, int k, int r, int is_int4) {
 
 // Scores per thread: the smallest of 8, 20 and 24 that holds the longest row,
 // so that no round of register slots is entirely empty for long rows of the
-// common lengths.
+// common lengths.  Per-head layouts take the widest class only (it holds
+// every length the fused path accepts), which keeps their instantiations few.
 hipError_t launch_decode_fused(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la,
                                int append, int rows, hipStream_t s, const KEvents& ev) {
   if (rows <= 0) return hipSuccess;
-  if (sa.max_seq <= kNT * 8) return launch_tpt<8>(sa, aa, la, append, rows, s, ev);
-  if (sa.max_seq <= kNT * 20) return launch_tpt<20>(sa, aa, la, append, rows, s, ev);
-  return launch_tpt<kDecodeFusedTPT>(sa, aa, la, append, rows, s, ev);
+  if (aa.heads) return launch_tpt<kDecodeFusedTPT, true>(sa, aa, la, append, rows, s, ev);
+  if (sa.max_seq <= kNT * 8) return launch_tpt<8, false>(sa, aa, la, append, rows, s, ev);
+  if (sa.max_seq <= kNT * 20) return launch_tpt<20, false>(sa, aa, la, append, rows, s, ev);
+  return launch_tpt<kDecodeFusedTPT, false>(sa, aa, la, append, rows, s, ev);
 }
 
 }  // namespace ds

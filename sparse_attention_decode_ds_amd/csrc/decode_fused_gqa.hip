@@ -53,9 +53,9 @@ struct FusedGScratch {
 
 // TPTC: tokens per thread before rounding up to whole label vectors.
 // PAGED: K/V in a paged pool (the row's page-table entries staged in LDS).
-template <int R, bool INT4, int TPTC, bool PAGED>
-__global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs aa, LabelArgs la,
-                                                       int append) {
+template <int R, bool INT4, int TPTC, bool PAGED, bool HEADS>
+__global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa_in, AttnArgs aa_in,
+                                                       LabelArgs la_in, int append) {
   using Vec = typename VecSel<R, INT4>::type;
   constexpr int VT = Vec::VT;
   constexpr int JMAX = (TPTC + VT - 1) / VT;  // rounds of vectors per thread
@@ -66,11 +66,26 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs 
   __shared__ FusedGScratch<JMAX, PAGED> f;
 
   const int row = blockIdx.x;
-  const int b = row / sa.Hkv;
-  const int g = row - b * sa.Hkv;
+  const int b = row / sa_in.Hkv;
+  const int g = row - b * sa_in.Hkv;
+  // HEADS: a per-head layout; the plain instantiation reads none of its
+  // fields (each argument read or rewritten here lengthens the chain of
+  // scalar loads before the first label load)
+  ScoreArgs sa = sa_in;
+  if (!HEADS) sa.keep_ld = sa.d_k;
+  const AttnArgs aa = HEADS ? with_head(aa_in, g) : aa_in;
+  const LabelArgs la = HEADS ? with_head(la_in, g) : la_in;
   const int S = row_len(sa, b);
   const int G = sa.G;
   const int tid = threadIdx.x;
+  if (HEADS && aa.d_k == 0) {  // a fully pruned head: no token, zero output
+    if (sa.pad_idx)
+      for (int i = tid; i < sa.idx_stride; i += kNTG) sa.idx[(int64_t)row * sa.idx_stride + i] = -1;
+    if (tid < G * (kDv / 8))
+      *reinterpret_cast<uint4*>(aa.out + ((int64_t)b * aa.Hq + (int64_t)g * G) * kDv + tid * 8) =
+          make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
   const int lane = tid & 63;
   const int w = wave_id();
   const int r = sa.r;
@@ -92,7 +107,7 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs 
   if (tid < nq) qv0 = qh[tid];
   if (tid + kNTG < nq) qv1 = qh[tid + kNTG];
   if (tid < r) chv = sa.chan[(int64_t)g * r + tid];
-  if (sa.keep && tid < sa.d_k) kpv = sa.keep[(int64_t)g * sa.d_k + tid];
+  if (sa.keep && tid < sa.keep_ld) kpv = sa.keep[(int64_t)g * sa.keep_ld + tid];
 
   const RowPtrs p = row_ptrs(sa, row);
   const int n_vec = sparse ? (S + VT - 1) / VT : 0;
@@ -113,7 +128,7 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs 
   if (tid < nq) f.qrows[tid / sa.d_q][tid % sa.d_q] = qv0;
   if (tid + kNTG < nq) f.qrows[(tid + kNTG) / sa.d_q][(tid + kNTG) % sa.d_q] = qv1;
   if (tid < r) f.chan[tid] = chv;
-  if (sa.keep && tid < sa.d_k) f.keep[tid] = kpv;
+  if (sa.keep && tid < sa.keep_ld) f.keep[tid] = kpv;
   __syncthreads();
   {
     // qg[j] = sum over the group's heads of q[h][keep[chan[j]]], in head order
@@ -275,27 +290,27 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa, AttnArgs 
   gqa_merge_out(aa, f.red, b, g, G);
 }
 
-template <int R, bool INT4, int TPTC>
+template <int R, bool INT4, int TPTC, bool HEADS>
 hipError_t launch_rt(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la, int append,
                      int rows, hipStream_t s, const KEvents& ev) {
   if (aa.ptab)
-    return launch_k(k_decode_fused_g<R, INT4, TPTC, true>, dim3(rows), dim3(kNTG), s, ev, sa, aa,
-                    la, append);
-  return launch_k(k_decode_fused_g<R, INT4, TPTC, false>, dim3(rows), dim3(kNTG), s, ev, sa, aa,
-                  la, append);
+    return launch_k(k_decode_fused_g<R, INT4, TPTC, true, HEADS>, dim3(rows), dim3(kNTG), s, ev,
+                    sa, aa, la, append);
+  return launch_k(k_decode_fused_g<R, INT4, TPTC, false, HEADS>, dim3(rows), dim3(kNTG), s, ev,
+                  sa, aa, la, append);
 }
 
-template <int TPTC>
+template <int TPTC, bool HEADS>
 hipError_t launch_tpt(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la, int append,
                       int rows, hipStream_t s, const KEvents& ev) {
   if (sa.is_int4) {
-    if (sa.r == 8) return launch_rt<8, true, TPTC>(sa, aa, la, append, rows, s, ev);
-    if (sa.r == 16) return launch_rt<16, true, TPTC>(sa, aa, la, append, rows, s, ev);
-    return launch_rt<0, true, TPTC>(sa, aa, la, append, rows, s, ev);
+    if (sa.r == 8) return launch_rt<8, true, TPTC, HEADS>(sa, aa, la, append, rows, s, ev);
+    if (sa.r == 16) return launch_rt<16, true, TPTC, HEADS>(sa, aa, la, append, rows, s, ev);
+    return launch_rt<0, true, TPTC, HEADS>(sa, aa, la, append, rows, s, ev);
   }
-  if (sa.r == 8) return launch_rt<8, false, TPTC>(sa, aa, la, append, rows, s, ev);
-  if (sa.r == 16) return launch_rt<16, false, TPTC>(sa, aa, la, append, rows, s, ev);
-  return launch_rt<0, false, TPTC>(sa, aa, la, append, rows, s, ev);
+  if (sa.r == 8) return launch_rt<8, false, TPTC, HEADS>(sa, aa, la, append, rows, s, ev);
+  if (sa.r == 16) return launch_rt<16, false, TPTC, HEADS>(sa, aa, la, append, rows, s, ev);
+  return launch_rt<0, false, TPTC, HEADS>(sa, aa, la, append, rows, s, ev);
 }
 
 // Tokens per thread before rounding up to whole label vectors (1, 2 or 4
@@ -322,11 +337,13 @@ bool decode_fused_g_fits(int max_seq, int k, int r, int is_int4, int G) {
 hipError_t launch_decode_fused_g(const ScoreArgs& sa, const AttnArgs& aa, const LabelArgs& la,
                                  int append, int rows, hipStream_t s, const KEvents& ev) {
   if (rows <= 0) return hipSuccess;
+  // per-head layouts: the widest class only (it holds every accepted length)
+  if (aa.heads) return launch_tpt<kTptClass[2], true>(sa, aa, la, append, rows, s, ev);
   if (sa.max_seq <= rows_capacity(kTptClass[0], sa.r, sa.is_int4))
-    return launch_tpt<kTptClass[0]>(sa, aa, la, append, rows, s, ev);
+    return launch_tpt<kTptClass[0], false>(sa, aa, la, append, rows, s, ev);
   if (sa.max_seq <= rows_capacity(kTptClass[1], sa.r, sa.is_int4))
-    return launch_tpt<kTptClass[1]>(sa, aa, la, append, rows, s, ev);
-  return launch_tpt<kTptClass[2]>(sa, aa, la, append, rows, s, ev);
+    return launch_tpt<kTptClass[1], false>(sa, aa, la, append, rows, s, ev);
+  return launch_tpt<kTptClass[2], false>(sa, aa, la, append, rows, s, ev);
 }
 
 }  // namespace ds

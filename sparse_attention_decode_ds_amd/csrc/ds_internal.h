@@ -59,6 +59,7 @@ struct LabelArgs {
   // paged K pool (ptab != nullptr): ks0 is the page stride
   const int32_t* ptab;
   int32_t pshift, max_pages;
+  const ds_head_layout* heads;  // per-head K layout, or null
 };
 
 struct ScoreArgs {
@@ -89,6 +90,8 @@ struct ScoreArgs {
   int32_t* cand_cnt;    // [rows][n_chunks], -1: overflow
   uint32_t* cand_theta; // [rows][n_chunks], smallest kept key (0: chunk kept whole)
   int32_t cand_stride;  // candidate slots per row (<= kMergeCap)
+  const ds_head_layout* heads;  // per-head K layout (fully pruned heads), or null
+  int32_t keep_ld;              // row stride of the keep table (the widest d_k)
 };
 
 struct AttnArgs {
@@ -113,7 +116,39 @@ struct AttnArgs {
   // kernels address tokens by physical id (page << pshift | slot)
   const int32_t* ptab;
   int32_t pshift, pmask, max_pages;
+  const ds_head_layout* heads;  // per-head K/V layout, or null
+  int32_t keep_ld;              // row stride of the keep table (the widest d_k)
 };
+
+// The arguments as seen by one KV head g: with a per-head layout, K and V
+// point at the head's blocks, the head stride is 0 and K's token stride and
+// width are the head's kept count (0: a fully pruned head).
+__device__ __forceinline__ AttnArgs with_head(AttnArgs a, int g) {
+  if (a.heads) {
+    const ds_head_layout h = a.heads[g];
+    a.K += h.k_off;
+    a.V += h.v_off;
+    a.ks1 = 0;
+    a.vs1 = 0;
+    a.ks2 = h.k_cols;
+    a.d_k = (int32_t)h.k_cols;
+  }
+  return a;
+}
+__device__ __forceinline__ LabelArgs with_head(LabelArgs a, int g) {
+  if (a.heads) {
+    const ds_head_layout h = a.heads[g];
+    a.K += h.k_off;
+    a.ks1 = 0;
+    a.ks2 = h.k_cols;
+    a.d_k = (int32_t)h.k_cols;
+  }
+  return a;
+}
+// Kept K columns of head g (d_k without a per-head layout).
+__device__ __forceinline__ int head_cols(const ds_head_layout* heads, int g, int d_k) {
+  return heads ? (int)heads[g].k_cols : d_k;
+}
 
 // Optional timing events recorded by a launch itself, at the kernel's start
 // and end (both or neither).

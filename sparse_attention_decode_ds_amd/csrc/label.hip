@@ -24,6 +24,7 @@ __global__ __launch_bounds__(kThreads) void k_label(LabelArgs a) {
   __shared__ __align__(16) __half rows[kItems][kMaxDk + kRowPad];
   __shared__ int64_t src_off[kItems];
   __shared__ int64_t dst_tok[kItems];  // label slot index (row * slots + t), -1 if idle
+  __shared__ int32_t src_c8[kItems];   // 16-byte pieces of the item's K row
 
   const int tid = threadIdx.x;
   if (tid < kItems) {
@@ -43,23 +44,32 @@ __global__ __launch_bounds__(kThreads) void k_label(LabelArgs a) {
       t = a.t_begin + tile * kItems + tid;
       if (t >= a.t_end) t = -1;
     }
+    int c8 = a.d_k >> 3;
     if (t >= 0 && t < a.cap) {
       const int b = row / a.Hkv;
       const int g = row - b * a.Hkv;
-      so = kv_off(a.ptab, a.pshift, a.max_pages, b, t, a.ks0, a.ks2) + (int64_t)g * a.ks1;
-      dt = (int64_t)row * a.slots + t;
+      // per-head layout: the head's block, rows of its kept columns; a fully
+      // pruned head (no K columns) has no label
+      const LabelArgs h = with_head(a, g);
+      c8 = h.d_k >> 3;
+      if (c8 > 0) {
+        so = kv_off(h.ptab, h.pshift, h.max_pages, b, t, h.ks0, h.ks2) + (int64_t)g * h.ks1 +
+             (h.K - a.K);
+        dt = (int64_t)row * a.slots + t;
+      }
     }
     src_off[tid] = so;
     dst_tok[tid] = dt;
+    src_c8[tid] = c8;
   }
   __syncthreads();
 
   // Stage the K rows: d_k / 8 lanes per row, one 16-byte load each.
-  const int c8n = a.d_k >> 3;
+  const int c8n = a.d_k >> 3;  // the widest row
   for (int i = tid; i < kItems * c8n; i += kThreads) {
     const int item = i / c8n;
     const int c8 = i - item * c8n;
-    if (dst_tok[item] >= 0) {
+    if (dst_tok[item] >= 0 && c8 < src_c8[item]) {
       const uint4 v = *reinterpret_cast<const uint4*>(a.K + src_off[item] + c8 * 8);
       *reinterpret_cast<uint4*>(&rows[item][c8 * 8]) = v;
     }

@@ -113,7 +113,7 @@ __device__ __forceinline__ void gather_query(const ScoreArgs& a, int b, int g, Q
   float acc = 0.0f;
   if (j < a.r) {
     const int col = a.chan[(int64_t)g * a.r + j];
-    const int qc = a.keep ? a.keep[(int64_t)g * a.d_k + col] : col;
+    const int qc = a.keep ? a.keep[(int64_t)g * a.keep_ld + col] : col;
     const __half* qh = a.q + ((int64_t)b * a.Hq + (int64_t)g * a.G) * a.d_q + qc;
     for (int h = 0; h < a.G; ++h) acc += h2f(qh[(int64_t)h * a.d_q]);
   }
@@ -1003,6 +1003,20 @@ __device__ __forceinline__ RegSel list_select_b(const float* sc, Valid valid, Or
 
 __device__ __forceinline__ int row_len(const ScoreArgs& a, int b) {
   return min(max(a.seq_lens[b], 0), a.max_seq);
+}
+
+// A fully pruned KV head (no K columns) selects no token: its set is empty
+// (all -1 when the caller asked for it) and its list length 0.  Returns true
+// for such a row; every thread of the workgroup calls it.
+template <int NT>
+__device__ __forceinline__ bool pruned_row(const ScoreArgs& a, int row, int g) {
+  if (!a.heads || a.heads[g].k_cols != 0) return false;
+  if (a.pad_idx) {
+    int32_t* out = a.idx + (int64_t)row * a.idx_stride;
+    for (int t = threadIdx.x; t < a.idx_stride; t += NT) out[t] = -1;
+  }
+  if (threadIdx.x == 0) a.count[row] = 0;
+  return true;
 }
 
 }  // namespace ds

@@ -37,6 +37,7 @@ __global__ __launch_bounds__(NT) void k_score_chunk(ScoreArgs a) {
   const int g = row - b * a.Hkv;
   const int S = row_len(a, b);
   if (a.k <= 0 || S <= a.k) return;
+  if (a.heads && a.heads[g].k_cols == 0) return;  // a fully pruned head: no labels
   const int t_beg = c * a.chunk;
   const int t_end = min(S, t_beg + a.chunk);
   if (t_beg >= t_end) return;
@@ -58,6 +59,7 @@ __global__ __launch_bounds__(NT) void k_select_stream(ScoreArgs a) {
   const int row = blockIdx.x;
   const int b = row / a.Hkv;
   const int S = row_len(a, b);
+  if (pruned_row<NT>(a, row, row - b * a.Hkv)) return;
   if (emit_all_if_short<NT>(a, row, S)) return;
   const uint32_t* kr = a.keys + (int64_t)row * a.keys_stride;
   const Threshold th = radix_select_global<NT>(kr, S, (uint32_t)a.k, hist, scan_tmp, sel);

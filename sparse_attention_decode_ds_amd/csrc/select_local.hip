@@ -61,7 +61,7 @@ struct LocalScratch {
 // NT threads score a chunk of at most NT * TPT tokens.  Empty slots (past
 // the chunk, and the appended token until its score is known) hold -inf.
 template <int NT, int TPT, int R, bool INT4>
-__global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la, int append) {
+__global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_in, int append) {
   constexpr int kWavesL = NT / 64;
   using Vec = typename VecSel<R, INT4>::type;
   constexpr int VT = Vec::VT;
@@ -76,6 +76,8 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la, 
   const int c = blockIdx.x - row * sa.n_chunks;
   const int b = row / sa.Hkv;
   const int g = row - b * sa.Hkv;
+  if (sa.heads && sa.heads[g].k_cols == 0) return;  // a fully pruned head: no labels
+  const LabelArgs la = with_head(la_in, g);
   const int S = row_len(sa, b);
   const int CH = sa.chunk;
   const int tid = threadIdx.x;
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la, 
     const __half* qh = sa.q + ((int64_t)b * sa.Hq + (int64_t)g * sa.G) * sa.d_q;
     for (int i = tid; i < sa.G * sa.d_q; i += NT) f.qrows[i / sa.d_q][i % sa.d_q] = qh[i];
     if (sa.keep)
-      for (int i = tid; i < sa.d_k; i += NT) f.keep[i] = sa.keep[(int64_t)g * sa.d_k + i];
+      for (int i = tid; i < sa.keep_ld; i += NT) f.keep[i] = sa.keep[(int64_t)g * sa.keep_ld + i];
   }
   for (int j = tid; j < r; j += NT) f.chan[j] = sa.chan[(int64_t)g * r + j];
   if (has_new && tid < (la.d_k >> 3)) {
@@ -327,6 +329,7 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
   const int S = row_len(sa, b);
   const int tid = threadIdx.x;
   int32_t* out = sa.idx + (int64_t)row * sa.idx_stride;
+  if (pruned_row<kNTM>(sa, row, g)) return;
 
   if (S <= sa.k) {  // every token
     for (int t = tid; t < S; t += kNTM) out[t] = t;

@@ -33,7 +33,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ds_abi_version() == 3
+    assert lib.ds_abi_version() == 4
     for code in range(0, -7, -1):
         s = lib.ds_status_str(code).decode()
         assert s and s != "unknown status"

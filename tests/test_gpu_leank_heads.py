@@ -121,3 +121,106 @@ def test_fully_pruned_head_and_pruned_v_columns():
         w = res["out"][:, h, :64]
         err = (np.abs(out[:, h, :64] - w).max(axis=1) / np.abs(w).max(axis=1)).max()
         assert err <= 2e-3, (h, err)
+
+
+# ---------------------------------------------------------------------------
+# Per-head storage (ds_head_layout): every KV head stores only its own kept
+# K columns, and a fully pruned head stores neither K nor V (LeanK section
+# 2.2: hardware-aligned per-head counts; section 4.4: heads with no K channel
+# left drop their V cache too).  Reading: a fully pruned head contributes a
+# zero output and selects no token.
+# ---------------------------------------------------------------------------
+
+def _per_head_case(B, Hkv, G, D, cap, counts, r, seed, pages_P=0):
+    g0 = torch.Generator().manual_seed(seed)
+    d_k = max(counts)
+    Ks = [torch.randn((B, cap, n), generator=g0).half() for n in counts]
+    Vs = [torch.randn((B, cap, D), generator=g0).half() for _ in counts]
+    q = torch.randn((B, Hkv * G, D), generator=g0).half()
+    keep = torch.stack([torch.randperm(D, generator=g0)[:d_k].sort().values
+                        for _ in range(Hkv)]).to(torch.int32)
+    chan = torch.stack([torch.randperm(max(n, r), generator=g0)[:r].sort().values
+                        for n in counts]).to(torch.int32)
+    tokens = pages_P if pages_P else cap
+    lay = ds.HeadLayout.packed(counts, tokens)
+    if not pages_P:
+        Kb = torch.zeros((B, lay.k_row), dtype=torch.float16, device="cuda")
+        Vb = torch.zeros((B, max(lay.v_row, 8)), dtype=torch.float16, device="cuda")
+        for g, n in enumerate(counts):
+            if n:
+                lay.head_k(Kb, g).copy_(Ks[g])
+                lay.head_v(Vb, g).copy_(Vs[g])
+        return q, Ks, Vs, keep, chan, lay, Kb, Vb, None
+    # paged: pool of P-token pages, each page holding every head's block
+    P = pages_P
+    mp = cap // P
+    n_pages = B * mp + 2
+    perm = torch.randperm(n_pages, generator=g0)[:B * mp].view(B, mp).to(torch.int32)
+    Kb = torch.zeros((n_pages, lay.k_row), dtype=torch.float16, device="cuda")
+    Vb = torch.zeros((n_pages, max(lay.v_row, 8)), dtype=torch.float16, device="cuda")
+    for b in range(B):
+        for p in range(mp):
+            pg = int(perm[b, p])
+            for g, n in enumerate(counts):
+                if n:
+                    lay.head_k(Kb[pg:pg + 1], g)[0].copy_(Ks[g][b, p * P:(p + 1) * P])
+                    lay.head_v(Vb[pg:pg + 1], g)[0].copy_(Vs[g][b, p * P:(p + 1) * P])
+    return q, Ks, Vs, keep, chan, lay, Kb, Vb, ds.Pages(perm.cuda(), P)
+
+
+@pytest.mark.parametrize("G", [1, 2])
+@pytest.mark.parametrize("mode", ["fused", "unfused", "stream", "paged", "dense"])
+def test_per_head_storage_matches_oracle(mode, G):
+    """G = 1 runs the vector-unit kernels, G = 2 the matrix-core ones."""
+    B, Hkv, D, cap, S, r = 2, 4, 128, 768, 700, 8
+    k = 0 if mode == "dense" else 64
+    counts = [16, 48, 0, 32]
+    fl = {"unfused": ds.DECODE_UNFUSED, "stream": ds.DECODE_STREAM}.get(mode, 0)
+    q, Ks, Vs, keep, chan, lay, Kb, Vb, pages = _per_head_case(
+        B, Hkv, G, D, cap, counts, r, 44, pages_P=16 if mode == "paged" else 0)
+    print("per-head storage %s G=%d counts %s" % (mode, G, counts), flush=True)
+    scale = 1.0 / np.sqrt(D)
+    labels = ds.LabelCache.allocate(B, Hkv, cap, r, False)
+    ds.label_build(Kb, chan.cuda(), labels, 0, S - 1, pages=pages, heads=lay)
+    seq = torch.full((B,), S, dtype=torch.int32, device="cuda")
+    topk = torch.full((B, Hkv, max(k, 1)), -7, dtype=torch.int32, device="cuda") if k else None
+    out = ds.decode_attn(q.cuda(), Kb, Vb, seq, S, k, scale, chan=chan.cuda(), labels=labels,
+                         keep=keep.cuda(), topk_idx=topk, flags=fl | ds.DECODE_APPEND,
+                         validate_tables=True, pages=pages, heads=lay)
+    torch.cuda.synchronize()
+    out = out.cpu().double().numpy()
+    tk = topk.cpu().numpy() if topk is not None else None
+    for g, n in enumerate(counts):
+        o = out[:, g * G:(g + 1) * G]
+        if n == 0:  # fully pruned: zero output, no token
+            assert np.all(o == 0.0), g
+            if tk is not None:
+                assert np.all(tk[:, g] == -1), g
+            continue
+        qg = q[:, g * G:(g + 1) * G].contiguous().numpy()
+        Kg = Ks[g][:, None].contiguous().numpy()
+        Vg = Vs[g][:, None].contiguous().numpy()
+        cg = chan[g:g + 1].numpy()
+        lab = oracle.Labels.empty(B, 1, labels.slots, r, False)
+        oracle.label_build(Kg, cg, lab, 0, S)
+        got_lab = labels.codes[:, g, :S].cpu().numpy().view(np.uint16)
+        assert np.array_equal(lab.f16[:, 0, :S], got_lab), g  # appended label included
+        res = oracle.decode(qg, Kg, Vg, np.full(B, S, np.int32), k, scale, chan=cg if k else None,
+                            lab=lab if k else None, keep=keep[g:g + 1, :n].numpy(),
+                            want_scores=k > 0)
+        for b in range(B):
+            w = res["out"][b]
+            if k > 0:
+                got, want = set(tk[b, g].tolist()), set(res["topk"][b, 0].tolist())
+                if got != want:
+                    s = res["scores"][b, 0, :S]
+                    sk = np.sort(s)[::-1][k - 1]
+                    tol = 1e-3 * abs(sk) + 1e-6 * np.abs(s).max()
+                    for t in got ^ want:
+                        assert abs(s[t] - sk) <= tol, (g, b, t)
+                    sets = np.full((B, 1, k), -1, np.int32)
+                    sets[b, 0] = tk[b, g]
+                    w = oracle.attend_sets(qg, Kg, Vg, sets, scale, keep=keep[g:g + 1, :n].numpy(),
+                                           rows=[(b, 0)])[b]
+            err = (np.abs(o[b] - w).max(axis=1) / np.abs(w).max(axis=1)).max()
+            assert err <= 2e-3, (g, b, err)
