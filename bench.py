@@ -160,6 +160,50 @@ def stored_traffic(workload, kernel):
     return rec.get("bytes_per_launch")
 
 
+def kstats_path(workload):
+    return os.path.join(ROOT, "profiles", "kstats_%s.json" % workload)
+
+
+def stored_kstats(workload):
+    """Per-kernel rocprofv3 average durations (us) from the stored kernel-trace
+    record, or {} if there is none or the kernel sources changed since."""
+    try:
+        rec = json.load(open(kstats_path(workload)))
+    except (OSError, ValueError):
+        return {}
+    if rec.get("source_hash") != source_hash():
+        return {}
+    return {k: v["avg_us"] for k, v in rec.get("kernels", {}).items()}
+
+
+def write_kstats(args):
+    """Turn a rocprofv3 --kernel-trace --stats kernel_stats.csv of this
+    script's default run of a workload into the stored record: calls and
+    call-weighted average duration of each library kernel."""
+    import csv
+    import re
+    import synth
+    name = synth.CONFIGS[args.workload].name if args.workload in synth.CONFIGS else args.workload
+    kern = {}
+    with open(args.stats_from, newline="") as f:
+        for r in csv.DictReader(f):
+            m = re.search(r"\bds::.*?\b(k_[a-z0-9_]+)", r["Name"])
+            if not m:
+                continue
+            calls, avg = int(r["Calls"]), float(r["AverageNs"]) / 1e3
+            c0, a0 = kern.get(m.group(1), (0, 0.0))
+            kern[m.group(1)] = (c0 + calls, (a0 * c0 + avg * calls) / (c0 + calls))
+    rec = {"workload": name, "source_hash": source_hash(),
+           "kernels": {k: {"calls": c, "avg_us": round(a, 3)} for k, (c, a) in sorted(kern.items())},
+           "commands": args.traffic_cmd or []}
+    dst = args.traffic_out or kstats_path(name)
+    with open(dst, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+    return 0
+
+
 def _pmc_rows(path):
     import csv
     with open(path, newline="") as f:
@@ -537,6 +581,16 @@ def measure(cfg, args, torch, ds, lib, layers=0, offload=False, cpu=True):
             step_ms.append(events.elapsed_ms(b, b + ds.STAGE_COUNT))
         events.close()
 
+    # stored counter and kernel-trace records describe the workload's default
+    # run (contiguous rows, automatic split, default path)
+    plain = (args.page_size == 0 and not args.head_cols and not offload and not args.unfused
+             and args.n_split == 0)
+    ks = stored_kstats(cfg.name) if plain else {}
+    for d in per_kernel:
+        if d["kernel"] in ks:
+            d["rocprof_avg_us"] = ks[d["kernel"]]
+            d["rocprof_frac"] = round(d["algorithmic_bytes"] / (ks[d["kernel"]] * 1e-6) / 1e9 /
+                                      HBM_PEAK_GBS, 4)
     step_bytes = sum(ab.values())
     dom_stage = max(per_kernel, key=lambda d: d["avg_us"])["stage"] if per_kernel else "attn"
     dom = kernels.get(dom_stage, kernels.get("attn"))
@@ -550,7 +604,10 @@ def measure(cfg, args, torch, ds, lib, layers=0, offload=False, cpu=True):
                      "achieved": round(achieved, 1) if achieved else None,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
-                     "traffic": stored_traffic(cfg.name, dom),
+                     "traffic": stored_traffic(cfg.name, dom) if plain else None,
+                     "rocprof_avg_us": ks.get(dom),
+                     "frac_rocprof": (round(dom_bytes / (ks[dom] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                      if dom in ks else None),
                      "algorithmic_bytes_per_launch": dom_bytes,
                      "avg_launch_us": round(dom_ms * 1e3, 3) if dom_ms else None,
                      "launch_us_p50_p90": pct_us(stage_ms.get(dom_stage)),
@@ -627,6 +684,9 @@ def main():
                     help="write the stored counter record from two rocprofv3 --pmc runs "
                          "(FETCH_SIZE, WRITE_SIZE counter_collection.csv) and exit")
     ap.add_argument("--traffic-kernel", default="k_decode_fused")
+    ap.add_argument("--stats-from", default=None, metavar="KERNEL_STATS_CSV",
+                    help="write the stored kernel-trace record of --workload from a rocprofv3 "
+                         "--kernel-trace --stats run of its default bench and exit")
     ap.add_argument("--traffic-cmd", action="append", help="command recorded with the counters")
     ap.add_argument("--traffic-out", default=None, help="record path (default: under profiles/)")
     ap.add_argument("--head-cols", default=None,
@@ -650,6 +710,8 @@ def main():
         return 2
     if args.traffic_from:
         return write_traffic(args)
+    if args.stats_from:
+        return write_kstats(args)
     if args.calibrate:
         return run_calibration(args)
 

@@ -100,3 +100,26 @@ def test_traffic_record_for_the_calibration_workload(tmp_path):
     assert rec["calibration"]["fetch_factor"] == 2.0 and rec["calibration"]["write_factor"] == 1.0
     assert rec["bytes_per_launch"] == int(round((66000.0 * 2 + 1000.0) * 1024))
     assert rec["dispatches"] == [2, 2]
+
+
+def test_kernel_stats_record(tmp_path):
+    # a synthetic rocprofv3 kernel_stats.csv: two instantiations of one
+    # library kernel (averaged by calls), another library kernel, and a
+    # framework kernel that the record leaves out
+    p = tmp_path / "run_kernel_stats.csv"
+    p.write_text(
+        '"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+        '"void ds::(anonymous namespace)::k_attn<1, false, false>(ds::AttnArgs)",30,0,10000.0,1,1,1,1\n'
+        '"void ds::(anonymous namespace)::k_attn<1, true, false>(ds::AttnArgs)",10,0,20000.0,1,1,1,1\n'
+        '"void ds::(anonymous namespace)::k_combine(ds::AttnArgs, int)",40,0,4000.0,1,1,1,1\n'
+        '"void at::native::vectorized_elementwise_kernel<4>(int)",5,0,999.0,1,1,1,1\n')
+    out = tmp_path / "kstats.json"
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "long_128k",
+                        "--stats-from", str(p), "--traffic-out", str(out)],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    import json
+    rec = json.loads(out.read_text())
+    assert rec["workload"] == "long_128k" and rec["source_hash"] == bench.source_hash()
+    assert rec["kernels"] == {"k_attn": {"calls": 40, "avg_us": 12.5},
+                              "k_combine": {"calls": 40, "avg_us": 4.0}}
