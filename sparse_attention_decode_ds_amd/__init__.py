@@ -262,6 +262,21 @@ class LabelCache:
         return d
 
 
+def check_pages(pages: Pages, n_pages: int, max_seq_len: int):
+    """Check the page-table entries a call reads (the pages of tokens below
+    max_seq_len of every batch row) against the pool of n_pages pages; the C
+    ABI does not read the table on the host.  Copies the entries to the host."""
+    P = pages.page_size
+    used = (max(max_seq_len, 0) + P - 1) // P
+    if used > pages.table.shape[1]:
+        raise ValueError("page table: %d pages per row needed, %d given" % (used, pages.table.shape[1]))
+    if used == 0:
+        return
+    t = pages.table[:, :used].to("cpu")
+    if int(t.min()) < 0 or int(t.max()) >= n_pages:
+        raise ValueError("page table: entries outside [0, %d)" % n_pages)
+
+
 def check_tables(chan, d_k: int, r: int | None = None, keep=None, d_q: int | None = None,
                  n_kv_heads: int | None = None, head_cols=None):
     """Check the contents of the index tables, which the C ABI does not read
@@ -410,7 +425,8 @@ def decode_attn(q, K, V, seq_lens, max_seq_len: int, k: int, sm_scale: float,
                 pages: Pages | None = None, heads: HeadLayout | None = None):
     """One decode step (ds_decode_attn).  Returns ``out`` fp16 [B][H_q][d_v].
     ``stage_events``: optional ctypes array of STAGE_COUNT + 1 hipEvent_t.
-    ``validate_tables``: check chan and keep first (check_tables; synchronises).
+    ``validate_tables``: check chan and keep first (check_tables; synchronises),
+    and with ``pages`` the page-table entries in use (check_pages).
     ``sparse_decode_threshold``: apply the batch policy (needs ``min_seq_len``,
     the host's shortest sequence); a dense step then runs with k = 0 (and
     still appends labels when DECODE_APPEND is set), and ``topk_idx`` is left
@@ -434,6 +450,8 @@ def decode_attn(q, K, V, seq_lens, max_seq_len: int, k: int, sm_scale: float,
             check_tables(chan if uses_chan else None, K.shape[3],
                          labels.r if labels is not None else None, keep, d_q, K.shape[1])
     kv = kv_desc(K, V, Hq, d_q, pages=pages, heads=heads)
+    if validate_tables and pages is not None:
+        check_pages(pages, kv.n_pages, max_seq_len)
     lab = labels.desc() if labels is not None and (k > 0 or flags & DECODE_APPEND) else None
     lib = load()
     need = int(lib.ds_decode_attn_workspace_size(

@@ -364,3 +364,17 @@ def test_calibrate_binding_rejects_a_bad_window():
         ds.calibrate_channels(K, 8, "qk", qwin=torch.zeros((2, 3, 4, 128), dtype=torch.float32))
     with pytest.raises(ValueError):
         ds.calibrate_channels(K, 8, "qk", qwin=torch.zeros((3, 3, 4, 128), dtype=torch.float16))
+
+
+def test_check_pages_reads_only_the_pages_in_use():
+    # 2 batch rows, 4 logical pages of 16 tokens each, a pool of 6 pages
+    table = torch.tensor([[5, 0, 9, -1], [1, 2, 3, 4]], dtype=torch.int32)
+    pages = ds.Pages(table, 16)
+    ds.check_pages(pages, 6, 32)           # tokens 0..31: pages 0 and 1 of each row
+    with pytest.raises(ValueError, match="outside"):
+        ds.check_pages(pages, 6, 33)       # page 2 of row 0 is 9 >= 6
+    with pytest.raises(ValueError, match="outside"):
+        ds.check_pages(ds.Pages(torch.tensor([[0, -1]], dtype=torch.int32), 16), 2, 17)
+    with pytest.raises(ValueError, match="needed"):
+        ds.check_pages(pages, 16, 65)      # 5 pages per row, the table has 4
+    ds.check_pages(pages, 6, 0)            # no token: nothing read
