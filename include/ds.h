@@ -366,8 +366,9 @@ ds_status ds_calibrate_channels(const ds_kv_desc* kv, const void* K, int32_t n_t
                                 int32_t criterion, int32_t r, int32_t* chan, float* norms,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Static text for a status code (never NULL). */
-const char* ds_status_str(ds_status s);
+/* Static text for a status code, any int32 value ("unknown status" for one
+ * that is not a ds_status; never NULL). */
+const char* ds_status_str(int32_t status);
 
 /* DS_ABI_VERSION of the loaded library. */
 int32_t ds_abi_version(void);

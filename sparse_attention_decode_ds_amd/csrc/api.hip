@@ -283,8 +283,10 @@ using namespace ds;
 
 extern "C" {
 
-const char* ds_status_str(ds_status s) {
-  switch (s) {
+// Takes the code as a plain integer: any value may arrive here, and a
+// ds_status outside its enumerators would not be a valid enum value.
+const char* ds_status_str(int32_t status) {
+  switch (status) {
     case DS_OK: return "ok";
     case DS_ERR_ARG: return "invalid argument";
     case DS_ERR_SHAPE: return "unsupported or inconsistent shape";
