@@ -498,7 +498,7 @@ ds_status decode_impl(const ds_kv_desc* kv, const void* q, const void* K, const 
     sa.keys_stride = p.keys_stride;
     sa.chunk = kScoreChunk;
     sa.n_chunks = p.n_chunks;
-    sa.cand_key = reinterpret_cast<uint32_t*>(ws + p.off_cand_key);
+    sa.cand_score = reinterpret_cast<float*>(ws + p.off_cand_key);
     sa.cand_idx = reinterpret_cast<int32_t*>(ws + p.off_cand_idx);
     sa.cand_cnt = reinterpret_cast<int32_t*>(ws + p.off_cand_cnt);
     sa.cand_theta = reinterpret_cast<uint32_t*>(ws + p.off_cand_theta);

@@ -85,7 +85,7 @@ struct ScoreArgs {
   int32_t n_chunks;
   // local top-M path: per row kMergeCap candidate slots, chunk c owns
   // [c * cap_row, (c + 1) * cap_row) with cap_row = kMergeCap / chunks_of_row
-  uint32_t* cand_key;   // [rows][kMergeCap]
+  float* cand_score;    // [rows][kMergeCap]: kept scores
   int32_t* cand_idx;    // [rows][kMergeCap]
   int32_t* cand_cnt;    // [rows][n_chunks], -1: overflow
   uint32_t* cand_theta; // [rows][n_chunks], smallest kept key (0: chunk kept whole)

@@ -5,10 +5,13 @@
 //   current token's label when the chunk holds it ([DS] "offline
 //   calibration"), scores the chunk into registers and keeps a superset of
 //   the chunk's share of the row's top k: with quota M, every token whose
-//   linear bin (between the chunk's min and max score) is at or above the bin
-//   of the chunk's M-th largest score.  Kept tokens (key, index) go to the
-//   row's candidate area in ascending index order, together with the
-//   smallest kept key theta (0 when the chunk is kept whole).
+//   score reaches the lower edge T of the linear bin (between the chunk's min
+//   and max score) that holds the chunk's M-th largest score.  Any threshold
+//   keeps the merge exact (every dropped score is below T, every kept one at
+//   or above it); the bin edge makes the kept count about M.  Kept tokens
+//   (score, index) go to the row's candidate area in ascending index order,
+//   together with the smallest kept key theta (0 when the chunk is kept
+//   whole); a chunk whose kept count exceeds its slots reports an overflow.
 //
 // k_select_merge: one workgroup per row gathers the candidates (chunk order,
 //   so ascending token order), selects the k largest exactly (linear bins +
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_i
   int kept = n_c;
   // bit (j * VT + e) of keptm: slot kept
   uint32_t keptm = 0u;
-  uint32_t tmin = 0xFFFFFFFFu;
+  float tmin = __builtin_huge_valf();  // smallest kept score
   if (!keep_all) {
     block_minmax<NT>(mn, mx, f.mm_tmp);
     const LinBins bin(mn, mx);
@@ -220,30 +223,29 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_i
     for (int j = 0; j < JMAX; ++j)
       if (j < jn) {
 #pragma unroll
-        for (int e = 0; e < VT; ++e) {
-          const uint32_t bi = bin(sc[j * VT + e]);
-          if (bi != 0u) atomicAdd(&ss.hist[bi], 1u);  // bin 0: empty slots
-        }
+        for (int e = 0; e < VT; ++e)  // empty slots count in bin 0, which the
+          atomicAdd(&ss.hist[bin(sc[j * VT + e])], 1u);  // search for the M-th never reaches
       }
     __syncthreads();
     // the bin of the M-th largest: every valid key lies in bins 1 .. 2047
     find_digit<NT>(ss.hist, (uint32_t)M, ss.misc + 4, f.scan_tmp);
     const uint32_t bM = ss.misc[4];
-    kept = (int)(ss.misc[5] + ss.misc[6]);
-    if (kept > cap) {  // the boundary bin is too full for this chunk's slots
+    if (ss.misc[5] + ss.misc[6] > (uint32_t)cap) {  // the boundary bin overflows the slots
       if (tid == 0) sa.cand_cnt[(int64_t)row * sa.n_chunks + c] = -1;
       return;
     }
+    // T: the lower edge of bin bM in score units (empty slots, -inf, stay
+    // below it)
+    const float thr = mn + ((float)bM - 1.5f) / bin.scale;
 #pragma unroll
     for (int j = 0; j < JMAX; ++j)
       if (j < jn) {
 #pragma unroll
         for (int e = 0; e < VT; ++e) {
-          const uint32_t bj = bin(sc[j * VT + e]);
-          if (bj >= bM) {
-            keptm |= 1u << (j * VT + e);
-            if (bj == bM) tmin = min(tmin, score_key(sc[j * VT + e]));
-          }
+          const float sv = sc[j * VT + e];
+          const bool k = sv >= thr;
+          keptm |= (k ? 1u : 0u) << (j * VT + e);
+          tmin = fminf(tmin, k ? sv : __builtin_huge_valf());
         }
       }
   } else {
@@ -255,8 +257,12 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_i
   }
 
   // --- ordered emission of the kept tokens ---------------------------------------
-  uint32_t* ck = sa.cand_key + (int64_t)row * sa.cand_stride + (int64_t)c * cap;
-  int32_t* ci = sa.cand_idx + (int64_t)row * sa.cand_stride + (int64_t)c * cap;
+  // The chunk's slot arrays are addressed as a workgroup-uniform base plus a
+  // 32-bit byte offset per store (no 64-bit address arithmetic per item).
+  char* const ck = reinterpret_cast<char*>(sa.cand_score + (int64_t)row * sa.cand_stride +
+                                           (int64_t)c * cap);
+  char* const ci = reinterpret_cast<char*>(sa.cand_idx + (int64_t)row * sa.cand_stride +
+                                           (int64_t)c * cap);
   uint32_t ex[JMAX];
 #pragma unroll
   for (int j = 0; j < JMAX; ++j) {
@@ -268,10 +274,13 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_i
     if (lane == 63) f.tot[j][w] = incl;
   }
   if (!keep_all) {
-    tmin = wave_min_u32(tmin);
-    if (lane == 0) atomicMin(&f.theta, tmin);
+    const uint32_t tk = wave_min_u32(score_key(tmin));
+    if (lane == 0) atomicMin(&f.theta, tk);
   }
   __syncthreads();
+  // Stores stop at the chunk's slots; a kept count beyond them is reported
+  // as an overflow below.
+  const uint32_t lim = (uint32_t)cap * 4u;
   uint32_t run = 0u;
 #pragma unroll
   for (int j = 0; j < JMAX; ++j) {
@@ -283,19 +292,21 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_i
       pre += ww < w ? t : 0u;
       rowt += t;
     }
-    uint32_t pos = run + pre + ex[j];
+    uint32_t off = (run + pre + ex[j]) * 4u;  // < 4 * kMergeCap
 #pragma unroll
     for (int e = 0; e < VT; ++e) {
-      if (keptm & (1u << (j * VT + e))) {
-        ck[pos] = score_key(sc[j * VT + e]);
-        ci[pos] = token(j, e);
-        ++pos;
+      if ((keptm & (1u << (j * VT + e))) && off < lim) {
+        *reinterpret_cast<float*>(ck + off) = sc[j * VT + e];
+        *reinterpret_cast<int32_t*>(ci + off) = token(j, e);
+        off += 4u;
       }
     }
     run += rowt;
   }
+  kept = (int)run;  // every thread holds the total
   if (tid == 0) {
-    sa.cand_cnt[(int64_t)row * sa.n_chunks + c] = kept;
+    // more scores at or above T than the chunk's slots: overflow
+    sa.cand_cnt[(int64_t)row * sa.n_chunks + c] = kept > cap ? -1 : kept;
     sa.cand_theta[(int64_t)row * sa.n_chunks + c] = keep_all ? 0u : f.theta;
   }
 }
@@ -347,7 +358,7 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
   // is token order.  Every load is issued before the counts are known (a
   // group of four that starts below `slots` lies inside the row's area).
   constexpr int VTM = kMergeVT;
-  const uint32_t* ck = sa.cand_key + (int64_t)row * sa.cand_stride;
+  const float* ck = sa.cand_score + (int64_t)row * sa.cand_stride;
   const int32_t* ci = sa.cand_idx + (int64_t)row * sa.cand_stride;
   float sc[kMergeJ * VTM];
   int32_t tok[kMergeJ * VTM];
@@ -363,7 +374,7 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
     const uint32_t tv[4] = {tt.x, tt.y, tt.z, tt.w};
 #pragma unroll
     for (int e = 0; e < VTM; ++e) {
-      sc[j * VTM + e] = key_float(kv[e]);
+      sc[j * VTM + e] = __uint_as_float(kv[e]);
       tok[j * VTM + e] = (int32_t)tv[e];
     }
   }
