@@ -304,6 +304,11 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_i
     run += rowt;
   }
   kept = (int)run;  // every thread holds the total
+  // the chunk's unused slots hold -inf, which the merge's select treats as
+  // empty (so the merge reads no per-chunk counts to mask them)
+  if (kept <= cap)
+    for (int i = kept + tid; i < cap; i += NT)
+      *reinterpret_cast<float*>(ck + (uint32_t)i * 4u) = -__builtin_huge_valf();
   if (tid == 0) {
     // more scores at or above T than the chunk's slots: overflow
     sa.cand_cnt[(int64_t)row * sa.n_chunks + c] = kept > cap ? -1 : kept;
@@ -316,7 +321,6 @@ constexpr int kMergeJ = kMergeCap / (kNTM * kMergeVT);  // rounds
 
 struct MergeScratch {
   SelScratch sel;
-  int32_t ch_cnt[kMaxLocalChunks];
   uint32_t ch_theta[kMaxLocalChunks];
   uint32_t scan_tmp[kNTM / 64];
   float mm_tmp[2 * kNTM / 64];
@@ -354,9 +358,10 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
   const int slots = n_ch * cap;  // <= cand_stride <= kMergeCap
 
   // Candidate slots (j * kNTM + tid) * 4 + e of this thread; chunk c owns
-  // slots [c * cap, c * cap + cnt_c), in ascending token order, so slot order
-  // is token order.  Every load is issued before the counts are known (a
-  // group of four that starts below `slots` lies inside the row's area).
+  // slots [c * cap, (c + 1) * cap): its kept scores in ascending token order
+  // (so slot order is token order), then -inf.  Every load of the row's area
+  // is issued before the row's length arrives; slots past the chunks' (from
+  // an earlier call) are masked once it has.
   constexpr int VTM = kMergeVT;
   const float* ck = sa.cand_score + (int64_t)row * sa.cand_stride;
   const int32_t* ci = sa.cand_idx + (int64_t)row * sa.cand_stride;
@@ -366,7 +371,7 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
   for (int j = 0; j < kMergeJ; ++j) {
     const int i = (j * kNTM + tid) * VTM;
     uint4 kk = make_uint4(0u, 0u, 0u, 0u), tt = make_uint4(0u, 0u, 0u, 0u);
-    if (i < slots) {
+    if (i < sa.cand_stride) {
       kk = *reinterpret_cast<const uint4*>(ck + i);
       tt = *reinterpret_cast<const uint4*>(ci + i);
     }
@@ -385,7 +390,6 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
   __syncthreads();
   if (tid < min(n_ch, kMaxLocalChunks)) {
     const int cnt = sa.cand_cnt[(int64_t)row * sa.n_chunks + tid];
-    f.ch_cnt[tid] = cnt;
     f.ch_theta[tid] = sa.cand_theta[(int64_t)row * sa.n_chunks + tid];
     if (cnt < 0 || cnt > cap) atomicOr(&f.flag, 1u);
     atomicAdd(&f.total, (uint32_t)max(cnt, 0));
@@ -394,28 +398,18 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
   bool full = f.flag != 0u || f.total < (uint32_t)sa.k;
 
   if (!full) {
-    // Slots past their chunk's count become empty (-inf); the chunk of slot
-    // i is floor(i / cap).
+    // Slots past the chunks become empty (-inf) too; mn is over the
+    // non-empty slots.
     float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
-    const float inv_cap = 1.0f / (float)cap;
 #pragma unroll
     for (int j = 0; j < kMergeJ; ++j)
 #pragma unroll
       for (int e = 0; e < VTM; ++e) {
         const int i = (j * kNTM + tid) * VTM + e;
-        bool ok = false;
-        if (i < slots) {
-          int c = (int)((float)i * inv_cap);
-          c += (i >= (c + 1) * cap) ? 1 : 0;
-          c -= (i < c * cap) ? 1 : 0;
-          ok = i - c * cap < f.ch_cnt[c];
-        }
-        if (ok) {
-          mn = fminf(mn, sc[j * VTM + e]);
-          mx = fmaxf(mx, sc[j * VTM + e]);
-        } else {
-          sc[j * VTM + e] = -__builtin_huge_valf();
-        }
+        const float v = i < slots ? sc[j * VTM + e] : -__builtin_huge_valf();
+        sc[j * VTM + e] = v;
+        mx = fmaxf(mx, v);
+        mn = fminf(mn, v == -__builtin_huge_valf() ? __builtin_huge_valf() : v);
       }
     sel_clear<kNTM>(f.sel);  // published by block_minmax's barriers
     block_minmax<kNTM>(mn, mx, f.mm_tmp);
