@@ -48,16 +48,21 @@ __device__ __forceinline__ RowPtrs row_ptrs(const ScoreArgs& a, int row) {
 // ---------------------------------------------------------------------------
 // qg[j] (fp32) for every label dtype.  For int4 labels with r <= 16 also a
 // fixed-point copy: with e the exponent such that max_j |qg[j]| < 2^e,
-// qi[j] = rint(qg[j] * 2^(24 - e)) is split into seven balanced base-16
-// digits in [-8, 7]; dig[w][d] packs digit d of channels 8w .. 8w + 7 (nibble
-// i = channel 8w + i, the order of the int4 codes).  Then
+// qi[j] = rint(qg[j] * 2^(kQBits - e)) is split into kQDigits balanced
+// base-16 digits in [-8, 7] (five digits hold any |qi| <= 2^18: their range
+// is [-559240, 489335]); dig[w][d] packs digit d of channels 8w .. 8w + 7
+// (nibble i = channel 8w + i, the order of the int4 codes).  Then
 // sum_j qi[j] * c[j] = sum_d 16^d * (4-bit dot products of dig[.][d] with the
-// code words), exactly in int32 (|qi| <= 2^24, |c| <= 7, r <= 16), and the
-// score is that integer times 2^(e - 24) times the token's scale.
+// code words), exactly in int32 (|qi| <= 2^18, |c| <= 7, r <= 16), and the
+// score is that integer times 2^(e - kQBits) times the token's scale.  The
+// query's rounding, at most 2^-18 of max|qg| per channel, lies far below the
+// 4-bit labels' own (a code step is 1/7 of the token's largest label).
+constexpr int kQBits = 18;
+constexpr int kQDigits = 5;
 struct QueryLds {
   float qg[128];
-  uint32_t dig[2][7];
-  float inv;  // 2^(e - 24)
+  uint32_t dig[2][kQDigits];
+  float inv;  // 2^(e - kQBits)
 };
 
 // Reductions over lanes 0 .. 15 of a wave with DPP row shifts (lanes with no
@@ -86,16 +91,16 @@ __device__ __forceinline__ void make_qdig(float qgv, int r, QueryLds& q) {
   const float amax =
       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(row_max16(on ? fabsf(qgv) : 0.0f)), 15));
   const int e = amax > 0.0f ? ilogbf(amax) + 1 : 0;
-  int x = on ? (int)rintf(ldexpf(qgv, 24 - e)) : 0;
+  int x = on ? (int)rintf(ldexpf(qgv, kQBits - e)) : 0;
 #pragma unroll
-  for (int d = 0; d < 7; ++d) {
+  for (int d = 0; d < kQDigits; ++d) {
     const int dg = ((x + 8) & 15) - 8;
     x = (x - dg) / 16;  // exact: x - dg is a multiple of 16
     const uint32_t wd = row_or8(on ? (uint32_t)(dg & 15) << (4 * (lane & 7)) : 0u);
     if (lane == 7) q.dig[0][d] = wd;
     if (lane == 15) q.dig[1][d] = wd;
   }
-  if (lane == 0) q.inv = ldexpf(1.0f, e - 24);
+  if (lane == 0) q.inv = ldexpf(1.0f, e - kQBits);
 }
 
 // Thread tid < r holds qg[tid] in qgv: store it, and for int4 labels with
@@ -131,13 +136,13 @@ struct QFloat {
 };
 template <int W>
 struct QDig {
-  uint32_t d[W][7];
+  uint32_t d[W][kQDigits];
   float inv;
   __device__ __forceinline__ void load(const QueryLds& l) {
 #pragma unroll
     for (int w = 0; w < W; ++w)
 #pragma unroll
-      for (int i = 0; i < 7; ++i) d[w][i] = l.dig[w][i];
+      for (int i = 0; i < kQDigits; ++i) d[w][i] = l.dig[w][i];
     inv = l.inv;
   }
 };
@@ -151,7 +156,7 @@ template <int W>
 __device__ __forceinline__ int dot_dig(const QDig<W>& q, const uint32_t* w) {
   int acc = 0;
 #pragma unroll
-  for (int d = 6; d >= 0; --d) {
+  for (int d = kQDigits - 1; d >= 0; --d) {
     acc *= 16;
 #pragma unroll
     for (int i = 0; i < W; ++i) acc = __builtin_amdgcn_sdot8((int)q.d[i][d], (int)w[i], acc, false);
@@ -167,7 +172,7 @@ __device__ __forceinline__ void dot_dig_n(const QDig<W>& q, const uint32_t* w, i
 #pragma unroll
   for (int n = 0; n < N; ++n) acc[n] = 0;
 #pragma unroll
-  for (int d = 6; d >= 0; --d) {
+  for (int d = kQDigits - 1; d >= 0; --d) {
 #pragma unroll
     for (int n = 0; n < N; ++n) acc[n] *= 16;
 #pragma unroll
