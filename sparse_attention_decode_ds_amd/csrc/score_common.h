@@ -54,7 +54,9 @@ __device__ __forceinline__ RowPtrs row_ptrs(const ScoreArgs& a, int row) {
 // (nibble i = channel 8w + i, the order of the int4 codes).  Then
 // sum_j qi[j] * c[j] = sum_d 16^d * (4-bit dot products of dig[.][d] with the
 // code words), exactly in int32 (|qi| <= 2^18, |c| <= 7, r <= 16), and the
-// score is that integer times 2^(e - kQBits) times the token's scale.  The
+// score is that integer times the token's scale.  The row's common factor
+// 2^(e - kQBits) is left out: an exact power of two that scales every score
+// of the row alike, it changes no comparison, so no selected set.  The
 // query's rounding, at most 2^-18 of max|qg| per channel, lies far below the
 // 4-bit labels' own (a code step is 1/7 of the token's largest label).
 constexpr int kQBits = 18;
@@ -62,7 +64,6 @@ constexpr int kQDigits = 5;
 struct QueryLds {
   float qg[128];
   uint32_t dig[2][kQDigits];
-  float inv;  // 2^(e - kQBits)
 };
 
 // Reductions over lanes 0 .. 15 of a wave with DPP row shifts (lanes with no
@@ -100,7 +101,6 @@ __device__ __forceinline__ void make_qdig(float qgv, int r, QueryLds& q) {
     if (lane == 7) q.dig[0][d] = wd;
     if (lane == 15) q.dig[1][d] = wd;
   }
-  if (lane == 0) q.inv = ldexpf(1.0f, e - kQBits);
 }
 
 // Thread tid < r holds qg[tid] in qgv: store it, and for int4 labels with
@@ -137,13 +137,11 @@ struct QFloat {
 template <int W>
 struct QDig {
   uint32_t d[W][kQDigits];
-  float inv;
   __device__ __forceinline__ void load(const QueryLds& l) {
 #pragma unroll
     for (int w = 0; w < W; ++w)
 #pragma unroll
       for (int i = 0; i < kQDigits; ++i) d[w][i] = l.dig[w][i];
-    inv = l.inv;
   }
 };
 struct QPtr {
@@ -214,7 +212,7 @@ struct LabelVec<8, true> {  // 4 tokens: 16 B of codes + 8 B of scales
     int acc[4];
     dot_dig_n<1, 4>(q, w, acc);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) out[u] = (float)acc[u] * (sc[u] * q.inv);
+    for (int u = 0; u < 4; ++u) out[u] = (float)acc[u] * sc[u];
   }
 };
 
@@ -235,7 +233,7 @@ struct LabelVec<16, true> {  // 2 tokens: 16 B of codes + 4 B of scales
     int acc[2];
     dot_dig_n<2, 2>(q, w, acc);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) out[u] = (float)acc[u] * (sc[u] * q.inv);
+    for (int u = 0; u < 2; ++u) out[u] = (float)acc[u] * sc[u];
   }
 };
 
@@ -588,7 +586,7 @@ __device__ __forceinline__ void append_label(const LabelArgs& la, int row, int t
     if (with_score && lane == 0) {
       QDig<(R == 16 ? 2 : 1)> qd;
       qd.load(f.q);
-      f.snew = (float)dot_dig(qd, w) * (sf * qd.inv);
+      f.snew = (float)dot_dig(qd, w) * sf;
     }
   } else if (with_score && lane == 0) {
     float acc = 0.0f;
