@@ -49,6 +49,7 @@ struct FusedScratch {
   SelScratch sel;
   uint32_t tot[TPT * kWaves];  // per round and wave: taken | equal << 16
   int32_t lidx[kDecodeFusedMaxK];
+  int32_t junk[64];  // spare words of the list writes
   AttnRed<1> red;
   int32_t ptab[PAGED ? kFusedPages : 1];  // the row's page-table entries (paged pool)
 };
@@ -252,8 +253,8 @@ __global__ __launch_bounds__(kNT, 4) void k_decode_fused(ScoreArgs sa_in, AttnAr
 
     // --- exact select into the LDS token list --------------------------------
     const LinBins bin(mn, mx);
-    const ListSel ls = list_select_a<kNT, VT, JMAX>(sc, valid, token, (uint32_t)sa.k, bin, f.sel,
-                                                    f.scan_tmp, f.lidx);
+    const ListSel ls = list_select_a<kNT, VT, JMAX, true>(sc, valid, token, (uint32_t)sa.k, bin,
+                                                          f.sel, f.scan_tmp, f.lidx, f.junk);
     const int n_a = (int)ls.n_a;
     if (!sa.pad_idx && ls.cnt <= (uint32_t)kRankMax) {
       // Common case: the tokens of the bins above the boundary bin are

@@ -47,6 +47,7 @@ struct FusedGScratch {
   uint32_t tot[JMAX * kWG];  // per round and wave: taken | equal << 16
   alignas(16) __half qk[kMaxGroup][kDv];  // query rows at the stored K columns' channels
   int32_t lidx[kDecodeFusedMaxK];
+  int32_t junk[64];  // spare words of the list writes
   AttnRed<kMaxGroup, kWG> red;
   int32_t ptab[PAGED ? kFusedGPages : 1];  // the row's page-table entries (paged pool)
 };
@@ -256,8 +257,8 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa_in, AttnAr
 
     // --- exact select into the LDS token list --------------------------------
     const LinBins bin(mn, mx);
-    const ListSel ls = list_select_a<kNTG, VT, JMAX>(sc, valid, token, (uint32_t)sa.k, bin,
-                                                     f.sel, f.scan_tmp, f.lidx);
+    const ListSel ls = list_select_a<kNTG, VT, JMAX, true>(sc, valid, token, (uint32_t)sa.k, bin,
+                                                           f.sel, f.scan_tmp, f.lidx, f.junk);
     if (!sa.pad_idx && ls.cnt <= (uint32_t)kRankMax) {
       list_rank<kNTG>(ls, f.sel, f.lidx);
     } else {

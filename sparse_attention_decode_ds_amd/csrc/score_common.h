@@ -843,10 +843,13 @@ struct ListSel {
 // kRankMax of them, the items of b* to the candidate arrays (key, position),
 // both ordered by (wave, lane, round, element) through one exchange of wave
 // totals.  Ends with a barrier, after which list[0 .. n_a) is complete.
-template <int NT, int VT, int JMAX, typename Valid, typename Order>
+// JUNK (a list in LDS with 64 spare words at `junk`): every item is written
+// without a branch, the ones below b* into the lane's own spare word.
+template <int NT, int VT, int JMAX, bool JUNK = false, typename Valid, typename Order>
 __device__ __forceinline__ ListSel list_select_a(const float* sc, Valid valid, Order order,
                                                  uint32_t k, const LinBins& bin, SelScratch& ss,
-                                                 uint32_t* scan_tmp, int32_t* list) {
+                                                 uint32_t* scan_tmp, int32_t* list,
+                                                 int32_t* junk = nullptr) {
   constexpr int N = JMAX * VT;
   static_assert(N <= 32, "one bit per item");
   const int lane = threadIdx.x & 63;
@@ -896,21 +899,43 @@ __device__ __forceinline__ ListSel list_select_a(const float* sc, Valid valid, O
 #pragma unroll
   for (int i = 0; i < NT / 64; ++i) pos += i < w ? scan_tmp[i] : 0u;
   uint32_t pa = pos & 0xFFFFu, pb = pos >> 16;
+  if (JUNK) {
 #pragma unroll
-  for (int j = 0; j < JMAX; ++j)
+    for (int j = 0; j < JMAX; ++j)
 #pragma unroll
-    for (int e = 0; e < VT; ++e) {
-      const int i = j * VT + e;
-      if ((above >> i) & 1u) {
-        list[pa++] = order(j, e);
-      } else if ((equal >> i) & 1u) {
-        if (few) {
-          ss.cand_key[pb] = score_key(sc[i]);
-          ss.cand_idx[pb] = order(j, e);
-        }
-        ++pb;
+      for (int e = 0; e < VT; ++e) {
+        const uint32_t a = (above >> (j * VT + e)) & 1u;
+        *(a ? list + pa : junk + lane) = order(j, e);
+        pa += a;
       }
+    if (few && equal) {  // the few items of b*: most threads have none
+#pragma unroll
+      for (int j = 0; j < JMAX; ++j)
+#pragma unroll
+        for (int e = 0; e < VT; ++e)
+          if ((equal >> (j * VT + e)) & 1u) {
+            ss.cand_key[pb] = score_key(sc[j * VT + e]);
+            ss.cand_idx[pb] = order(j, e);
+            ++pb;
+          }
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < JMAX; ++j)
+#pragma unroll
+      for (int e = 0; e < VT; ++e) {
+        const int i = j * VT + e;
+        if ((above >> i) & 1u) {
+          list[pa++] = order(j, e);
+        } else if ((equal >> i) & 1u) {
+          if (few) {
+            ss.cand_key[pb] = score_key(sc[i]);
+            ss.cand_idx[pb] = order(j, e);
+          }
+          ++pb;
+        }
+      }
+  }
   __syncthreads();
   return ls;
 }
