@@ -325,6 +325,7 @@ struct MergeScratch {
   uint32_t scan_tmp[kNTM / 64];
   float mm_tmp[2 * kNTM / 64];
   uint32_t tot[kMergeJ * (kNTM / 64)];
+  int32_t junk[64];  // spare words of the LDS list writes
   uint32_t flag;  // 1: fall back to the full select
   uint32_t total; // candidates of the row
 };
@@ -422,8 +423,11 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
     const LinBins bin(mn, mx);
     const bool in_lds = sa.k <= kMergeLdsList;
     int32_t* list = in_lds ? lds_list : out;
-    const ListSel ls = list_select_a<kNTM, VTM, kMergeJ>(sc, valid, order, (uint32_t)sa.k, bin,
-                                                         f.sel, f.scan_tmp, list);
+    const ListSel ls =
+        in_lds ? list_select_a<kNTM, VTM, kMergeJ, true>(sc, valid, order, (uint32_t)sa.k, bin,
+                                                         f.sel, f.scan_tmp, list, f.junk)
+               : list_select_a<kNTM, VTM, kMergeJ>(sc, valid, order, (uint32_t)sa.k, bin, f.sel,
+                                                   f.scan_tmp, list);
     const RegSel rs =
         ls.cnt <= (uint32_t)kRankMax
             ? list_rank<kNTM>(ls, f.sel, list)
