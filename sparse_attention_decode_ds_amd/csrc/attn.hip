@@ -58,9 +58,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a_in) {
   attn_finish<G, FINAL>(a, acc, red, b, g, split);
 }
 
-// Log-sum-exp merge of the split partials: 16 lanes per (batch, query head).
-__global__ __launch_bounds__(kAttnThreads) void k_combine(AttnArgs a, int n_rows) {
-  const int rq = blockIdx.x * (kAttnThreads / 16) + (threadIdx.x >> 4);
+// Log-sum-exp merge of the split partials: 16 lanes per (batch, query head),
+// one wave of four rows per workgroup, so that the few rows of a long-context
+// batch spread over many compute units (one round of dependent loads each).
+constexpr int kCombineThreads = 64;
+__global__ __launch_bounds__(kCombineThreads) void k_combine(AttnArgs a, int n_rows) {
+  const int rq = blockIdx.x * (kCombineThreads / 16) + (threadIdx.x >> 4);
   if (rq >= n_rows) return;
   merge_partials(a, rq, threadIdx.x & 15);
 }
@@ -90,8 +93,9 @@ hipError_t launch_attn(const AttnArgs& a, int rows, int G, bool final_out, hipSt
 hipError_t launch_combine(const AttnArgs& a, int B, hipStream_t s, const KEvents& ev) {
   const int n_rows = B * a.Hq;
   if (n_rows <= 0) return hipSuccess;
-  const int per = kAttnThreads / 16;
-  return launch_k(k_combine, dim3((n_rows + per - 1) / per), dim3(kAttnThreads), s, ev, a, n_rows);
+  const int per = kCombineThreads / 16;
+  return launch_k(k_combine, dim3((n_rows + per - 1) / per), dim3(kCombineThreads), s, ev, a,
+                  n_rows);
 }
 
 }  // namespace ds
