@@ -169,6 +169,9 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa_in, AttnAr
   auto token = [&](int j, int e) { return (j * kNTG + tid) * VT + e; };
   auto valid = [&](int j, int) { return j < jn; };  // empty slots hold -inf
   const int n_att = sparse ? sa.k : S;  // tokens attended
+  const GqaLane ln(aa, b, g, PAGED);
+  GqaTile cur;         // the wave's tile in registers
+  bool early = false;  // its first tile was loaded during the select
   if (!sparse) {
     if (do_append && w == kAppendWave) append_new(false);
     if (sa.pad_idx) {
@@ -260,6 +263,14 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa_in, AttnAr
     const ListSel ls = list_select_a<kNTG, VT, JMAX, true>(sc, valid, token, (uint32_t)sa.k, bin,
                                                            f.sel, f.scan_tmp, f.lidx, f.junk);
     if (!sa.pad_idx && ls.cnt <= (uint32_t)kRankMax) {
+      // The wave's first tile, when it lies in the part of the list already
+      // complete (tokens above the boundary bin), is loaded while the few
+      // boundary candidates are ranked.
+      const int i0 = w * kGqaTile;
+      if (i0 + kGqaTile <= (int)ls.n_a) {
+        gqa_load<PAGED>(aa, ln, i0, n_att, tok, cur);
+        early = true;
+      }
       list_rank<kNTG>(ls, f.sel, f.lidx);
     } else {
       const RegSel rs = list_select_b<kNTG, VT, JMAX>(sc, valid, token, bin, ls, f.sel,
@@ -275,15 +286,14 @@ __global__ __launch_bounds__(kNTG) void k_decode_fused_g(ScoreArgs sa_in, AttnAr
 
   // --- attention -----------------------------------------------------------------
   // Each wave takes every 16th tile of the list, one tile in registers.
-  const GqaLane ln(aa, b, g, PAGED);
   half4_t qb[8];
   gqa_query(&f.qk[0][0], G, ln, qb);
   GqaState st;
   gqa_init(st);
   constexpr int D = kWG * kGqaTile;  // the wave's tiles are D positions apart
   for (int i0 = w * kGqaTile; i0 < n_att; i0 += D) {
-    GqaTile cur;
-    gqa_load<PAGED>(aa, ln, i0, n_att, tok, cur);
+    if (!early) gqa_load<PAGED>(aa, ln, i0, n_att, tok, cur);
+    early = false;
     gqa_tile(cur, qb, i0, n_att, aa.scale_log2, ln.kg, st);
   }
   gqa_to_red(st, ln, G, w, f.red);
