@@ -14,16 +14,17 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a_in) {
   __shared__ int32_t lidx[kMaxTokensPerSplit];
   __shared__ AttnRed<G> red;
 
-  const int row = blockIdx.x / a_in.n_split;
-  const int split = blockIdx.x - row * a_in.n_split;
-  const int b = row / a_in.Hkv;
-  const int g = row - b * a_in.Hkv;
+  const SplitItem it = split_item(a_in, blockIdx.x);
+  if (it.n == 0) return;  // every head pruned: the combine writes zeros
+  const int b = it.b, g = it.g;
+  const int row = b * a_in.Hkv + g;
   const AttnArgs a = with_head(a_in, g);
   const int S = min(max(a.seq_lens[b], 0), a.max_seq);
   // a fully pruned head (no K columns) attends nothing: zero output
   const int n_tok = a.d_k == 0 ? 0 : (a.sparse ? min(a.count[row], S) : S);
-  const int t0 = split * a.tps;
-  const int n_here = max(0, min(n_tok - t0, a.tps));
+  const int tps = split_tokens(a, it, n_tok);
+  const int t0 = it.split * tps;
+  const int n_here = max(0, min(n_tok - t0, tps));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -55,7 +56,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a_in) {
   } else {
     attend<G, false>(a, Kr, Vr, slot, n_here, [&](int i) { return (int64_t)(t0 + i); }, qf, acc);
   }
-  attn_finish<G, FINAL>(a, acc, red, b, g, split);
+  attn_finish<G, FINAL>(a, acc, red, b, g, it.split);
 }
 
 // Log-sum-exp merge of the split partials: 16 lanes per (batch, query head),
@@ -63,9 +64,25 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a_in) {
 // batch spread over many compute units (one round of dependent loads each).
 constexpr int kCombineThreads = 64;
 __global__ __launch_bounds__(kCombineThreads) void k_combine(AttnArgs a, int n_rows) {
-  const int rq = blockIdx.x * (kCombineThreads / 16) + (threadIdx.x >> 4);
-  if (rq >= n_rows) return;
-  merge_partials(a, rq, threadIdx.x & 15);
+  const int rq0 = blockIdx.x * (kCombineThreads / 16) + (threadIdx.x >> 4);
+  if (!split_by_bytes(a)) {
+    if (rq0 >= n_rows) return;
+    merge_partials(a.part + (int64_t)rq0 * a.n_split * kPartStride, a.n_split, kPartStride,
+                   a.out + (int64_t)rq0 * kDv, threadIdx.x & 15);
+    return;
+  }
+  const int rq = min(rq0, n_rows - 1);
+  const int G = a.Hq / a.Hkv;
+  const int b = rq / a.Hq;
+  const int hq = rq - b * a.Hq;
+  const int g = hq / G;
+  const int h = hq - g * G;
+  int base, n;
+  head_items(a, g, base, n);  // every lane of the wave takes part
+  if (rq0 >= n_rows) return;
+  const int64_t slot0 = ((int64_t)b * a.Hkv * a.n_split + base) * G + h;
+  merge_partials(a.part + slot0 * kPartStride, n, (int64_t)G * kPartStride,
+                 a.out + (int64_t)rq * kDv, threadIdx.x & 15);
 }
 
 template <int G>

@@ -37,6 +37,102 @@ struct AttnRed {
   alignas(16) float v[NW][G][kDv + 4];  // o[0 .. kDv), m, l, 2 floats of padding
 };
 
+// ---- Work items of the split attention pass ----
+// Plain layouts (and one split per row): workgroup blk takes split
+// blk % n_split of row blk / n_split, each split `tps` tokens long.
+// Per-head layouts with several splits (up to 64 KV heads): the heads differ
+// in bytes per token (kept K columns plus the V row; none for a pruned head),
+// so the R = Hkv * n_split workgroups of a batch row are dealt to its heads by
+// those bytes w_g, keeping the largest bytes per workgroup, max w_g / n_g,
+// low.  Every storing head first gets 1 + floor((R - live) * w_g / wtot)
+// (live: the storing heads, wtot: the sum of their w_g), which leaves
+// u < live workgroups over; those go one each to the u heads with the most
+// bytes per workgroup so far (ties to the lower head).  A pruned head gets
+// none, and a head's splits share its token list evenly.  Head g takes the
+// row's work items [cum(g - 1), cum(g)).  Partial results: plain layouts keep
+// the splits of a query head together (slot (row * G + h) * n_split +
+// split); byte-dealt work items write slots blk * G + h.
+struct SplitItem {
+  int b, g, split, n;  // batch row, KV head, split of n (n == 0: no work)
+};
+
+constexpr int kMaxByteSplitHeads = 64;  // one lane per head
+
+__device__ __forceinline__ bool split_by_bytes(const AttnArgs& a) {
+  return a.heads != nullptr && a.n_split > 1 && a.Hkv <= kMaxByteSplitHeads;
+}
+
+// cum(g) for the head g = lane of the calling lane (lanes past the last head:
+// R, or 0 when no head stores anything).  Every lane of the wave calls it.
+__device__ __forceinline__ uint32_t head_cum(const AttnArgs& a) {
+  const int lane = threadIdx.x & 63;
+  uint32_t w = 0;
+  if (lane < a.Hkv) {
+    const uint32_t kc = (uint32_t)a.heads[lane].k_cols;
+    w = kc ? kc + (uint32_t)kDv : 0u;
+  }
+  const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(w), 63);
+  const uint32_t live = (uint32_t)__popcll(__ballot(w != 0u));
+  if (live == 0) return 0u;
+  const uint32_t R = (uint32_t)(a.Hkv * a.n_split);
+  uint32_t n = w ? 1u + (R - live) * w / wtot : 0u;
+  const uint32_t u = R - (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(n), 63);
+  // bytes per workgroup as a fixed-point key, made unique by the lane
+  const uint32_t key = w ? (((w << 16) / n) << 6) | (uint32_t)(63 - lane) : 0u;
+  uint32_t rank = 0;
+  for (int j = 0; j < a.Hkv; ++j) rank += (uint32_t)__builtin_amdgcn_readlane((int)key, j) > key;
+  n += (w && rank < u) ? 1u : 0u;
+  return wave_incl_scan(n);
+}
+
+// The work item of attention workgroup blk (uniform over the workgroup).
+__device__ __forceinline__ SplitItem split_item(const AttnArgs& a, int blk) {
+  SplitItem it;
+  if (!split_by_bytes(a)) {
+    const int row = blk / a.n_split;
+    it.split = blk - row * a.n_split;
+    it.b = row / a.Hkv;
+    it.g = row - it.b * a.Hkv;
+    it.n = a.n_split;
+    return it;
+  }
+  const int R = a.Hkv * a.n_split;
+  it.b = blk / R;
+  const uint32_t r = (uint32_t)(blk - it.b * R);
+  const uint32_t c = head_cum(a);
+  const int lane = threadIdx.x & 63;
+  // cum is non-decreasing over the heads: the first k end at or before r
+  const int k = __popcll(__ballot(lane < a.Hkv && c <= r));
+  if (k >= a.Hkv) {  // no head stores anything
+    it.g = 0;
+    it.split = 0;
+    it.n = 0;
+    return it;
+  }
+  const uint32_t lo = k ? (uint32_t)__builtin_amdgcn_readlane((int)c, k - 1) : 0u;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)c, k);
+  it.g = k;
+  it.split = (int)(r - lo);
+  it.n = (int)(hi - lo);
+  return it;
+}
+
+// Tokens per split of a work item whose head attends n_tok tokens.
+__device__ __forceinline__ int split_tokens(const AttnArgs& a, const SplitItem& it, int n_tok) {
+  if (!split_by_bytes(a)) return a.tps;
+  return max(16, (((n_tok + it.n - 1) / it.n + 15) / 16) * 16);
+}
+
+// The work items [base, base + n) of head g (each lane its own g < Hkv)
+// within its batch row, for byte-dealt splits.  Every lane of the wave calls it.
+__device__ __forceinline__ void head_items(const AttnArgs& a, int g, int& base, int& n) {
+  const uint32_t c = head_cum(a);
+  const uint32_t hi = (uint32_t)__shfl((int)c, g);
+  const uint32_t lo = (uint32_t)__shfl((int)c, max(g - 1, 0));
+  base = g ? (int)lo : 0;
+  n = (int)(hi - (uint32_t)base);
+}
+
 // Merge weights of two online-softmax states; either may be empty (m = -inf).
 __device__ __forceinline__ void merge_weights(float m, float m2, float& w1, float& w2, float& mx) {
   mx = fmaxf(m, m2);
@@ -246,6 +342,7 @@ __device__ __forceinline__ void attn_finish(const AttnArgs& a, AttnAcc<G>& acc, 
 
 // Workgroup merge of the NW wave states in `red` and the store, by threads
 // (h, c) with h < ng (the others do nothing); ng <= G heads in the group.
+// Partial slots as split_item describes (blockIdx.x is the work item).
 template <int G, bool FINAL, int NW>
 __device__ __forceinline__ void attn_store(const AttnArgs& a, AttnRed<G, NW>& red, int b, int g,
                                            int split, int ng) {
@@ -278,7 +375,9 @@ __device__ __forceinline__ void attn_store(const AttnArgs& a, AttnRed<G, NW>& re
     for (int i = 0; i < 4; ++i) r2[i] = __floats2half2_rn(O[2 * i] * inv, O[2 * i + 1] * inv);
     *reinterpret_cast<uint4*>(a.out + bh * kDv + cc * 8) = *reinterpret_cast<const uint4*>(r2);
   } else {
-    float* dst = a.part + (bh * a.n_split + split) * kPartStride;
+    const int64_t slot =
+        split_by_bytes(a) ? (int64_t)blockIdx.x * ng + h : bh * a.n_split + split;
+    float* dst = a.part + slot * kPartStride;
     *reinterpret_cast<float4*>(dst + cc * 8) = make_float4(O[0], O[1], O[2], O[3]);
     *reinterpret_cast<float4*>(dst + cc * 8 + 4) = make_float4(O[4], O[5], O[6], O[7]);
     if (cc == 0) {
@@ -288,17 +387,17 @@ __device__ __forceinline__ void attn_store(const AttnArgs& a, AttnRed<G, NW>& re
   }
 }
 
-// Log-sum-exp merge of the n_split partials of query head row `rq`
-// (16 lanes, lane c covers channels [8c, 8c+8)); fp16 output.  The partials
-// are read in groups of 8 whose loads are all in flight together, and
-// merged into a running (max, sum, output) state.
-__device__ __forceinline__ void merge_partials(const AttnArgs& a, int64_t rq, int c) {
+// Log-sum-exp merge of the n partials at p, p + stride, ... of one query
+// head row (16 lanes, lane c covers channels [8c, 8c+8)) into its fp16
+// output row `out`.  The partials are read in groups of 8 whose loads are all
+// in flight together, and merged into a running (max, sum, output) state.
+__device__ __forceinline__ void merge_partials(const float* p, int n, int64_t stride, __half* out,
+                                               int c) {
   constexpr int kB = 8;
-  const float* p = a.part + rq * a.n_split * kPartStride;
   float M = kNegInf, L = 0.0f, O[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) O[i] = 0.0f;
-  for (int s0 = 0; s0 < a.n_split; s0 += kB) {
+  for (int s0 = 0; s0 < n; s0 += kB) {
     float4 x0[kB], x1[kB];
     float m[kB], l[kB];
 #pragma unroll
@@ -306,8 +405,8 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, int64_t rq, in
       m[u] = kNegInf;
       l[u] = 0.0f;
       x0[u] = x1[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      if (s0 + u < a.n_split) {
-        const float* q = p + (int64_t)(s0 + u) * kPartStride;
+      if (s0 + u < n) {
+        const float* q = p + (int64_t)(s0 + u) * stride;
         x0[u] = *reinterpret_cast<const float4*>(q + c * 8);
         x1[u] = *reinterpret_cast<const float4*>(q + c * 8 + 4);
         const float2 ml = *reinterpret_cast<const float2*>(q + kDv);
@@ -342,7 +441,7 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, int64_t rq, in
   __half2 r2[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) r2[i] = __floats2half2_rn(O[2 * i] * inv, O[2 * i + 1] * inv);
-  *reinterpret_cast<uint4*>(a.out + rq * kDv + c * 8) = *reinterpret_cast<const uint4*>(r2);
+  *reinterpret_cast<uint4*>(out + c * 8) = *reinterpret_cast<const uint4*>(r2);
 }
 
 }  // namespace ds

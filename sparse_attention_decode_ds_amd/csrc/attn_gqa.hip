@@ -29,16 +29,17 @@ struct GqaLds {
 template <int G, bool FINAL, bool RING, bool PAGED>
 __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a_in) {
   __shared__ GqaLds<G> f;
-  const int row = blockIdx.x / a_in.n_split;
-  const int split = blockIdx.x - row * a_in.n_split;
-  const int b = row / a_in.Hkv;
-  const int g = row - b * a_in.Hkv;
+  const SplitItem it = split_item(a_in, blockIdx.x);
+  if (it.n == 0) return;  // every head pruned: the combine writes zeros
+  const int b = it.b, g = it.g;
+  const int row = b * a_in.Hkv + g;
   const AttnArgs a = with_head(a_in, g);
   const int S = min(max(a.seq_lens[b], 0), a.max_seq);
   // a fully pruned head (no K columns) attends nothing: zero output
   const int n_tok = a.d_k == 0 ? 0 : (a.sparse ? min(a.count[row], S) : S);
-  const int t0 = split * a.tps;
-  const int n_here = max(0, min(n_tok - t0, a.tps));
+  const int tps = split_tokens(a, it, n_tok);
+  const int t0 = it.split * tps;
+  const int n_here = max(0, min(n_tok - t0, tps));
   const int tid = threadIdx.x;
   const int w = wave_id();
   const GqaLane ln(a, b, g, PAGED);
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a_in) {
   // The wave's state into LDS, then the four waves merged per head.
   gqa_to_red(st, ln, G, w, f.red);
   __syncthreads();
-  attn_store<G, FINAL>(a, f.red, b, g, split);
+  attn_store<G, FINAL>(a, f.red, b, g, it.split);
 }
 
 template <int G, bool PAGED>

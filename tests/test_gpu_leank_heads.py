@@ -188,8 +188,18 @@ def test_per_head_storage_matches_oracle(mode, G):
                          keep=keep.cuda(), topk_idx=topk, flags=fl | ds.DECODE_APPEND,
                          validate_tables=True, pages=pages, heads=lay)
     torch.cuda.synchronize()
+    _check_per_head(out, topk, q, Ks, Vs, keep, chan, labels, counts, G, k, S, scale)
+
+
+def _check_per_head(out, topk, q, Ks, Vs, keep, chan, labels, counts, G, k, S, scale):
+    """Each head's output (and selected set) against the oracle run on that
+    head alone with only its own columns; pruned heads give zeros and no
+    token.  S: the sequence length of every row, or one per row."""
     out = out.cpu().double().numpy()
     tk = topk.cpu().numpy() if topk is not None else None
+    B = out.shape[0]
+    r = chan.shape[1]
+    seqs = np.broadcast_to(np.asarray(S, np.int32), (B,)).copy()
     for g, n in enumerate(counts):
         o = out[:, g * G:(g + 1) * G]
         if n == 0:  # fully pruned: zero output, no token
@@ -202,10 +212,11 @@ def test_per_head_storage_matches_oracle(mode, G):
         Vg = Vs[g][:, None].contiguous().numpy()
         cg = chan[g:g + 1].numpy()
         lab = oracle.Labels.empty(B, 1, labels.slots, r, False)
-        oracle.label_build(Kg, cg, lab, 0, S)
-        got_lab = labels.codes[:, g, :S].cpu().numpy().view(np.uint16)
-        assert np.array_equal(lab.f16[:, 0, :S], got_lab), g  # appended label included
-        res = oracle.decode(qg, Kg, Vg, np.full(B, S, np.int32), k, scale, chan=cg if k else None,
+        oracle.label_build(Kg, cg, lab, 0, int(seqs.max()))
+        got_lab = labels.codes[:, g].cpu().numpy().view(np.uint16)
+        for b in range(B):  # appended label included
+            assert np.array_equal(lab.f16[b, 0, :seqs[b]], got_lab[b, :seqs[b]]), (g, b)
+        res = oracle.decode(qg, Kg, Vg, seqs, k, scale, chan=cg if k else None,
                             lab=lab if k else None, keep=keep[g:g + 1, :n].numpy(),
                             want_scores=k > 0)
         for b in range(B):
@@ -213,8 +224,9 @@ def test_per_head_storage_matches_oracle(mode, G):
             if k > 0:
                 got, want = set(tk[b, g].tolist()), set(res["topk"][b, 0].tolist())
                 if got != want:
-                    s = res["scores"][b, 0, :S]
-                    sk = np.sort(s)[::-1][k - 1]
+                    kk = min(k, int(seqs[b]))
+                    s = res["scores"][b, 0, :seqs[b]]
+                    sk = np.sort(s)[::-1][kk - 1]
                     tol = 1e-3 * abs(sk) + 1e-6 * np.abs(s).max()
                     for t in got ^ want:
                         assert abs(s[t] - sk) <= tol, (g, b, t)
@@ -224,3 +236,54 @@ def test_per_head_storage_matches_oracle(mode, G):
                                            rows=[(b, 0)])[b]
             err = (np.abs(o[b] - w).max(axis=1) / np.abs(w).max(axis=1)).max()
             assert err <= 2e-3, (g, b, err)
+
+
+@pytest.mark.parametrize("mode,G,n_split,counts", [
+    ("unfused", 2, 3, [16, 48, 0, 32]),
+    ("unfused", 1, 7, [48, 0, 8, 24]),
+    ("stream", 4, 5, [0, 32, 16, 0]),
+    ("paged", 2, 4, [24, 0, 48, 8]),
+    ("dense", 2, 6, [8, 48, 0, 0]),
+    ("dense", 1, 9, [32, 16, 40, 0]),
+])
+def test_per_head_splits_dealt_by_bytes(mode, G, n_split, counts):
+    """With a per-head layout and several splits, a batch row's workgroups go
+    to its heads in proportion to their bytes per token (pruned heads get
+    none) and the combine finds each head's partials again: split counts
+    that do not divide evenly, heads of one to several splits, pruned heads
+    first, in the middle and last."""
+    B, Hkv, D, cap, S, r = 3, 4, 128, 768, 701, 8
+    k = 0 if mode == "dense" else 200
+    fl = {"unfused": ds.DECODE_UNFUSED, "stream": ds.DECODE_STREAM,
+          "paged": ds.DECODE_UNFUSED}.get(mode, 0)
+    q, Ks, Vs, keep, chan, lay, Kb, Vb, pages = _per_head_case(
+        B, Hkv, G, D, cap, counts, r, 45, pages_P=16 if mode == "paged" else 0)
+    print("per-head splits %s G=%d n_split=%d counts %s" % (mode, G, n_split, counts), flush=True)
+    scale = 1.0 / np.sqrt(D)
+    labels = ds.LabelCache.allocate(B, Hkv, cap, r, False)
+    ds.label_build(Kb, chan.cuda(), labels, 0, S - 1, pages=pages, heads=lay)
+    seq = torch.tensor([S, 517, 1], dtype=torch.int32, device="cuda")
+    topk = torch.full((B, Hkv, max(k, 1)), -7, dtype=torch.int32, device="cuda") if k else None
+    out = ds.decode_attn(q.cuda(), Kb, Vb, seq, S, k, scale, chan=chan.cuda(), labels=labels,
+                         keep=keep.cuda(), topk_idx=topk, n_split=n_split,
+                         flags=fl | ds.DECODE_APPEND, validate_tables=True, pages=pages,
+                         heads=lay)
+    torch.cuda.synchronize()
+    _check_per_head(out, topk, q, Ks, Vs, keep, chan, labels, counts, G, k, seq.cpu().numpy(),
+                    scale)
+
+
+def test_per_head_every_head_pruned_with_splits():
+    """No head stores anything: every workgroup of the split pass has no work
+    and the combine writes zeros."""
+    B, Hkv, G, D, cap, S = 2, 3, 2, 128, 256, 200
+    lay = ds.HeadLayout.packed([0, 0, 0], cap)
+    Kb = torch.zeros((B, max(lay.k_row, 8)), dtype=torch.float16, device="cuda")
+    Vb = torch.zeros((B, max(lay.v_row, 8)), dtype=torch.float16, device="cuda")
+    q = torch.randn((B, Hkv * G, D)).half().cuda()
+    keep = torch.zeros((Hkv, 8), dtype=torch.int32, device="cuda")
+    seq = torch.full((B,), S, dtype=torch.int32, device="cuda")
+    out = torch.full((B, Hkv * G, D), 7.0, dtype=torch.float16, device="cuda")
+    ds.decode_attn(q, Kb, Vb, seq, S, 0, 0.1, keep=keep, n_split=4, heads=lay, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0.0)
