@@ -10,8 +10,9 @@
 //   keeps the merge exact (every dropped score is below T, every kept one at
 //   or above it); the bin edge makes the kept count about M.  Kept tokens
 //   (score, index) go to the row's candidate area in ascending index order,
-//   together with the smallest kept key theta (0 when the chunk is kept
-//   whole); a chunk whose kept count exceeds its slots reports an overflow.
+//   together with theta, the key of T (0 when the chunk is kept whole): every
+//   dropped score lies strictly below it.  A chunk whose kept count exceeds
+//   its slots reports an overflow.
 //
 // k_select_merge: one workgroup per row gathers the candidates (chunk order,
 //   so ascending token order), selects the k largest exactly (linear bins +
@@ -58,7 +59,6 @@ struct LocalScratch {
   uint32_t scan_tmp[NT / 64];
   SelScratch sel;
   uint32_t tot[TPT][NT / 64];
-  uint32_t theta;
 };
 
 // NT threads score a chunk of at most NT * TPT tokens.  Empty slots (past
@@ -211,13 +211,12 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_i
   int kept = n_c;
   // bit (j * VT + e) of keptm: slot kept
   uint32_t keptm = 0u;
-  float tmin = __builtin_huge_valf();  // smallest kept score
+  uint32_t theta = 0u;
   if (!keep_all) {
     block_minmax<NT>(mn, mx, f.mm_tmp);
     const LinBins bin(mn, mx);
     SelScratch& ss = f.sel;
     for (int i = tid; i < kHistBins; i += NT) ss.hist[i] = 0u;
-    if (tid == 0) f.theta = 0xFFFFFFFFu;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < JMAX; ++j)
@@ -237,16 +236,13 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_i
     // T: the lower edge of bin bM in score units (empty slots, -inf, stay
     // below it)
     const float thr = mn + ((float)bM - 1.5f) / bin.scale;
+    theta = score_key(thr);
 #pragma unroll
     for (int j = 0; j < JMAX; ++j)
       if (j < jn) {
 #pragma unroll
-        for (int e = 0; e < VT; ++e) {
-          const float sv = sc[j * VT + e];
-          const bool k = sv >= thr;
-          keptm |= (k ? 1u : 0u) << (j * VT + e);
-          tmin = fminf(tmin, k ? sv : __builtin_huge_valf());
-        }
+        for (int e = 0; e < VT; ++e)
+          keptm |= (sc[j * VT + e] >= thr ? 1u : 0u) << (j * VT + e);
       }
   } else {
 #pragma unroll
@@ -273,26 +269,41 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_i
     ex[j] = incl - cnt;
     if (lane == 63) f.tot[j][w] = incl;
   }
-  if (!keep_all) {
-    const uint32_t tk = wave_min_u32(score_key(tmin));
-    if (lane == 0) atomicMin(&f.theta, tk);
-  }
   __syncthreads();
+  // Item order is round j first, then wave, then lane.  With at most 64
+  // (round, wave) groups one scan over their totals gives every group's base
+  // (lane j * kWavesL + w holds group (j, w)); otherwise each wave sums the
+  // totals before it.
+  constexpr bool kOneScan = JMAX * kWavesL <= 64;
+  uint32_t gbase = 0u, run = 0u;
+  if (kOneScan) {
+    const int gj = lane / kWavesL;
+    const uint32_t t = (lane < JMAX * kWavesL && gj < jn) ? f.tot[gj][lane % kWavesL] : 0u;
+    const uint32_t incl = wave_incl_scan(t);
+    gbase = incl - t;
+    run = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  }
   // Stores stop at the chunk's slots; a kept count beyond them is reported
   // as an overflow below.
   const uint32_t lim = (uint32_t)cap * 4u;
-  uint32_t run = 0u;
 #pragma unroll
   for (int j = 0; j < JMAX; ++j) {
     if (j >= jn) continue;
-    uint32_t pre = 0u, rowt = 0u;
+    uint32_t base;
+    if (kOneScan) {
+      base = (uint32_t)__builtin_amdgcn_readlane((int)gbase, j * kWavesL + w);
+    } else {
+      uint32_t pre = 0u, rowt = 0u;
 #pragma unroll
-    for (int ww = 0; ww < kWavesL; ++ww) {
-      const uint32_t t = f.tot[j][ww];
-      pre += ww < w ? t : 0u;
-      rowt += t;
+      for (int ww = 0; ww < kWavesL; ++ww) {
+        const uint32_t t = f.tot[j][ww];
+        pre += ww < w ? t : 0u;
+        rowt += t;
+      }
+      base = run + pre;
+      run += rowt;
     }
-    uint32_t off = (run + pre + ex[j]) * 4u;  // < 4 * kMergeCap
+    uint32_t off = (base + ex[j]) * 4u;  // < 4 * kMergeCap
 #pragma unroll
     for (int e = 0; e < VT; ++e) {
       if ((keptm & (1u << (j * VT + e))) && off < lim) {
@@ -301,7 +312,6 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_i
         off += 4u;
       }
     }
-    run += rowt;
   }
   kept = (int)run;  // every thread holds the total
   // the chunk's unused slots hold -inf, which the merge's select treats as
@@ -312,7 +322,7 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_i
   if (tid == 0) {
     // more scores at or above T than the chunk's slots: overflow
     sa.cand_cnt[(int64_t)row * sa.n_chunks + c] = kept > cap ? -1 : kept;
-    sa.cand_theta[(int64_t)row * sa.n_chunks + c] = keep_all ? 0u : f.theta;
+    sa.cand_theta[(int64_t)row * sa.n_chunks + c] = keep_all ? 0u : theta;
   }
 }
 
@@ -433,8 +443,9 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
             ? list_rank<kNTM>(ls, f.sel, list)
             : list_select_b<kNTM, VTM, kMergeJ>(sc, valid, order, bin, ls, f.sel, f.scan_tmp,
                                                 f.tot, list);
-    // Complete iff every chunk that dropped tokens (theta != 0) has theta at
-    // or below the smallest selected key; e_lo is at or below that key.
+    // Complete iff every chunk that dropped tokens (theta != 0) has theta,
+    // which lies above each of its dropped keys, at or below the smallest
+    // selected key; e_lo is at or below that key.
     if (tid < min(n_ch, kMaxLocalChunks) && f.ch_theta[tid] > rs.e_lo) atomicOr(&f.flag, 1u);
     __syncthreads();
     full = f.flag != 0u;
