@@ -209,8 +209,9 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_i
   const int n_c = t_end - t_beg;
   const bool keep_all = n_c <= M;
   int kept = n_c;
-  // bit (j * VT + e) of keptm: slot kept
-  uint32_t keptm = 0u;
+  // a slot is kept iff its score is at least thr (a whole chunk: every
+  // non-empty slot)
+  float thr = -3.402823466e38f;
   uint32_t theta = 0u;
   if (!keep_all) {
     block_minmax<NT>(mn, mx, f.mm_tmp);
@@ -235,21 +236,8 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_i
     }
     // T: the lower edge of bin bM in score units (empty slots, -inf, stay
     // below it)
-    const float thr = mn + ((float)bM - 1.5f) / bin.scale;
+    thr = mn + ((float)bM - 1.5f) / bin.scale;
     theta = score_key(thr);
-#pragma unroll
-    for (int j = 0; j < JMAX; ++j)
-      if (j < jn) {
-#pragma unroll
-        for (int e = 0; e < VT; ++e)
-          keptm |= (sc[j * VT + e] >= thr ? 1u : 0u) << (j * VT + e);
-      }
-  } else {
-#pragma unroll
-    for (int j = 0; j < JMAX; ++j)
-#pragma unroll
-      for (int e = 0; e < VT; ++e)
-        if (j < jn && sc[j * VT + e] != kEmpty) keptm |= 1u << (j * VT + e);
   }
 
   // --- ordered emission of the kept tokens ---------------------------------------
@@ -264,7 +252,9 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_i
   for (int j = 0; j < JMAX; ++j) {
     ex[j] = 0u;
     if (j >= jn) continue;
-    const uint32_t cnt = __builtin_popcount((keptm >> (j * VT)) & ((1u << VT) - 1u));
+    uint32_t cnt = 0u;
+#pragma unroll
+    for (int e = 0; e < VT; ++e) cnt += sc[j * VT + e] >= thr ? 1u : 0u;
     const uint32_t incl = wave_incl_scan(cnt);
     ex[j] = incl - cnt;
     if (lane == 63) f.tot[j][w] = incl;
@@ -284,11 +274,13 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_i
     run = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
   }
   // Stores stop at the chunk's slots; a kept count beyond them is reported
-  // as an overflow below.
+  // as an overflow below (with one scan the count is known before the
+  // stores, which then only run when it fits).
   const uint32_t lim = (uint32_t)cap * 4u;
+  const int jlim = (kOneScan && run > (uint32_t)cap) ? 0 : jn;
 #pragma unroll
   for (int j = 0; j < JMAX; ++j) {
-    if (j >= jn) continue;
+    if (j >= jlim) continue;
     uint32_t base;
     if (kOneScan) {
       base = (uint32_t)__builtin_amdgcn_readlane((int)gbase, j * kWavesL + w);
@@ -306,7 +298,7 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_i
     uint32_t off = (base + ex[j]) * 4u;  // < 4 * kMergeCap
 #pragma unroll
     for (int e = 0; e < VT; ++e) {
-      if ((keptm & (1u << (j * VT + e))) && off < lim) {
+      if (sc[j * VT + e] >= thr && (kOneScan || off < lim)) {
         *reinterpret_cast<float*>(ck + off) = sc[j * VT + e];
         *reinterpret_cast<int32_t*>(ci + off) = token(j, e);
         off += 4u;
