@@ -127,7 +127,8 @@ struct Plan {
   int local_nch;    // and chunks per row
   int cand_stride;  // candidate slots per row
   int split_cap;
-  size_t off_count, off_idx, off_keys, off_cand_key, off_cand_idx, off_cand_cnt, off_cand_theta;
+  size_t off_count, off_idx, off_keys, off_cand_key, off_cand_idx, off_cand_cnt, off_cand_theta,
+      off_cand_range;
   size_t off_part, total;
 };
 
@@ -185,6 +186,7 @@ Plan make_plan(const ds_kv_desc* kv, int k, int max_seq) {
   p.off_cand_idx = take(rows * (size_t)p.cand_stride * sizeof(int32_t));
   p.off_cand_cnt = take(rows * nch * sizeof(int32_t));
   p.off_cand_theta = take(rows * nch * sizeof(uint32_t));
+  p.off_cand_range = take(rows * nch * 2 * sizeof(float));
   p.off_part = take((size_t)kv->batch * kv->n_q_heads * p.split_cap * kPartStride * sizeof(float));
   p.total = off;
   return p;
@@ -502,6 +504,7 @@ ds_status decode_impl(const ds_kv_desc* kv, const void* q, const void* K, const 
     sa.cand_idx = reinterpret_cast<int32_t*>(ws + p.off_cand_idx);
     sa.cand_cnt = reinterpret_cast<int32_t*>(ws + p.off_cand_cnt);
     sa.cand_theta = reinterpret_cast<uint32_t*>(ws + p.off_cand_theta);
+    sa.cand_range = reinterpret_cast<float2*>(ws + p.off_cand_range);
     sa.cand_stride = p.cand_stride;
     idx = sa.idx;
     idx_stride = sa.idx_stride;

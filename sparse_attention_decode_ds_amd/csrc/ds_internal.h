@@ -88,7 +88,8 @@ struct ScoreArgs {
   float* cand_score;    // [rows][kMergeCap]: kept scores
   int32_t* cand_idx;    // [rows][kMergeCap]
   int32_t* cand_cnt;    // [rows][n_chunks], -1: overflow
-  uint32_t* cand_theta; // [rows][n_chunks], smallest kept key (0: chunk kept whole)
+  uint32_t* cand_theta; // [rows][n_chunks], key of the chunk's threshold (0: kept whole)
+  float2* cand_range;   // [rows][n_chunks], (lowest kept score bound, largest score)
   int32_t cand_stride;  // candidate slots per row (<= kMergeCap)
   const ds_head_layout* heads;  // per-head K layout (fully pruned heads), or null
   int32_t keep_ld;              // row stride of the keep table (the widest d_k)
@@ -343,6 +344,11 @@ __device__ __forceinline__ float wave_min(float x) {
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
   return __float_as_uint(wave_reduce(__uint_as_float(x), [](float a, float b) {
     return __uint_as_float(min(__float_as_uint(a), __float_as_uint(b)));
+  }));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  return __float_as_uint(wave_reduce(__uint_as_float(x), [](float a, float b) {
+    return __uint_as_float(max(__float_as_uint(a), __float_as_uint(b)));
   }));
 }
 

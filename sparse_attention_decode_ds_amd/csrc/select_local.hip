@@ -213,8 +213,8 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_i
   // non-empty slot)
   float thr = -3.402823466e38f;
   uint32_t theta = 0u;
+  block_minmax<NT>(mn, mx, f.mm_tmp);  // the chunk's range goes to the merge
   if (!keep_all) {
-    block_minmax<NT>(mn, mx, f.mm_tmp);
     const LinBins bin(mn, mx);
     SelScratch& ss = f.sel;
     for (int i = tid; i < kHistBins; i += NT) ss.hist[i] = 0u;
@@ -315,21 +315,27 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_i
     // more scores at or above T than the chunk's slots: overflow
     sa.cand_cnt[(int64_t)row * sa.n_chunks + c] = kept > cap ? -1 : kept;
     sa.cand_theta[(int64_t)row * sa.n_chunks + c] = keep_all ? 0u : theta;
+    sa.cand_range[(int64_t)row * sa.n_chunks + c] = make_float2(keep_all ? mn : thr, mx);
   }
 }
 
 constexpr int kMergeVT = 4;                             // consecutive slots per thread and round
 constexpr int kMergeJ = kMergeCap / (kNTM * kMergeVT);  // rounds
 
+// Per-wave summary of the chunk records (wave w: chunks 64w .. 64w + 63).
+struct MergeRec {
+  uint32_t bad;    // a chunk overflowed its slots
+  uint32_t total;  // kept candidates
+  uint32_t theta;  // largest threshold key of a chunk that dropped tokens
+  float lo, hi;    // range of the kept scores
+};
+
 struct MergeScratch {
   SelScratch sel;
-  uint32_t ch_theta[kMaxLocalChunks];
+  MergeRec rec[kMaxLocalChunks / 64];
   uint32_t scan_tmp[kNTM / 64];
-  float mm_tmp[2 * kNTM / 64];
   uint32_t tot[kMergeJ * (kNTM / 64)];
   int32_t junk[64];  // spare words of the LDS list writes
-  uint32_t flag;  // 1: fall back to the full select
-  uint32_t total; // candidates of the row
 };
 
 // Token lists up to this long are built in LDS and copied out in one
@@ -342,29 +348,16 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
   __shared__ MergeScratch f;
   __shared__ int32_t lds_list[kMergeLdsList];
   const int row = blockIdx.x;
-  const int b = row / sa.Hkv;
-  const int g = row - b * sa.Hkv;
-  const int S = row_len(sa, b);
   const int tid = threadIdx.x;
-  int32_t* out = sa.idx + (int64_t)row * sa.idx_stride;
-  if (pruned_row<kNTM>(sa, row, g)) return;
-
-  if (S <= sa.k) {  // every token
-    for (int t = tid; t < S; t += kNTM) out[t] = t;
-    if (sa.pad_idx)
-      for (int t = S + tid; t < sa.idx_stride; t += kNTM) out[t] = -1;
-    if (tid == 0) sa.count[row] = S;
-    return;
-  }
-  const int n_ch = chunks_of(S, sa.chunk);
-  const int cap = Quota(S, sa.k, sa.chunk, sa.cand_stride, n_ch).cap;
-  const int slots = n_ch * cap;  // <= cand_stride <= kMergeCap
+  const int lane = tid & 63;
+  const int w = wave_id();
 
   // Candidate slots (j * kNTM + tid) * 4 + e of this thread; chunk c owns
   // slots [c * cap, (c + 1) * cap): its kept scores in ascending token order
-  // (so slot order is token order), then -inf.  Every load of the row's area
-  // is issued before the row's length arrives; slots past the chunks' (from
-  // an earlier call) are masked once it has.
+  // (so slot order is token order), then -inf.  The loads of the row's area
+  // and of the chunk records depend on the kernel arguments only, so they go
+  // out first, before the row's length and head arrive; slots past the
+  // row's chunks (from an earlier call) are masked once they have.
   constexpr int VTM = kMergeVT;
   const float* ck = sa.cand_score + (int64_t)row * sa.cand_stride;
   const int32_t* ci = sa.cand_idx + (int64_t)row * sa.cand_stride;
@@ -386,36 +379,72 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
       tok[j * VTM + e] = (int32_t)tv[e];
     }
   }
-  if (tid == 0) {
-    f.flag = n_ch > kMaxLocalChunks ? 1u : 0u;
-    f.total = 0u;
+  int rc_cnt = 0;
+  uint32_t rc_theta = 0u;
+  float2 rc_range = make_float2(0.0f, 0.0f);
+  if (tid < min(sa.n_chunks, kMaxLocalChunks)) {
+    const int64_t at = (int64_t)row * sa.n_chunks + tid;
+    rc_cnt = sa.cand_cnt[at];
+    rc_theta = sa.cand_theta[at];
+    rc_range = sa.cand_range[at];
+  }
+
+  const int b = row / sa.Hkv;
+  const int g = row - b * sa.Hkv;
+  const int S = row_len(sa, b);
+  int32_t* out = sa.idx + (int64_t)row * sa.idx_stride;
+  if (pruned_row<kNTM>(sa, row, g)) return;
+
+  if (S <= sa.k) {  // every token
+    for (int t = tid; t < S; t += kNTM) out[t] = t;
+    if (sa.pad_idx)
+      for (int t = S + tid; t < sa.idx_stride; t += kNTM) out[t] = -1;
+    if (tid == 0) sa.count[row] = S;
+    return;
+  }
+  const int n_ch = chunks_of(S, sa.chunk);
+  const int cap = Quota(S, sa.k, sa.chunk, sa.cand_stride, n_ch).cap;
+  const int slots = n_ch * cap;  // <= cand_stride <= kMergeCap
+
+  // The chunk records, summarised per wave and then over the waves (one
+  // barrier, which also publishes the cleared histogram).
+  sel_clear<kNTM>(f.sel);
+  if (w < kMaxLocalChunks / 64) {
+    const bool in = tid < min(n_ch, kMaxLocalChunks);
+    const uint32_t cnt = in ? (uint32_t)max(rc_cnt, 0) : 0u;
+    const uint64_t bad = __ballot(in && (rc_cnt < 0 || rc_cnt > cap));
+    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(cnt), 63);
+    const uint32_t th = wave_max_u32(in ? rc_theta : 0u);
+    const float lo = wave_min(in ? rc_range.x : __builtin_huge_valf());
+    const float hi = wave_max(in ? rc_range.y : -__builtin_huge_valf());
+    if (lane == 0) f.rec[w] = MergeRec{bad != 0u ? 1u : 0u, tot, th, lo, hi};
   }
   __syncthreads();
-  if (tid < min(n_ch, kMaxLocalChunks)) {
-    const int cnt = sa.cand_cnt[(int64_t)row * sa.n_chunks + tid];
-    f.ch_theta[tid] = sa.cand_theta[(int64_t)row * sa.n_chunks + tid];
-    if (cnt < 0 || cnt > cap) atomicOr(&f.flag, 1u);
-    atomicAdd(&f.total, (uint32_t)max(cnt, 0));
+  uint32_t bad = n_ch > kMaxLocalChunks ? 1u : 0u, total = 0u, theta_max = 0u;
+  float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
+#pragma unroll
+  for (int i = 0; i < kMaxLocalChunks / 64; ++i) {
+    const MergeRec r = f.rec[i];
+    bad |= r.bad;
+    total += r.total;
+    theta_max = max(theta_max, r.theta);
+    mn = fminf(mn, r.lo);
+    mx = fmaxf(mx, r.hi);
   }
-  __syncthreads();
-  bool full = f.flag != 0u || f.total < (uint32_t)sa.k;
+  bool full = bad != 0u || total < (uint32_t)sa.k;
 
   if (!full) {
-    // Slots past the chunks become empty (-inf) too; mn is over the
-    // non-empty slots.
-    float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
+    // Slots past the chunks become empty (-inf) too.  [mn, mx] holds every
+    // kept score: the chunks report a bound at or below their kept scores
+    // (the threshold, or the smallest score of a chunk kept whole) and their
+    // largest score.
 #pragma unroll
     for (int j = 0; j < kMergeJ; ++j)
 #pragma unroll
       for (int e = 0; e < VTM; ++e) {
         const int i = (j * kNTM + tid) * VTM + e;
-        const float v = i < slots ? sc[j * VTM + e] : -__builtin_huge_valf();
-        sc[j * VTM + e] = v;
-        mx = fmaxf(mx, v);
-        mn = fminf(mn, v == -__builtin_huge_valf() ? __builtin_huge_valf() : v);
+        if (i >= slots) sc[j * VTM + e] = -__builtin_huge_valf();
       }
-    sel_clear<kNTM>(f.sel);  // published by block_minmax's barriers
-    block_minmax<kNTM>(mn, mx, f.mm_tmp);
     auto valid = [&](int j, int) { return j * kNTM * VTM < slots; };  // empty slots hold -inf
     // slot order is token order, so ties go to the lower token either way
     auto order = [&](int j, int e) { return tok[j * VTM + e]; };
@@ -437,10 +466,8 @@ __global__ __launch_bounds__(kNTM) void k_select_merge(ScoreArgs sa) {
                                                 f.tot, list);
     // Complete iff every chunk that dropped tokens (theta != 0) has theta,
     // which lies above each of its dropped keys, at or below the smallest
-    // selected key; e_lo is at or below that key.
-    if (tid < min(n_ch, kMaxLocalChunks) && f.ch_theta[tid] > rs.e_lo) atomicOr(&f.flag, 1u);
-    __syncthreads();
-    full = f.flag != 0u;
+    // selected key; e_lo is at or below that key (the same on every thread).
+    full = theta_max > rs.e_lo;
     if (!full && sa.pad_idx) {
       reg_emit<kNTM, VTM, kMergeJ>(sc, valid, rs, f.tot, [&](uint32_t pos, int j, int e) {
         out[pos] = tok[j * VTM + e];
