@@ -19,6 +19,22 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a_in) {
   const int b = it.b, g = it.g;
   const int row = b * a_in.Hkv + g;
   const AttnArgs a = with_head(a_in, g);
+  const int tid = threadIdx.x;
+  // With plain splits the first batch of the split's token list depends on
+  // the kernel arguments only: its loads go out before the row's length and
+  // count arrive (entries past the count are read but never used).
+  constexpr int kPre = kMaxTokensPerSplit / kAttnThreads;
+  const bool early = a.sparse && !split_by_bytes(a);
+  int32_t pre[kPre];
+  if (early) {
+    const int te = it.split * a.tps;
+    const int32_t* src = a.idx + (int64_t)row * a.idx_stride + te;
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int i = u * kAttnThreads + tid;
+      pre[u] = (i < a.tps && te + i < a.idx_stride) ? src[i] : 0;
+    }
+  }
   const int S = min(max(a.seq_lens[b], 0), a.max_seq);
   // a fully pruned head (no K columns) attends nothing: zero output
   const int n_tok = a.d_k == 0 ? 0 : (a.sparse ? min(a.count[row], S) : S);
@@ -26,7 +42,6 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a_in) {
   const int t0 = it.split * tps;
   const int n_here = max(0, min(n_tok - t0, tps));
 
-  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int c = lane & 15;
   const int slot = (tid >> 6) * 4 + (lane >> 4);
@@ -42,16 +57,38 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a_in) {
   const int32_t* ptab = PAGED ? a.ptab + (int64_t)b * a.max_pages : nullptr;
 
   if (a.sparse || PAGED) {
-    for (int bat = 0; bat < n_here; bat += kMaxTokensPerSplit) {
-      const int nb = min(kMaxTokensPerSplit, n_here - bat);
-      __syncthreads();
+    auto stage = [&](int bat, int nb) {
       const int32_t* src = a.idx + (int64_t)row * a.idx_stride + t0 + bat;
       for (int i = tid; i < nb; i += kAttnThreads) {
         const int t = a.sparse ? src[i] : t0 + bat + i;
         lidx[i] = PAGED ? phys_tok(ptab, a.pshift, t) : t;
       }
-      __syncthreads();
+    };
+    auto run = [&](int nb) {
       attend<G, PAGED>(a, Kr, Vr, slot, nb, [&](int i) { return (int64_t)lidx[i]; }, qf, acc);
+    };
+    // The first batch on its own, so that the prefetched entries are dead
+    // before the attention loop (no registers held across it).
+    if (n_here > 0) {
+      const int nb = min(kMaxTokensPerSplit, n_here);
+      if (early) {
+#pragma unroll
+        for (int u = 0; u < kPre; ++u) {
+          const int i = u * kAttnThreads + tid;
+          if (i < nb) lidx[i] = PAGED ? phys_tok(ptab, a.pshift, pre[u]) : pre[u];
+        }
+      } else {
+        stage(0, nb);
+      }
+      __syncthreads();
+      run(nb);
+    }
+    for (int bat = kMaxTokensPerSplit; bat < n_here; bat += kMaxTokensPerSplit) {
+      const int nb = min(kMaxTokensPerSplit, n_here - bat);
+      __syncthreads();
+      stage(bat, nb);
+      __syncthreads();
+      run(nb);
     }
   } else {
     attend<G, false>(a, Kr, Vr, slot, n_here, [&](int i) { return (int64_t)(t0 + i); }, qf, acc);

@@ -34,13 +34,28 @@ __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a_in) {
   const int b = it.b, g = it.g;
   const int row = b * a_in.Hkv + g;
   const AttnArgs a = with_head(a_in, g);
+  const int tid = threadIdx.x;
+  // With plain splits the first batch of the split's token list depends on
+  // the kernel arguments only: its loads go out before the row's length and
+  // count arrive (entries past the count are read but never used).
+  constexpr int kPre = kMaxTokensPerSplit / kGT;
+  const bool early = a.sparse && !split_by_bytes(a);
+  int32_t pre[kPre];
+  if (early) {
+    const int te = it.split * a.tps;
+    const int32_t* src = a.idx + (int64_t)row * a.idx_stride + te;
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int i = u * kGT + tid;
+      pre[u] = (i < a.tps && te + i < a.idx_stride) ? src[i] : 0;
+    }
+  }
   const int S = min(max(a.seq_lens[b], 0), a.max_seq);
   // a fully pruned head (no K columns) attends nothing: zero output
   const int n_tok = a.d_k == 0 ? 0 : (a.sparse ? min(a.count[row], S) : S);
   const int tps = split_tokens(a, it, n_tok);
   const int t0 = it.split * tps;
   const int n_here = max(0, min(n_tok - t0, tps));
-  const int tid = threadIdx.x;
   const int w = wave_id();
   const GqaLane ln(a, b, g, PAGED);
   const int32_t* ptab = PAGED ? a.ptab + (int64_t)b * a.max_pages : nullptr;
@@ -53,8 +68,16 @@ __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a_in) {
 
   // The first batch of the token list and the query rows are fetched
   // together (one round trip, one barrier).
-  if (a.sparse || kStaged)
+  if (early) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int i = u * kGT + tid;
+      if (i < min(n_here, kMaxTokensPerSplit))
+        f.lidx[i] = PAGED ? phys_tok(ptab, a.pshift, pre[u]) : pre[u];
+    }
+  } else if (a.sparse || kStaged) {
     for (int i = tid; i < min(n_here, kMaxTokensPerSplit); i += kGT) f.lidx[i] = stage(t0 + i);
+  }
   for (int i = tid; i < G * kDv; i += kGT) {
     const int h = i / kDv, c = i - h * kDv;
     __half v = __float2half(0.0f);
