@@ -445,8 +445,8 @@ struct LinBins {
 
 struct SelScratch {
   uint32_t hist[kHistBins];
-  uint32_t cand_key[kRankMax];
-  int32_t cand_idx[kRankMax];
+  alignas(16) uint32_t cand_key[kRankMax];
+  alignas(16) int32_t cand_idx[kRankMax];
   uint32_t misc[12];
 };
 
@@ -944,6 +944,7 @@ __device__ __forceinline__ ListSel list_select_a(const float* sc, Valid valid, O
 // each one's rank (key descending, then position ascending) is counted and
 // the first `need` ranks go to list[n_a .. k).  Ends with a barrier; returns
 // the whole selection characterised as by reg_select (for reg_emit).
+static_assert(kRankMax % 8 == 0, "list_rank reads candidates in groups of eight");
 template <int NT>
 __device__ __forceinline__ RegSel list_rank(const ListSel& ls, SelScratch& ss, int32_t* list) {
   const int cnt = (int)ls.cnt;
@@ -951,21 +952,21 @@ __device__ __forceinline__ RegSel list_rank(const ListSel& ls, SelScratch& ss, i
     const uint32_t ki = ss.cand_key[i];
     const int ti = ss.cand_idx[i];
     uint32_t above = 0, tied = 0;
-    // eight candidates per step, their LDS reads in flight together (slots
-    // past cnt read as key 0 with index INT_MAX: never above or tied-below)
+    // eight candidates per step in four 16-byte LDS reads, all in flight
+    // together: the reads are unconditional (m + 8 <= kRankMax, as
+    // cnt <= kRankMax), and slots past cnt do not count
     for (int m = 0; m < cnt; m += 8) {
-      uint32_t km[8];
-      int tm[8];
+      const uint4 k0 = *reinterpret_cast<const uint4*>(&ss.cand_key[m]);
+      const uint4 k1 = *reinterpret_cast<const uint4*>(&ss.cand_key[m + 4]);
+      const int4 t0 = *reinterpret_cast<const int4*>(&ss.cand_idx[m]);
+      const int4 t1 = *reinterpret_cast<const int4*>(&ss.cand_idx[m + 4]);
+      const uint32_t km[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+      const int tm[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const bool in = m + u < cnt;
-        km[u] = in ? ss.cand_key[m + u] : 0u;
-        tm[u] = in ? ss.cand_idx[m + u] : 0x7FFFFFFF;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        above += km[u] > ki;
-        tied += km[u] == ki && tm[u] < ti;
+        above += (in && km[u] > ki) ? 1u : 0u;
+        tied += (in && km[u] == ki && tm[u] < ti) ? 1u : 0u;
       }
     }
     const uint32_t rank = above + tied;
