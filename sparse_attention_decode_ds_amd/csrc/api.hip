@@ -146,9 +146,11 @@ Plan make_plan(const ds_kv_desc* kv, int k, int max_seq) {
   // chunks run in rounds of as many workgroups as the chip holds at once
   // (1024 of 512 threads, 2048 of 256): a single round costs its latency
   // however full it is, while beyond one round workgroups start as others
-  // finish, so the rounds count in proportion to the workgroups.  The merge then costs about its candidates
-  // (quota per chunk, twice the expected share of k) per merge thread.  Pick
-  // the chunk count with the lowest total.
+  // finish, so the rounds count in proportion to the workgroups.  A
+  // 512-thread workgroup's fixed latency is one unit above a 256-thread
+  // one's (its barriers and block scans span eight waves).  The merge then
+  // costs about its candidates (quota per chunk, twice the expected share of
+  // k) per merge thread.  Pick the chunk count with the lowest total.
   {
     const int64_t S = std::max(max_seq, 1);
     double best = 1e300;
@@ -162,7 +164,8 @@ Plan make_plan(const ds_kv_desc* kv, int k, int max_seq) {
       const double rounds = std::max(1.0, (double)(rows * nch) / (double)slots);
       const double quota = std::min<double>((double)chunk,
                                             std::max(64.0, 2.0 * std::max(k, 0) * chunk / S + 1));
-      const double cost = rounds * (16.0 + (double)ceil_div(chunk, threads)) + nch * quota / 1024.0;
+      const double fixed = threads == 512 ? 17.0 : 16.0;
+      const double cost = rounds * (fixed + (double)ceil_div(chunk, threads)) + nch * quota / 1024.0;
       if (cost < best - 1e-9) {
         best = cost;
         p.local_chunk = (int)chunk;
