@@ -647,7 +647,36 @@ def measure(cfg, args, torch, ds, lib, layers=0, offload=False, cpu=True):
             "avg_launch_us": round(at_ms * 1e3, 3) if at_ms else None})
         res["offload"] = {"link_bytes_per_step": link,
                           "link_gbs": round(link / (ms_step * 1e-3) / 1e9, 2)}
+    if cfg.k > 0 and not offload and heads is None:
+        res["prefill"] = time_prefill(cfg, torch, ds, Ks[0], inp.chan, labs[0], pages[0])
     return res
+
+
+def time_prefill(cfg, torch, ds, K, chan, lab, pages, reps=5):
+    """The label build of one layer's prefill (k_label over the first S0
+    tokens of every row), timed by events around the call on its stream; it
+    rewrites the same labels.  Bytes: every token's stored K row is read (the
+    r heavy channels lie spread over the row, so the whole row is what a
+    gather of them moves) and its label is written."""
+    ds.label_build(K, chan, lab, 0, cfg.S0, pages=pages)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    ms = []
+    for _ in range(reps):
+        e0.record()
+        ds.label_build(K, chan, lab, 0, cfg.S0, pages=pages)
+        e1.record()
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    tok = cfg.B * cfg.Hkv * cfg.S0
+    lam = cfg.r // 2 + 2 if cfg.int4 else 2 * cfg.r
+    nbytes = tok * (cfg.d_k * 2 + lam)
+    mean = sum(ms) / len(ms)
+    gbs = nbytes / (mean * 1e-3) / 1e9
+    return {"kernel": "k_label", "tokens": tok, "avg_us": round(mean * 1e3, 2),
+            "algorithmic_bytes": nbytes, "gbs": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "timing": "HIP events around %d label builds on the call's stream" % reps}
 
 
 def release(torch, res):
@@ -778,7 +807,7 @@ def main():
             return 1
         others[w] = {"queries_per_s": r2["value"], "ms_per_step": r2["ms_per_step"],
                      "config": r2["config"], "step": r2["step"], "roofline": r2["roofline"],
-                     "process": "own"}
+                     "prefill": r2.get("prefill"), "process": "own"}
     copy_gbs = copy_ceiling_gbs(torch)
     rf = res["roofline"]
     rf["copy_gbs"] = round(copy_gbs, 1)
@@ -800,6 +829,8 @@ def main():
         "roofline": rf,
         "step": res["step"],
     }
+    if "prefill" in res:
+        result["prefill"] = res["prefill"]
     if "offload" in res:
         result["offload"] = res["offload"]
     if others:
