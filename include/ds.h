@@ -322,6 +322,16 @@ ds_status ds_decode_attn_plan(const ds_kv_desc* kv, const ds_label_desc* lab, in
 int32_t ds_sparse_decode_enabled(int32_t max_seq_len, int32_t min_seq_len, int32_t k,
                                  int32_t threshold);
 
+/* Agreement of two heavy-channel tables, [DS] "offline calibration" (the
+ * article compares the outlier channels fixed offline with those an online
+ * pass finds, by the share they have in common).  chan_a, chan_b: host
+ * int32 [n_kv_heads][r], read only; overlap: host float [n_kv_heads],
+ * written: for head g, the number of distinct channels of chan_a[g] that
+ * chan_b[g] also holds, divided by r.  Host-only: no device memory, nothing
+ * enqueued.  Errors: DS_ERR_ARG (a pointer NULL, n_kv_heads or r below 1). */
+ds_status ds_channel_overlap(const int32_t* chan_a, const int32_t* chan_b, int32_t n_kv_heads,
+                             int32_t r, float* overlap);
+
 /* Heavy-channel calibration criteria ([DS] offline calibration: channels
  * found from outliers of K, of the query, or of their product). */
 typedef enum { DS_CALIB_K = 0, DS_CALIB_Q = 1, DS_CALIB_QK = 2 } ds_calib_criterion;

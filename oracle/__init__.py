@@ -71,6 +71,8 @@ def _load():
         lib.oracle_attend_sets.restype = I
         lib.oracle_calibrate.argtypes = [P, P, I, I, I, I, P, I, I, I, P, I, I, P, P]
         lib.oracle_calibrate.restype = I
+        lib.oracle_channel_overlap.argtypes = [P, P, I, I, P]
+        lib.oracle_channel_overlap.restype = I
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = I
         _lib = lib
@@ -307,3 +309,18 @@ def calibrate(K, criterion, r, qwin=None, Hq=None, keep=None, n_tok=None):
     if rc != 0:
         raise ValueError("oracle_calibrate: status %d" % rc)
     return chan, norms
+
+
+def channel_overlap(a, b):
+    """Per KV head, the share of a's distinct channels that b also holds
+    ("Double Sparsity", section "offline calibration": offline against online
+    outlier channels).  a, b: int [Hkv][r].  Returns float64 [Hkv]."""
+    aa = np.ascontiguousarray(np.asarray(a), np.int32)
+    bb = np.ascontiguousarray(np.asarray(b), np.int32)
+    if aa.ndim != 2 or aa.shape != bb.shape:
+        raise ValueError("oracle.channel_overlap: two [Hkv][r] tables of one shape expected")
+    out = np.zeros(aa.shape[0], np.float64)
+    rc = _load().oracle_channel_overlap(_ptr(aa), _ptr(bb), aa.shape[0], aa.shape[1], _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_channel_overlap: status %d" % rc)
+    return out

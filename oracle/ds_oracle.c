@@ -435,6 +435,28 @@ int oracle_max_threads(void) {
 /* Q the queries of an observation window, K the whole key matrix).          */
 /* ------------------------------------------------------------------------ */
 
+/* Agreement of two heavy-channel tables ([DS] "offline calibration": the
+ * outlier channels found offline against those found online, whose overlap
+ * the article reports): for every KV head g, the number of distinct channels
+ * of a[g] that also occur in b[g], divided by r.  a, b: [Hkv][r].
+ * Returns ORC_OK or ORC_ERR_ARG. */
+int oracle_channel_overlap(const int32_t* a, const int32_t* b, int Hkv, int r, double* out) {
+  if (!a || !b || !out || Hkv < 1 || r < 1) return ORC_ERR_ARG;
+  for (int g = 0; g < Hkv; ++g) {
+    const int32_t* ag = a + (int64_t)g * r;
+    const int32_t* bg = b + (int64_t)g * r;
+    int shared = 0;
+    for (int i = 0; i < r; ++i) {
+      int seen = 0, found = 0;
+      for (int j = 0; j < i; ++j) seen |= ag[j] == ag[i];
+      for (int j = 0; j < r; ++j) found |= bg[j] == ag[i];
+      if (!seen && found) ++shared;
+    }
+    out[g] = (double)shared / (double)r;
+  }
+  return ORC_OK;
+}
+
 /* For KV head g and stored K column c (query channel qc = keep[g][c], or c):
  *   kn_b = sum_{t < n_tok} K[b][g][t][c]^2                 (sample b's K column)
  *   qn_b = sum_{w < n_win} sum_{h in group g} q[b][w][h][qc]^2

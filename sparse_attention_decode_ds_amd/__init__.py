@@ -38,7 +38,8 @@ PATHS = ("dense", "fused", "local", "stream")
 EXPORTS = ("ds_label_build", "ds_label_append", "ds_decode_attn_workspace_size",
            "ds_decode_attn_plan", "ds_decode_attn", "ds_decode_attn_noalloc",
            "ds_calibrate_workspace_size",
-           "ds_calibrate_channels", "ds_sparse_decode_enabled", "ds_status_str",
+           "ds_calibrate_channels", "ds_channel_overlap", "ds_sparse_decode_enabled",
+           "ds_status_str",
            "ds_abi_version")
 
 
@@ -106,6 +107,8 @@ def load() -> ctypes.CDLL:
         lib.ds_decode_attn_noalloc.argtypes = [P, P, P, P, P, I32, P, P, P, I32, ctypes.c_float,
                                                P, P, P, P]
         lib.ds_decode_attn_noalloc.restype = ctypes.c_int
+        lib.ds_channel_overlap.argtypes = [P, P, I32, I32, P]
+        lib.ds_channel_overlap.restype = ctypes.c_int
         lib.ds_calibrate_workspace_size.argtypes = [P, I32, I32]
         lib.ds_calibrate_workspace_size.restype = ctypes.c_size_t
         lib.ds_calibrate_channels.argtypes = [P, P, I32, P, I32, P, I32, I32, P, P, P,
@@ -373,16 +376,19 @@ def calibrate_channels(K, r: int, criterion="qk", qwin=None, keep=None, n_tok: i
 
 
 def channel_overlap(chan_a, chan_b):
-    """Per KV head, the fraction of heavy channels two tables share: the check
-    of offline-calibrated channels against those found online at decode time
-    ("Double Sparsity", section "offline calibration").  Host computation on
-    [H_kv][r] tables (copies them to the host); returns a list of floats."""
-    a = chan_a.detach().to("cpu", torch.int64) if hasattr(chan_a, "detach") else torch.as_tensor(chan_a)
-    b = chan_b.detach().to("cpu", torch.int64) if hasattr(chan_b, "detach") else torch.as_tensor(chan_b)
+    """Per KV head, the share of heavy channels two tables have in common
+    (ds_channel_overlap; "Double Sparsity", section "offline calibration":
+    offline-calibrated channels against those found online).  [H_kv][r]
+    tables (copied to the host); returns a list of floats."""
+    a = chan_a.detach().to("cpu", torch.int32) if hasattr(chan_a, "detach") else torch.as_tensor(chan_a, dtype=torch.int32)
+    b = chan_b.detach().to("cpu", torch.int32) if hasattr(chan_b, "detach") else torch.as_tensor(chan_b, dtype=torch.int32)
     if a.dim() != 2 or a.shape != b.shape or a.shape[1] == 0:
         raise ValueError("channel_overlap: two [n_kv_heads][r] tables of one shape expected")
-    r = a.shape[1]
-    return [len(set(a[g].tolist()) & set(b[g].tolist())) / r for g in range(a.shape[0])]
+    a, b = a.contiguous(), b.contiguous()
+    out = torch.zeros(a.shape[0], dtype=torch.float32)
+    _check("ds_channel_overlap", load().ds_channel_overlap(
+        _p(a), _p(b), int(a.shape[0]), int(a.shape[1]), _p(out)))
+    return out.tolist()
 
 
 def workspace_size(K, V, n_q_heads, d_q, labels: LabelCache | None, k, max_seq_len,

@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <cmath>
 #include <mutex>
+#include <vector>
 
 #include "ds_internal.h"
 
@@ -622,6 +623,36 @@ ds_status ds_decode_attn_noalloc(const ds_kv_desc* kv, const void* q, const void
 int32_t ds_sparse_decode_enabled(int32_t max_seq_len, int32_t min_seq_len, int32_t k,
                                  int32_t threshold) {
   return (k > 0 && max_seq_len >= threshold && min_seq_len >= k) ? 1 : 0;
+}
+
+ds_status ds_channel_overlap(const int32_t* chan_a, const int32_t* chan_b, int32_t n_kv_heads,
+                             int32_t r, float* overlap) {
+  if (!chan_a || !chan_b || !overlap || n_kv_heads < 1 || r < 1) return DS_ERR_ARG;
+  std::vector<int32_t> x, y;
+  for (int32_t g = 0; g < n_kv_heads; ++g) {
+    // both rows sorted without repeats, then one merge pass counts the
+    // channels they share
+    x.assign(chan_a + (int64_t)g * r, chan_a + (int64_t)(g + 1) * r);
+    y.assign(chan_b + (int64_t)g * r, chan_b + (int64_t)(g + 1) * r);
+    std::sort(x.begin(), x.end());
+    std::sort(y.begin(), y.end());
+    x.erase(std::unique(x.begin(), x.end()), x.end());
+    y.erase(std::unique(y.begin(), y.end()), y.end());
+    size_t i = 0, j = 0, shared = 0;
+    while (i < x.size() && j < y.size()) {
+      if (x[i] < y[j]) {
+        ++i;
+      } else if (y[j] < x[i]) {
+        ++j;
+      } else {
+        ++shared;
+        ++i;
+        ++j;
+      }
+    }
+    overlap[g] = (float)shared / (float)r;
+  }
+  return DS_OK;
 }
 
 size_t ds_calibrate_workspace_size(const ds_kv_desc* kv, int32_t n_tok, int32_t n_win) {

@@ -345,6 +345,31 @@ def test_channel_overlap_host_logic():
         ds.channel_overlap(a, b[:, :2])
 
 
+def test_channel_overlap_matches_the_oracle(lib):
+    """ds_channel_overlap against the oracle on seeded tables: distinct
+    sorted channels as calibration writes them, and rows with repeats."""
+    import numpy as np
+
+    import oracle
+    rng = np.random.default_rng(5)
+    for H, r, d in [(1, 1, 4), (4, 8, 16), (32, 16, 128), (7, 32, 40)]:
+        a = np.sort(np.stack([rng.choice(d, r, replace=False) for _ in range(H)]), axis=1)
+        b = np.sort(np.stack([rng.choice(d, r, replace=False) for _ in range(H)]), axis=1)
+        c = rng.integers(0, d, size=(H, r))  # repeats allowed
+        for x, y in [(a, b), (a, a), (a, c), (c, b)]:
+            got = ds.channel_overlap(torch.from_numpy(x.astype(np.int32)),
+                                     torch.from_numpy(y.astype(np.int32)))
+            ref = oracle.channel_overlap(x, y)
+            assert np.array_equal(np.float32(got), np.float32(ref)), (H, r, got, ref)
+    out = (ctypes.c_float * 2)()
+    ok = (ctypes.c_int32 * 4)(1, 2, 3, 4)
+    assert lib.ds_channel_overlap(None, ok, 2, 2, out) == -1
+    assert lib.ds_channel_overlap(ok, ok, 0, 2, out) == -1
+    assert lib.ds_channel_overlap(ok, ok, 2, 0, out) == -1
+    assert lib.ds_channel_overlap(ok, ok, 2, 2, None) == -1
+    assert lib.ds_channel_overlap(ok, ok, 2, 2, out) == 0 and list(out) == [1.0, 1.0]
+
+
 def test_sparse_decode_threshold_policy(lib):
     """[DS] "use in SGLang": Double Sparsity decodes a batch only when its
     longest sequence reaches the threshold and its shortest reaches k."""

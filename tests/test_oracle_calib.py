@@ -117,3 +117,18 @@ def test_bad_arguments_and_non_finite_inputs_are_rejected():
     K[0, 0, 1, 2] = np.inf
     with pytest.raises(ValueError):
         oracle.calibrate(K, oracle.CALIB_K, 2)
+
+
+def test_channel_overlap_hand_worked():
+    """The overlap of two channel tables ("Double Sparsity", section "offline
+    calibration", offline against online outlier channels), worked by hand:
+    head 0 shares {3, 4} of 4 channels, head 1 all 4 (another order), head 2
+    none; a table with a repeated channel counts it once ({1, 2, 3} against
+    {1, 2, 9}: 2 of r = 4)."""
+    a = [[1, 2, 3, 4], [5, 6, 7, 8], [0, 10, 20, 30]]
+    b = [[4, 3, 9, 10], [8, 7, 6, 5], [1, 11, 21, 31]]
+    np.testing.assert_array_equal(oracle.channel_overlap(a, b), [0.5, 1.0, 0.0])
+    np.testing.assert_array_equal(oracle.channel_overlap([[1, 1, 2, 3]], [[1, 2, 2, 9]]), [0.5])
+    np.testing.assert_array_equal(oracle.channel_overlap(b, a), [0.5, 1.0, 0.0])
+    with pytest.raises(ValueError):
+        oracle.channel_overlap(a, [[1, 2, 3, 4]])
