@@ -695,8 +695,12 @@ def measure_in_child(workload, args):
     through; returns its JSON result, or None if it failed."""
     import subprocess
     cmd = [sys.executable, "-u", os.path.abspath(__file__), "--workload", workload,
-           "--also", "none", "--no-cpu-baseline", "--steps", str(args.steps),
+           "--also", "none", "--steps", str(args.steps),
            "--warmup", str(args.warmup), "--stage-events", args.stage_events]
+    # the oracle on a bounded sample of this workload too (shorter than the
+    # headline's), or not at all when the headline has none
+    cmd += (["--no-cpu-baseline"] if args.no_cpu_baseline else
+            ["--cpu-seconds", str(min(args.cpu_seconds, 5.0))])
     if args.unfused:
         cmd.append("--unfused")
     if args.page_size:
@@ -807,7 +811,8 @@ def main():
             return 1
         others[w] = {"queries_per_s": r2["value"], "ms_per_step": r2["ms_per_step"],
                      "config": r2["config"], "step": r2["step"], "roofline": r2["roofline"],
-                     "prefill": r2.get("prefill"), "process": "own"}
+                     "prefill": r2.get("prefill"), "cpu_baseline": r2.get("cpu_baseline"),
+                     "process": "own"}
     copy_gbs = copy_ceiling_gbs(torch)
     rf = res["roofline"]
     rf["copy_gbs"] = round(copy_gbs, 1)
