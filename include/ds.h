@@ -328,7 +328,8 @@ int32_t ds_sparse_decode_enabled(int32_t max_seq_len, int32_t min_seq_len, int32
  * int32 [n_kv_heads][r], read only; overlap: host float [n_kv_heads],
  * written: for head g, the number of distinct channels of chan_a[g] that
  * chan_b[g] also holds, divided by r.  Host-only: no device memory, nothing
- * enqueued.  Errors: DS_ERR_ARG (a pointer NULL, n_kv_heads or r below 1). */
+ * enqueued, nothing allocated.  Errors: DS_ERR_ARG (a pointer NULL, n_kv_heads
+ * or r below 1, a channel id outside [0, 4096)). */
 ds_status ds_channel_overlap(const int32_t* chan_a, const int32_t* chan_b, int32_t n_kv_heads,
                              int32_t r, float* overlap);
 

@@ -12,7 +12,6 @@
 #include <algorithm>
 #include <cmath>
 #include <mutex>
-#include <vector>
 
 #include "ds_internal.h"
 
@@ -628,26 +627,22 @@ int32_t ds_sparse_decode_enabled(int32_t max_seq_len, int32_t min_seq_len, int32
 ds_status ds_channel_overlap(const int32_t* chan_a, const int32_t* chan_b, int32_t n_kv_heads,
                              int32_t r, float* overlap) {
   if (!chan_a || !chan_b || !overlap || n_kv_heads < 1 || r < 1) return DS_ERR_ARG;
-  std::vector<int32_t> x, y;
+  constexpr int kIds = 4096;  // channel ids are K columns: far below this
+  for (int64_t i = 0; i < (int64_t)n_kv_heads * r; ++i)
+    if (chan_a[i] < 0 || chan_a[i] >= kIds || chan_b[i] < 0 || chan_b[i] >= kIds) return DS_ERR_ARG;
   for (int32_t g = 0; g < n_kv_heads; ++g) {
-    // both rows sorted without repeats, then one merge pass counts the
-    // channels they share
-    x.assign(chan_a + (int64_t)g * r, chan_a + (int64_t)(g + 1) * r);
-    y.assign(chan_b + (int64_t)g * r, chan_b + (int64_t)(g + 1) * r);
-    std::sort(x.begin(), x.end());
-    std::sort(y.begin(), y.end());
-    x.erase(std::unique(x.begin(), x.end()), x.end());
-    y.erase(std::unique(y.begin(), y.end()), y.end());
-    size_t i = 0, j = 0, shared = 0;
-    while (i < x.size() && j < y.size()) {
-      if (x[i] < y[j]) {
-        ++i;
-      } else if (y[j] < x[i]) {
-        ++j;
-      } else {
+    // b's channels as a bitmap; each of a's channels counts once, when its
+    // bit is still set, and clears it
+    uint64_t bits[kIds / 64] = {};
+    const int32_t* a = chan_a + (int64_t)g * r;
+    const int32_t* b = chan_b + (int64_t)g * r;
+    for (int32_t j = 0; j < r; ++j) bits[b[j] >> 6] |= 1ull << (b[j] & 63);
+    int32_t shared = 0;
+    for (int32_t j = 0; j < r; ++j) {
+      const uint64_t m = 1ull << (a[j] & 63);
+      if (bits[a[j] >> 6] & m) {
         ++shared;
-        ++i;
-        ++j;
+        bits[a[j] >> 6] &= ~m;
       }
     }
     overlap[g] = (float)shared / (float)r;

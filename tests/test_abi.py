@@ -368,6 +368,10 @@ def test_channel_overlap_matches_the_oracle(lib):
     assert lib.ds_channel_overlap(ok, ok, 2, 0, out) == -1
     assert lib.ds_channel_overlap(ok, ok, 2, 2, None) == -1
     assert lib.ds_channel_overlap(ok, ok, 2, 2, out) == 0 and list(out) == [1.0, 1.0]
+    bad = (ctypes.c_int32 * 4)(1, 2, 3, 4096)
+    assert lib.ds_channel_overlap(ok, bad, 2, 2, out) == -1
+    neg = (ctypes.c_int32 * 4)(1, -2, 3, 4)
+    assert lib.ds_channel_overlap(neg, ok, 2, 2, out) == -1
 
 
 def test_sparse_decode_threshold_policy(lib):
