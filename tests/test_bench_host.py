@@ -123,3 +123,39 @@ def test_kernel_stats_record(tmp_path):
     assert rec["workload"] == "long_128k" and rec["source_hash"] == bench.source_hash()
     assert rec["kernels"] == {"k_attn": {"calls": 40, "avg_us": 12.5},
                               "k_combine": {"calls": 40, "avg_us": 4.0}}
+
+
+def test_further_workload_measured_in_a_child_process(monkeypatch, capsys):
+    """A further workload runs in a child process of its own: the command
+    names it (with a bounded oracle sample, or none when the headline has
+    none), the child's progress lines pass through, its JSON line is returned,
+    and a failing child yields None."""
+    import io
+    import types
+
+    calls = []
+
+    class Child:
+        def __init__(self, cmd, stdout=None, text=None):
+            calls.append(cmd)
+            self.rc = 0 if "long_128k" in cmd else 3
+            self.stdout = io.StringIO('bench: progress\n{"value": 1.5, "ms_per_step": 0.1}\n')
+            self.returncode = None
+
+        def wait(self):
+            self.returncode = self.rc
+            return self.rc
+
+    monkeypatch.setattr(subprocess, "Popen", Child)
+    args = types.SimpleNamespace(steps=16, warmup=4, stage_events="kernel", unfused=False,
+                                 page_size=0, no_cpu_baseline=False, cpu_seconds=10.0)
+    r = bench.measure_in_child("long_128k", args)
+    assert r == {"value": 1.5, "ms_per_step": 0.1}
+    cmd = calls[-1]
+    assert cmd[cmd.index("--workload") + 1] == "long_128k" and "--also" in cmd
+    assert cmd[cmd.index("--cpu-seconds") + 1] == "5.0" and "--no-cpu-baseline" not in cmd
+    assert "bench: progress" in capsys.readouterr().out
+    args.no_cpu_baseline = True
+    bench.measure_in_child("long_128k", args)
+    assert "--no-cpu-baseline" in calls[-1] and "--cpu-seconds" not in calls[-1]
+    assert bench.measure_in_child("leank_ds", args) is None
