@@ -78,16 +78,46 @@ __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a_in) {
   } else if (a.sparse || kStaged) {
     for (int i = tid; i < min(n_here, kMaxTokensPerSplit); i += kGT) f.lidx[i] = stage(t0 + i);
   }
-  for (int i = tid; i < G * kDv; i += kGT) {
-    const int h = i / kDv, c = i - h * kDv;
-    __half v = __float2half(0.0f);
-    if (c < a.d_k) {
-      const __half* qh = a.q + ((int64_t)b * a.Hq + (int64_t)g * G + h) * a.d_q;
-      v = qh[a.keep ? a.keep[(int64_t)g * a.keep_ld + c] : c];
+  // The query rows at the stored K columns' channels into registers: thread
+  // tid holds channel c = tid mod 128 of heads tid / 128, + 2, + 4, + 6.
+  constexpr int kQPer = kMaxGroup * kDv / kGT;
+  static_assert(kGT % kDv == 0, "one channel per thread");
+  const int qc = tid & (kDv - 1);
+  __half qv[kQPer];
+  {
+    const int kc = qc < a.d_k ? (a.keep ? a.keep[(int64_t)g * a.keep_ld + qc] : qc) : 0;
+    const __half* qh = a.q + ((int64_t)b * a.Hq + (int64_t)g * G) * a.d_q + kc;
+#pragma unroll
+    for (int m = 0; m < kQPer; ++m) {
+      const int h = tid / kDv + m * (kGT / kDv);
+      qv[m] = (h < G && qc < a.d_k) ? qh[(int64_t)h * a.d_q] : __float2half(0.0f);
     }
-    f.q[h][c] = v;
   }
-  __syncthreads();
+  auto stage_query = [&]() {
+#pragma unroll
+    for (int m = 0; m < kQPer; ++m) {
+      const int h = tid / kDv + m * (kGT / kDv);
+      if (h < G) f.q[h][qc] = qv[m];
+    }
+  };
+  constexpr int D = 4 * kGqaTile;  // the wave's tiles are D positions apart
+  const int i_first = w * kGqaTile;
+  const int nb0 = min(kMaxTokensPerSplit, n_here);
+  GqaTile nxt;
+  if (RING) {
+    stage_query();
+    __syncthreads();
+  } else {
+    // The first tile's loads go out before the query (behind the keep
+    // table, a second round trip) is staged.
+    __syncthreads();
+    auto tok0 = [&](int i) -> int64_t {
+      return (a.sparse || kStaged) ? (int64_t)f.lidx[i] : (int64_t)(t0 + i);
+    };
+    if (i_first < nb0) gqa_load<PAGED>(a, ln, i_first, nb0, tok0, nxt);
+    stage_query();
+    __syncthreads();
+  }
   half4_t qb[8];
   gqa_query(&f.q[0][0], G, ln, qb);
 
@@ -103,13 +133,12 @@ __global__ __launch_bounds__(kGT) void k_attn_gqa(AttnArgs a_in) {
     auto tok = [&](int i) -> int64_t {
       return (a.sparse || kStaged) ? (int64_t)f.lidx[i] : (int64_t)(t0 + bat + i);
     };
-    constexpr int D = 4 * kGqaTile;  // the wave's tiles are D positions apart
-    const int i_first = w * kGqaTile;
     if (i_first >= nb) continue;
     if (!RING) {
-      // The next tile's loads in flight while one is consumed.
-      GqaTile cur, nxt;
-      gqa_load<PAGED>(a, ln, i_first, nb, tok, nxt);
+      // The next tile's loads in flight while one is consumed (the first
+      // batch's first tile was issued in the prologue).
+      GqaTile cur;
+      if (bat > 0) gqa_load<PAGED>(a, ln, i_first, nb, tok, nxt);
       for (int i0 = i_first; i0 < nb; i0 += D) {
         cur = nxt;
         if (i0 + D < nb) gqa_load<PAGED>(a, ln, i0 + D, nb, tok, nxt);
