@@ -126,6 +126,7 @@ struct Plan {
   int local_chunk;  // local top-M select: tokens per chunk workgroup
   int local_nch;    // and chunks per row
   int cand_stride;  // candidate slots per row
+  bool local_half;  // the local quota of every row is at least 512
   int split_cap;
   size_t off_count, off_idx, off_keys, off_cand_key, off_cand_idx, off_cand_cnt, off_cand_theta,
       off_cand_range;
@@ -174,6 +175,18 @@ Plan make_plan(const ds_kv_desc* kv, int k, int max_seq) {
   }
   p.local_nch = (int)std::max<int64_t>(1, ceil_div(max_seq, p.local_chunk));
   p.cand_stride = p.sparse ? (int)std::min<int64_t>(kMergeCap, round_up(std::max(max_seq, 1), 64)) : 0;
+  {
+    // The local score kernel's quota for a row of max_seq tokens (the
+    // smallest of any row: shorter rows expect more of k per chunk and own
+    // more slots); at least 520 lets the large-chunk kernel take its
+    // threshold from a sample of half the chunk (the kernel checks 512).
+    const int64_t S = std::max(max_seq, 1);
+    const int64_t CH = p.local_chunk, nch = p.local_nch;
+    const double expected = (double)std::max(k, 0) * (double)CH / (double)S;
+    int64_t m0 = std::min<int64_t>(CH, std::max<int64_t>(64, (int64_t)(2.0 * expected) + 1));
+    const int64_t cap = std::min<int64_t>(p.cand_stride / nch, m0 + m0 / 8 + 64);
+    p.local_half = p.sparse && std::min<int64_t>(m0, cap - cap / 8) >= 520;
+  }
   p.split_cap = (int)std::min<int64_t>(kMaxSplit, std::max<int64_t>(1, ceil_div(p.kk, 16)));
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -509,6 +522,7 @@ ds_status decode_impl(const ds_kv_desc* kv, const void* q, const void* K, const 
     sa.cand_theta = reinterpret_cast<uint32_t*>(ws + p.off_cand_theta);
     sa.cand_range = reinterpret_cast<float2*>(ws + p.off_cand_range);
     sa.cand_stride = p.cand_stride;
+    sa.half_quota = p.local_half ? 1 : 0;
     idx = sa.idx;
     idx_stride = sa.idx_stride;
     // One kernel for the whole step when the row's scores fit in one

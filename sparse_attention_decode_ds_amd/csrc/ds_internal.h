@@ -91,6 +91,7 @@ struct ScoreArgs {
   uint32_t* cand_theta; // [rows][n_chunks], key of the chunk's threshold (0: kept whole)
   float2* cand_range;   // [rows][n_chunks], (lowest kept score bound, largest score)
   int32_t cand_stride;  // candidate slots per row (<= kMergeCap)
+  int32_t half_quota;   // every chunk's quota is at least 512 (sampled threshold)
   const ds_head_layout* heads;  // per-head K layout (fully pruned heads), or null
   int32_t keep_ld;              // row stride of the keep table (the widest d_k)
 };

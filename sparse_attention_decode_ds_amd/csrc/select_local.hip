@@ -63,7 +63,9 @@ struct LocalScratch {
 
 // NT threads score a chunk of at most NT * TPT tokens.  Empty slots (past
 // the chunk, and the appended token until its score is known) hold -inf.
-template <int NT, int TPT, int R, bool INT4>
+// HALF: the chunk threshold from the histogram of every other item (large
+// quotas only, chosen on the host).
+template <int NT, int TPT, int R, bool INT4, bool HALF = false>
 __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_in, int append) {
   constexpr int kWavesL = NT / 64;
   using Vec = typename VecSel<R, INT4>::type;
@@ -219,18 +221,32 @@ __global__ __launch_bounds__(NT) void k_score_local(ScoreArgs sa, LabelArgs la_i
     SelScratch& ss = f.sel;
     for (int i = tid; i < kHistBins; i += NT) ss.hist[i] = 0u;
     __syncthreads();
+    // With HALF (quotas of at least 512), the histogram holds every other
+    // item (even item index: every other token, or every other block of NT
+    // tokens with one token per vector) and the search is for its
+    // ceil(Ms / 2)-th largest, Ms = M less five standard deviations of the
+    // sample's count: the chunk's items at or above that bin then number
+    // about Ms, below M with the sample's noise and the boundary bin's items
+    // on top.  A smaller quota reports an overflow (the merge's full select).
+    if (HALF && M < 512) {
+      if (tid == 0) sa.cand_cnt[(int64_t)row * sa.n_chunks + c] = -1;
+      return;
+    }
+    const int need = HALF ? (M - (int)(5.0f * __builtin_sqrtf((float)M)) + 1) / 2 : M;
 #pragma unroll
     for (int j = 0; j < JMAX; ++j)
       if (j < jn) {
 #pragma unroll
-        for (int e = 0; e < VT; ++e)  // empty slots count in bin 0, which the
-          atomicAdd(&ss.hist[bin(sc[j * VT + e])], 1u);  // search for the M-th never reaches
+        for (int e = 0; e < VT; ++e)
+          if (!HALF || ((j * VT + e) & 1) == 0)  // empty slots count in bin 0,
+            atomicAdd(&ss.hist[bin(sc[j * VT + e])], 1u);  // which the search never reaches
       }
     __syncthreads();
-    // the bin of the M-th largest: every valid key lies in bins 1 .. 2047
-    find_digit<NT>(ss.hist, (uint32_t)M, ss.misc + 4, f.scan_tmp);
+    // the bin of the need-th largest: every valid key lies in bins 1 .. 2047,
+    // and a sample of every other item holds at least half the chunk (n_c > M)
+    find_digit<NT>(ss.hist, (uint32_t)need, ss.misc + 4, f.scan_tmp);
     const uint32_t bM = ss.misc[4];
-    if (ss.misc[5] + ss.misc[6] > (uint32_t)cap) {  // the boundary bin overflows the slots
+    if (!HALF && ss.misc[5] + ss.misc[6] > (uint32_t)cap) {  // the boundary bin overflows the slots
       if (tid == 0) sa.cand_cnt[(int64_t)row * sa.n_chunks + c] = -1;
       return;
     }
@@ -503,6 +519,8 @@ template <int R, bool INT4>
 hipError_t launch_local_rt(const ScoreArgs& sa, const LabelArgs& la, int append, int rows,
                            hipStream_t s, const KEvents& ev) {
   const dim3 grid(rows * sa.n_chunks);
+  if (sa.chunk > 512 * 16 && sa.half_quota)
+    return launch_k(k_score_local<512, 20, R, INT4, true>, grid, dim3(512), s, ev, sa, la, append);
   if (sa.chunk > 512 * 16)
     return launch_k(k_score_local<512, 20, R, INT4>, grid, dim3(512), s, ev, sa, la, append);
   if (sa.chunk > 256 * 16)

@@ -396,25 +396,28 @@ def test_local_select_fallbacks(mode):
         assert (topk < 150).all()
 
 
-@pytest.mark.parametrize("mode", [0, 1])
-def test_local_select_fallbacks_wide_chunks(mode):
+@pytest.mark.parametrize("mode,k", [(0, 400), (1, 400), (0, 2048), (1, 2048), (2, 2048)])
+def test_local_select_fallbacks_wide_chunks(mode, k):
     """The same two fallbacks with chunks of over 8192 tokens (512-thread
     score workgroups, 20 scores per thread): 256 rows of 32769 tokens in four
-    chunks, k = 400, a quota of about 200 per chunk.  mode 0: the top 450
+    chunks.  k = 400 gives a quota of about 200 per chunk (threshold from the
+    chunk's full histogram); k = 2048 a quota of about 1030, whose threshold
+    comes from the histogram of every other item.  mode 0: the top k + 50
     tokens all sit in chunk 0; mode 1: chunk 1 holds over 8000 equal scores,
-    more than its candidate slots."""
-    cfg, inp = _small_inputs("mha_int4_r8", B=2, Hq=128, Hkv=128, S0=32768, k=400)
-    _note("local fallbacks, wide chunks, mode %d" % mode)
+    more than its candidate slots; mode 2: no fallback."""
+    cfg, inp = _small_inputs("mha_int4_r8", B=2, Hq=128, Hkv=128, S0=32768, k=k)
+    _note("local fallbacks, wide chunks, mode %d, k %d" % (mode, k))
     S = cfg.S0 + 1
     q = inp.q.float()
+    top = k + 50
     for b in range(cfg.B):
         for g in range(cfg.Hkv):
             ch = inp.chan[g].long()
             if mode == 0:
                 sgn = torch.sign(q[b, g, ch]).to(torch.float16)
                 sgn[sgn == 0] = 1
-                inp.K[b, g, :450][:, ch] = 60 * sgn
-            else:
+                inp.K[b, g, :top][:, ch] = 60 * sgn
+            elif mode == 1:
                 inp.K[b, g, 8192:16384][:, ch] = 0
     seq = torch.full((cfg.B,), S, dtype=torch.int32, device="cuda")
     labels = prefill(cfg, inp, S)
@@ -424,7 +427,7 @@ def test_local_select_fallbacks_wide_chunks(mode):
     ds_check.check_rows(cfg, inp.q, inp.K, inp.V, inp.chan, inp.keep, labels, seq, cfg.k, out,
                         topk, ds_check.sample_rows(cfg, 24, seed=3))
     if mode == 0:
-        assert (topk < 450).all()
+        assert (topk < top).all()
     del inp, labels, out, topk
     gc.collect()
     torch.cuda.empty_cache()
